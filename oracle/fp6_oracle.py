@@ -1,0 +1,343 @@
+"""Plain CPU oracle of the weight-only FP6 (W6A16) linear layer.
+
+TEST INFRASTRUCTURE: imported only by tests, the smoke check and the
+benchmark's CPU-baseline leg.  Shares nothing with the HIP library.
+
+What is computed, and where it comes from
+-----------------------------------------
+* FP6-LLM (arXiv 2401.14112), abstract: six-bit floating-point weights with
+  16-bit activations; the two costs are irregular-width weight access and
+  weight de-quantisation.
+* TC-FPx explainer (duicuo.cn/w/184.html), section "redesigning the kernel
+  solution": FP6 weights are de-quantised to FP16 ("disguised" as FP16) and the
+  matrix product is then done in FP16; weights are re-ordered and packed
+  offline into power-of-two-aligned pieces (6 = 2 + 4 bits).
+
+The pages do not give the FP6 bit format, the scale granularity, rounding or a
+packed layout.  The readings used here (each one stated where it is used):
+
+* FP6 = e3m2: 1 sign, 3 exponent, 2 mantissa bits, exponent bias 3,
+  subnormals, no inf/NaN, largest magnitude 28 (the OCP MX FP6 E3M2 element
+  format).  Code bits (MSB..LSB): s e2 e1 e0 m1 m0.
+* One fp16 scale per output row n: s_n = fp16_RNE(max_k |W[n,k]| / 28).
+* Quantisation rounds |W/s_n| to the nearest e3m2 magnitude, ties to the even
+  code, saturating at 28; the sign bit is copied from W (so -0 is kept).
+* Dequantised weight Wdq[n,k] = fp16_RNE(v(c[n,k]) * s_n): the product is
+  formed exactly in float64 and rounded once (IEEE round-to-nearest-even,
+  gradual underflow, signed zero kept).
+* Y_ref = X . Wdq^T accumulated in float64 (nn.Linear convention: X is
+  [M,K], W is [N,K], Y is [M,N]).
+* Packed layout v1 (the library's private offline format; any bijection is
+  correct, this oracle checks the round trip): see :func:`unpack_scalar`.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# O1: explicit e3m2 decode table (64 entries, index = 6-bit code).
+# Codes 0..31 are the non-negative values (e = code>>2, m = code&3):
+#   e = 0 (subnormal): m * 2^-4          -> 0, 0.0625, 0.125, 0.1875
+#   e >= 1 (normal):   2^(e-3) * (1+m/4)
+# Codes 32..63 are the same magnitudes with the sign bit set.
+# ---------------------------------------------------------------------------
+E3M2_VALUES = (
+    0.0, 0.0625, 0.125, 0.1875,      # e=0 (subnormal)
+    0.25, 0.3125, 0.375, 0.4375,     # e=1
+    0.5, 0.625, 0.75, 0.875,         # e=2
+    1.0, 1.25, 1.5, 1.75,            # e=3
+    2.0, 2.5, 3.0, 3.5,              # e=4
+    4.0, 5.0, 6.0, 7.0,              # e=5
+    8.0, 10.0, 12.0, 14.0,           # e=6
+    16.0, 20.0, 24.0, 28.0,          # e=7
+    -0.0, -0.0625, -0.125, -0.1875,
+    -0.25, -0.3125, -0.375, -0.4375,
+    -0.5, -0.625, -0.75, -0.875,
+    -1.0, -1.25, -1.5, -1.75,
+    -2.0, -2.5, -3.0, -3.5,
+    -4.0, -5.0, -6.0, -7.0,
+    -8.0, -10.0, -12.0, -14.0,
+    -16.0, -20.0, -24.0, -28.0,
+)
+_TABLE = np.array(E3M2_VALUES, dtype=np.float64)
+_MAGS = _TABLE[:32]                      # ascending, exact dyadics
+_MIDS = (_MAGS[:-1] + _MAGS[1:]) / 2.0   # exact in float64 (short dyadics)
+E3M2_MAX = 28.0
+
+
+def decode(codes) -> np.ndarray:
+    """v(c) for an array of 6-bit codes, as float64 (table lookup)."""
+    c = np.asarray(codes)
+    if c.size and (c.min() < 0 or c.max() > 63):
+        raise ValueError("e3m2 codes must lie in 0..63")
+    return _TABLE[c.astype(np.int64)]
+
+
+def encode_rne(x) -> np.ndarray:
+    """Nearest e3m2 code for float64 values, ties to the even code.
+
+    The magnitude |x| is mapped to the closest of the 32 magnitudes; an exact
+    midpoint goes to the even code (m0 = 0); |x| >= 28 saturates to code 31.
+    The sign bit is the IEEE sign bit of x, so -0.0 and small negatives that
+    round to zero give code 0x20.  NaN is rejected.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any():
+        raise ValueError("NaN cannot be encoded in e3m2 (no NaN codes)")
+    a = np.abs(x)
+    # hi = number of midpoints strictly below a  -> candidate index above
+    below = np.searchsorted(_MIDS, a, side="left")   # mids[below-1] < a <= mids[below]
+    idx = below.copy()
+    # exact midpoint: a == mids[below]; choose the even one of (below, below+1)
+    at_mid = np.zeros(a.shape, dtype=bool)
+    inb = below < _MIDS.size
+    at_mid[inb] = a[inb] == _MIDS[below[inb]]
+    tie_idx = np.where(below % 2 == 0, below, below + 1)
+    idx = np.where(at_mid, tie_idx, idx)
+    idx = np.minimum(idx, 31)                         # saturate (also +inf)
+    sign = np.signbit(x).astype(np.int64)
+    return ((sign << 5) | idx).astype(np.uint8)
+
+
+def fp16_rne(x) -> np.ndarray:
+    """Round float64 values once to IEEE binary16 (RNE, subnormals kept)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# O2: per-row quantiser (input preparation, not part of the timed path).
+# ---------------------------------------------------------------------------
+def quantize_rows(W) -> tuple[np.ndarray, np.ndarray]:
+    """W fp32 [N,K] -> (codes uint8 [N,K], scales fp16 [N]).
+
+    s_n = fp16_RNE(float64(max_k |W[n,k]|) / 28); x = float64(W)/float64(s_n);
+    codes = encode_rne(x).  A row whose scale is 0 gets all-zero codes.
+    Rows whose scale is not finite or has |s| >= 16 are rejected: outside that
+    range s * 2^12 is not an exact fp16, which the fused kernel relies on.
+    """
+    W = np.asarray(W)
+    if W.dtype != np.float32 or W.ndim != 2:
+        raise ValueError("W must be a 2-D float32 array")
+    if not np.isfinite(W).all():
+        raise ValueError("W must be finite")
+    amax = np.abs(W).max(axis=1).astype(np.float64) if W.shape[1] else np.zeros(W.shape[0])
+    scales = fp16_rne(amax / 28.0)
+    s64 = scales.astype(np.float64)
+    if not np.isfinite(s64).all() or (np.abs(s64) >= 16.0).any():
+        raise ValueError("row scale out of the exact range |s| < 16")
+    codes = np.zeros(W.shape, dtype=np.uint8)
+    nz = s64 != 0.0
+    if nz.any():
+        q = W[nz].astype(np.float64) / s64[nz][:, None]
+        codes[nz] = encode_rne(q)
+    return codes, scales
+
+
+def quantize_rows_sampled(W_rows) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise a subset of rows (rows are independent); same as quantize_rows."""
+    return quantize_rows(W_rows)
+
+
+# ---------------------------------------------------------------------------
+# O3: packed layout v1.
+#
+# Codes c[n][k] with N % 16 == 0 and K % 256 == 0.  The buffer holds
+# N*K*3/4 bytes in tiles of 16 rows x 256 k (3072 bytes each).  Tile
+# (nb, kb) starts at byte (nb*(K/256) + kb) * 3072 (row-block major, k-block
+# minor).  Inside a tile, local row r in 0..15 and local k = 32*j + 8*g + i
+# (j: k-step 0..7, g: lane group 0..3, i: element 0..7) belong to lane
+# L = 16*g + r.  Each code splits into a 2-bit piece (bits s,e2 = c>>4) and a
+# 4-bit piece (bits e1,e0,m1,m0 = c&15).
+#   * 2-bit plane: bytes [0,1024) of the tile.  Lane L owns the 16 bytes at
+#     16*L, as 4 little-endian 32-bit words; word j//2 holds k-steps j and
+#     j+1.  With pair p = 4*(j%2) + i//2 and half h = i%2, bit e2 sits at
+#     position (12 + 16*h + 2*p) mod 32 and bit s at (15 + 16*h + 2*p) mod 32.
+#   * 4-bit plane: bytes [1024,3072).  k-steps 0..3 in [1024,2048), 4..7 in
+#     [2048,3072); lane L owns 16 bytes at 16*L in each half, word j%4 is
+#     k-step j.  Element i occupies nibble slot (i//2) + 4*(i%2), i.e. bits
+#     4*slot .. 4*slot+3 (slots hold elements 0,2,4,6,1,3,5,7).
+# ---------------------------------------------------------------------------
+TILE_N = 16
+TILE_K = 256
+TILE_BYTES = 3072
+
+
+def _check_shape(N: int, K: int) -> None:
+    if N <= 0 or K <= 0 or N % TILE_N or K % TILE_K:
+        raise ValueError("layout v1 needs N % 16 == 0 and K % 256 == 0, both > 0")
+
+
+def _locate(N: int, K: int, n: int, k: int):
+    """Byte offset of the 2-bit word, bit positions, and 4-bit word + shift for (n,k)."""
+    nb, r = divmod(n, TILE_N)
+    kb, kk = divmod(k, TILE_K)
+    j, rem = divmod(kk, 32)
+    g, i = divmod(rem, 8)
+    lane = 16 * g + r
+    base = (nb * (K // TILE_K) + kb) * TILE_BYTES
+    p = 4 * (j % 2) + i // 2
+    h = i % 2
+    w2 = base + 16 * lane + 4 * (j // 2)
+    bit_e2 = (12 + 16 * h + 2 * p) % 32
+    bit_s = (15 + 16 * h + 2 * p) % 32
+    w4 = base + 1024 + 1024 * (j // 4) + 16 * lane + 4 * (j % 4)
+    nib = 4 * ((i // 2) + 4 * (i % 2))
+    return w2, bit_e2, bit_s, w4, nib
+
+
+def _get_word(buf, off: int) -> int:
+    return buf[off] | (buf[off + 1] << 8) | (buf[off + 2] << 16) | (buf[off + 3] << 24)
+
+
+def _set_word(buf, off: int, val: int) -> None:
+    for b in range(4):
+        buf[off + b] = (val >> (8 * b)) & 0xFF
+
+
+def pack_scalar(codes) -> np.ndarray:
+    """Scalar packer of layout v1 (pure Python; small inputs only).
+
+    Used only to pin :func:`unpack_scalar` (bijection checks); the library has
+    its own packer.
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    N, K = c.shape
+    _check_shape(N, K)
+    if c.max(initial=0) > 63:
+        raise ValueError("codes must lie in 0..63")
+    buf = bytearray(N * K * 3 // 4)
+    for n in range(N):
+        for k in range(K):
+            code = int(c[n, k])
+            w2, b_e2, b_s, w4, nib = _locate(N, K, n, k)
+            v2 = _get_word(buf, w2)
+            v2 |= ((code >> 4) & 1) << b_e2
+            v2 |= ((code >> 5) & 1) << b_s
+            _set_word(buf, w2, v2)
+            v4 = _get_word(buf, w4)
+            v4 |= (code & 0xF) << nib
+            _set_word(buf, w4, v4)
+    return np.frombuffer(bytes(buf), dtype=np.uint8).copy()
+
+
+def unpack_scalar(packed, N: int, K: int) -> np.ndarray:
+    """Scalar unpacker of layout v1 (pure Python loop over every code)."""
+    _check_shape(N, K)
+    buf = bytes(np.asarray(packed, dtype=np.uint8).ravel())
+    if len(buf) != N * K * 3 // 4:
+        raise ValueError("packed buffer has the wrong size")
+    out = np.zeros((N, K), dtype=np.uint8)
+    for n in range(N):
+        for k in range(K):
+            w2, b_e2, b_s, w4, nib = _locate(N, K, n, k)
+            v2 = _get_word(buf, w2)
+            v4 = _get_word(buf, w4)
+            code = ((v2 >> b_s) & 1) << 5 | ((v2 >> b_e2) & 1) << 4 | ((v4 >> nib) & 0xF)
+            out[n, k] = code
+    return out
+
+
+def unpack_np(packed, N: int, K: int) -> np.ndarray:
+    """Vectorised unpacker of layout v1 (same definition, NumPy indexing)."""
+    _check_shape(N, K)
+    p = np.asarray(packed, dtype=np.uint8).ravel()
+    if p.size != N * K * 3 // 4:
+        raise ValueError("packed buffer has the wrong size")
+    nbk, kbk = N // TILE_N, K // TILE_K
+    tiles = p.reshape(nbk, kbk, TILE_BYTES)
+    # words: 2-bit plane [nbk,kbk,lane=64,word=4]; 4-bit [nbk,kbk,half=2,lane=64,word=4]
+    w2 = tiles[:, :, :1024].copy().view("<u4").reshape(nbk, kbk, 64, 4).astype(np.int64)
+    w4 = tiles[:, :, 1024:].copy().view("<u4").reshape(nbk, kbk, 2, 64, 4).astype(np.int64)
+    out = np.zeros((nbk, kbk, TILE_N, 8, 4, 8), dtype=np.int64)  # [nb,kb,r,j,g,i]
+    for j in range(8):
+        for i in range(8):
+            p_ = 4 * (j % 2) + i // 2
+            h = i % 2
+            b_e2 = (12 + 16 * h + 2 * p_) % 32
+            b_s = (15 + 16 * h + 2 * p_) % 32
+            nib = 4 * ((i // 2) + 4 * (i % 2))
+            for g in range(4):
+                lanes = slice(16 * g, 16 * g + 16)
+                v2 = w2[:, :, lanes, j // 2]
+                v4 = w4[:, :, j // 4, lanes, j % 4]
+                out[:, :, :, j, g, i] = (((v2 >> b_s) & 1) << 5) | (((v2 >> b_e2) & 1) << 4) | ((v4 >> nib) & 0xF)
+    # [nb,kb,r,j,g,i] -> [nb,r,kb,j,g,i] -> [N,K]
+    return out.transpose(0, 2, 1, 3, 4, 5).reshape(N, K).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# O4: dequantisation.
+# ---------------------------------------------------------------------------
+def dequant_ref(codes, scales) -> np.ndarray:
+    """Wdq[n,k] = fp16_RNE(v(c[n,k]) * s_n), product exact in float64, one rounding."""
+    v = decode(codes)
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    if v.ndim != 2 or s.shape != (v.shape[0],):
+        raise ValueError("codes [N,K] and scales [N] expected")
+    return fp16_rne(v * s[:, None])
+
+
+# ---------------------------------------------------------------------------
+# O5: GEMM in float64.
+# ---------------------------------------------------------------------------
+def gemm_ref(X, Wdq) -> np.ndarray:
+    """Y_ref[m,n] = sum_k X[m,k] * Wdq[n,k], float64 accumulation (BLAS dgemm)."""
+    X64 = np.asarray(X, dtype=np.float16).astype(np.float64)
+    W64 = np.asarray(Wdq, dtype=np.float16).astype(np.float64)
+    return X64 @ W64.T
+
+
+def gemm_naive(X, Wdq) -> np.ndarray:
+    """Triple loop in plain Python floats (tiny shapes only)."""
+    X64 = np.asarray(X, dtype=np.float16).astype(np.float64)
+    W64 = np.asarray(Wdq, dtype=np.float16).astype(np.float64)
+    M, K = X64.shape
+    N = W64.shape[0]
+    Y = np.zeros((M, N), dtype=np.float64)
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(X64[m, k]) * float(W64[n, k])
+            Y[m, n] = acc
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# Acceptance: fp16 output with fp32 accumulation is correct when every element
+# satisfies |Y - Y_ref| <= 2e-3 (|Y_ref| + rms(Y_ref)) and the relative
+# Frobenius error is <= 5e-4.
+# ---------------------------------------------------------------------------
+TOL_ELEM = 2e-3
+TOL_FROB = 5e-4
+
+
+def tolerance_report(Y, Y_ref, rms=None) -> dict:
+    """Compare a device result with Y_ref.  ``rms`` may be given when Y_ref is a
+    sample of a larger output (then it is the rms of the whole output)."""
+    Y64 = np.asarray(Y, dtype=np.float64)
+    R = np.asarray(Y_ref, dtype=np.float64)
+    if Y64.shape != R.shape:
+        raise ValueError("shape mismatch")
+    if R.size == 0:
+        return {"ok": True, "max_ratio": 0.0, "frob": 0.0, "rms": 0.0}
+    if rms is None:
+        rms = math.sqrt(float(np.mean(R * R)))
+    err = np.abs(Y64 - R)
+    bound = TOL_ELEM * (np.abs(R) + rms)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    nref = math.sqrt(float(np.sum(R * R)))
+    nerr = math.sqrt(float(np.sum((Y64 - R) ** 2)))
+    frob = nerr / nref if nref > 0 else (0.0 if nerr == 0 else math.inf)
+    finite = bool(np.isfinite(Y64).all())
+    max_ratio = float(ratio.max())
+    return {
+        "ok": finite and max_ratio <= 1.0 and frob <= TOL_FROB,
+        "max_ratio": max_ratio,
+        "frob": frob,
+        "rms": rms,
+    }
