@@ -1,0 +1,172 @@
+/*
+ * fp6.h -- C ABI of the MI355X (gfx950) weight-only FP6 linear layer (W6A16).
+ *
+ *   Y[M,N] = X[M,K] . dequant(W_fp6[N,K])^T
+ *
+ * X and Y are fp16, W is FP6 e3m2 (1 sign, 3 exponent, 2 mantissa bits,
+ * bias 3, subnormals, no inf/NaN, max 28) with one fp16 scale per output row.
+ * De-quantisation and the product run in one kernel, so no fp16 copy of W is
+ * ever written to memory (TC-FPx explainer, duicuo.cn, section "redesigning
+ * the kernel solution": one fused kernel instead of a de-quantise kernel plus
+ * a matmul kernel; FP6 values are turned into FP16 and multiplied as FP16).
+ * The weights are re-ordered and split into 2-bit and 4-bit pieces offline
+ * (same section: bit-level pre-packing into aligned words, 6 = 2 + 4 bit
+ * splitting, fragments re-ordered before run time).
+ *
+ * Conventions for every entry point:
+ *   - All functions return an int status (enum fp6_status); FP6_OK == 0.
+ *   - No function aborts, throws across the ABI or prints.
+ *   - Argument checks happen on the host before any HIP call, so an invalid
+ *     call never touches the GPU.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are GPU
+ *     memory of the current HIP device (e.g. a torch CUDA tensor's data_ptr).
+ *   - The caller owns every buffer it passes.  The library owns only the
+ *     split-K workspace described at fp6_linear.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream).  Device entry points only enqueue work on it and never
+ *     synchronise it, except where stated.
+ *
+ * Size limits: 16 <= N <= 2^24 with N % 16 == 0; 256 <= K <= 2^24 with
+ * K % 256 == 0; 0 <= M <= 2^24; N*K <= 2^36.  Violations give FP6_E_SHAPE.
+ */
+#ifndef FP6_AMD_H
+#define FP6_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fp6_status {
+  FP6_OK = 0,
+  FP6_E_NULL = 1,   /* a required pointer is NULL                           */
+  FP6_E_SHAPE = 2,  /* M, N or K outside the limits above                   */
+  FP6_E_ALIGN = 3,  /* a device pointer is not 16-byte aligned (scales: 2)  */
+  FP6_E_CODE = 4,   /* a weight code is > 63                                */
+  FP6_E_SCALE = 5,  /* a scale is not finite or |s| >= 16                   */
+  FP6_E_SIZE = 6,   /* a caller buffer size does not match                  */
+  FP6_E_HIP = 7,    /* a HIP runtime call or kernel launch failed           */
+  FP6_E_VALUE = 8,  /* an input value is invalid (NaN/inf weight) or a plan
+                       parameter is out of range                            */
+};
+
+/* Version of the packed weight layout produced by fp6_prepack (1). */
+int fp6_pack_version(void);
+
+/* Static, NUL-terminated text for a status code (never NULL). */
+const char* fp6_status_string(int status);
+
+/* Bytes of the packed buffer for an N x K weight: exactly N*K*3/4, or 0 if
+ * (N, K) is outside the limits. */
+size_t fp6_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * fp6_quantize_rows -- host, synchronous, deterministic.
+ * Quantises fp32 weights to e3m2 codes with one fp16 scale per row:
+ *   s_n = fp16_RNE(max_k |W[n,k]| / 28)   (quotient in double, one rounding)
+ *   c   = sign(W) << 5 | nearest e3m2 magnitude of |W / s_n| (double quotient;
+ *         ties to the even code; >= 28 saturates to 28; rows with s_n == 0
+ *         get all-zero codes).
+ * W: host float32 [N][K] row-major, finite.  codes: host uint8 [N][K] out.
+ * scales: host uint16 (fp16 bit patterns) [N] out.
+ * Any N >= 1, K >= 1 (no tiling constraint).  Errors: FP6_E_NULL, FP6_E_SHAPE,
+ * FP6_E_VALUE (non-finite W), FP6_E_SCALE (a row gives |s| >= 16); on error
+ * the outputs are unspecified.  The pages do not describe quantisation; this
+ * is the input preparation used by the tests and the benchmark.
+ */
+int fp6_quantize_rows(const float* W, int64_t N, int64_t K,
+                      uint8_t* codes, uint16_t* scales);
+
+/*
+ * fp6_prepack -- host, synchronous, pure and deterministic (offline step).
+ * Re-orders 6-bit codes into packed layout v1 (TC-FPx explainer, section
+ * "redesigning the kernel solution": bit-level pre-packing and 2+4 splitting
+ * before inference).
+ *
+ * codes:   host uint8 [N][K] row-major, every value in 0..63.
+ * scales:  host uint16 fp16 bit patterns [N]; checked only (finite, |s| < 16,
+ *          the range in which s * 2^12 is an exact fp16, which the fused
+ *          kernel relies on); pass the same values to fp6_linear.
+ * packed:  host out, packed_bytes == fp6_packed_bytes(N, K).
+ * Errors: FP6_E_NULL, FP6_E_SHAPE, FP6_E_CODE, FP6_E_SCALE, FP6_E_SIZE.
+ *
+ * Packed layout v1.  Tiles of 16 rows x 256 k, 3072 bytes each; tile
+ * (nb, kb) starts at byte (nb*(K/256) + kb)*3072.  Within a tile, local row r
+ * (0..15) and local k = 32*j + 8*g + i (k-step j 0..7, lane group g 0..3,
+ * element i 0..7) belong to wave lane L = 16*g + r.  Each code c is split into
+ * a 2-bit piece (s, e2) = c >> 4 and a 4-bit piece (e1 e0 m1 m0) = c & 15.
+ *   bytes [0,1024):    2-bit plane.  Lane L's 16 bytes at 16*L are four
+ *                      little-endian words; word j/2 covers k-steps j, j+1.
+ *                      With p = 4*(j%2) + i/2 and h = i%2, bit e2 is at
+ *                      (12 + 16h + 2p) mod 32 and bit s at (15 + 16h + 2p) mod 32.
+ *   bytes [1024,3072): 4-bit plane; k-steps 0..3 in the first 1024 bytes,
+ *                      4..7 in the second.  Lane L's 16 bytes at 16*L hold
+ *                      words j%4; element i is the nibble at bits
+ *                      4*(i/2 + 4*(i%2)) .. +3.
+ * A wave reads one tile with three fully coalesced 16-byte-per-lane loads,
+ * and each lane's words hold exactly the 8 k-values per k-step that a
+ * 16x16x32 fp16 MFMA A-operand lane consumes.
+ */
+int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
+                int64_t N, int64_t K, void* packed, size_t packed_bytes);
+
+/*
+ * fp6_linear -- device, asynchronous on `stream` (the hot path).
+ *   Y[m,n] = sum_k X[m,k] * Wdq[n,k],  Wdq[n,k] = fp16_RNE(v(c[n,k]) * s_n)
+ * with fp32 accumulation and one final rounding to fp16 (IEEE RNE).  FP6-LLM
+ * (arXiv 2401.14112) abstract: W6A16 linear layers on tensor cores; TC-FPx
+ * explainer, section "redesigning the kernel solution": one fused kernel.
+ *
+ * X:        device fp16 [M][K] row-major, 16-byte aligned.
+ * packed_W: device, the bytes of fp6_prepack(N, K) copied verbatim, 16-byte
+ *           aligned.
+ * scales:   device fp16 [N], the values given to fp6_prepack (unchecked here).
+ * Y:        device fp16 [M][N] row-major, 16-byte aligned, must not overlap
+ *           any input.
+ * M == 0 is a no-op returning FP6_OK (X and Y may then be NULL).
+ * Errors: FP6_E_NULL, FP6_E_SHAPE, FP6_E_ALIGN (before any HIP call);
+ *         FP6_E_HIP if the launch or a workspace allocation fails.
+ * Workspace: when the plan splits K (memory-bound small-M shapes) the library
+ * keeps an fp32 partial-sum buffer and a self-resetting counter array per
+ * (device, stream), allocated with hipMalloc on first need and grown on
+ * demand (growing synchronises that stream once).  Results are bitwise
+ * deterministic: split partials are summed in a fixed order.
+ * Concurrent calls on different streams are safe; concurrent calls on the
+ * same stream from several host threads are serialised by the stream.
+ */
+int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * fp6_linear_plan -- fp6_linear with the schedule forced (tuning and tests).
+ * variant: 0 = automatic, 1 = small-M streaming kernel (any M, M-blocks of
+ *          16 per pass), 2 = large-M kernel.
+ * splits:  0 = automatic, else the number of K-splits (1..K/256).
+ * The result equals fp6_linear's up to fp32 summation order.
+ * Errors: as fp6_linear, plus FP6_E_VALUE for an unknown variant or split.
+ */
+int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y,
+                    int64_t M, int64_t N, int64_t K, int variant, int splits,
+                    void* stream);
+
+/*
+ * fp6_dequant -- device, asynchronous; test and inspection export.
+ * Writes Wdq fp16 [N][K] row-major using the same splice-and-scale device
+ * function as fp6_linear (TC-FPx explainer, section "redesigning the kernel
+ * solution": FP6 weights rebuilt as FP16 in registers).  W16 must be 16-byte
+ * aligned and hold N*K halves.  Errors: FP6_E_NULL, FP6_E_SHAPE,
+ * FP6_E_ALIGN, FP6_E_HIP.
+ */
+int fp6_dequant(const void* packed_W, const void* scales, void* W16,
+                int64_t N, int64_t K, void* stream);
+
+/* Frees every workspace the library holds (synchronises the device first).
+ * Returns FP6_OK or FP6_E_HIP. */
+int fp6_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP6_AMD_H */

@@ -11,3 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # Name every GPU case on the real stderr before it runs, so a run that
+    # dies inside a kernel still says which case it was.
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,220 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+* De-quantisation export: bit-exact against oracle.dequant_ref.
+* Fused linear: |Y - Y_ref| <= 2e-3 (|Y_ref| + rms(Y_ref)) per element and
+  relative Frobenius error <= 5e-4, on every workload shape at full size
+  (sampled output columns for the two largest layers) and on small shapes that
+  span several tiles with ragged M; one-hot inputs must reproduce Wdq exactly.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_fp6_amd import synth
+
+from _workloads import Prepared, prepare_shape  # noqa: F401
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import weight_only_fp6_amd as fp6  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def _bits16(t):
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def _assert_tol(y_dev, y_ref, rms=None, what=""):
+    y = y_dev.detach().cpu().numpy().astype(np.float64)
+    rep = oracle.tolerance_report(y, y_ref, rms=rms)
+    assert rep["ok"], (what, rep)
+    return rep
+
+
+# ----------------------------------------------------------------------------
+# De-quantisation (bit-exact)
+# ----------------------------------------------------------------------------
+def _dequant_dev(codes, scales):
+    N, K = codes.shape
+    packed = torch.from_numpy(fp6.prepack(codes, scales)).to(DEV)
+    s = torch.from_numpy(np.ascontiguousarray(scales, np.float16)).to(DEV)
+    out = fp6.dequant(packed, s, N, K)
+    torch.cuda.synchronize()
+    return _bits16(out)
+
+
+def test_dequant_all_codes_unit_scale():
+    N, K = 64, 512
+    codes = ((np.arange(N)[:, None] * 7 + np.arange(K)[None, :]) % 64).astype(np.uint8)
+    scales = np.ones(N, np.float16)
+    got = _dequant_dev(codes, scales)
+    ref = oracle.dequant_ref(codes, scales).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_dequant_power_of_two_and_subnormal_scales():
+    js = list(range(-24, 4))
+    N, K = 16 * len(js), 256
+    codes = synth.codes_uniform(N, K, seed=3)
+    scales = np.repeat(np.array([2.0 ** j for j in js], np.float16), 16)
+    got = _dequant_dev(codes, scales)
+    ref = oracle.dequant_ref(codes, scales).view(np.uint16)
+    assert np.array_equal(got, ref)
+    # the tiny scales produce fp16 subnormal weights: they must survive
+    assert (ref[:16 * 10] & 0x7C00 == 0).any()
+
+
+def test_dequant_random_scales_full_range():
+    rng = np.random.default_rng(4)
+    N, K = 1024, 512
+    sb = rng.integers(1, 0x4C00, N).astype(np.uint16) | (rng.integers(0, 2, N).astype(np.uint16) << 15)
+    scales = sb.view(np.float16)
+    codes = synth.codes_uniform(N, K, seed=4)
+    got = _dequant_dev(codes, scales)
+    ref = oracle.dequant_ref(codes, scales).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+@functools.lru_cache(maxsize=2)
+def _prep(name, sample):
+    return prepare_shape(synth.SHAPES[name], sample=sample)
+
+
+_NK = {}
+for _n, _s in synth.SHAPES.items():
+    _NK.setdefault((_s.N, _s.K, _s.cfg), _n)
+
+
+@pytest.mark.parametrize("name", sorted(_NK.values()))
+def test_dequant_workload_weights(name):
+    shp = synth.SHAPES[name]
+    sample = None if shp.N * shp.K <= 16 * 2**20 else 256
+    p = _prep(name, sample)
+    packed = torch.from_numpy(p.packed).to(DEV)
+    s = torch.from_numpy(p.scales.copy()).to(DEV)
+    out = fp6.dequant(packed, s, shp.N, shp.K)
+    got = _bits16(out[torch.from_numpy(p.rows).to(DEV)])
+    assert np.array_equal(got, p.wdq_ref.view(np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# Fused linear at the workload shapes (automatic plan = the benchmarked launch)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(synth.SHAPES))
+def test_linear_workloads(name):
+    shp = synth.SHAPES[name]
+    sample = None if shp.N * shp.K <= 48 * 2**20 else 384
+    p = _prep(name, sample)
+    X, packed, s = p.to_device()
+    Y = fp6.linear(X, packed, s, shp.N, shp.K)
+    torch.cuda.synchronize()
+    ycols = Y[:, torch.from_numpy(p.rows).to(DEV)]
+    _assert_tol(ycols, p.y_ref, what=name)
+
+
+# ----------------------------------------------------------------------------
+# Small shapes spanning several tiles, ragged M, forced schedules
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 31, 33, 64, 100, 257])
+@pytest.mark.parametrize("NK", [(16, 256), (64, 1024), (80, 2816)])
+def test_linear_small_shapes_ragged_m(M, NK):
+    N, K = NK
+    p = Prepared(M, N, K, seed_w=N * 7 + K, seed_x=M * 11 + 1)
+    X, packed, s = p.to_device()
+    for variant in (0, 1, 2):
+        Y = fp6.linear_plan(X, packed, s, N, K, variant=variant)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 7, 8, 16, 43])
+def test_linear_forced_splits_long_k(splits):
+    # Llama-7B MLP down projection: K = 11008 = 43 tiles of 256 (43 is prime)
+    shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
+    p = _prep(shp.name, None)
+    X, packed, s = p.to_device()
+    for variant in (1, 2):
+        Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=variant, splits=splits)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(splits, variant))
+
+
+def test_linear_one_hot_reproduces_wdq_exactly():
+    N, K = 64, 1024
+    p = Prepared(16, N, K, seed_w=99, seed_x=1)
+    ks = np.array([0, 1, 7, 8, 255, 256, 300, 511, 512, 777, 1000, 1023, 31, 32, 33, 600])
+    X = np.zeros((16, K), np.float16)
+    X[np.arange(16), ks] = 1.0
+    Xd = torch.from_numpy(X).to(DEV)
+    _, packed, s = p.to_device()
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3)]:
+        Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
+        torch.cuda.synchronize()
+        got = Y.cpu().numpy().astype(np.float64)
+        want = p.wdq_ref[:, ks].T.astype(np.float64)
+        assert np.array_equal(got, want), (variant, splits)
+
+
+def test_linear_zero_activations_give_zero():
+    N, K = 64, 1024
+    p = Prepared(5, N, K, seed_w=98, seed_x=2)
+    _, packed, s = p.to_device()
+    X = torch.zeros((5, K), dtype=torch.float16, device=DEV)
+    for splits in (1, 4):
+        Y = fp6.linear_plan(X, packed, s, N, K, variant=1, splits=splits)
+        torch.cuda.synchronize()
+        assert not Y.cpu().numpy().astype(np.float64).any()
+
+
+def test_linear_is_deterministic():
+    shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
+    p = _prep(shp.name, None)
+    X, packed, s = p.to_device()
+    a = fp6.linear(X, packed, s, shp.N, shp.K).clone()
+    b = fp6.linear(X, packed, s, shp.N, shp.K).clone()
+    c = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=1, splits=8).clone()
+    d = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=1, splits=8).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c.view(torch.int16), d.view(torch.int16))
+
+
+def test_linear_very_long_k_and_minimum_shape():
+    for (M, N, K) in [(4, 16, 2**18), (1, 16, 256)]:
+        p = Prepared(M, N, K, seed_w=K + 5, seed_x=K + 6)
+        X, packed, s = p.to_device()
+        Y = fp6.linear(X, packed, s, N, K)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(M, N, K))
+
+
+def test_linear_m_zero_is_noop():
+    N, K = 16, 256
+    packed = torch.zeros(fp6.packed_bytes(N, K), dtype=torch.uint8, device=DEV)
+    s = torch.ones(N, dtype=torch.float16, device=DEV)
+    X = torch.zeros((0, K), dtype=torch.float16, device=DEV)
+    Y = fp6.linear(X, packed, s, N, K)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, N)
+
+
+def test_linear_on_side_stream_matches_default_stream():
+    shp = synth.SHAPES["llama7b_attn_1x4096x4096"]
+    p = _prep(shp.name, None)
+    X, packed, s = p.to_device()
+    a = fp6.linear(X, packed, s, shp.N, shp.K)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b = fp6.linear(X, packed, s, shp.N, shp.K)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    _assert_tol(b, p.y_ref)

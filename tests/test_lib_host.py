@@ -1,0 +1,172 @@
+"""Host-side library tests (no GPU): exported symbols, quantiser and packer
+parity with the oracle, and every argument error the C ABI can return before
+touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_fp6_amd as fp6
+from weight_only_fp6_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"\b(fp6_\w+)\s*\(", txt)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(fp6.lib, n), n
+    assert set(names) == set(fp6.EXPORTED)
+
+
+def test_version_sizes_and_status_strings():
+    assert fp6.pack_version() == 1
+    assert fp6.packed_bytes(16, 256) == 3072
+    assert fp6.packed_bytes(28672, 8192) == 176_160_768
+    for bad in [(0, 256), (16, 0), (8, 256), (16, 128), (16, 300), (2**25, 256), (2**24, 2**24)]:
+        assert fp6.packed_bytes(*bad) == 0
+    for s in range(10):
+        assert fp6.lib.fp6_status_string(s)
+
+
+@pytest.mark.parametrize("shape", [(5, 7), (16, 256), (37, 1000)])
+def test_quantizer_matches_oracle_random(shape):
+    W = synth.weights(*shape, seed=7 + shape[0])
+    c_lib, s_lib = fp6.quantize_rows(W)
+    c_ref, s_ref = oracle.quantize_rows(W)
+    assert np.array_equal(s_lib.view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(c_lib, c_ref)
+
+
+def test_quantizer_matches_oracle_adversarial():
+    rng = np.random.default_rng(5)
+    rows = []
+    # exact e3m2 midpoints times a power-of-two scale (ties), saturation, zeros
+    s = 2.0 ** -6
+    mids = [(a + b) / 2 for a, b in zip(oracle.E3M2_VALUES[:31], oracle.E3M2_VALUES[1:32])]
+    rows.append(np.array([28 * s] + [m * s for m in mids] + [-m * s for m in mids] + [0.0] * 1, np.float32))
+    rows.append(np.zeros(64, np.float32))
+    r = np.zeros(64, np.float32)
+    r[3] = -0.0
+    r[4] = np.float32(28 * (1 + 2.0 ** -11) * 0.01)
+    r[5] = -1e-9
+    rows.append(r)
+    rows.append((rng.standard_normal(64) * 1e-6).astype(np.float32))       # subnormal scales
+    rows.append((rng.standard_normal(64) * 100).astype(np.float32))        # large scales
+    width = max(len(x) for x in rows)
+    W = np.zeros((len(rows), width), np.float32)
+    for i, x in enumerate(rows):
+        W[i, : len(x)] = x
+    c_lib, s_lib = fp6.quantize_rows(W)
+    c_ref, s_ref = oracle.quantize_rows(W)
+    assert np.array_equal(s_lib.view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(c_lib, c_ref)
+
+
+def test_quantizer_errors():
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.quantize_rows(np.full((2, 4), 1000.0, np.float32))
+    assert e.value.name == "FP6_E_SCALE"
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.quantize_rows(np.array([[1.0, np.inf]], np.float32))
+    assert e.value.name == "FP6_E_VALUE"
+    assert fp6.lib.fp6_quantize_rows(None, 1, 1, None, None) == 1
+
+
+@pytest.mark.parametrize("shape", [(16, 256), (32, 512), (48, 768)])
+def test_prepack_matches_oracle_packer_bytewise(shape):
+    codes = synth.codes_uniform(*shape, seed=shape[1])
+    scales = np.ones(shape[0], np.float16)
+    got = fp6.prepack(codes, scales)
+    assert got.size == shape[0] * shape[1] * 3 // 4
+    assert np.array_equal(got, oracle.pack_scalar(codes))
+    assert np.array_equal(oracle.unpack_scalar(got, *shape), codes)
+
+
+def test_prepack_round_trip_llama_shape():
+    # a full-size row block of the Llama-70B MLP (K = 8192) and a ragged-tile count
+    for N, K in [(64, 8192), (32, 11008), (16, 7168)]:
+        W = synth.weights(N, K, seed=N + K)
+        codes, scales = fp6.quantize_rows(W)
+        packed = fp6.prepack(codes, scales)
+        assert np.array_equal(oracle.unpack_np(packed, N, K), codes)
+
+
+def test_prepack_adversarial_patterns():
+    N, K = 32, 512
+    for c in [np.full((N, K), 63, np.uint8), np.zeros((N, K), np.uint8),
+              (np.indices((N, K)).sum(axis=0) % 2 * 63).astype(np.uint8),
+              np.tile(np.array([1 << b for b in range(6)], np.uint8), (N, K // 6 + 1))[:, :K]]:
+        packed = fp6.prepack(c, np.ones(N, np.float16))
+        assert np.array_equal(oracle.unpack_np(packed, N, K), c)
+
+
+def test_prepack_errors():
+    codes = np.zeros((16, 256), np.uint8)
+    ones = np.ones(16, np.float16)
+    bad = codes.copy()
+    bad[3, 7] = 64
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.prepack(bad, ones)
+    assert e.value.name == "FP6_E_CODE"
+    for sv in [np.nan, np.inf, 16.0, -16.0, 60000.0]:
+        s = ones.copy()
+        s[5] = sv
+        with pytest.raises(fp6.FP6Error) as e:
+            fp6.prepack(codes, s)
+        assert e.value.name == "FP6_E_SCALE"
+    s = ones.copy()
+    s[5] = np.float16(15.99)          # largest accepted magnitude region
+    fp6.prepack(codes, s)
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.prepack(np.zeros((16, 100), np.uint8), ones)
+    assert e.value.name == "FP6_E_SHAPE"
+    out = np.zeros(3072, np.uint8)
+    vp = ctypes.c_void_p
+    p = lambda a: a.ctypes.data_as(vp)
+    assert fp6.lib.fp6_prepack(p(codes), p(ones), 16, 256, p(out), 3071) == 6      # size
+    assert fp6.lib.fp6_prepack(None, p(ones), 16, 256, p(out), 3072) == 1          # null
+    assert fp6.lib.fp6_prepack(p(codes), p(ones), 16, 256, None, 3072) == 1
+
+
+def test_linear_and_dequant_argument_errors_before_any_hip_call():
+    L = fp6.lib
+    A = 1 << 20  # a fake, 16-byte aligned "device" address: never dereferenced
+    # shape errors
+    assert L.fp6_linear(A, A, A, A, 4, 24, 256, None) == 2
+    assert L.fp6_linear(A, A, A, A, 4, 16, 200, None) == 2
+    assert L.fp6_linear(A, A, A, A, -1, 16, 256, None) == 2
+    assert L.fp6_linear(A, A, A, A, 2**25, 16, 256, None) == 2
+    # M == 0 is a no-op (no pointer needed)
+    assert L.fp6_linear(None, None, None, None, 0, 16, 256, None) == 0
+    # nulls
+    assert L.fp6_linear(None, A, A, A, 4, 16, 256, None) == 1
+    assert L.fp6_linear(A, A, None, A, 4, 16, 256, None) == 1
+    # alignment
+    assert L.fp6_linear(A + 8, A, A, A, 4, 16, 256, None) == 3
+    assert L.fp6_linear(A, A + 4, A, A, 4, 16, 256, None) == 3
+    assert L.fp6_linear(A, A, A + 1, A, 4, 16, 256, None) == 3
+    assert L.fp6_linear(A, A, A, A + 2, 4, 16, 256, None) == 3
+    # plan parameters
+    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 3, 0, None) == 8
+    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 0, 2, None) == 8   # 2 splits > 1 k-tile
+    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 0, -1, None) == 8
+    # dequant
+    assert L.fp6_dequant(A, A, A, 16, 100, None) == 2
+    assert L.fp6_dequant(None, A, A, 16, 256, None) == 1
+    assert L.fp6_dequant(A, A, A + 8, 16, 256, None) == 3

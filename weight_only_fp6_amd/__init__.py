@@ -1,0 +1,167 @@
+"""Thin Python binding of the MI355X FP6 (e3m2) weight-only linear library.
+
+Argument marshalling only: every step runs in ``libfp6amd.so`` (host packer
+and quantiser in C++, de-quantisation and the fused GEMM in HIP kernels for
+gfx950).  Host arrays are NumPy; device buffers are torch CUDA (ROCm) tensors
+used purely as memory, with the current torch stream passed to the library.
+
+The names follow the C ABI in ``include/fp6.h``:
+
+* :func:`packed_bytes`, :func:`pack_version`
+* :func:`quantize_rows` (host) -> ``(codes uint8 [N,K], scales fp16 [N])``
+* :func:`prepack` (host) -> ``uint8 [N*K*3/4]`` packed layout v1
+* :func:`linear` (device) -> ``Y fp16 [M,N] = X . dequant(W)^T``
+* :func:`linear_plan` (device, forced schedule), :func:`dequant` (device export)
+
+There is no fallback: if the shared library is missing or fails to load,
+importing this package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp6amd.so")
+
+FP6_OK = 0
+STATUS_NAMES = {
+    0: "FP6_OK", 1: "FP6_E_NULL", 2: "FP6_E_SHAPE", 3: "FP6_E_ALIGN", 4: "FP6_E_CODE",
+    5: "FP6_E_SCALE", 6: "FP6_E_SIZE", 7: "FP6_E_HIP", 8: "FP6_E_VALUE",
+}
+EXPORTED = (
+    "fp6_pack_version", "fp6_status_string", "fp6_packed_bytes", "fp6_quantize_rows",
+    "fp6_prepack", "fp6_linear", "fp6_linear_plan", "fp6_dequant", "fp6_release",
+)
+
+
+class FP6Error(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, func: str, status: int):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{func}: {self.name} ({_lib.fp6_status_string(status).decode()})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m weight_only_fp6_amd.build_lib` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "fp6_pack_version": ([], i32),
+        "fp6_status_string": ([i32], ctypes.c_char_p),
+        "fp6_packed_bytes": ([i64, i64], sz),
+        "fp6_quantize_rows": ([vp, i64, i64, vp, vp], i32),
+        "fp6_prepack": ([vp, vp, i64, i64, vp, sz], i32),
+        "fp6_linear": ([vp, vp, vp, vp, i64, i64, i64, vp], i32),
+        "fp6_linear_plan": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp], i32),
+        "fp6_dequant": ([vp, vp, vp, i64, i64, vp], i32),
+        "fp6_release": ([], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def _check(func: str, status: int) -> None:
+    if status != FP6_OK:
+        raise FP6Error(func, status)
+
+
+def pack_version() -> int:
+    return int(_lib.fp6_pack_version())
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(_lib.fp6_packed_bytes(N, K))
+
+
+def _host_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def quantize_rows(W: np.ndarray):
+    """Host quantiser: float32 [N,K] -> (codes uint8 [N,K], scales float16 [N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    N, K = W.shape
+    codes = np.empty((N, K), dtype=np.uint8)
+    scales = np.empty(N, dtype=np.uint16)
+    _check("fp6_quantize_rows", _lib.fp6_quantize_rows(_host_ptr(W), N, K, _host_ptr(codes), _host_ptr(scales)))
+    return codes, scales.view(np.float16)
+
+
+def prepack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Host packer: codes uint8 [N,K] + scales fp16 [N] -> packed uint8 [N*K*3/4]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float16).view(np.uint16)
+    if codes.ndim != 2 or scales.shape != (codes.shape[0],):
+        raise ValueError("codes [N,K] and scales [N] expected")
+    N, K = codes.shape
+    nbytes = packed_bytes(N, K)
+    out = np.empty(max(nbytes, 1), dtype=np.uint8)
+    _check("fp6_prepack", _lib.fp6_prepack(_host_ptr(codes), _host_ptr(scales), N, K, _host_ptr(out), nbytes))
+    return out[:nbytes]
+
+
+def _stream_handle(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dev_ptr(t) -> int:
+    return int(t.data_ptr()) if t is not None else 0
+
+
+def linear(X, packed, scales, N: int, K: int, out=None, stream=None):
+    """Y[M,N] fp16 = X[M,K] . dequant(W)^T on the GPU (asynchronous)."""
+    return linear_plan(X, packed, scales, N, K, variant=0, splits=0, out=out, stream=stream)
+
+
+def linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int = 0,
+                out=None, stream=None):
+    import torch
+    if X.dtype != torch.float16 or X.dim() != 2 or X.shape[1] != K or not X.is_contiguous():
+        raise ValueError("X must be a contiguous fp16 [M,K] tensor")
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp16 [M,N] tensor")
+    if packed.numel() != packed_bytes(N, K) or packed.dtype != torch.uint8:
+        raise ValueError("packed must be the uint8 output of prepack for (N, K)")
+    if scales.dtype != torch.float16 or scales.numel() != N:
+        raise ValueError("scales must be fp16 [N]")
+    st = _lib.fp6_linear_plan(_dev_ptr(X), _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out),
+                              M, N, K, variant, splits, _stream_handle(stream))
+    _check("fp6_linear_plan", st)
+    return out
+
+
+def dequant(packed, scales, N: int, K: int, out=None, stream=None):
+    """Wdq fp16 [N,K] from the packed weights (same device splice as linear)."""
+    import torch
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    st = _lib.fp6_dequant(_dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), N, K, _stream_handle(stream))
+    _check("fp6_dequant", st)
+    return out
+
+
+def release() -> None:
+    _check("fp6_release", _lib.fp6_release())

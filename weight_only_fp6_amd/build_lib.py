@@ -1,0 +1,61 @@
+"""Build the HIP library ``libfp6amd.so`` in-tree for gfx950.
+
+Host code (fp6_host.cpp) is compiled with g++ and the kernels plus device
+entry points (fp6_kernels.hip) with hipcc; both are linked into one shared
+library next to this file.  Run ``python -m weight_only_fp6_amd.build_lib``.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfp6amd.so")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+# Packed-fp32 instruction selection is switched off for every device
+# compilation (see the library's design notes on v_pk_*_f32).
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"build step failed: {' '.join(cmd[:3])} ...")
+    return res
+
+
+def build(verbose: bool = False) -> str:
+    """Compile and link the library; returns its path.  Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", CSRC]
+    host_o = os.path.join(BUILD, "fp6_host.o")
+    kern_o = os.path.join(BUILD, "fp6_kernels.o")
+    _run(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "fp6_host.cpp"), "-o", host_o], verbose)
+    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "fp6_kernels.hip"), "-o", kern_o], verbose)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, host_o, kern_o], verbose)
+    shutil.move(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,422 @@
+// Fused FP6 (e3m2) weight-only linear layer for gfx950 (MI355X): kernels,
+// schedule choice and the device entry points of the C ABI.
+//
+// FP6-LLM (arXiv 2401.14112), abstract: the two costs of FP6 weights on GPUs
+// are irregular-width memory access and de-quantisation overhead.  TC-FPx
+// explainer (duicuo.cn), section "redesigning the kernel solution": one
+// kernel de-quantises in registers and feeds FP16 matrix units; weights are
+// pre-split into 2-bit and 4-bit pieces so the splice is a few bit operations.
+//
+// gfx950 design (this file):
+//  * A wave owns 16 weight rows (one 16x16x32 MFMA A-operand row block) and a
+//    range of 256-wide k-tiles.  Per tile it issues three coalesced 16-byte
+//    loads per lane (1 KiB per wave instruction): one 2-bit word quad and two
+//    4-bit word quads, exactly the bits of its 64 codes.
+//  * Splice: for the fp16 pair (2r, 2r+1) of k-step j,
+//      bits = ((d4 shifted into bits 8..11 / 24..27) & 0x0F000F00)
+//           | (rotr(d2, 2p) & 0x90009000),      p = 4*(j%2) + r
+//    which is the fp16 pattern of v(c) * 2^-12 (sign at bit 15, e2 at bit 12,
+//    e1 e0 m1 m0 at bits 11..8; e3m2 subnormals become fp16 subnormals).
+//  * Scale fold: one v_pk_mul_f16 by s_n * 2^12, an exact fp16 for |s| < 16,
+//    so the single rounding gives fp16_RNE(v * s_n) bit for bit.
+//  * fp32 MFMA accumulation (v_mfma_f32_16x16x32_f16), A = weights (rows n),
+//    B = X^T (columns m), so the accumulator tile is Y^T.
+//  * Split-K for the memory-bound small-M regime: each split writes an fp32
+//    partial tile; the last split to arrive (agent-scope counter) sums the
+//    partials in split order and stores fp16 Y, then resets the counter.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "fp6.h"
+#include "fp6_limits.h"
+
+namespace {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaveSize = 64;
+constexpr int kTileWords = 192;  // 3072 bytes / 16 bytes per lane-quad
+
+// ---------------------------------------------------------------------------
+// Splice + scale of one k-step: 8 fp16 weights of this lane (elements
+// 8g..8g+7 of the k-step, row r), from the 2-bit word d2 (covering k-steps
+// 2*(j/2) and 2*(j/2)+1) and the 4-bit word d4 (k-step j).
+// ---------------------------------------------------------------------------
+template <int JODD>
+__device__ __forceinline__ half8v splice_kstep(uint32_t d2, uint32_t d4, half2v s2) {
+  constexpr uint32_t kM4 = 0x0F000F00u, kM2 = 0x90009000u;
+  constexpr int sh = 8 * JODD;  // 2*p for pair 0 of this k-step
+  const uint32_t t0 = ((d4 << 8) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 0) & kM2);
+  const uint32_t t1 = ((d4 << 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 2) & kM2);
+  const uint32_t t2 = (d4 & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 4) & kM2);
+  const uint32_t t3 = ((d4 >> 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 6) & kM2);
+  const half2v h0 = __builtin_bit_cast(half2v, t0) * s2;
+  const half2v h1 = __builtin_bit_cast(half2v, t1) * s2;
+  const half2v h2 = __builtin_bit_cast(half2v, t2) * s2;
+  const half2v h3 = __builtin_bit_cast(half2v, t3) * s2;
+  half8v a;
+  a[0] = h0[0]; a[1] = h0[1]; a[2] = h1[0]; a[3] = h1[1];
+  a[4] = h2[0]; a[5] = h2[1]; a[6] = h3[0]; a[7] = h3[1];
+  return a;
+}
+
+template <int J>
+__device__ __forceinline__ half8v splice_tile_step(const u32x4& q2, const u32x4& q4a,
+                                                   const u32x4& q4b, half2v s2) {
+  const uint32_t d2 = q2[J >> 1];
+  const uint32_t d4 = (J < 4) ? q4a[J & 3] : q4b[J & 3];
+  return splice_kstep<J & 1>(d2, d4, s2);
+}
+
+__device__ __forceinline__ half2v row_scale2(const _Float16* scales, int64_t n) {
+  const _Float16 s = scales[n] * static_cast<_Float16>(4096.0f);  // exact for |s| < 16
+  half2v s2;
+  s2[0] = s;
+  s2[1] = s;
+  return s2;
+}
+
+// ---------------------------------------------------------------------------
+// De-quantisation export: one wave per tile, Wdq fp16 [N][K] row-major.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restrict__ wp,
+                                                          const _Float16* __restrict__ scales,
+                                                          _Float16* __restrict__ w16,
+                                                          int64_t N, int64_t K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ktiles = K >> 8;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (tile >= (N >> 4) * ktiles) return;
+  const int64_t nb = tile / ktiles, kt = tile % ktiles;
+  const int r = lane & 15, g = lane >> 4;
+  const u32x4* t = wp + tile * kTileWords + lane;
+  const u32x4 q2 = t[0], q4a = t[64], q4b = t[128];
+  const int64_t n = nb * 16 + r;
+  const half2v s2 = row_scale2(scales, n);
+  half8v* out = reinterpret_cast<half8v*>(w16 + n * K + kt * 256 + 8 * g);
+  out[0] = splice_tile_step<0>(q2, q4a, q4b, s2);
+  out[4] = splice_tile_step<1>(q2, q4a, q4b, s2);
+  out[8] = splice_tile_step<2>(q2, q4a, q4b, s2);
+  out[12] = splice_tile_step<3>(q2, q4a, q4b, s2);
+  out[16] = splice_tile_step<4>(q2, q4a, q4b, s2);
+  out[20] = splice_tile_step<5>(q2, q4a, q4b, s2);
+  out[24] = splice_tile_step<6>(q2, q4a, q4b, s2);
+  out[28] = splice_tile_step<7>(q2, q4a, q4b, s2);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming fused kernel.  Work unit = (m-group, row block nb, K-split).
+// A workgroup holds 4 waves = 4 consecutive row blocks with the same m-group
+// and split (they read the same X slice).  MB = number of 16-column m-blocks
+// per wave (the A fragment is reused MB times).
+// ---------------------------------------------------------------------------
+template <int MB>
+__global__ __launch_bounds__(256) void fp6_gemm_stream(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y,
+    float4v* __restrict__ part, unsigned* __restrict__ counters,
+    int64_t M, int64_t N, int64_t K, int splits, int64_t mg_base) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t nquads = (nblocks + 3) >> 2;
+  int64_t b = blockIdx.x;
+  const int split = static_cast<int>(b % splits);
+  b /= splits;
+  const int64_t nq = b % nquads;
+  const int64_t mg = b / nquads + mg_base;
+  const int64_t nb = nq * 4 + wave;
+  if (nb >= nblocks) return;
+  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int r = lane & 15, g = lane >> 4;
+
+  const half2v s2 = row_scale2(scales, nb * 16 + r);
+
+  // B operand rows: m = mg*16*MB + mb*16 + r, k = kt*256 + 32*j + 8*g.  Rows
+  // m >= M read row M-1 instead: they only feed accumulator columns that are
+  // never stored, so no masking is needed in the loop.
+  const _Float16* xrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    int64_t m = (mg * MB + mb) * 16 + r;
+    if (m >= M) m = M - 1;
+    xrow[mb] = X + m * K + 8 * g;
+  }
+
+  float4v acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4* w = wp + (nb * ktiles) * kTileWords + lane;
+  auto tile_mac = [&](int64_t kt, const u32x4& q2, const u32x4& q4a, const u32x4& q4b) {
+    half8v xb[8][MB];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        xb[j][mb] = *reinterpret_cast<const half8v*>(xrow[mb] + kt * 256 + 32 * j);
+    }
+#define FP6_STEP(J)                                                              \
+  {                                                                              \
+    const half8v a = splice_tile_step<J>(q2, q4a, q4b, s2);                      \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) acc[mb] =                  \
+        __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb[J][mb], acc[mb], 0, 0, 0);  \
+  }
+    FP6_STEP(0) FP6_STEP(1) FP6_STEP(2) FP6_STEP(3)
+    FP6_STEP(4) FP6_STEP(5) FP6_STEP(6) FP6_STEP(7)
+#undef FP6_STEP
+  };
+  if (kt0 < kt1) {
+    u32x4 q2 = w[kt0 * kTileWords];
+    u32x4 q4a = w[kt0 * kTileWords + 64];
+    u32x4 q4b = w[kt0 * kTileWords + 128];
+    for (int64_t kt = kt0; kt + 1 < kt1; ++kt) {
+      const u32x4 n2 = w[(kt + 1) * kTileWords];
+      const u32x4 n4a = w[(kt + 1) * kTileWords + 64];
+      const u32x4 n4b = w[(kt + 1) * kTileWords + 128];
+      tile_mac(kt, q2, q4a, q4b);
+      q2 = n2;
+      q4a = n4a;
+      q4b = n4b;
+    }
+    tile_mac(kt1 - 1, q2, q4a, q4b);
+  }
+
+  // acc[mb][v] = Y[m = (mg*MB+mb)*16 + r][n = nb*16 + 4*g + v]
+  if (splits == 1) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t m = (mg * MB + mb) * 16 + r;
+      if (m < M) {
+        half4v o;
+        o[0] = static_cast<_Float16>(acc[mb][0]);
+        o[1] = static_cast<_Float16>(acc[mb][1]);
+        o[2] = static_cast<_Float16>(acc[mb][2]);
+        o[3] = static_cast<_Float16>(acc[mb][3]);
+        *reinterpret_cast<half4v*>(Y + m * N + nb * 16 + 4 * g) = o;
+      }
+    }
+    return;
+  }
+
+  const int64_t tile = mg * nblocks + nb;  // one counter per (m-group, row block)
+  float4v* mypart = part + (tile * splits) * (MB * kWaveSize) + lane;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) mypart[split * MB * kWaveSize + mb * kWaveSize] = acc[mb];
+  __threadfence();
+  unsigned prev = 0;
+  if (lane == 0) prev = atomicAdd(counters + tile, 1u);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != static_cast<unsigned>(splits - 1)) return;
+  __threadfence();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float4v sum = mypart[mb * kWaveSize];
+    for (int s = 1; s < splits; ++s) sum += mypart[s * MB * kWaveSize + mb * kWaveSize];
+    const int64_t m = (mg * MB + mb) * 16 + r;
+    if (m < M) {
+      half4v o;
+      o[0] = static_cast<_Float16>(sum[0]);
+      o[1] = static_cast<_Float16>(sum[1]);
+      o[2] = static_cast<_Float16>(sum[2]);
+      o[3] = static_cast<_Float16>(sum[3]);
+      *reinterpret_cast<half4v*>(Y + m * N + nb * 16 + 4 * g) = o;
+    }
+  }
+  if (lane == 0) counters[tile] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host: workspace per (device, stream), CU count per device.
+// ---------------------------------------------------------------------------
+struct Workspace {
+  void* part = nullptr;
+  size_t part_bytes = 0;
+  unsigned* counters = nullptr;
+  size_t counter_count = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+std::map<int, int> g_cus;
+
+int device_cus(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  g_cus[dev] = cus;
+  return cus;
+}
+
+// Ensure the (device, stream) workspace holds at least the given sizes.
+int get_workspace(int dev, void* stream, size_t part_bytes, size_t counter_count, Workspace** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& ws = g_ws[{dev, stream}];
+  if (ws.part_bytes < part_bytes || ws.counter_count < counter_count) {
+    if (ws.part || ws.counters) {
+      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return FP6_E_HIP;
+      if (ws.part) (void)hipFree(ws.part);
+      if (ws.counters) (void)hipFree(ws.counters);
+      ws = Workspace{};
+    }
+    const size_t pb = part_bytes > ws.part_bytes ? part_bytes : ws.part_bytes;
+    const size_t cc = counter_count > ws.counter_count ? counter_count : ws.counter_count;
+    if (hipMalloc(&ws.part, pb) != hipSuccess) { ws = Workspace{}; return FP6_E_HIP; }
+    if (hipMalloc(reinterpret_cast<void**>(&ws.counters), cc * sizeof(unsigned)) != hipSuccess) {
+      (void)hipFree(ws.part);
+      ws = Workspace{};
+      return FP6_E_HIP;
+    }
+    if (hipMemset(ws.counters, 0, cc * sizeof(unsigned)) != hipSuccess) return FP6_E_HIP;
+    ws.part_bytes = pb;
+    ws.counter_count = cc;
+  }
+  *out = &ws;
+  return FP6_OK;
+}
+
+bool shape_ok(int64_t N, int64_t K) {
+  return N >= fp6::kTileN && K >= fp6::kTileK && N <= fp6::kMaxDim && K <= fp6::kMaxDim &&
+         N % fp6::kTileN == 0 && K % fp6::kTileK == 0 && N * K <= fp6::kMaxNK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_linear_args(const void* X, const void* W, const void* s, void* Y, int64_t M, int64_t N,
+                      int64_t K) {
+  if (!shape_ok(N, K) || M < 0 || M > fp6::kMaxDim) return FP6_E_SHAPE;
+  if (M == 0) return FP6_OK;
+  if (!X || !W || !s || !Y) return FP6_E_NULL;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || (reinterpret_cast<uintptr_t>(s) & 1u))
+    return FP6_E_ALIGN;
+  return FP6_OK;
+}
+
+struct Plan {
+  int mb;      // m-blocks of 16 per wave (1 or 4)
+  int splits;  // K-splits
+};
+
+Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
+  Plan p;
+  p.mb = (variant == 1) ? 1 : (variant == 2 ? 4 : (M <= 16 ? 1 : 4));
+  const int64_t ktiles = K >> 8, nblocks = N >> 4;
+  const int64_t mgroups = (M + 16 * p.mb - 1) / (16 * p.mb);
+  if (splits > 0) {
+    p.splits = splits;
+    return p;
+  }
+  // Aim for ~8 waves per CU so every CU has enough loads in flight.
+  const int64_t target = static_cast<int64_t>(cus) * 8;
+  const int64_t units = mgroups * nblocks;
+  int64_t s = (target + units - 1) / units;
+  if (s > ktiles) s = ktiles;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  p.splits = static_cast<int>(s);
+  return p;
+}
+
+template <int MB>
+int launch_gemm(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                int64_t K, int splits, Workspace* ws, hipStream_t stream) {
+  const int64_t nblocks = N >> 4, nquads = (nblocks + 3) >> 2;
+  const int64_t mgroups = (M + 16 * MB - 1) / (16 * MB);
+  // Keep each launch below 2^24 workgroups.
+  const int64_t per_mg = nquads * splits;
+  int64_t mg_chunk = (int64_t(1) << 24) / per_mg;
+  if (mg_chunk < 1) mg_chunk = 1;
+  for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
+    const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
+    const dim3 grid(static_cast<unsigned>(nmg * per_mg));
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(fp6_gemm_stream<MB>), grid, dim3(256), 0, stream,
+                       static_cast<const _Float16*>(X), static_cast<const u32x4*>(W),
+                       static_cast<const _Float16*>(S), static_cast<_Float16*>(Y),
+                       ws ? static_cast<float4v*>(ws->part) : nullptr,
+                       ws ? ws->counters : nullptr, M, N, K, splits, mg0);
+    if (hipGetLastError() != hipSuccess) return FP6_E_HIP;
+  }
+  return FP6_OK;
+}
+
+int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                int64_t K, int variant, int splits, void* stream) {
+  int st = check_linear_args(X, W, S, Y, M, N, K);
+  if (st != FP6_OK || M == 0) return st;
+  if (variant < 0 || variant > 2 || splits < 0 || splits > (K >> 8) || splits > 4096)
+    return FP6_E_VALUE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
+  const Plan p = choose_plan(M, N, K, device_cus(dev), variant, splits);
+  Workspace* ws = nullptr;
+  if (p.splits > 1) {
+    const int64_t nblocks = N >> 4;
+    const int64_t mgroups = (M + 16 * p.mb - 1) / (16 * p.mb);
+    const size_t part_bytes = static_cast<size_t>(mgroups * nblocks) * p.splits * p.mb * kWaveSize *
+                              sizeof(float4v);
+    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(mgroups * nblocks), &ws);
+    if (st != FP6_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.mb == 1) return launch_gemm<1>(X, W, S, Y, M, N, K, p.splits, ws, s);
+  return launch_gemm<4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
+               int64_t N, int64_t K, void* stream) {
+  return linear_impl(X, packed_W, scales, Y, M, N, K, 0, 0, stream);
+}
+
+int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
+                    int64_t N, int64_t K, int variant, int splits, void* stream) {
+  return linear_impl(X, packed_W, scales, Y, M, N, K, variant, splits, stream);
+}
+
+int fp6_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, int64_t K,
+                void* stream) {
+  if (!shape_ok(N, K)) return FP6_E_SHAPE;
+  if (!packed_W || !scales || !W16) return FP6_E_NULL;
+  if (!aligned16(packed_W) || !aligned16(W16) || (reinterpret_cast<uintptr_t>(scales) & 1u))
+    return FP6_E_ALIGN;
+  const int64_t tiles = (N >> 4) * (K >> 8);
+  const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
+  hipLaunchKernelGGL(fp6_dequant_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(packed_W), static_cast<const _Float16*>(scales),
+                     static_cast<_Float16*>(W16), N, K);
+  return hipGetLastError() == hipSuccess ? FP6_OK : FP6_E_HIP;
+}
+
+int fp6_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_ws.empty()) return FP6_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return FP6_E_HIP;
+  int st = FP6_OK;
+  for (auto& kv : g_ws) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(kv.first.first);
+    if (kv.second.part && hipFree(kv.second.part) != hipSuccess) st = FP6_E_HIP;
+    if (kv.second.counters && hipFree(kv.second.counters) != hipSuccess) st = FP6_E_HIP;
+    (void)hipSetDevice(cur);
+  }
+  g_ws.clear();
+  return st;
+}
+
+}  // extern "C"
