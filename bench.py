@@ -128,7 +128,10 @@ def main():
     y_d = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(R)]
     ptrs = [(x_d[i].data_ptr(), pk_d[i].data_ptr(), sc_d[i].data_ptr(), y_d[i].data_ptr()) for i in range(R)]
     L = fp6.lib
-    stream = torch.cuda.current_stream()
+    # All work runs on one side stream (graph capture needs a non-default one).
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    torch.cuda.set_stream(stream)
     sh = stream.cuda_stream
 
     def launch(i):

@@ -48,6 +48,11 @@ class FP6Error(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (same SONAME as the system one).  Import
+    # torch first so the dynamic linker binds this library to that runtime:
+    # loading the library first would bring in a second HIP runtime, whose
+    # streams and launches do not interoperate with torch's.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m weight_only_fp6_amd.build_lib` "

@@ -336,17 +336,23 @@ int launch_gemm(const void* X, const void* W, const void* S, void* Y, int64_t M,
   const int64_t mgroups = (M + 16 * MB - 1) / (16 * MB);
   // Keep each launch below 2^24 workgroups.
   const int64_t per_mg = nquads * splits;
-  int64_t mg_chunk = (int64_t(1) << 24) / per_mg;
+  int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
   if (mg_chunk < 1) mg_chunk = 1;
   for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
     const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(fp6_gemm_stream<MB>), grid, dim3(256), 0, stream,
-                       static_cast<const _Float16*>(X), static_cast<const u32x4*>(W),
-                       static_cast<const _Float16*>(S), static_cast<_Float16*>(Y),
-                       ws ? static_cast<float4v*>(ws->part) : nullptr,
-                       ws ? ws->counters : nullptr, M, N, K, splits, mg0);
-    if (hipGetLastError() != hipSuccess) return FP6_E_HIP;
+    const _Float16* x = static_cast<const _Float16*>(X);
+    const u32x4* w = static_cast<const u32x4*>(W);
+    const _Float16* sc = static_cast<const _Float16*>(S);
+    _Float16* y = static_cast<_Float16*>(Y);
+    float4v* part = ws ? static_cast<float4v*>(ws->part) : nullptr;
+    unsigned* cnt = ws ? ws->counters : nullptr;
+    int64_t mg_base = mg0;
+    void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
+    // The launch's own status (not the thread's sticky last error).
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_stream<MB>), grid, dim3(256), args, 0,
+                        stream) != hipSuccess)
+      return FP6_E_HIP;
   }
   return FP6_OK;
 }
@@ -356,6 +362,12 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
   int st = check_linear_args(X, W, S, Y, M, N, K);
   if (st != FP6_OK || M == 0) return st;
   if (variant < 0 || variant > 2 || splits < 0 || splits > (K >> 8) || splits > 4096)
+    return FP6_E_VALUE;
+  // One launch covers at least one m-group: its workgroup count must stay
+  // below 2^24 (so that blocks x 256 threads fits in 32 bits).  Automatic
+  // plans only split when there are fewer row blocks than ~8 waves per CU, far
+  // inside this bound.
+  if (splits > 0 && ((N >> 4) + 3) / 4 * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
     return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
@@ -396,10 +408,14 @@ int fp6_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, 
     return FP6_E_ALIGN;
   const int64_t tiles = (N >> 4) * (K >> 8);
   const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
-  hipLaunchKernelGGL(fp6_dequant_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(packed_W), static_cast<const _Float16*>(scales),
-                     static_cast<_Float16*>(W16), N, K);
-  return hipGetLastError() == hipSuccess ? FP6_OK : FP6_E_HIP;
+  const u32x4* w = static_cast<const u32x4*>(packed_W);
+  const _Float16* sc = static_cast<const _Float16*>(scales);
+  _Float16* out = static_cast<_Float16*>(W16);
+  void* args[] = {&w, &sc, &out, &N, &K};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_dequant_kernel), grid, dim3(256), args, 0,
+                         static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FP6_OK
+             : FP6_E_HIP;
 }
 
 int fp6_release(void) {
