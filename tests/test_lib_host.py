@@ -163,7 +163,7 @@ def test_linear_and_dequant_argument_errors_before_any_hip_call():
     assert L.fp6_linear(A, A, A + 1, A, 4, 16, 256, None) == 3
     assert L.fp6_linear(A, A, A, A + 2, 4, 16, 256, None) == 3
     # plan parameters
-    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 3, 0, None) == 8
+    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 99, 0, None) == 8
     assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 0, 2, None) == 8   # 2 splits > 1 k-tile
     assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 0, -1, None) == 8
     # dequant

@@ -115,35 +115,118 @@ __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Streaming fused kernel.  Work unit = (m-group, row block nb, K-split).
-// A workgroup holds 4 waves = 4 consecutive row blocks with the same m-group
-// and split (they read the same X slice).  MB = number of 16-column m-blocks
-// per wave (the A fragment is reused MB times).
+// Split-K fix-up.  Every split of a work unit stores its fp32 accumulators
+// with device-scope (sc1) stores, waits for them to complete, then bumps the
+// unit's counter with a device-scope atomic.  The split that sees count
+// splits-1 is the last one: it reads the other partials with device-scope
+// loads, sums all splits in split order (deterministic), and resets the
+// counter for the next call.  Device-scope accesses keep the partials
+// coherent across the XCDs' L2 caches without any whole-cache write-back or
+// invalidate (which agent-scope fences would issue in every wave).
+// Partial layout: [unit][split][acc i][component c][lane] floats, so each
+// store instruction writes 256 contiguous bytes.
 // ---------------------------------------------------------------------------
+template <int NACC>
+__device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __restrict__ unit_part,
+                                             unsigned* __restrict__ counter, int split, int splits,
+                                             int lane) {
+  float* mine = unit_part + static_cast<int64_t>(split) * NACC * 256 + lane;
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      __hip_atomic_store(mine + (i * 4 + c) * 64, acc[i][c], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
+  unsigned prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != static_cast<unsigned>(splits - 1)) return false;
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) {
+    float4v sum = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; ++s) {
+      if (s == split) {
+        sum += acc[i];
+      } else {
+        const float* src = unit_part + (static_cast<int64_t>(s) * NACC + i) * 256 + lane;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sum[c] += __hip_atomic_load(src + c * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    acc[i] = sum;
+  }
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Store one 16x16 accumulator block (Y^T layout: lane holds Y[m][n0+4g .. +3]).
+__device__ __forceinline__ void store_y_block(_Float16* __restrict__ Y, const float4v& v, int64_t m,
+                                              int64_t M, int64_t N, int64_t n0, int g) {
+  if (m >= M) return;
+  half4v o;
+  o[0] = static_cast<_Float16>(v[0]);
+  o[1] = static_cast<_Float16>(v[1]);
+  o[2] = static_cast<_Float16>(v[2]);
+  o[3] = static_cast<_Float16>(v[3]);
+  *reinterpret_cast<half4v*>(Y + m * N + n0 + 4 * g) = o;
+}
+
+// ---------------------------------------------------------------------------
+// Streaming fused kernel (memory-bound regime).
+// Work unit = (m-group of 16*MB columns, row group of A row blocks, K-split).
+// A workgroup holds 4 waves = 4 consecutive row groups with the same m-group
+// and split, so they read the same X slice (L1/L2 reuse).  Each wave keeps a
+// ring of D packed tiles per row block in flight (3 x 16 B per lane per tile)
+// and the X fragments of the next tile, splices each k-step once and reuses
+// it for MB MFMAs; each X fragment is reused for A row blocks.
+// ---------------------------------------------------------------------------
+template <int A, int MB>
+struct WStage {
+  u32x4 q2[A], q4a[A], q4b[A];
+};
+
 template <int MB>
+struct XStage {
+  half8v b[8][MB];
+};
+
+template <int A, int MB, int D>
 __global__ __launch_bounds__(256) void fp6_gemm_stream(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
-    const _Float16* __restrict__ scales, _Float16* __restrict__ Y,
-    float4v* __restrict__ part, unsigned* __restrict__ counters,
-    int64_t M, int64_t N, int64_t K, int splits, int64_t mg_base) {
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
+    int64_t mg_base) {
+  static_assert(D % 2 == 0, "X double buffer indexes by parity");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
-  const int64_t nquads = (nblocks + 3) >> 2;
+  const int64_t ngroups = (nblocks + A - 1) / A;
+  const int64_t gquads = (ngroups + 3) >> 2;
   int64_t b = blockIdx.x;
   const int split = static_cast<int>(b % splits);
   b /= splits;
-  const int64_t nq = b % nquads;
-  const int64_t mg = b / nquads + mg_base;
-  const int64_t nb = nq * 4 + wave;
-  if (nb >= nblocks) return;
+  const int64_t gq = b % gquads;
+  const int64_t mg = b / gquads + mg_base;
+  const int64_t rg = gq * 4 + wave;
+  if (rg >= ngroups) return;
   const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
   const int r = lane & 15, g = lane >> 4;
 
-  const half2v s2 = row_scale2(scales, nb * 16 + r);
-
-  // B operand rows: m = mg*16*MB + mb*16 + r, k = kt*256 + 32*j + 8*g.  Rows
-  // m >= M read row M-1 instead: they only feed accumulator columns that are
-  // never stored, so no masking is needed in the loop.
+  // Row blocks of this wave; a ragged last group repeats the last block and
+  // drops its result.
+  const u32x4* w[A];
+  half2v s2[A];
+#pragma unroll
+  for (int a = 0; a < A; ++a) {
+    int64_t nb = rg * A + a;
+    if (nb >= nblocks) nb = nblocks - 1;
+    w[a] = wp + (nb * ktiles) * kTileWords + lane;
+    s2[a] = row_scale2(scales, nb * 16 + r);
+  }
+  // B operand rows m = (mg*MB + mb)*16 + r; rows >= M read row M-1 (their
+  // accumulator columns are never stored).
   const _Float16* xrow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -152,87 +235,82 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
     xrow[mb] = X + m * K + 8 * g;
   }
 
-  float4v acc[MB];
+  float4v acc[A * MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < A * MB; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  const u32x4* w = wp + (nb * ktiles) * kTileWords + lane;
-  auto tile_mac = [&](int64_t kt, const u32x4& q2, const u32x4& q4a, const u32x4& q4b) {
-    half8v xb[8][MB];
+  auto load_w = [&](WStage<A, MB>& st, int64_t kt) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int a = 0; a < A; ++a) {
+      st.q2[a] = w[a][kt * kTileWords];
+      st.q4a[a] = w[a][kt * kTileWords + 64];
+      st.q4b[a] = w[a][kt * kTileWords + 128];
+    }
+  };
+  auto load_x = [&](XStage<MB>& xs, int64_t kt) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        xb[j][mb] = *reinterpret_cast<const half8v*>(xrow[mb] + kt * 256 + 32 * j);
-    }
-#define FP6_STEP(J)                                                              \
-  {                                                                              \
-    const half8v a = splice_tile_step<J>(q2, q4a, q4b, s2);                      \
-    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) acc[mb] =                  \
-        __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb[J][mb], acc[mb], 0, 0, 0);  \
+        xs.b[j][mb] = *reinterpret_cast<const half8v*>(xrow[mb] + kt * 256 + 32 * j);
+  };
+  auto mac = [&](const WStage<A, MB>& st, const XStage<MB>& xs) {
+#define FP6_STEP(J)                                                                   \
+  _Pragma("unroll") for (int a = 0; a < A; ++a) {                                     \
+    const half8v av = splice_tile_step<J>(st.q2[a], st.q4a[a], st.q4b[a], s2[a]);     \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) acc[a * MB + mb] =              \
+        __builtin_amdgcn_mfma_f32_16x16x32_f16(av, xs.b[J][mb], acc[a * MB + mb], 0, 0, 0); \
   }
     FP6_STEP(0) FP6_STEP(1) FP6_STEP(2) FP6_STEP(3)
     FP6_STEP(4) FP6_STEP(5) FP6_STEP(6) FP6_STEP(7)
 #undef FP6_STEP
   };
-  if (kt0 < kt1) {
-    u32x4 q2 = w[kt0 * kTileWords];
-    u32x4 q4a = w[kt0 * kTileWords + 64];
-    u32x4 q4b = w[kt0 * kTileWords + 128];
-    for (int64_t kt = kt0; kt + 1 < kt1; ++kt) {
-      const u32x4 n2 = w[(kt + 1) * kTileWords];
-      const u32x4 n4a = w[(kt + 1) * kTileWords + 64];
-      const u32x4 n4b = w[(kt + 1) * kTileWords + 128];
-      tile_mac(kt, q2, q4a, q4b);
-      q2 = n2;
-      q4a = n4a;
-      q4b = n4b;
+
+  // Steady state: a branch-free loop over groups of D tiles, every load
+  // issued unconditionally (tile index clamped to the unit's last tile; the
+  // few extra loads at the end hit in cache).  The loads in flight are then
+  // the same on every path, so the in-order vmcnt waits only ever wait for
+  // the stage being consumed.  The last (< D) tiles run in an explicit tail.
+  WStage<A, MB> ring[D];
+  XStage<MB> xs[2];
+  const int64_t klast = kt1 > kt0 ? kt1 - 1 : kt0;
+  auto clampk = [&](int64_t t) { return t < klast ? t : klast; };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_w(ring[d], clampk(kt0 + d));
+  load_x(xs[0], clampk(kt0));
+  int64_t kt = kt0;
+  for (; kt + D <= kt1; kt += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int64_t t = kt + d;
+      load_x(xs[(d + 1) & 1], clampk(t + 1));
+      mac(ring[d], xs[d & 1]);
+      load_w(ring[d], clampk(t + D));
     }
-    tile_mac(kt1 - 1, q2, q4a, q4b);
+  }
+  // Tail: tiles kt .. kt1-1 sit in ring[0 .. kt1-kt-1]; xs[0] holds X(kt).
+  const int64_t rem = kt1 - kt;
+#pragma unroll
+  for (int d = 0; d + 1 < D; ++d) {
+    if (d < rem) {
+      load_x(xs[(d + 1) & 1], clampk(kt + d + 1));
+      mac(ring[d], xs[d & 1]);
+    }
   }
 
-  // acc[mb][v] = Y[m = (mg*MB+mb)*16 + r][n = nb*16 + 4*g + v]
-  if (splits == 1) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int64_t m = (mg * MB + mb) * 16 + r;
-      if (m < M) {
-        half4v o;
-        o[0] = static_cast<_Float16>(acc[mb][0]);
-        o[1] = static_cast<_Float16>(acc[mb][1]);
-        o[2] = static_cast<_Float16>(acc[mb][2]);
-        o[3] = static_cast<_Float16>(acc[mb][3]);
-        *reinterpret_cast<half4v*>(Y + m * N + nb * 16 + 4 * g) = o;
-      }
-    }
-    return;
+  if (splits > 1) {
+    const int64_t unit = mg * ngroups + rg;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (A * MB * 256);
+    if (!splitk_fixup<A * MB>(acc, unit_part, counters + unit, split, splits, lane)) return;
   }
-
-  const int64_t tile = mg * nblocks + nb;  // one counter per (m-group, row block)
-  float4v* mypart = part + (tile * splits) * (MB * kWaveSize) + lane;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) mypart[split * MB * kWaveSize + mb * kWaveSize] = acc[mb];
-  __threadfence();
-  unsigned prev = 0;
-  if (lane == 0) prev = atomicAdd(counters + tile, 1u);
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  if (prev != static_cast<unsigned>(splits - 1)) return;
-  __threadfence();
+  for (int a = 0; a < A; ++a) {
+    const int64_t nb = rg * A + a;
+    if (nb >= nblocks) continue;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    float4v sum = mypart[mb * kWaveSize];
-    for (int s = 1; s < splits; ++s) sum += mypart[s * MB * kWaveSize + mb * kWaveSize];
-    const int64_t m = (mg * MB + mb) * 16 + r;
-    if (m < M) {
-      half4v o;
-      o[0] = static_cast<_Float16>(sum[0]);
-      o[1] = static_cast<_Float16>(sum[1]);
-      o[2] = static_cast<_Float16>(sum[2]);
-      o[3] = static_cast<_Float16>(sum[3]);
-      *reinterpret_cast<half4v*>(Y + m * N + nb * 16 + 4 * g) = o;
-    }
+    for (int mb = 0; mb < MB; ++mb)
+      store_y_block(Y, acc[a * MB + mb], (mg * MB + mb) * 16 + r, M, N, nb * 16, g);
   }
-  if (lane == 0) counters[tile] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -304,24 +382,45 @@ int check_linear_args(const void* X, const void* W, const void* s, void* Y, int6
   return FP6_OK;
 }
 
-struct Plan {
-  int mb;      // m-blocks of 16 per wave (1 or 4)
-  int splits;  // K-splits
+// Kernel configurations reachable through fp6_linear_plan's `variant`.
+struct KernelCfg {
+  int a, mb, d;
 };
+constexpr KernelCfg kCfgs[] = {
+    {0, 0, 0},  // 0: automatic
+    {1, 1, 4},  // 1: streaming, 1 row block per wave, 16 columns, ring depth 4
+    {1, 4, 2},  // 2: streaming, 1 row block per wave, 64 columns, ring depth 2
+    {2, 1, 4},  // 3: streaming, 2 row blocks per wave, 16 columns, ring depth 4
+    {4, 1, 2},  // 4: streaming, 4 row blocks per wave, 16 columns, ring depth 2
+};
+constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
+
+struct Plan {
+  int variant;
+  int splits;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
   Plan p;
-  p.mb = (variant == 1) ? 1 : (variant == 2 ? 4 : (M <= 16 ? 1 : 4));
-  const int64_t ktiles = K >> 8, nblocks = N >> 4;
-  const int64_t mgroups = (M + 16 * p.mb - 1) / (16 * p.mb);
+  if (variant == 0) {
+    if (M <= 4) p.variant = 1;
+    else if (M <= 16) p.variant = 3;
+    else p.variant = 2;
+  } else {
+    p.variant = variant;
+  }
+  const KernelCfg& c = kCfgs[p.variant];
+  const int64_t ktiles = K >> 8;
+  const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
   if (splits > 0) {
     p.splits = splits;
     return p;
   }
   // Aim for ~8 waves per CU so every CU has enough loads in flight.
   const int64_t target = static_cast<int64_t>(cus) * 8;
-  const int64_t units = mgroups * nblocks;
-  int64_t s = (target + units - 1) / units;
+  int64_t s = ceil_div(target, units);
   if (s > ktiles) s = ktiles;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -329,29 +428,29 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
   return p;
 }
 
-template <int MB>
-int launch_gemm(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                int64_t K, int splits, Workspace* ws, hipStream_t stream) {
-  const int64_t nblocks = N >> 4, nquads = (nblocks + 3) >> 2;
-  const int64_t mgroups = (M + 16 * MB - 1) / (16 * MB);
+template <int A, int MB, int D>
+int launch_stream(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                  int64_t K, int splits, Workspace* ws, hipStream_t stream) {
+  const int64_t ngroups = ceil_div(N >> 4, A), gquads = ceil_div(ngroups, 4);
+  const int64_t mgroups = ceil_div(M, 16 * MB);
   // Keep each launch below 2^24 workgroups.
-  const int64_t per_mg = nquads * splits;
+  const int64_t per_mg = gquads * splits;
   int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
   if (mg_chunk < 1) mg_chunk = 1;
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  float* part = ws ? static_cast<float*>(ws->part) : nullptr;
+  unsigned* cnt = ws ? ws->counters : nullptr;
   for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
     const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
-    const _Float16* x = static_cast<const _Float16*>(X);
-    const u32x4* w = static_cast<const u32x4*>(W);
-    const _Float16* sc = static_cast<const _Float16*>(S);
-    _Float16* y = static_cast<_Float16*>(Y);
-    float4v* part = ws ? static_cast<float4v*>(ws->part) : nullptr;
-    unsigned* cnt = ws ? ws->counters : nullptr;
     int64_t mg_base = mg0;
     void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
     // The launch's own status (not the thread's sticky last error).
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_stream<MB>), grid, dim3(256), args, 0,
-                        stream) != hipSuccess)
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_stream<A, MB, D>), grid, dim3(256),
+                        args, 0, stream) != hipSuccess)
       return FP6_E_HIP;
   }
   return FP6_OK;
@@ -361,29 +460,34 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
                 int64_t K, int variant, int splits, void* stream) {
   int st = check_linear_args(X, W, S, Y, M, N, K);
   if (st != FP6_OK || M == 0) return st;
-  if (variant < 0 || variant > 2 || splits < 0 || splits > (K >> 8) || splits > 4096)
+  if (variant < 0 || variant >= kNumVariants || splits < 0 || splits > (K >> 8) || splits > 4096)
     return FP6_E_VALUE;
   // One launch covers at least one m-group: its workgroup count must stay
   // below 2^24 (so that blocks x 256 threads fits in 32 bits).  Automatic
-  // plans only split when there are fewer row blocks than ~8 waves per CU, far
+  // plans only split when there are fewer units than ~8 waves per CU, far
   // inside this bound.
-  if (splits > 0 && ((N >> 4) + 3) / 4 * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
+  if (splits > 0 && ceil_div(N >> 4, 4) * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
     return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const Plan p = choose_plan(M, N, K, device_cus(dev), variant, splits);
+  const KernelCfg& c = kCfgs[p.variant];
   Workspace* ws = nullptr;
   if (p.splits > 1) {
-    const int64_t nblocks = N >> 4;
-    const int64_t mgroups = (M + 16 * p.mb - 1) / (16 * p.mb);
-    const size_t part_bytes = static_cast<size_t>(mgroups * nblocks) * p.splits * p.mb * kWaveSize *
-                              sizeof(float4v);
-    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(mgroups * nblocks), &ws);
+    const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
+    const size_t part_bytes =
+        static_cast<size_t>(units) * p.splits * c.a * c.mb * 256 * sizeof(float);
+    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
     if (st != FP6_OK) return st;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.mb == 1) return launch_gemm<1>(X, W, S, Y, M, N, K, p.splits, ws, s);
-  return launch_gemm<4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+  switch (p.variant) {
+    case 1: return launch_stream<1, 1, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 2: return launch_stream<1, 4, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 3: return launch_stream<2, 1, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 4: return launch_stream<4, 1, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    default: return FP6_E_VALUE;
+  }
 }
 
 }  // namespace
