@@ -26,6 +26,9 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import weight_only_fp6_amd as fp6  # noqa: E402
 
 DEV = torch.device("cuda:0")
+# Kernel configurations of fp6_linear_plan: 0 = automatic, 1-4 streaming,
+# 5-6 tiled.
+ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6)
 
 
 def _bits16(t):
@@ -129,7 +132,7 @@ def test_linear_small_shapes_ragged_m(M, NK):
     N, K = NK
     p = Prepared(M, N, K, seed_w=N * 7 + K, seed_x=M * 11 + 1)
     X, packed, s = p.to_device()
-    for variant in (0, 1, 2):
+    for variant in ALL_VARIANTS:
         Y = fp6.linear_plan(X, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
@@ -141,7 +144,7 @@ def test_linear_forced_splits_long_k(splits):
     shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
     p = _prep(shp.name, None)
     X, packed, s = p.to_device()
-    for variant in (1, 2):
+    for variant in (1, 3, 5, 6):
         Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(splits, variant))
@@ -155,7 +158,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     X[np.arange(16), ks] = 1.0
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
-    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3)]:
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         got = Y.cpu().numpy().astype(np.float64)

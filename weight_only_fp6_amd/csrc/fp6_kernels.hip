@@ -29,6 +29,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <type_traits>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -314,6 +315,159 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 }
 
 // ---------------------------------------------------------------------------
+// Tiled fused kernel (compute-bound regime, M > 16).
+// Workgroup = 4 waves; tile = 256 weight rows (each wave 4 row blocks = 64
+// rows) x BM = 16*B columns of X.  Every weight is spliced once per
+// workgroup and reused for B MFMAs; every X fragment (16 columns x 32 k) is
+// read from LDS and reused for the wave's 4 row blocks.  X is staged in LDS in
+// half-tiles (BM x 128 k, two buffers, one barrier per half-tile), with rows
+// XOR-swizzled in 16-byte units so both the staging writes and the B-fragment
+// reads are free of bank conflicts.  The packed weights of the next k-tile
+// sit in registers while the current one is consumed.
+// ---------------------------------------------------------------------------
+constexpr int kTA = 4;  // row blocks per wave in the tiled kernel
+
+template <int B>
+__global__ __launch_bounds__(256) void fp6_gemm_tiled(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
+    int64_t mg_base) {
+  constexpr int BM = 16 * B;
+  constexpr int kHalfUnits = BM * 16;             // 16-byte units per X half-tile buffer
+  constexpr int kLoadsPerThread = kHalfUnits / 256;
+  __shared__ __attribute__((aligned(16))) half8v xs_lds[2][kHalfUnits];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
+  int64_t bidx = blockIdx.x;
+  const int split = static_cast<int>(bidx % splits);
+  bidx /= splits;
+  const int64_t nt = bidx % ntiles;
+  const int64_t mg = bidx / ntiles + mg_base;
+  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t m0 = mg * BM;
+
+  // Weights: this wave's 4 row blocks (ragged N: repeat the last block).
+  const u32x4* w[kTA];
+  half2v s2[kTA];
+#pragma unroll
+  for (int a = 0; a < kTA; ++a) {
+    int64_t nb = nt * 16 + wave * kTA + a;
+    if (nb >= nblocks) nb = nblocks - 1;
+    w[a] = wp + (nb * ktiles) * kTileWords + lane;
+    s2[a] = row_scale2(scales, nb * 16 + r);
+  }
+
+  // X staging: thread tid moves units q = i*256 + tid, i < kLoadsPerThread;
+  // unit q = (row mm = q/16, chunk c = q%16) holds X[m0+mm][k + 8c .. 8c+7]
+  // and is stored at LDS unit mm*16 + (c ^ (mm & 15)).
+  const _Float16* xsrc[kLoadsPerThread];
+  int xdst[kLoadsPerThread];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int q = i * 256 + tid, mm = q >> 4, c = q & 15;
+    int64_t m = m0 + mm;
+    if (m >= M) m = M - 1;
+    xsrc[i] = X + m * K + 8 * c;
+    xdst[i] = mm * 16 + (c ^ (mm & 15));
+  }
+  half8v xstage[kLoadsPerThread];
+  auto gload_x = [&](int64_t h) {  // half-tile h: k-tile h>>1, k-steps 4*(h&1)..+3
+    const int64_t koff = (h >> 1) * 256 + (h & 1) * 128;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i)
+      xstage[i] = *reinterpret_cast<const half8v*>(xsrc[i] + koff);
+  };
+  auto swrite_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) xs_lds[buf][xdst[i]] = xstage[i];
+  };
+
+  float4v acc[kTA * B];
+#pragma unroll
+  for (int i = 0; i < kTA * B; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  WStage<kTA, 1> wcur, wnext;
+  auto load_w = [&](WStage<kTA, 1>& st, int64_t kt) {
+#pragma unroll
+    for (int a = 0; a < kTA; ++a) {
+      st.q2[a] = w[a][kt * kTileWords];
+      st.q4a[a] = w[a][kt * kTileWords + 64];
+      st.q4b[a] = w[a][kt * kTileWords + 128];
+    }
+  };
+
+  // One k-step: 4 A fragments (spliced once) x B fragments (from LDS).
+  auto kstep = [&](const half8v* buf, int jj, auto JC) {
+    constexpr int J = decltype(JC)::value;
+    half8v bf[B];
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) {
+      const int mm = bi * 16 + r, c = 4 * jj + g;
+      bf[bi] = buf[mm * 16 + (c ^ (mm & 15))];
+    }
+#pragma unroll
+    for (int a = 0; a < kTA; ++a) {
+      const half8v av = splice_tile_step<J>(wcur.q2[a], wcur.q4a[a], wcur.q4b[a], s2[a]);
+#pragma unroll
+      for (int bi = 0; bi < B; ++bi)
+        acc[a * B + bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bf[bi], acc[a * B + bi], 0, 0, 0);
+    }
+  };
+
+  // Branch-free pipeline (all prefetch indices clamped to the split's last
+  // half-tile / k-tile, so every path has the same loads in flight).
+  const int64_t h0 = 2 * kt0, h1 = 2 * kt1;  // half-tiles of this split
+  if (h0 < h1) {
+    auto clamph = [&](int64_t h) { return h < h1 - 1 ? h : h1 - 1; };
+    auto clampk = [&](int64_t t) { return t < kt1 - 1 ? t : kt1 - 1; };
+    load_w(wcur, kt0);
+    gload_x(h0);
+    swrite_x(0);
+    gload_x(h0 + 1);
+    __syncthreads();
+    for (int64_t h = h0; h < h1; h += 2) {
+      // half 0 of k-tile h/2: stage X(h+1) into buffer 1, prefetch X(h+2)
+      // and the next k-tile's weights, compute from buffer 0.
+      swrite_x(1);
+      gload_x(clamph(h + 2));
+      load_w(wnext, clampk((h >> 1) + 1));
+      kstep(xs_lds[0], 0, std::integral_constant<int, 0>{});
+      kstep(xs_lds[0], 1, std::integral_constant<int, 1>{});
+      kstep(xs_lds[0], 2, std::integral_constant<int, 2>{});
+      kstep(xs_lds[0], 3, std::integral_constant<int, 3>{});
+      __syncthreads();
+      // half 1: stage X(h+2) into buffer 0, prefetch X(h+3), compute buffer 1.
+      swrite_x(0);
+      gload_x(clamph(h + 3));
+      kstep(xs_lds[1], 0, std::integral_constant<int, 4>{});
+      kstep(xs_lds[1], 1, std::integral_constant<int, 5>{});
+      kstep(xs_lds[1], 2, std::integral_constant<int, 6>{});
+      kstep(xs_lds[1], 3, std::integral_constant<int, 7>{});
+      __syncthreads();
+      wcur = wnext;
+    }
+  }
+
+  if (splits > 1) {
+    const int64_t unit = (mg * ntiles + nt) * 4 + wave;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (kTA * B * 256);
+    if (!splitk_fixup<kTA * B>(acc, unit_part, counters + unit, split, splits, lane)) return;
+  }
+#pragma unroll
+  for (int a = 0; a < kTA; ++a) {
+    const int64_t nb = nt * 16 + wave * kTA + a;
+    if (nb >= nblocks) continue;
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi)
+      store_y_block(Y, acc[a * B + bi], m0 + bi * 16 + r, M, N, nb * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host: workspace per (device, stream), CU count per device.
 // ---------------------------------------------------------------------------
 struct Workspace {
@@ -383,15 +537,19 @@ int check_linear_args(const void* X, const void* W, const void* s, void* Y, int6
 }
 
 // Kernel configurations reachable through fp6_linear_plan's `variant`.
+enum class Kind { kAuto, kStream, kTiled };
 struct KernelCfg {
-  int a, mb, d;
+  Kind kind;
+  int a, mb, d;  // stream: row blocks/wave, 16-col blocks/wave, ring depth; tiled: B = mb
 };
 constexpr KernelCfg kCfgs[] = {
-    {0, 0, 0},  // 0: automatic
-    {1, 1, 4},  // 1: streaming, 1 row block per wave, 16 columns, ring depth 4
-    {1, 4, 2},  // 2: streaming, 1 row block per wave, 64 columns, ring depth 2
-    {2, 1, 4},  // 3: streaming, 2 row blocks per wave, 16 columns, ring depth 4
-    {4, 1, 2},  // 4: streaming, 4 row blocks per wave, 16 columns, ring depth 2
+    {Kind::kAuto, 0, 0, 0},    // 0: automatic
+    {Kind::kStream, 1, 1, 4},  // 1: streaming, 1 row block per wave, 16 columns, ring depth 4
+    {Kind::kStream, 1, 4, 2},  // 2: streaming, 1 row block per wave, 64 columns, ring depth 2
+    {Kind::kStream, 2, 1, 4},  // 3: streaming, 2 row blocks per wave, 16 columns, ring depth 4
+    {Kind::kStream, 4, 1, 2},  // 4: streaming, 4 row blocks per wave, 16 columns, ring depth 2
+    {Kind::kTiled, 4, 4, 0},   // 5: tiled, 256 rows x 64 columns per workgroup
+    {Kind::kTiled, 4, 8, 0},   // 6: tiled, 256 rows x 128 columns per workgroup
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -402,26 +560,47 @@ struct Plan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Work units (each with its own split-K counter) and the number of partial
+// floats per unit and split.
+void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats) {
+  if (c.kind == Kind::kTiled) {
+    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16) * 4;
+    *floats = static_cast<int64_t>(kTA) * c.mb * 256;
+  } else {
+    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
+    *floats = static_cast<int64_t>(c.a) * c.mb * 256;
+  }
+}
+
 Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
   Plan p;
   if (variant == 0) {
     if (M <= 4) p.variant = 1;
     else if (M <= 16) p.variant = 3;
-    else p.variant = 2;
+    else if (M <= 64) p.variant = 5;
+    else p.variant = 6;
   } else {
     p.variant = variant;
   }
   const KernelCfg& c = kCfgs[p.variant];
   const int64_t ktiles = K >> 8;
-  const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
   if (splits > 0) {
     p.splits = splits;
     return p;
   }
-  // Aim for ~8 waves per CU so every CU has enough loads in flight.
-  const int64_t target = static_cast<int64_t>(cus) * 8;
-  int64_t s = ceil_div(target, units);
-  if (s > ktiles) s = ktiles;
+  int64_t s;
+  if (c.kind == Kind::kTiled) {
+    // One 4-wave workgroup per CU: split K until the workgroups cover the CUs,
+    // keeping at least 2 k-tiles per split.
+    const int64_t wgs = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16);
+    s = ceil_div(cus, wgs);
+    if (s > ktiles / 2) s = ktiles / 2;
+  } else {
+    // Aim for ~8 waves per CU so every CU has enough loads in flight.
+    const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
+    s = ceil_div(static_cast<int64_t>(cus) * 8, units);
+    if (s > ktiles) s = ktiles;
+  }
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   p.splits = static_cast<int>(s);
@@ -456,6 +635,32 @@ int launch_stream(const void* X, const void* W, const void* S, void* Y, int64_t 
   return FP6_OK;
 }
 
+template <int B>
+int launch_tiled(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                 int64_t K, int splits, Workspace* ws, hipStream_t stream) {
+  const int64_t ntiles = ceil_div(N >> 4, 16);
+  const int64_t mgroups = ceil_div(M, 16 * B);
+  const int64_t per_mg = ntiles * splits;
+  int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
+  if (mg_chunk < 1) mg_chunk = 1;
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  float* part = ws ? static_cast<float*>(ws->part) : nullptr;
+  unsigned* cnt = ws ? ws->counters : nullptr;
+  for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
+    const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
+    const dim3 grid(static_cast<unsigned>(nmg * per_mg));
+    int64_t mg_base = mg0;
+    void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_tiled<B>), grid, dim3(256), args, 0,
+                        stream) != hipSuccess)
+      return FP6_E_HIP;
+  }
+  return FP6_OK;
+}
+
 int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                 int64_t K, int variant, int splits, void* stream) {
   int st = check_linear_args(X, W, S, Y, M, N, K);
@@ -474,9 +679,9 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
   const KernelCfg& c = kCfgs[p.variant];
   Workspace* ws = nullptr;
   if (p.splits > 1) {
-    const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
-    const size_t part_bytes =
-        static_cast<size_t>(units) * p.splits * c.a * c.mb * 256 * sizeof(float);
+    int64_t units = 0, floats = 0;
+    plan_units(c, M, N, &units, &floats);
+    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
     st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
     if (st != FP6_OK) return st;
   }
@@ -486,6 +691,8 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
     case 2: return launch_stream<1, 4, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 3: return launch_stream<2, 1, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 4: return launch_stream<4, 1, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 5: return launch_tiled<4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 6: return launch_tiled<8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     default: return FP6_E_VALUE;
   }
 }
