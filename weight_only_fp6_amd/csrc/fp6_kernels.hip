@@ -319,13 +319,32 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 // Workgroup = 4 waves; tile = 256 weight rows (each wave 4 row blocks = 64
 // rows) x BM = 16*B columns of X.  Every weight is spliced once per
 // workgroup and reused for B MFMAs; every X fragment (16 columns x 32 k) is
-// read from LDS and reused for the wave's 4 row blocks.  X is staged in LDS in
-// half-tiles (BM x 128 k, two buffers, one barrier per half-tile), with rows
-// XOR-swizzled in 16-byte units so both the staging writes and the B-fragment
-// reads are free of bank conflicts.  The packed weights of the next k-tile
-// sit in registers while the current one is consumed.
+// read from LDS and reused for the wave's 4 row blocks.
+// Pipeline per half-tile h (128 k = 4 k-steps):
+//   * X(h+1) is copied global -> LDS by direct LDS loads (no registers) into
+//     the buffer freed by the previous barrier; rows are XOR-swizzled in
+//     16-byte units (on the global side, since the LDS side of a direct load
+//     is linear) so the B-fragment reads are free of bank conflicts;
+//   * the packed weight words of half-tile h+1 are loaded into registers;
+//   * the 4*B MFMAs of k-step J run while the A fragments of k-step J+1 are
+//     spliced and its B fragments read (sched_group_barrier interleaves one
+//     MFMA with three VALU ops);
+//   * each wave waits for its own direct loads, then one barrier.
 // ---------------------------------------------------------------------------
 constexpr int kTA = 4;  // row blocks per wave in the tiled kernel
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct WHalf {           // packed words of one half-tile for kTA row blocks
+  u32x2 q2[kTA];         // 2-bit words for k-steps 4h'..4h'+3 (two words)
+  u32x4 q4[kTA];         // 4-bit words, one per k-step
+};
+
+template <int JJ>
+__device__ __forceinline__ void splice_half(half8v (&dst)[kTA], const WHalf& w, const half2v (&s2)[kTA]) {
+#pragma unroll
+  for (int a = 0; a < kTA; ++a) dst[a] = splice_kstep<JJ & 1>(w.q2[a][JJ >> 1], w.q4[a][JJ], s2[a]);
+}
 
 template <int B>
 __global__ __launch_bounds__(256) void fp6_gemm_tiled(
@@ -336,7 +355,8 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
   constexpr int BM = 16 * B;
   constexpr int kHalfUnits = BM * 16;             // 16-byte units per X half-tile buffer
   constexpr int kLoadsPerThread = kHalfUnits / 256;
-  __shared__ __attribute__((aligned(16))) half8v xs_lds[2][kHalfUnits];
+  __shared__ __attribute__((aligned(16))) half8v xbuf0[kHalfUnits];
+  __shared__ __attribute__((aligned(16))) half8v xbuf1[kHalfUnits];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
@@ -360,95 +380,107 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
     w[a] = wp + (nb * ktiles) * kTileWords + lane;
     s2[a] = row_scale2(scales, nb * 16 + r);
   }
+  auto load_wh = [&](WHalf& st, int64_t h) {  // half-tile h: k-tile h>>1, half h&1
+    const int64_t kt = h >> 1;
+    const int hh = static_cast<int>(h & 1);
+#pragma unroll
+    for (int a = 0; a < kTA; ++a) {
+      st.q2[a] = reinterpret_cast<const u32x2*>(w[a] + kt * kTileWords)[hh];
+      st.q4[a] = w[a][kt * kTileWords + 64 + 64 * hh];
+    }
+  };
 
-  // X staging: thread tid moves units q = i*256 + tid, i < kLoadsPerThread;
-  // unit q = (row mm = q/16, chunk c = q%16) holds X[m0+mm][k + 8c .. 8c+7]
-  // and is stored at LDS unit mm*16 + (c ^ (mm & 15)).
+  // X direct loads: instruction i of this wave fills LDS units
+  // [i*256 + wave*64, +64) linearly; unit u = (row mm = u/16, slot c' = u%16)
+  // receives global chunk c = c' ^ (mm & 15) of X row m0+mm.
   const _Float16* xsrc[kLoadsPerThread];
-  int xdst[kLoadsPerThread];
 #pragma unroll
   for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int q = i * 256 + tid, mm = q >> 4, c = q & 15;
+    const int u = i * 256 + tid, mm = u >> 4, c = (u & 15) ^ (mm & 15);
     int64_t m = m0 + mm;
     if (m >= M) m = M - 1;
     xsrc[i] = X + m * K + 8 * c;
-    xdst[i] = mm * 16 + (c ^ (mm & 15));
   }
-  half8v xstage[kLoadsPerThread];
-  auto gload_x = [&](int64_t h) {  // half-tile h: k-tile h>>1, k-steps 4*(h&1)..+3
+  auto dma_x = [&](half8v* buf, int64_t h) {
     const int64_t koff = (h >> 1) * 256 + (h & 1) * 128;
 #pragma unroll
     for (int i = 0; i < kLoadsPerThread; ++i)
-      xstage[i] = *reinterpret_cast<const half8v*>(xsrc[i] + koff);
-  };
-  auto swrite_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) xs_lds[buf][xdst[i]] = xstage[i];
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(xsrc[i] + koff),
+          reinterpret_cast<__attribute__((address_space(3))) void*>(
+              reinterpret_cast<uintptr_t>(buf + i * 256 + wave * 64)),
+          16, 0, 0);
   };
 
   float4v acc[kTA * B];
 #pragma unroll
   for (int i = 0; i < kTA * B; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  WStage<kTA, 1> wcur, wnext;
-  auto load_w = [&](WStage<kTA, 1>& st, int64_t kt) {
-#pragma unroll
-    for (int a = 0; a < kTA; ++a) {
-      st.q2[a] = w[a][kt * kTileWords];
-      st.q4a[a] = w[a][kt * kTileWords + 64];
-      st.q4b[a] = w[a][kt * kTileWords + 128];
-    }
-  };
-
-  // One k-step: 4 A fragments (spliced once) x B fragments (from LDS).
-  auto kstep = [&](const half8v* buf, int jj, auto JC) {
-    constexpr int J = decltype(JC)::value;
-    half8v bf[B];
+  half8v afr[2][kTA];
+  half8v bfr[2][B];
+  auto read_b = [&](half8v (&bf)[B], const half8v* buf, int jj) {
 #pragma unroll
     for (int bi = 0; bi < B; ++bi) {
       const int mm = bi * 16 + r, c = 4 * jj + g;
       bf[bi] = buf[mm * 16 + (c ^ (mm & 15))];
     }
+  };
+  auto mfmas = [&](const half8v (&av)[kTA], const half8v (&bf)[B]) {
 #pragma unroll
-    for (int a = 0; a < kTA; ++a) {
-      const half8v av = splice_tile_step<J>(wcur.q2[a], wcur.q4a[a], wcur.q4b[a], s2[a]);
+    for (int a = 0; a < kTA; ++a)
 #pragma unroll
       for (int bi = 0; bi < B; ++bi)
-        acc[a * B + bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bf[bi], acc[a * B + bi], 0, 0, 0);
+        acc[a * B + bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[a], bf[bi], acc[a * B + bi], 0, 0, 0);
+  };
+  auto interleave = [&](auto NDS) {
+    constexpr int nds = decltype(NDS)::value;
+    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);
+#pragma unroll
+    for (int i = 0; i < kTA * B; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using IB = std::integral_constant<int, B>;
+  // Wait for this wave's direct LDS loads of the next half-tile (issued
+  // before the kTA*2 weight loads of that half-tile), then the barrier makes
+  // every wave's copy visible.
+  constexpr int kWLoads = kTA * 2;
+  constexpr int kWaitDma = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (7 << 4) | (15 << 8);
 
-  // Branch-free pipeline (all prefetch indices clamped to the split's last
-  // half-tile / k-tile, so every path has the same loads in flight).
+  // One half-tile: k-steps 0..3 from buffer `cur`; prefetch X(h+1) into
+  // `nxt` and the weights of h+1 into `wn`; overlap the last k-step with the
+  // splice of h+1's first k-step.
+  auto half_step = [&](half8v* cur, half8v* nxt, const WHalf& wc, WHalf& wn, int64_t hnext) {
+    dma_x(nxt, hnext);
+    __builtin_amdgcn_sched_barrier(0);
+    load_wh(wn, hnext);
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(bfr[0], cur, 0);
+    read_b(bfr[1], cur, 1); splice_half<1>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
+    read_b(bfr[0], cur, 2); splice_half<2>(afr[0], wc, s2); mfmas(afr[1], bfr[1]); interleave(IB{});
+    read_b(bfr[1], cur, 3); splice_half<3>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
+                            splice_half<0>(afr[0], wn, s2); mfmas(afr[1], bfr[1]); interleave(I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitDma);
+    __syncthreads();
+  };
+
   const int64_t h0 = 2 * kt0, h1 = 2 * kt1;  // half-tiles of this split
   if (h0 < h1) {
+    // Branch-free steady state: prefetch indices are clamped to the split's
+    // last half-tile, so every path has the same loads in flight.
     auto clamph = [&](int64_t h) { return h < h1 - 1 ? h : h1 - 1; };
-    auto clampk = [&](int64_t t) { return t < kt1 - 1 ? t : kt1 - 1; };
-    load_w(wcur, kt0);
-    gload_x(h0);
-    swrite_x(0);
-    gload_x(h0 + 1);
+    WHalf wa, wb;
+    dma_x(xbuf0, h0);
+    load_wh(wa, h0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    splice_half<0>(afr[0], wa, s2);
     for (int64_t h = h0; h < h1; h += 2) {
-      // half 0 of k-tile h/2: stage X(h+1) into buffer 1, prefetch X(h+2)
-      // and the next k-tile's weights, compute from buffer 0.
-      swrite_x(1);
-      gload_x(clamph(h + 2));
-      load_w(wnext, clampk((h >> 1) + 1));
-      kstep(xs_lds[0], 0, std::integral_constant<int, 0>{});
-      kstep(xs_lds[0], 1, std::integral_constant<int, 1>{});
-      kstep(xs_lds[0], 2, std::integral_constant<int, 2>{});
-      kstep(xs_lds[0], 3, std::integral_constant<int, 3>{});
-      __syncthreads();
-      // half 1: stage X(h+2) into buffer 0, prefetch X(h+3), compute buffer 1.
-      swrite_x(0);
-      gload_x(clamph(h + 3));
-      kstep(xs_lds[1], 0, std::integral_constant<int, 4>{});
-      kstep(xs_lds[1], 1, std::integral_constant<int, 5>{});
-      kstep(xs_lds[1], 2, std::integral_constant<int, 6>{});
-      kstep(xs_lds[1], 3, std::integral_constant<int, 7>{});
-      __syncthreads();
-      wcur = wnext;
+      half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));
+      half_step(xbuf1, xbuf0, wb, wa, clamph(h + 2));
     }
   }
 
