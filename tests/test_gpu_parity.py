@@ -26,9 +26,10 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import weight_only_fp6_amd as fp6  # noqa: E402
 
 DEV = torch.device("cuda:0")
-# Kernel configurations of fp6_linear_plan: 0 = automatic, 1-4 streaming,
-# 5-6 tiled.
-ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6)
+# Kernel configurations of fp6_linear_plan: 0 = automatic, 1-4 and 7-8
+# streaming, 5-6 tiled, 9 k-split persistent (M <= 16, K <= 8192 only).
+ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8)
+KSPLIT = 9
 
 
 def _bits16(t):
@@ -132,7 +133,7 @@ def test_linear_small_shapes_ragged_m(M, NK):
     N, K = NK
     p = Prepared(M, N, K, seed_w=N * 7 + K, seed_x=M * 11 + 1)
     X, packed, s = p.to_device()
-    for variant in ALL_VARIANTS:
+    for variant in ALL_VARIANTS + ((KSPLIT,) if M <= 16 else ()):
         Y = fp6.linear_plan(X, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
@@ -150,6 +151,19 @@ def test_linear_forced_splits_long_k(splits):
         _assert_tol(Y, p.y_ref, what=(splits, variant))
 
 
+@pytest.mark.parametrize("K", [256, 512, 1280, 2048, 4096, 6144, 8192])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_linear_ksplit_k_coverage(M, K):
+    # the k-split kernel at every per-wave tile count (1..4, ragged ranges),
+    # with more row blocks than workgroups (N = 16 * 300 > 256 CUs)
+    N = 16 * 300
+    p = Prepared(M, N, K, seed_w=K + M, seed_x=K * 3 + M, sample=64)
+    X, packed, s = p.to_device()
+    Y = fp6.linear_plan(X, packed, s, N, K, variant=KSPLIT)
+    torch.cuda.synchronize()
+    _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(M, K))
+
+
 def test_linear_one_hot_reproduces_wdq_exactly():
     N, K = 64, 1024
     p = Prepared(16, N, K, seed_w=99, seed_x=1)
@@ -158,7 +172,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     X[np.arange(16), ks] = 1.0
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
-    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2)]:
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         got = Y.cpu().numpy().astype(np.float64)

@@ -315,6 +315,105 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 }
 
 // ---------------------------------------------------------------------------
+// K-split persistent kernel (memory-bound regime, M <= 16, K <= 8*KTW*256).
+// One workgroup of 8 waves per CU.  Wave w owns the k-tiles
+// [w*KT/8, (w+1)*KT/8) for the whole kernel, so its X fragments (16 columns x
+// at most KTW k-tiles) are loaded once into registers.  The workgroup walks
+// the row blocks nb = blockIdx.x, +gridDim.x, ...; for each, every wave
+// multiplies its k-slice (packed tiles prefetched one row block ahead) and
+// the 8 partial 16x16 tiles are summed through LDS in wave order
+// (deterministic) by wave 0, which stores fp16 Y.  No global workspace, no
+// X re-reads, all 8 k-slices of a row block stream concurrently.
+// ---------------------------------------------------------------------------
+constexpr int kKsWaves = 8;
+
+template <int KTW>
+__global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
+    int64_t K) {
+  __shared__ float4v red[2][kKsWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kw0 = wave * ktiles / kKsWaves, kw1 = (wave + 1) * ktiles / kKsWaves;
+  const int ktw = static_cast<int>(kw1 - kw0);  // 0..KTW tiles for this wave
+  // Tile indices clamped into the wave's range (or tile 0 for an empty
+  // range): clamped slots are loaded but never multiplied.
+  auto tile_of = [&](int t) -> int64_t {
+    if (ktw == 0) return 0;
+    return kw0 + (t < ktw ? t : ktw - 1);
+  };
+
+  // X fragments for this wave's k-slice; rows m >= M read row M-1 (their
+  // accumulator columns are never stored).
+  const int64_t m = r < M ? r : M - 1;
+  half8v xf[KTW][8];
+#pragma unroll
+  for (int t = 0; t < KTW; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      xf[t][j] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 256 + 32 * j + 8 * g);
+
+  WStage<1, 1> wst[2][KTW];
+  auto load_rb = [&](WStage<1, 1> (&st)[KTW], int64_t nb) {
+    const u32x4* base = wp + (nb * ktiles) * kTileWords + lane;
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      const int64_t kt = tile_of(t);
+      st[t].q2[0] = base[kt * kTileWords];
+      st[t].q4a[0] = base[kt * kTileWords + 64];
+      st[t].q4b[0] = base[kt * kTileWords + 128];
+    }
+  };
+  auto rb_mac = [&](const WStage<1, 1> (&st)[KTW], int64_t nb) {
+    const half2v s2 = row_scale2(scales, nb * 16 + r);
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      if (t < ktw) {
+#define FP6_KS_STEP(J)                                                                     \
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                            \
+      splice_tile_step<J>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[t][J], acc, 0, 0, 0);
+        FP6_KS_STEP(0) FP6_KS_STEP(1) FP6_KS_STEP(2) FP6_KS_STEP(3)
+        FP6_KS_STEP(4) FP6_KS_STEP(5) FP6_KS_STEP(6) FP6_KS_STEP(7)
+#undef FP6_KS_STEP
+      }
+    }
+    return acc;
+  };
+  auto reduce_store = [&](const float4v& acc, int buf, int64_t nb) {
+    red[buf][wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      float4v sum = red[buf][0][lane];
+#pragma unroll
+      for (int w = 1; w < kKsWaves; ++w) sum += red[buf][w][lane];
+      store_y_block(Y, sum, r, M, N, nb * 16, g);
+    }
+  };
+
+  const int64_t stride = gridDim.x;
+  int64_t nb = blockIdx.x;
+  if (nb >= nblocks) return;  // uniform for the workgroup
+  load_rb(wst[0], nb);
+  // Two row blocks per iteration so the register double buffer is static.
+  // The partial-tile buffers alternate too: a buffer is rewritten only after
+  // the next barrier, by which time wave 0 has finished reading it.
+  while (true) {
+    int64_t nb1 = nb + stride;
+    load_rb(wst[1], nb1 < nblocks ? nb1 : nb);
+    reduce_store(rb_mac(wst[0], nb), 0, nb);
+    if (nb1 >= nblocks) break;
+    int64_t nb2 = nb1 + stride;
+    load_rb(wst[0], nb2 < nblocks ? nb2 : nb1);
+    reduce_store(rb_mac(wst[1], nb1), 1, nb1);
+    if (nb2 >= nblocks) break;
+    nb = nb2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled fused kernel (compute-bound regime, M > 16).
 // Workgroup = 4 waves; tile = 256 weight rows (each wave 4 row blocks = 64
 // rows) x BM = 16*B columns of X.  Every weight is spliced once per
@@ -569,7 +668,7 @@ int check_linear_args(const void* X, const void* W, const void* s, void* Y, int6
 }
 
 // Kernel configurations reachable through fp6_linear_plan's `variant`.
-enum class Kind { kAuto, kStream, kTiled };
+enum class Kind { kAuto, kStream, kTiled, kKsplit };
 struct KernelCfg {
   Kind kind;
   int a, mb, d;  // stream: row blocks/wave, 16-col blocks/wave, ring depth; tiled: B = mb
@@ -582,6 +681,9 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kStream, 4, 1, 2},  // 4: streaming, 4 row blocks per wave, 16 columns, ring depth 2
     {Kind::kTiled, 4, 4, 0},   // 5: tiled, 256 rows x 64 columns per workgroup
     {Kind::kTiled, 4, 8, 0},   // 6: tiled, 256 rows x 128 columns per workgroup
+    {Kind::kStream, 1, 1, 8},  // 7: streaming, 1 row block per wave, 16 columns, ring depth 8
+    {Kind::kStream, 2, 1, 6},  // 8: streaming, 2 row blocks per wave, 16 columns, ring depth 6
+    {Kind::kKsplit, 1, 1, 0},  // 9: k-split persistent, M <= 16, K <= 8192 (X in registers)
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -591,6 +693,35 @@ struct Plan {
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kKsMaxKtw = 4;  // k-split kernel: at most 4 k-tiles per wave (K <= 8192)
+
+template <int KTW>
+int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                    int64_t K, int cus, hipStream_t stream) {
+  const int64_t nblocks = N >> 4;
+  const dim3 grid(static_cast<unsigned>(nblocks < cus ? nblocks : cus));
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_ksplit<KTW>), grid,
+                         dim3(64 * kKsWaves), args, 0, stream) == hipSuccess
+             ? FP6_OK
+             : FP6_E_HIP;
+}
+
+int launch_ksplit(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                  int64_t K, int cus, hipStream_t stream) {
+  switch (ceil_div(K >> 8, kKsWaves)) {
+    case 1: return launch_ksplit_t<1>(X, W, S, Y, M, N, K, cus, stream);
+    case 2: return launch_ksplit_t<2>(X, W, S, Y, M, N, K, cus, stream);
+    case 3: return launch_ksplit_t<3>(X, W, S, Y, M, N, K, cus, stream);
+    case 4: return launch_ksplit_t<4>(X, W, S, Y, M, N, K, cus, stream);
+    default: return FP6_E_VALUE;
+  }
+}
 
 // Work units (each with its own split-K counter) and the number of partial
 // floats per unit and split.
@@ -606,16 +737,24 @@ void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_
 
 Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
   Plan p;
+  const int64_t ktiles = K >> 8;
   if (variant == 0) {
-    if (M <= 4) p.variant = 1;
-    else if (M <= 16) p.variant = 3;
+    // Measured on MI355X: the k-split kernel wins while each wave holds at
+    // most 2 k-tiles (K <= 4096); beyond that the 2-row-block streaming
+    // kernel (ring depth 4 for M <= 4, 6 for M <= 16) is faster.
+    if (M <= 16 && ktiles <= kKsWaves * 2) p.variant = 9;
+    else if (M <= 4) p.variant = 3;
+    else if (M <= 16) p.variant = 8;
     else if (M <= 64) p.variant = 5;
     else p.variant = 6;
   } else {
     p.variant = variant;
   }
   const KernelCfg& c = kCfgs[p.variant];
-  const int64_t ktiles = K >> 8;
+  if (c.kind == Kind::kKsplit) {
+    p.splits = 1;
+    return p;
+  }
   if (splits > 0) {
     p.splits = splits;
     return p;
@@ -705,9 +844,15 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
   // inside this bound.
   if (splits > 0 && ceil_div(N >> 4, 4) * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
     return FP6_E_VALUE;
+  // The k-split kernel keeps each wave's X slice in registers: M <= 16 and
+  // at most kKsMaxKtw k-tiles per wave; it never splits across workgroups.
+  if (variant > 0 && kCfgs[variant].kind == Kind::kKsplit &&
+      (M > 16 || (K >> 8) > kKsWaves * kKsMaxKtw || splits > 1))
+    return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
-  const Plan p = choose_plan(M, N, K, device_cus(dev), variant, splits);
+  const int cus = device_cus(dev);
+  const Plan p = choose_plan(M, N, K, cus, variant, splits);
   const KernelCfg& c = kCfgs[p.variant];
   Workspace* ws = nullptr;
   if (p.splits > 1) {
@@ -725,6 +870,9 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
     case 4: return launch_stream<4, 1, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 5: return launch_tiled<4>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 6: return launch_tiled<8>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 7: return launch_stream<1, 1, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 8: return launch_stream<2, 1, 6>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 9: return launch_ksplit(X, W, S, Y, M, N, K, cus, s);
     default: return FP6_E_VALUE;
   }
 }
