@@ -3,36 +3,51 @@
 
 One step = one fused ``fp6_linear`` call (de-quantise + fp16 MFMA GEMM) over
 one batch of synthetic activations, with the packed weights already resident
-in HBM.  Weight copies are rotated so every call streams from HBM rather than
-the 256 MB Infinity Cache.  The timed steps are replayed from a HIP graph
-(captured from plain library launches on torch's current stream), bracketed
-by torch.cuda.synchronize(); HIP events on the same stream give the average
-launch duration.
+in HBM.  Weight copies are rotated (>= 1 GiB in all) so every call streams
+from HBM rather than the 256 MB Infinity Cache.  The timed steps are replayed
+from a HIP graph captured from plain library launches on a side stream and
+bracketed by torch.cuda.synchronize(); HIP events recorded on that stream give
+the average launch duration.
 
 Default workload: the Llama-7B attention projection, M=1 (decode GEMV),
 N=4096, K=4096.  ``--workload`` selects another shape of
-weight_only_fp6_amd.synth.SHAPES.
+weight_only_fp6_amd.synth.SHAPES.  Prints ONE JSON line.
 
-Prints ONE JSON line.  The CPU baseline is the plain oracle (NumPy), timed on
-this host on a bounded sample of the same workload.
+Also reported, as context:
+* ``cpu_baseline``: the plain NumPy oracle timed on this host on a bounded
+  sample of the same workload (a baseline, not a target);
+* ``fp16_blas``: the same layer as an fp16 torch linear (hipBLASLt) on
+  de-quantised weights, with rotated cold copies -- the W16A16 reference the
+  FP6-LLM pages normalise their kernel speedups to;
+* ``read_ceiling_gbs``: a plain streaming-read probe over a buffer of the
+  packed-weight size (the practical HBM ceiling at this size).
+
+Helper modes for the committed rocprofv3 summaries (see the profile files for
+the exact commands): ``--calibrate-copy`` runs a torch copy of a known size so
+FETCH_SIZE/WRITE_SIZE can be scaled to bytes; ``--summarize DIR`` turns the
+rocprofv3 CSV outputs in DIR into a short text summary.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
 import sys
 import time
 
-import numpy as np
-
+ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "W6A16 GEMM TFLOP/s + weight HBM GB/s (% of peak), Llama-shaped layers M=1..128"
 DEFAULT_WORKLOAD = "llama7b_attn_1x4096x4096"
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
-ROT_BYTES = 1 << 30            # >= 1 GiB of rotated weight copies (> 256 MB MALL)
+ROT_BYTES = 1 << 30             # >= 1 GiB of rotated copies (> 256 MB Infinity Cache)
+COPY_BYTES = 1 << 30            # --calibrate-copy: bytes read (and written) per copy
+KERNEL_SRC = os.path.join(ROOT, "weight_only_fp6_amd", "csrc", "fp6_kernels.hip")
 
 
 def _parse():
@@ -43,9 +58,19 @@ def _parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-graph", action="store_true", help="time direct launches instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", type=int, default=0, help="force kernel variant (0 = auto)")
-    ap.add_argument("--splits", type=int, default=0, help="force K-splits (0 = auto)")
+    ap.add_argument("--no-context", action="store_true", help="skip the fp16 BLAS and read-probe context numbers")
+    ap.add_argument("--variant", type=int, default=0, help="force kernel variant (0 = automatic)")
+    ap.add_argument("--splits", type=int, default=0, help="force K-splits (0 = automatic)")
+    ap.add_argument("--calibrate-copy", action="store_true", help="run a known-size torch copy and exit")
+    ap.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 CSVs under DIR and exit")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc runs into a traffic summary for --workload and exit")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def algorithmic_bytes(M, N, K):
@@ -53,60 +78,216 @@ def algorithmic_bytes(M, N, K):
     return N * K * 3 // 4 + 2 * N + 2 * M * K + 2 * M * N
 
 
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, on a bounded row sample.
+# ---------------------------------------------------------------------------
 def cpu_baseline(shape, packed, scales, X, budget_s=20.0):
-    """Time the oracle (unpack + dequant + fp64 GEMM) on a bounded row sample."""
     import oracle
     from threadpoolctl import threadpool_limits
     with threadpool_limits(limits=1):
-        return _cpu_baseline(oracle, shape, packed, scales, X, budget_s)
+        M, N, K = shape.M, shape.N, shape.K
+        row_bytes = 16 * K * 3 // 4                     # one packed row block
 
-
-def _cpu_baseline(oracle, shape, packed, scales, X, budget_s):
-    M, N, K = shape.M, shape.N, shape.K
-    # rows in multiples of 16 (one packed row block = 16 rows x K)
-    row_bytes = 16 * K * 3 // 4
-    rows16 = max(1, min(N // 16, (16 * 2**20) // row_bytes))   # start with <= ~16 MB
-    def run(nblk):
-        nrows = 16 * nblk
-        part = packed[: nblk * row_bytes]
-        t0 = time.perf_counter()
-        codes = oracle.unpack_np(part, nrows, K)
-        wdq = oracle.dequant_ref(codes, scales[:nrows])
-        oracle.gemm_ref(X, wdq)
-        return time.perf_counter() - t0
-    t = run(rows16)
-    # grow or shrink the sample to about budget_s / 3 per run, then median of 3
-    target = budget_s / 3
-    scale = target / max(t, 1e-3)
-    rows16 = int(max(1, min(N // 16, rows16 * scale)))
-    ts = sorted(run(rows16) for _ in range(3))
-    tmed = ts[1]
-    nrows = 16 * rows16
+        def run(nblk):
+            t0 = time.perf_counter()
+            codes = oracle.unpack_np(packed[: nblk * row_bytes], 16 * nblk, K)
+            wdq = oracle.dequant_ref(codes, scales[: 16 * nblk])
+            oracle.gemm_ref(X, wdq)
+            return time.perf_counter() - t0
+        nblk = max(1, min(N // 16, (4 * 2**20) // row_bytes))
+        t = run(nblk)
+        nblk = int(max(1, min(N // 16, nblk * (budget_s / 3) / max(t, 1e-3))))
+        ts = sorted(run(nblk) for _ in range(3))
+        tmed = ts[1]
+    nrows = 16 * nblk
     wbytes = nrows * K * 3 // 4
     return {
         "value": round(wbytes / tmed / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{nrows} of {N} weight rows x K={K}, M={M}: unpack_np + dequant_ref + gemm_ref, "
-                  f"median of 3 runs ({tmed:.2f} s each), BLAS limited to 1 thread",
+        "sample": f"{nrows} of {N} weight rows x K={K}, M={M}: oracle.unpack_np + dequant_ref + gemm_ref "
+                  f"(float64), median of 3 runs of {tmed:.2f} s, single thread (BLAS limited to 1)",
         "tflops": round(2.0 * M * nrows * K / tmed / 1e12, 6),
     }
 
 
+# ---------------------------------------------------------------------------
+# Traffic from committed counter summaries (only while the kernel source is
+# the one the counters were taken with).
+# ---------------------------------------------------------------------------
+def committed_traffic(workload):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return {"bytes_per_launch": float(vals["hbm_bytes_per_launch"]),
+                "fetch_bytes": float(vals["fetch_bytes_per_launch"]),
+                "write_bytes": float(vals["write_bytes_per_launch"])}
+    except KeyError:
+        return None
+
+
+def _time_graph(torch, stream, launch, n):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n   # microseconds per launch
+
+
+def fp16_blas_context(torch, fp6, stream, pk, sc, x, M, N, K):
+    """fp16 torch linear (hipBLASLt) on the de-quantised weights, cold copies."""
+    W16 = fp6.dequant(pk, sc, N, K, stream=stream)
+    torch.cuda.synchronize()
+    R = int(min(32, max(2, math.ceil(ROT_BYTES / (2 * N * K)))))
+    ws = [W16.clone() for _ in range(R)]
+    ys = [torch.empty((M, N), dtype=torch.float16, device=x.device) for _ in range(R)]
+
+    def launch(i):
+        torch.matmul(x, ws[i % R].t(), out=ys[i % R])
+    launch(0)
+    torch.cuda.synchronize()
+    us = _time_graph(torch, stream, launch, 200)
+    del ws, ys, W16
+    return us
+
+
+def read_ceiling(torch, nbytes, stream):
+    """Plain streaming read of a buffer of nbytes, rotated over >= 1 GiB."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_fp6_amd", "libfp6probe.so"))
+    lib.fp6probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    nbytes = (nbytes // 1024) * 1024
+    R = int(min(64, max(2, math.ceil(ROT_BYTES / nbytes))))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    best = None
+    for per_wave in (8, 32):
+        def launch(i):
+            if lib.fp6probe_read(bufs[i % R].data_ptr(), nbytes, per_wave, out.data_ptr(), stream.cuda_stream):
+                raise RuntimeError("probe launch failed")
+        launch(0)
+        torch.cuda.synchronize()
+        us = _time_graph(torch, stream, launch, 100)
+        gbs = nbytes / us / 1e3
+        best = gbs if best is None else max(best, gbs)
+    del bufs
+    return best
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+def summarize(directory):
+    lines = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*_kernel_stats.csv"), recursive=True)):
+        lines.append(f"# kernel stats: {os.path.relpath(path, directory)}")
+        lines.append("name | calls | average_ns | min_ns | max_ns | percent")
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                lines.append(f"{r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']):.1f} | "
+                             f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f}")
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*_counter_collection.csv"), recursive=True)):
+        agg = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"][:110], r["Counter_Name"])
+                agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        lines.append(f"# counters: {os.path.relpath(path, directory)}")
+        lines.append("kernel | counter | dispatches | mean_per_dispatch")
+        for (k, c), v in sorted(agg.items()):
+            lines.append(f"{k} | {c} | {len(v)} | {sum(v) / len(v):.1f}")
+    print("\n".join(lines))
+
+
+def _pmc_mean(directory, counter, name_filter):
+    vals = []
+    for path in glob.glob(os.path.join(directory, "**", "*_counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and name_filter(r["Kernel_Name"]):
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples in {directory}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """FETCH_SIZE/WRITE_SIZE (KiB per dispatch) of the fp6 kernel, scaled by
+    what the same counters read for a torch copy of COPY_BYTES."""
+    is_fp6 = lambda n: "fp6_gemm" in n
+    is_copy = lambda n: "fp6" not in n and ("copy" in n.lower() or "elementwise" in n)
+    f_kib, nf = _pmc_mean(fetch_dir, "FETCH_SIZE", is_fp6)
+    w_kib, nw = _pmc_mean(write_dir, "WRITE_SIZE", is_fp6)
+    cf_kib, _ = _pmc_mean(copy_fetch_dir, "FETCH_SIZE", is_copy)
+    cw_kib, _ = _pmc_mean(copy_write_dir, "WRITE_SIZE", is_copy)
+    kf = COPY_BYTES / (cf_kib * 1024)
+    kw = COPY_BYTES / (cw_kib * 1024)
+    fetch = f_kib * 1024 * kf
+    write = w_kib * 1024 * kw
+    print(f"# HBM traffic of the fp6 kernel for workload {workload}")
+    print(f"# FETCH_SIZE {f_kib:.1f} KiB/dispatch over {nf} dispatches, WRITE_SIZE {w_kib:.1f} KiB over {nw};")
+    print(f"# a torch copy of {COPY_BYTES} bytes reads FETCH_SIZE {cf_kib:.1f} KiB and WRITE_SIZE {cw_kib:.1f} KiB,")
+    print(f"# so the counters are scaled by {kf:.4f} (fetch) and {kw:.4f} (write).")
+    print(f"workload = {workload}")
+    print(f"kernel_source_sha256_16 = {kernel_source_hash()}")
+    print(f"fetch_scale = {kf:.6f}")
+    print(f"write_scale = {kw:.6f}")
+    print(f"fetch_bytes_per_launch = {fetch:.0f}")
+    print(f"write_bytes_per_launch = {write:.0f}")
+    print(f"hbm_bytes_per_launch = {fetch + write:.0f}")
+
+
+def calibrate_copy():
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "copies": 5}))
+
+
 def main():
     args = _parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.traffic:
+        traffic_summary(args.workload, *args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     import torch
-    import weight_only_fp6_amd as fp6
-    from weight_only_fp6_amd import synth
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import weight_only_fp6_amd as fp6
+    from weight_only_fp6_amd import synth
+
     if args.workload not in synth.SHAPES:
         print(f"unknown workload {args.workload}; choose from {sorted(synth.SHAPES)}", file=sys.stderr)
         sys.exit(2)
@@ -114,7 +295,7 @@ def main():
     M, N, K = shape.M, shape.N, shape.K
     dev = torch.device("cuda:0")
 
-    # ---- inputs (host quantise + prepack, then upload R rotated copies) ----
+    # ---- inputs: host quantise + prepack, then R rotated device copies ----
     W = synth.weights(N, K, shape.seed_w)
     codes, scales = fp6.quantize_rows(W)
     del W
@@ -133,6 +314,10 @@ def main():
     stream.wait_stream(torch.cuda.current_stream())
     torch.cuda.set_stream(stream)
     sh = stream.cuda_stream
+    if args.variant:
+        variant, splits = args.variant, args.splits
+    else:
+        variant, splits = fp6.plan_query(M, N, K)
 
     def launch(i):
         x, w, s, y = ptrs[i % R]
@@ -175,8 +360,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_s = t1 - t0
-    ev_ms = ev0.elapsed_time(ev1)
-    per_launch_s = ev_ms / 1e3 / args.steps
+    per_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
 
     wbytes = N * K * 3 // 4
     abytes = algorithmic_bytes(M, N, K)
@@ -185,21 +369,25 @@ def main():
     tflops = flops * args.steps / wall_s / 1e12
     # Ridge: 2500 TFLOP/s / 8 TB/s = 312.5 flop/byte; per packed weight byte the
     # layer does 2*M*N*K / (0.75*N*K) = 2.67*M flop, so M < 117 is HBM-bound.
-    hbm_bound = M < 117
-    if hbm_bound:
+    traffic = committed_traffic(args.workload) if not args.variant else None
+    if M < 117:
         achieved = abytes / per_launch_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": round(traffic["bytes_per_launch"]) if traffic else None}
         value, unit = round(weight_gbs, 1), "GB/s"
     else:
         achieved = flops / per_launch_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
+                    "traffic": round(traffic["bytes_per_launch"]) if traffic else None}
         value, unit = round(tflops, 2), "TFLOP/s"
-    roofline["kernel"] = "fp6_gemm_stream"
+    roofline["kernel"] = fp6.KERNEL_NAMES.get(variant, str(variant))
+    roofline["splits"] = splits
     roofline["per_launch_us"] = round(per_launch_s * 1e6, 3)
     roofline["algorithmic_bytes"] = abytes
     roofline["flops"] = flops
+    roofline["traffic_unit"] = "HBM bytes/launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
 
     out = {
         "metric": METRIC,
@@ -217,14 +405,21 @@ def main():
         "config": {"workload": args.workload, "M": M, "N": N, "K": K,
                    "weights": "fp6 e3m2 + fp16 row scale (packed layout v1)",
                    "activations": "fp16", "accumulate": "fp32",
-                   "rotated_weight_copies": R, "graph": not args.no_graph,
-                   "variant": args.variant, "splits": args.splits},
+                   "rotated_weight_copies": R, "graph": not args.no_graph},
         "weight_gbps": round(weight_gbs, 1),
         "weight_hbm_frac": round(weight_gbs / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 3),
         "mfma_frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 5),
         "roofline": roofline,
     }
+    if not args.no_context:
+        blas_us = fp16_blas_context(torch, fp6, stream, pk_d[0], sc_d[0], x_d[0], M, N, K)
+        out["fp16_blas"] = {"kind": "torch.matmul fp16 (hipBLASLt), de-quantised weights, cold copies",
+                            "us": round(blas_us, 3),
+                            "fp6_speedup": round(blas_us / (per_launch_s * 1e6), 3)}
+        ceil_gbs = read_ceiling(torch, wbytes, stream)
+        out["read_ceiling_gbs"] = round(ceil_gbs, 1)
+        out["weight_frac_of_read_ceiling"] = round(wbytes / per_launch_s / 1e9 / ceil_gbs, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, packed, scales, X)
     print(json.dumps(out), flush=True)

@@ -141,15 +141,37 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
 
 /*
  * fp6_linear_plan -- fp6_linear with the schedule forced (tuning and tests).
- * variant: 0 = automatic, 1 = small-M streaming kernel (any M, M-blocks of
- *          16 per pass), 2 = large-M kernel.
- * splits:  0 = automatic, else the number of K-splits (1..K/256).
+ * variant: 0 = automatic (what fp6_linear does), else one kernel
+ *   configuration:
+ *     1  streaming, 1 row block (16 rows) per wave, prefetch ring of 4 tiles
+ *     2  streaming, 1 row block x 64 columns per wave, ring of 2 tiles
+ *     3  streaming, 2 row blocks per wave, ring of 4 tiles
+ *     4  streaming, 4 row blocks per wave, ring of 2 tiles
+ *     5  tiled, 256 rows x 64 columns per 4-wave workgroup (X staged in LDS)
+ *     6  tiled, 256 rows x 128 columns per 4-wave workgroup
+ *     7  streaming, 1 row block per wave, ring of 8 tiles
+ *     8  streaming, 2 row blocks per wave, ring of 6 tiles
+ *     9  k-split persistent: one 8-wave workgroup per CU, waves split K and
+ *        keep their X slice in registers; requires M <= 16, K <= 8192
+ *   Streaming and tiled kernels handle any M (16-column groups per pass).
+ * splits:  0 = automatic, else the number of K-splits across workgroups
+ *          (1..K/256; must be 0 or 1 for variant 9).
  * The result equals fp6_linear's up to fp32 summation order.
- * Errors: as fp6_linear, plus FP6_E_VALUE for an unknown variant or split.
+ * Errors: as fp6_linear, plus FP6_E_VALUE for an unknown variant, a split
+ * count out of range, or a shape variant 9 does not cover.
  */
 int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y,
                     int64_t M, int64_t N, int64_t K, int variant, int splits,
                     void* stream);
+
+/*
+ * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
+ * for (M, N, K) on the current device: *variant (1..9, see fp6_linear_plan)
+ * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
+ * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
+ * >= 1 here), FP6_E_HIP.
+ */
+int fp6_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits);
 
 /*
  * fp6_dequant -- device, asynchronous; test and inspection export.

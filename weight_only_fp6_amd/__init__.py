@@ -34,7 +34,8 @@ STATUS_NAMES = {
 }
 EXPORTED = (
     "fp6_pack_version", "fp6_status_string", "fp6_packed_bytes", "fp6_quantize_rows",
-    "fp6_prepack", "fp6_linear", "fp6_linear_plan", "fp6_dequant", "fp6_release",
+    "fp6_prepack", "fp6_linear", "fp6_linear_plan", "fp6_linear_plan_query", "fp6_dequant",
+    "fp6_release",
 )
 
 
@@ -55,7 +56,7 @@ def _load() -> ctypes.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m weight_only_fp6_amd.build_lib` "
+            f"{LIB_PATH} is not built; run `python weight_only_fp6_amd/build_lib.py` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, sz, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
@@ -67,6 +68,7 @@ def _load() -> ctypes.CDLL:
         "fp6_prepack": ([vp, vp, i64, i64, vp, sz], i32),
         "fp6_linear": ([vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp6_linear_plan": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp], i32),
+        "fp6_linear_plan_query": ([i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "fp6_dequant": ([vp, vp, vp, i64, i64, vp], i32),
         "fp6_release": ([], i32),
     }
@@ -156,6 +158,20 @@ def linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int
                               M, N, K, variant, splits, _stream_handle(stream))
     _check("fp6_linear_plan", st)
     return out
+
+
+KERNEL_NAMES = {
+    1: "fp6_gemm_stream<1,1,4>", 2: "fp6_gemm_stream<1,4,2>", 3: "fp6_gemm_stream<2,1,4>",
+    4: "fp6_gemm_stream<4,1,2>", 5: "fp6_gemm_tiled<4>", 6: "fp6_gemm_tiled<8>",
+    7: "fp6_gemm_stream<1,1,8>", 8: "fp6_gemm_stream<2,1,6>", 9: "fp6_gemm_ksplit",
+}
+
+
+def plan_query(M: int, N: int, K: int):
+    """(variant, splits) that fp6_linear picks for this shape on the current GPU."""
+    v, s = ctypes.c_int(0), ctypes.c_int(0)
+    _check("fp6_linear_plan_query", _lib.fp6_linear_plan_query(M, N, K, ctypes.byref(v), ctypes.byref(s)))
+    return v.value, s.value
 
 
 def dequant(packed, scales, N: int, K: int, out=None, stream=None):

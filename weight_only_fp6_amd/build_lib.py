@@ -2,7 +2,8 @@
 
 Host code (fp6_host.cpp) is compiled with g++ and the kernels plus device
 entry points (fp6_kernels.hip) with hipcc; both are linked into one shared
-library next to this file.  Run ``python -m weight_only_fp6_amd.build_lib``.
+library next to this file.  Run ``python weight_only_fp6_amd/build_lib.py`` (by
+path, so the package -- which loads the library -- is not imported first).
 """
 
 from __future__ import annotations
@@ -18,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp6amd.so")
+PROBE_LIB = os.path.join(PKG, "libfp6probe.so")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -54,6 +56,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, host_o, kern_o], verbose)
     shutil.move(tmp, LIB)
+    # Bandwidth probe used only by the benchmark's roofline measurement.
+    probe_tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", os.path.join(CSRC, "fp6_probe.hip"), "-o", probe_tmp], verbose)
+    shutil.move(probe_tmp, PROBE_LIB)
     return LIB
 
 

@@ -891,6 +891,17 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
   return linear_impl(X, packed_W, scales, Y, M, N, K, variant, splits, stream);
 }
 
+int fp6_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits) {
+  if (!variant || !splits) return FP6_E_NULL;
+  if (!shape_ok(N, K) || M < 1 || M > fp6::kMaxDim) return FP6_E_SHAPE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
+  const Plan p = choose_plan(M, N, K, device_cus(dev), 0, 0);
+  *variant = p.variant;
+  *splits = p.splits;
+  return FP6_OK;
+}
+
 int fp6_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, int64_t K,
                 void* stream) {
   if (!shape_ok(N, K)) return FP6_E_SHAPE;
