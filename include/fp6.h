@@ -153,6 +153,9 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *     8  streaming, 2 row blocks per wave, ring of 6 tiles
  *     9  k-split persistent: one 8-wave workgroup per CU, waves split K and
  *        keep their X slice in registers; requires M <= 16, K <= 8192
+ *    10  tiled, 256 rows x 128 columns per 8-wave workgroup (2 row blocks
+ *        per wave, two waves per SIMD)
+ *    11  tiled, 256 rows x 64 columns per 8-wave workgroup
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
  *          (1..K/256; must be 0 or 1 for variant 9).
@@ -166,7 +169,7 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
 
 /*
  * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
- * for (M, N, K) on the current device: *variant (1..9, see fp6_linear_plan)
+ * for (M, N, K) on the current device: *variant (1..11, see fp6_linear_plan)
  * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
  * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
  * >= 1 here), FP6_E_HIP.

@@ -430,30 +430,34 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 //     MFMA with three VALU ops);
 //   * each wave waits for its own direct loads, then one barrier.
 // ---------------------------------------------------------------------------
-constexpr int kTA = 4;  // row blocks per wave in the tiled kernel
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-struct WHalf {           // packed words of one half-tile for kTA row blocks
-  u32x2 q2[kTA];         // 2-bit words for k-steps 4h'..4h'+3 (two words)
-  u32x4 q4[kTA];         // 4-bit words, one per k-step
+template <int TA>
+struct WHalf {           // packed words of one half-tile for TA row blocks
+  u32x2 q2[TA];          // 2-bit words for k-steps 4h'..4h'+3 (two words)
+  u32x4 q4[TA];          // 4-bit words, one per k-step
 };
 
-template <int JJ>
-__device__ __forceinline__ void splice_half(half8v (&dst)[kTA], const WHalf& w, const half2v (&s2)[kTA]) {
+template <int JJ, int TA>
+__device__ __forceinline__ void splice_half(half8v (&dst)[TA], const WHalf<TA>& w, const half2v (&s2)[TA]) {
 #pragma unroll
-  for (int a = 0; a < kTA; ++a) dst[a] = splice_kstep<JJ & 1>(w.q2[a][JJ >> 1], w.q4[a][JJ], s2[a]);
+  for (int a = 0; a < TA; ++a) dst[a] = splice_kstep<JJ & 1>(w.q2[a][JJ >> 1], w.q4[a][JJ], s2[a]);
 }
 
-template <int B>
-__global__ __launch_bounds__(256) void fp6_gemm_tiled(
+// TA row blocks per wave, NW waves per workgroup, TA * NW = 16 (256 rows).
+template <int B, int TA, int NW>
+__global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
     unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
     int64_t mg_base) {
   constexpr int BM = 16 * B;
   constexpr int kHalfUnits = BM * 16;             // 16-byte units per X half-tile buffer
-  constexpr int kLoadsPerThread = kHalfUnits / 256;
+  constexpr int kTA = TA;
+  constexpr int kThreads = 64 * NW;
+  static_assert(TA * NW == 16, "a workgroup covers 16 row blocks");
+  constexpr int kLoadsPerThread = kHalfUnits / kThreads;
   __shared__ __attribute__((aligned(16))) half8v xbuf0[kHalfUnits];
   __shared__ __attribute__((aligned(16))) half8v xbuf1[kHalfUnits];
 
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
     w[a] = wp + (nb * ktiles) * kTileWords + lane;
     s2[a] = row_scale2(scales, nb * 16 + r);
   }
-  auto load_wh = [&](WHalf& st, int64_t h) {  // half-tile h: k-tile h>>1, half h&1
+  auto load_wh = [&](WHalf<TA>& st, int64_t h) {  // half-tile h: k-tile h>>1, half h&1
     const int64_t kt = h >> 1;
     const int hh = static_cast<int>(h & 1);
 #pragma unroll
@@ -490,12 +494,12 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
   };
 
   // X direct loads: instruction i of this wave fills LDS units
-  // [i*256 + wave*64, +64) linearly; unit u = (row mm = u/16, slot c' = u%16)
-  // receives global chunk c = c' ^ (mm & 15) of X row m0+mm.
+  // [i*kThreads + wave*64, +64) linearly; unit u = (row mm = u/16, slot
+  // c' = u%16) receives global chunk c = c' ^ (mm & 15) of X row m0+mm.
   const _Float16* xsrc[kLoadsPerThread];
 #pragma unroll
   for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int u = i * 256 + tid, mm = u >> 4, c = (u & 15) ^ (mm & 15);
+    const int u = i * kThreads + tid, mm = u >> 4, c = (u & 15) ^ (mm & 15);
     int64_t m = m0 + mm;
     if (m >= M) m = M - 1;
     xsrc[i] = X + m * K + 8 * c;
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
       __builtin_amdgcn_global_load_lds(
           static_cast<const void*>(xsrc[i] + koff),
           reinterpret_cast<__attribute__((address_space(3))) void*>(
-              reinterpret_cast<uintptr_t>(buf + i * 256 + wave * 64)),
+              reinterpret_cast<uintptr_t>(buf + i * kThreads + wave * 64)),
           16, 0, 0);
   };
 
@@ -551,16 +555,16 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
   // One half-tile: k-steps 0..3 from buffer `cur`; prefetch X(h+1) into
   // `nxt` and the weights of h+1 into `wn`; overlap the last k-step with the
   // splice of h+1's first k-step.
-  auto half_step = [&](half8v* cur, half8v* nxt, const WHalf& wc, WHalf& wn, int64_t hnext) {
+  auto half_step = [&](half8v* cur, half8v* nxt, const WHalf<TA>& wc, WHalf<TA>& wn, int64_t hnext) {
     dma_x(nxt, hnext);
     __builtin_amdgcn_sched_barrier(0);
     load_wh(wn, hnext);
     __builtin_amdgcn_sched_barrier(0);
     read_b(bfr[0], cur, 0);
-    read_b(bfr[1], cur, 1); splice_half<1>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
-    read_b(bfr[0], cur, 2); splice_half<2>(afr[0], wc, s2); mfmas(afr[1], bfr[1]); interleave(IB{});
-    read_b(bfr[1], cur, 3); splice_half<3>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
-                            splice_half<0>(afr[0], wn, s2); mfmas(afr[1], bfr[1]); interleave(I0{});
+    read_b(bfr[1], cur, 1); splice_half<1, TA>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
+    read_b(bfr[0], cur, 2); splice_half<2, TA>(afr[0], wc, s2); mfmas(afr[1], bfr[1]); interleave(IB{});
+    read_b(bfr[1], cur, 3); splice_half<3, TA>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
+                            splice_half<0, TA>(afr[0], wn, s2); mfmas(afr[1], bfr[1]); interleave(I0{});
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitDma);
     __syncthreads();
@@ -571,12 +575,12 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
     // Branch-free steady state: prefetch indices are clamped to the split's
     // last half-tile, so every path has the same loads in flight.
     auto clamph = [&](int64_t h) { return h < h1 - 1 ? h : h1 - 1; };
-    WHalf wa, wb;
+    WHalf<TA> wa, wb;
     dma_x(xbuf0, h0);
     load_wh(wa, h0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    splice_half<0>(afr[0], wa, s2);
+    splice_half<0, TA>(afr[0], wa, s2);
     for (int64_t h = h0; h < h1; h += 2) {
       half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));
       half_step(xbuf1, xbuf0, wb, wa, clamph(h + 2));
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_tiled(
   }
 
   if (splits > 1) {
-    const int64_t unit = (mg * ntiles + nt) * 4 + wave;
+    const int64_t unit = (mg * ntiles + nt) * NW + wave;
     float* unit_part = part + unit * static_cast<int64_t>(splits) * (kTA * B * 256);
     if (!splitk_fixup<kTA * B>(acc, unit_part, counters + unit, split, splits, lane)) return;
   }
@@ -679,11 +683,13 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kStream, 1, 4, 2},  // 2: streaming, 1 row block per wave, 64 columns, ring depth 2
     {Kind::kStream, 2, 1, 4},  // 3: streaming, 2 row blocks per wave, 16 columns, ring depth 4
     {Kind::kStream, 4, 1, 2},  // 4: streaming, 4 row blocks per wave, 16 columns, ring depth 2
-    {Kind::kTiled, 4, 4, 0},   // 5: tiled, 256 rows x 64 columns per workgroup
-    {Kind::kTiled, 4, 8, 0},   // 6: tiled, 256 rows x 128 columns per workgroup
+    {Kind::kTiled, 4, 4, 4},   // 5: tiled, 256 rows x 64 columns, 4 waves x 4 row blocks
+    {Kind::kTiled, 4, 8, 4},   // 6: tiled, 256 rows x 128 columns, 4 waves x 4 row blocks
     {Kind::kStream, 1, 1, 8},  // 7: streaming, 1 row block per wave, 16 columns, ring depth 8
     {Kind::kStream, 2, 1, 6},  // 8: streaming, 2 row blocks per wave, 16 columns, ring depth 6
     {Kind::kKsplit, 1, 1, 0},  // 9: k-split persistent, M <= 16, K <= 8192 (X in registers)
+    {Kind::kTiled, 2, 8, 8},   // 10: tiled, 256 rows x 128 columns, 8 waves x 2 row blocks
+    {Kind::kTiled, 2, 4, 8},   // 11: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -727,8 +733,9 @@ int launch_ksplit(const void* X, const void* W, const void* S, void* Y, int64_t 
 // floats per unit and split.
 void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats) {
   if (c.kind == Kind::kTiled) {
-    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16) * 4;
-    *floats = static_cast<int64_t>(kTA) * c.mb * 256;
+    // c.a = row blocks per wave, c.d = waves per workgroup (c.a * c.d = 16)
+    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16) * c.d;
+    *floats = static_cast<int64_t>(c.a) * c.mb * 256;
   } else {
     *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
     *floats = static_cast<int64_t>(c.a) * c.mb * 256;
@@ -745,8 +752,8 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     if (M <= 16 && ktiles <= kKsWaves * 2) p.variant = 9;
     else if (M <= 4) p.variant = 3;
     else if (M <= 16) p.variant = 8;
-    else if (M <= 64) p.variant = 5;
-    else p.variant = 6;
+    else if (M <= 64) p.variant = 11;
+    else p.variant = 10;
   } else {
     p.variant = variant;
   }
@@ -761,10 +768,11 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
   }
   int64_t s;
   if (c.kind == Kind::kTiled) {
-    // One 4-wave workgroup per CU: split K until the workgroups cover the CUs,
-    // keeping at least 2 k-tiles per split.
+    // One workgroup per CU: split K while a whole extra round of workgroups
+    // fits on the CUs (rounding down: a partial second round costs more than
+    // it gains), keeping at least 2 k-tiles per split.
     const int64_t wgs = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16);
-    s = ceil_div(cus, wgs);
+    s = cus / wgs;
     if (s > ktiles / 2) s = ktiles / 2;
   } else {
     // Aim for ~8 waves per CU so every CU has enough loads in flight.
@@ -806,7 +814,7 @@ int launch_stream(const void* X, const void* W, const void* S, void* Y, int64_t 
   return FP6_OK;
 }
 
-template <int B>
+template <int B, int TA, int NW>
 int launch_tiled(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                  int64_t K, int splits, Workspace* ws, hipStream_t stream) {
   const int64_t ntiles = ceil_div(N >> 4, 16);
@@ -825,8 +833,8 @@ int launch_tiled(const void* X, const void* W, const void* S, void* Y, int64_t M
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
     int64_t mg_base = mg0;
     void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_tiled<B>), grid, dim3(256), args, 0,
-                        stream) != hipSuccess)
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_tiled<B, TA, NW>), grid, dim3(64 * NW),
+                        args, 0, stream) != hipSuccess)
       return FP6_E_HIP;
   }
   return FP6_OK;
@@ -868,11 +876,13 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
     case 2: return launch_stream<1, 4, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 3: return launch_stream<2, 1, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 4: return launch_stream<4, 1, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 5: return launch_tiled<4>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 6: return launch_tiled<8>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 5: return launch_tiled<4, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 6: return launch_tiled<8, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 7: return launch_stream<1, 1, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 8: return launch_stream<2, 1, 6>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 9: return launch_ksplit(X, W, S, Y, M, N, K, cus, s);
+    case 10: return launch_tiled<8, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 11: return launch_tiled<4, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     default: return FP6_E_VALUE;
   }
 }
