@@ -163,8 +163,8 @@ def linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int
 KERNEL_NAMES = {
     1: "fp6_gemm_stream<1,1,4>", 2: "fp6_gemm_stream<1,4,2>", 3: "fp6_gemm_stream<2,1,4>",
     4: "fp6_gemm_stream<4,1,2>", 5: "fp6_gemm_tiled<4,4,4>", 6: "fp6_gemm_tiled<8,4,4>",
-    7: "fp6_gemm_stream<1,1,8>", 8: "fp6_gemm_stream<2,1,6>", 9: "fp6_gemm_ksplit",
-    10: "fp6_gemm_tiled<8,2,8>", 11: "fp6_gemm_tiled<4,2,8>",
+    7: "fp6_gemm_stream<1,1,8>", 8: "fp6_gemm_stream<2,1,6>", 9: "fp6_gemm_ksplit<8 waves>",
+    10: "fp6_gemm_tiled<8,2,8>", 11: "fp6_gemm_tiled<4,2,8>", 12: "fp6_gemm_ksplit<16 waves>",
 }
 
 

@@ -315,19 +315,18 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 }
 
 // ---------------------------------------------------------------------------
-// K-split persistent kernel (memory-bound regime, M <= 16, K <= 8*KTW*256).
-// One workgroup of 8 waves per CU.  Wave w owns the k-tiles
-// [w*KT/8, (w+1)*KT/8) for the whole kernel, so its X fragments (16 columns x
+// K-split persistent kernel (memory-bound regime, M <= 16,
+// K <= kKsWaves*KTW*256).  One workgroup of kKsWaves (8 or 16) waves per CU.
+// Wave w owns the k-tiles [w*KT/W, (w+1)*KT/W) (W = kKsWaves) for the whole
+// kernel, so its X fragments (16 columns x
 // at most KTW k-tiles) are loaded once into registers.  The workgroup walks
 // the row blocks nb = blockIdx.x, +gridDim.x, ...; for each, every wave
 // multiplies its k-slice (packed tiles prefetched one row block ahead) and
-// the 8 partial 16x16 tiles are summed through LDS in wave order
+// the partial 16x16 tiles are summed through LDS in wave order
 // (deterministic) by wave 0, which stores fp16 Y.  No global workspace, no
-// X re-reads, all 8 k-slices of a row block stream concurrently.
+// X re-reads, all k-slices of a row block stream concurrently.
 // ---------------------------------------------------------------------------
-constexpr int kKsWaves = 8;
-
-template <int KTW>
+template <int KTW, int kKsWaves>
 __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
@@ -687,9 +686,10 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kTiled, 4, 8, 4},   // 6: tiled, 256 rows x 128 columns, 4 waves x 4 row blocks
     {Kind::kStream, 1, 1, 8},  // 7: streaming, 1 row block per wave, 16 columns, ring depth 8
     {Kind::kStream, 2, 1, 6},  // 8: streaming, 2 row blocks per wave, 16 columns, ring depth 6
-    {Kind::kKsplit, 1, 1, 0},  // 9: k-split persistent, M <= 16, K <= 8192 (X in registers)
+    {Kind::kKsplit, 1, 1, 8},  // 9: k-split persistent, M <= 16, K <= 8192 (X in registers)
     {Kind::kTiled, 2, 8, 8},   // 10: tiled, 256 rows x 128 columns, 8 waves x 2 row blocks
     {Kind::kTiled, 2, 4, 8},   // 11: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks
+    {Kind::kKsplit, 1, 1, 16}, // 12: k-split persistent with 16 waves per workgroup
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -700,9 +700,9 @@ struct Plan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kKsMaxKtw = 4;  // k-split kernel: at most 4 k-tiles per wave (K <= 8192)
+constexpr int kKsMaxTiles = 32;  // k-split kernels: K <= 8192
 
-template <int KTW>
+template <int KTW, int WK>
 int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                     int64_t K, int cus, hipStream_t stream) {
   const int64_t nblocks = N >> 4;
@@ -712,19 +712,23 @@ int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
   void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_ksplit<KTW>), grid,
-                         dim3(64 * kKsWaves), args, 0, stream) == hipSuccess
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_ksplit<KTW, WK>), grid,
+                         dim3(64 * WK), args, 0, stream) == hipSuccess
              ? FP6_OK
              : FP6_E_HIP;
 }
 
+// WK waves per workgroup; each wave holds ceil(K/256 / WK) k-tiles.
+template <int WK>
 int launch_ksplit(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                   int64_t K, int cus, hipStream_t stream) {
-  switch (ceil_div(K >> 8, kKsWaves)) {
-    case 1: return launch_ksplit_t<1>(X, W, S, Y, M, N, K, cus, stream);
-    case 2: return launch_ksplit_t<2>(X, W, S, Y, M, N, K, cus, stream);
-    case 3: return launch_ksplit_t<3>(X, W, S, Y, M, N, K, cus, stream);
-    case 4: return launch_ksplit_t<4>(X, W, S, Y, M, N, K, cus, stream);
+  switch (ceil_div(K >> 8, WK)) {
+    case 1: return launch_ksplit_t<1, WK>(X, W, S, Y, M, N, K, cus, stream);
+    case 2: return launch_ksplit_t<2, WK>(X, W, S, Y, M, N, K, cus, stream);
+    case 3: if constexpr (WK == 8) return launch_ksplit_t<3, WK>(X, W, S, Y, M, N, K, cus, stream);
+            return FP6_E_VALUE;
+    case 4: if constexpr (WK == 8) return launch_ksplit_t<4, WK>(X, W, S, Y, M, N, K, cus, stream);
+            return FP6_E_VALUE;
     default: return FP6_E_VALUE;
   }
 }
@@ -746,10 +750,12 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
   Plan p;
   const int64_t ktiles = K >> 8;
   if (variant == 0) {
-    // Measured on MI355X: the k-split kernel wins while each wave holds at
-    // most 2 k-tiles (K <= 4096); beyond that the 2-row-block streaming
-    // kernel (ring depth 4 for M <= 4, 6 for M <= 16) is faster.
-    if (M <= 16 && ktiles <= kKsWaves * 2) p.variant = 9;
+    // Measured on MI355X: the k-split kernels win while each wave holds one
+    // k-tile (8 waves up to K = 2048, 16 waves up to K = 4096); beyond that
+    // the 2-row-block streaming kernel (ring depth 4 for M <= 4, 6 for
+    // M <= 16) is faster.
+    if (M <= 16 && ktiles <= 8) p.variant = 9;
+    else if (M <= 16 && ktiles <= 16) p.variant = 12;
     else if (M <= 4) p.variant = 3;
     else if (M <= 16) p.variant = 8;
     else if (M <= 64) p.variant = 11;
@@ -853,9 +859,10 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
   if (splits > 0 && ceil_div(N >> 4, 4) * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
     return FP6_E_VALUE;
   // The k-split kernel keeps each wave's X slice in registers: M <= 16 and
-  // at most kKsMaxKtw k-tiles per wave; it never splits across workgroups.
+  // at most K = 8192 (and a per-wave tile count it is instantiated for); it
+  // never splits across workgroups.
   if (variant > 0 && kCfgs[variant].kind == Kind::kKsplit &&
-      (M > 16 || (K >> 8) > kKsWaves * kKsMaxKtw || splits > 1))
+      (M > 16 || (K >> 8) > kKsMaxTiles || splits > 1))
     return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
@@ -880,7 +887,8 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
     case 6: return launch_tiled<8, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 7: return launch_stream<1, 1, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 8: return launch_stream<2, 1, 6>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 9: return launch_ksplit(X, W, S, Y, M, N, K, cus, s);
+    case 9: return launch_ksplit<8>(X, W, S, Y, M, N, K, cus, s);
+    case 12: return launch_ksplit<16>(X, W, S, Y, M, N, K, cus, s);
     case 10: return launch_tiled<8, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 11: return launch_tiled<4, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     default: return FP6_E_VALUE;
