@@ -157,6 +157,9 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *        per wave, two waves per SIMD)
  *    11  tiled, 256 rows x 64 columns per 8-wave workgroup
  *    12  k-split persistent with 16 waves per workgroup (same limits as 9)
+ *    13  k-slice: the waves of a workgroup (8 or 16, by K) split
+ *        one row block's K, X streamed per tile; requires M <= 16,
+ *        K <= 8192
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
  *          (1..K/256; must be 0 or 1 for variant 9).
@@ -170,7 +173,7 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
 
 /*
  * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
- * for (M, N, K) on the current device: *variant (1..12, see fp6_linear_plan)
+ * for (M, N, K) on the current device: *variant (1..13, see fp6_linear_plan)
  * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
  * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
  * >= 1 here), FP6_E_HIP.

@@ -31,6 +31,7 @@ DEV = torch.device("cuda:0")
 ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11)
 KSPLIT = 9
 KSPLIT16 = 12
+KSLICE = 13
 
 
 def _bits16(t):
@@ -134,7 +135,7 @@ def test_linear_small_shapes_ragged_m(M, NK):
     N, K = NK
     p = Prepared(M, N, K, seed_w=N * 7 + K, seed_x=M * 11 + 1)
     X, packed, s = p.to_device()
-    for variant in ALL_VARIANTS + ((KSPLIT, KSPLIT16) if M <= 16 else ()):
+    for variant in ALL_VARIANTS + ((KSPLIT, KSPLIT16, KSLICE) if M <= 16 else ()):
         Y = fp6.linear_plan(X, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
@@ -155,12 +156,12 @@ def test_linear_forced_splits_long_k(splits):
 @pytest.mark.parametrize("K", [256, 512, 1280, 2048, 4096, 6144, 8192])
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_linear_ksplit_k_coverage(M, K):
-    # the k-split kernel at every per-wave tile count (1..4, ragged ranges),
-    # with more row blocks than workgroups (N = 16 * 300 > 256 CUs)
+    # the k-split and k-slice kernels at every per-wave tile count (1..4,
+    # ragged ranges), with more row blocks than workgroups (N = 16*300 > 256)
     N = 16 * 300
     p = Prepared(M, N, K, seed_w=K + M, seed_x=K * 3 + M, sample=64)
     X, packed, s = p.to_device()
-    for variant in (KSPLIT, KSPLIT16):
+    for variant in (KSPLIT, KSPLIT16, KSLICE):
         Y = fp6.linear_plan(X, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
         _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(M, K, variant))
@@ -174,7 +175,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     X[np.arange(16), ks] = 1.0
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
-    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (10, 1), (10, 3), (11, 2)]:
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (KSLICE, 0), (10, 1), (10, 3), (11, 2)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         got = Y.cpu().numpy().astype(np.float64)

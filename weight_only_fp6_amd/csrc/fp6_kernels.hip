@@ -413,6 +413,78 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 }
 
 // ---------------------------------------------------------------------------
+// K-slice kernel (memory-bound regime, M <= 16, few row blocks, long K).
+// Like the k-split kernel, WK waves of a workgroup split the K range of a row
+// block and reduce through LDS, but each wave issues the loads of all its
+// packed tiles at once and streams its X fragments tile by tile (double
+// buffered) instead of keeping them resident: meant for N/16 <= CUs, where a
+// workgroup handles a single row block and X is used once.
+// ---------------------------------------------------------------------------
+template <int KTW, int WK>
+__global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
+    int64_t K) {
+  __shared__ float4v red[WK][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kw0 = wave * ktiles / WK, kw1 = (wave + 1) * ktiles / WK;
+  const int ktw = static_cast<int>(kw1 - kw0);
+  auto tile_of = [&](int t) -> int64_t {
+    if (ktw == 0) return 0;
+    return kw0 + (t < ktw ? t : ktw - 1);
+  };
+  const int64_t m = r < M ? r : M - 1;
+  const _Float16* xrow = X + m * K + 8 * g;
+  auto load_x = [&](half8v (&xf)[8], int t) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      xf[j] = *reinterpret_cast<const half8v*>(xrow + tile_of(t) * 256 + 32 * j);
+  };
+
+  for (int64_t nb = blockIdx.x; nb < nblocks; nb += gridDim.x) {
+    const u32x4* base = wp + (nb * ktiles) * kTileWords + lane;
+    WStage<1, 1> st[KTW];
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      const int64_t kt = tile_of(t);
+      st[t].q2[0] = base[kt * kTileWords];
+      st[t].q4a[0] = base[kt * kTileWords + 64];
+      st[t].q4b[0] = base[kt * kTileWords + 128];
+    }
+    const half2v s2 = row_scale2(scales, nb * 16 + r);
+    half8v xf[2][8];
+    load_x(xf[0], 0);
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      if (t + 1 < KTW) load_x(xf[(t + 1) & 1], t + 1);
+      if (t < ktw) {
+#define FP6_KX_STEP(J)                                                                     \
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                            \
+      splice_tile_step<J>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[t & 1][J], acc, 0, 0, 0);
+        FP6_KX_STEP(0) FP6_KX_STEP(1) FP6_KX_STEP(2) FP6_KX_STEP(3)
+        FP6_KX_STEP(4) FP6_KX_STEP(5) FP6_KX_STEP(6) FP6_KX_STEP(7)
+#undef FP6_KX_STEP
+      }
+      // Keep the X prefetch one tile ahead: without this fence the scheduler
+      // hoists every tile's X loads to the top and runs out of registers.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      float4v sum = red[0][lane];
+#pragma unroll
+      for (int w = 1; w < WK; ++w) sum += red[w][lane];
+      store_y_block(Y, sum, r, M, N, nb * 16, g);
+    }
+    __syncthreads();  // red[] is rewritten by the next row block
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled fused kernel (compute-bound regime, M > 16).
 // Workgroup = 4 waves; tile = 256 weight rows (each wave 4 row blocks = 64
 // rows) x BM = 16*B columns of X.  Every weight is spliced once per
@@ -671,7 +743,7 @@ int check_linear_args(const void* X, const void* W, const void* s, void* Y, int6
 }
 
 // Kernel configurations reachable through fp6_linear_plan's `variant`.
-enum class Kind { kAuto, kStream, kTiled, kKsplit };
+enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice };
 struct KernelCfg {
   Kind kind;
   int a, mb, d;  // stream: row blocks/wave, 16-col blocks/wave, ring depth; tiled: B = mb
@@ -690,6 +762,7 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kTiled, 2, 8, 8},   // 10: tiled, 256 rows x 128 columns, 8 waves x 2 row blocks
     {Kind::kTiled, 2, 4, 8},   // 11: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks
     {Kind::kKsplit, 1, 1, 16}, // 12: k-split persistent with 16 waves per workgroup
+    {Kind::kKslice, 1, 1, 16}, // 13: k-slice, 16 waves per row block, X streamed
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -733,6 +806,36 @@ int launch_ksplit(const void* X, const void* W, const void* S, void* Y, int64_t 
   }
 }
 
+constexpr int kKsliceMaxTiles = 32;  // k-slice kernels: K <= 8192
+
+template <int KTW, int WK>
+int launch_kslice_t(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                    int64_t K, int cus, hipStream_t stream) {
+  const int64_t nblocks = N >> 4;
+  const dim3 grid(static_cast<unsigned>(nblocks < cus ? nblocks : cus));
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_kslice<KTW, WK>), grid, dim3(64 * WK),
+                         args, 0, stream) == hipSuccess
+             ? FP6_OK
+             : FP6_E_HIP;
+}
+
+// One k-tile per wave up to K = 4096 (8 waves up to K = 2048, else 16);
+// beyond, 8 waves (two per SIMD, so up to 256 registers each) with up to 4
+// k-tiles each.
+int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                  int64_t K, int cus, hipStream_t stream) {
+  const int64_t kt = K >> 8;
+  if (kt <= 8) return launch_kslice_t<1, 8>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 16) return launch_kslice_t<1, 16>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 32) return launch_kslice_t<4, 8>(X, W, S, Y, M, N, K, cus, stream);
+  return FP6_E_VALUE;
+}
+
 // Work units (each with its own split-K counter) and the number of partial
 // floats per unit and split.
 void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats) {
@@ -750,12 +853,16 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
   Plan p;
   const int64_t ktiles = K >> 8;
   if (variant == 0) {
-    // Measured on MI355X: the k-split kernels win while each wave holds one
-    // k-tile (8 waves up to K = 2048, 16 waves up to K = 4096); beyond that
-    // the 2-row-block streaming kernel (ring depth 4 for M <= 4, 6 for
-    // M <= 16) is faster.
-    if (M <= 16 && ktiles <= 8) p.variant = 9;
+    // Measured on MI355X: with at most one row block per CU the k-slice
+    // kernel is fastest; with more row blocks the k-split kernels win while
+    // each wave holds one k-tile (8 waves up to K = 2048, 16 waves up to
+    // K = 4096); beyond that the 2-row-block streaming kernel (ring depth 4
+    // for M <= 4, 6 for M <= 16) is faster.
+    const bool one_rb_per_cu = (N >> 4) <= cus;
+    if (M <= 16 && ktiles <= kKsliceMaxTiles && one_rb_per_cu) p.variant = 13;
+    else if (M <= 16 && ktiles <= 8) p.variant = 9;
     else if (M <= 16 && ktiles <= 16) p.variant = 12;
+    else if (M <= 16 && (N >> 4) < 4 * cus) p.variant = 1;   // few row blocks: 1 per wave
     else if (M <= 4) p.variant = 3;
     else if (M <= 16) p.variant = 8;
     else if (M <= 64) p.variant = 11;
@@ -764,7 +871,7 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     p.variant = variant;
   }
   const KernelCfg& c = kCfgs[p.variant];
-  if (c.kind == Kind::kKsplit) {
+  if (c.kind == Kind::kKsplit || c.kind == Kind::kKslice) {
     p.splits = 1;
     return p;
   }
@@ -781,10 +888,12 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     s = cus / wgs;
     if (s > ktiles / 2) s = ktiles / 2;
   } else {
-    // Aim for ~8 waves per CU so every CU has enough loads in flight.
+    // No split once there are two waves per CU; otherwise split K towards
+    // ~4 waves per CU (measured: more splits cost more in the fix-up than
+    // they add in loads in flight).
     const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
-    s = ceil_div(static_cast<int64_t>(cus) * 8, units);
-    if (s > ktiles) s = ktiles;
+    s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
+    if (s > ktiles / 2) s = ktiles / 2;
   }
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -864,6 +973,9 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
   if (variant > 0 && kCfgs[variant].kind == Kind::kKsplit &&
       (M > 16 || (K >> 8) > kKsMaxTiles || splits > 1))
     return FP6_E_VALUE;
+  if (variant > 0 && kCfgs[variant].kind == Kind::kKslice &&
+      (M > 16 || (K >> 8) > kKsliceMaxTiles || splits > 1))
+    return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const int cus = device_cus(dev);
@@ -889,6 +1001,7 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
     case 8: return launch_stream<2, 1, 6>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 9: return launch_ksplit<8>(X, W, S, Y, M, N, K, cus, s);
     case 12: return launch_ksplit<16>(X, W, S, Y, M, N, K, cus, s);
+    case 13: return launch_kslice(X, W, S, Y, M, N, K, cus, s);
     case 10: return launch_tiled<8, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 11: return launch_tiled<4, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     default: return FP6_E_VALUE;
