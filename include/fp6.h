@@ -158,8 +158,8 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *    11  tiled, 256 rows x 64 columns per 8-wave workgroup
  *    12  k-split persistent with 16 waves per workgroup (same limits as 9)
  *    13  k-slice: the waves of a workgroup (8 or 16, by K) split
- *        one row block's K, X streamed per tile; requires M <= 16,
- *        K <= 8192
+ *        one row block's K, X streamed per half-tile; requires M <= 16,
+ *        K <= 12288
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
  *          (1..K/256; must be 0 or 1 for variant 9).

@@ -416,9 +416,10 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 // K-slice kernel (memory-bound regime, M <= 16, few row blocks, long K).
 // Like the k-split kernel, WK waves of a workgroup split the K range of a row
 // block and reduce through LDS, but each wave issues the loads of all its
-// packed tiles at once and streams its X fragments tile by tile (double
-// buffered) instead of keeping them resident: meant for N/16 <= CUs, where a
-// workgroup handles a single row block and X is used once.
+// packed tiles at once and streams its X fragments half-tile by half-tile
+// (a ring of three, two ahead) instead of keeping them resident.  One
+// workgroup per row block: meant for N/16 <= CUs, where X is used once per CU
+// anyway.
 // ---------------------------------------------------------------------------
 template <int KTW, int WK>
 __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
@@ -437,13 +438,20 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
   };
   const int64_t m = r < M ? r : M - 1;
   const _Float16* xrow = X + m * K + 8 * g;
-  auto load_x = [&](half8v (&xf)[8], int t) {
+  // X fragments stream through a ring of 3 half-tiles (4 k-steps each),
+  // loaded two half-tiles ahead of their use.
+  auto load_xh = [&](half8v (&xf)[4], int hh) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      xf[j] = *reinterpret_cast<const half8v*>(xrow + tile_of(t) * 256 + 32 * j);
+    for (int j = 0; j < 4; ++j)
+      xf[j] = *reinterpret_cast<const half8v*>(xrow + tile_of(hh >> 1) * 256 + 128 * (hh & 1) + 32 * j);
   };
 
-  for (int64_t nb = blockIdx.x; nb < nblocks; nb += gridDim.x) {
+  {
+    // One row block per workgroup (the grid has one workgroup per row
+    // block).  With a loop over row blocks the compiler would hoist the X
+    // loads (they do not depend on the row block) and keep them all live.
+    const int64_t nb = blockIdx.x;
+    if (nb >= nblocks) return;  // uniform for the workgroup
     const u32x4* base = wp + (nb * ktiles) * kTileWords + lane;
     WStage<1, 1> st[KTW];
 #pragma unroll
@@ -454,23 +462,47 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
       st[t].q4b[0] = base[kt * kTileWords + 128];
     }
     const half2v s2 = row_scale2(scales, nb * 16 + r);
-    half8v xf[2][8];
-    load_x(xf[0], 0);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KTW == 1) {
+      // One tile per wave: all of its X fragments are loaded at once.
+      half8v xf[8];
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) {
-      if (t + 1 < KTW) load_x(xf[(t + 1) & 1], t + 1);
-      if (t < ktw) {
-#define FP6_KX_STEP(J)                                                                     \
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                            \
-      splice_tile_step<J>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[t & 1][J], acc, 0, 0, 0);
-        FP6_KX_STEP(0) FP6_KX_STEP(1) FP6_KX_STEP(2) FP6_KX_STEP(3)
-        FP6_KX_STEP(4) FP6_KX_STEP(5) FP6_KX_STEP(6) FP6_KX_STEP(7)
-#undef FP6_KX_STEP
+      for (int j = 0; j < 8; ++j)
+        xf[j] = *reinterpret_cast<const half8v*>(xrow + tile_of(0) * 256 + 32 * j);
+      if (ktw > 0) {
+#define FP6_KX1(J)                                                                          \
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                             \
+      splice_tile_step<J>(st[0].q2[0], st[0].q4a[0], st[0].q4b[0], s2), xf[J], acc, 0, 0, 0);
+        FP6_KX1(0) FP6_KX1(1) FP6_KX1(2) FP6_KX1(3) FP6_KX1(4) FP6_KX1(5) FP6_KX1(6) FP6_KX1(7)
+#undef FP6_KX1
       }
-      // Keep the X prefetch one tile ahead: without this fence the scheduler
-      // hoists every tile's X loads to the top and runs out of registers.
+    } else {
+    half8v xr[3][4];
+    load_xh(xr[0], 0);
+    load_xh(xr[1], 1);
+#pragma unroll
+    for (int hh = 0; hh < 2 * KTW; ++hh) {
+      if (hh + 2 < 2 * KTW) load_xh(xr[(hh + 2) % 3], hh + 2);
+      const int t = hh >> 1;
+      if (t < ktw) {
+        const half8v* xf = xr[hh % 3];
+        if (hh & 1) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<4>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<5>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<6>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<7>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[3], acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<0>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<1>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<2>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<3>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[3], acc, 0, 0, 0);
+        }
+      }
+      // Keep the X prefetch two half-tiles ahead: without this fence the
+      // scheduler hoists every half-tile's X loads to the top and runs out of
+      // registers.
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
     red[wave][lane] = acc;
     __syncthreads();
@@ -480,7 +512,6 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
       for (int w = 1; w < WK; ++w) sum += red[w][lane];
       store_y_block(Y, sum, r, M, N, nb * 16, g);
     }
-    __syncthreads();  // red[] is rewritten by the next row block
   }
 }
 
@@ -806,13 +837,13 @@ int launch_ksplit(const void* X, const void* W, const void* S, void* Y, int64_t 
   }
 }
 
-constexpr int kKsliceMaxTiles = 32;  // k-slice kernels: K <= 8192
+constexpr int kKsliceMaxTiles = 48;  // k-slice kernels: K <= 12288
 
 template <int KTW, int WK>
 int launch_kslice_t(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                     int64_t K, int cus, hipStream_t stream) {
-  const int64_t nblocks = N >> 4;
-  const dim3 grid(static_cast<unsigned>(nblocks < cus ? nblocks : cus));
+  (void)cus;
+  const dim3 grid(static_cast<unsigned>(N >> 4));  // one workgroup per row block
   const _Float16* x = static_cast<const _Float16*>(X);
   const u32x4* w = static_cast<const u32x4*>(W);
   const _Float16* sc = static_cast<const _Float16*>(S);
@@ -824,15 +855,14 @@ int launch_kslice_t(const void* X, const void* W, const void* S, void* Y, int64_
              : FP6_E_HIP;
 }
 
-// One k-tile per wave up to K = 4096 (8 waves up to K = 2048, else 16);
-// beyond, 8 waves (two per SIMD, so up to 256 registers each) with up to 4
-// k-tiles each.
+// 8 waves up to K = 2048, else 16 waves with up to 3 k-tiles each.
 int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                   int64_t K, int cus, hipStream_t stream) {
   const int64_t kt = K >> 8;
   if (kt <= 8) return launch_kslice_t<1, 8>(X, W, S, Y, M, N, K, cus, stream);
   if (kt <= 16) return launch_kslice_t<1, 16>(X, W, S, Y, M, N, K, cus, stream);
-  if (kt <= 32) return launch_kslice_t<4, 8>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 32) return launch_kslice_t<2, 16>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 48) return launch_kslice_t<3, 16>(X, W, S, Y, M, N, K, cus, stream);
   return FP6_E_VALUE;
 }
 
