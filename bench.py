@@ -40,6 +40,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "W6A16 GEMM TFLOP/s + weight HBM GB/s (% of peak), Llama-shaped layers M=1..128"
 DEFAULT_WORKLOAD = "llama7b_attn_1x4096x4096"
@@ -48,6 +50,17 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
 ROT_BYTES = 1 << 30             # >= 1 GiB of rotated copies (> 256 MB Infinity Cache)
 COPY_BYTES = 1 << 30            # --calibrate-copy: bytes read (and written) per copy
 KERNEL_SRC = os.path.join(ROOT, "weight_only_fp6_amd", "csrc", "fp6_kernels.hip")
+
+
+# Linear layers of one decoder layer, (name, N, K) with the projections that
+# share an input fused along N: Llama-7B (hidden 4096, MLP 11008) and
+# Llama-70B (hidden 8192, 8 KV heads of 128, MLP 28672).
+DECODERS = {
+    "llama7b": [("qkv", 3 * 4096, 4096), ("o", 4096, 4096), ("gate_up", 2 * 11008, 4096),
+                ("down", 4096, 11008)],
+    "llama70b": [("qkv", 8192 + 2 * 1024, 8192), ("o", 8192, 8192), ("gate_up", 2 * 28672, 8192),
+                 ("down", 8192, 28672)],
+}
 
 
 def _parse():
@@ -65,6 +78,8 @@ def _parse():
     ap.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 CSVs under DIR and exit")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn four rocprofv3 --pmc runs into a traffic summary for --workload and exit")
+    ap.add_argument("--decoder", choices=sorted(DECODERS),
+                    help="time one decoder layer's linear chain (FP6 vs fp16 hipBLASLt) at M=1..16 and exit")
     return ap.parse_args()
 
 
@@ -256,6 +271,71 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
     print(f"hbm_bytes_per_launch = {fetch + write:.0f}")
 
 
+def decoder_chain(name):
+    """One decoder layer's four linears at M = 1, 2, 4, 8, 16: FP6 path vs the
+    same chain in fp16 (hipBLASLt) on the de-quantised weights.  Codes are
+    uniform over all 64 e3m2 values (timing does not depend on them); enough
+    layer copies rotate to keep the weights out of the 256 MB Infinity Cache."""
+    import torch
+    import weight_only_fp6_amd as fp6
+    from weight_only_fp6_amd import synth
+    layers = DECODERS[name]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    fp6_bytes = sum(n * k * 3 // 4 for _, n, k in layers)
+    copies = int(max(1, math.ceil(ROT_BYTES / fp6_bytes)))
+    packed, scales, w16 = [], [], []
+    for ci in range(copies):
+        pc, sc, wc = [], [], []
+        for li, (_, n, k) in enumerate(layers):
+            codes = synth.codes_uniform(n, k, seed=100 * ci + li)
+            s_ = np.full(n, 0.003, dtype=np.float16)
+            pk = torch.from_numpy(fp6.prepack(codes, s_)).to(dev)
+            st = torch.from_numpy(s_).to(dev)
+            pc.append(pk)
+            sc.append(st)
+            if ci == 0:
+                wc.append(fp6.dequant(pk, st, n, k, stream=stream))
+        packed.append(pc)
+        scales.append(sc)
+        if ci == 0:
+            w16 = wc
+    torch.cuda.synchronize()
+    w16_copies = int(max(1, math.ceil(ROT_BYTES / sum(2 * n * k for _, n, k in layers))))
+    w16s = [w16] + [[w.clone() for w in w16] for _ in range(w16_copies - 1)]
+    rows = []
+    for M in (1, 2, 4, 8, 16):
+        xs = {k: torch.randn(M, k, device=dev).to(torch.float16) for _, _, k in layers}
+        ys = [torch.empty(M, n, dtype=torch.float16, device=dev) for _, n, _ in layers]
+        L = fp6.lib
+
+        def fp6_step(i):
+            c = i % copies
+            for li, (_, n, k) in enumerate(layers):
+                st = L.fp6_linear(xs[k].data_ptr(), packed[c][li].data_ptr(), scales[c][li].data_ptr(),
+                                  ys[li].data_ptr(), M, n, k, stream.cuda_stream)
+                if st:
+                    raise fp6.FP6Error("fp6_linear", st)
+
+        def f16_step(i):
+            c = i % w16_copies
+            for li, (_, n, k) in enumerate(layers):
+                torch.matmul(xs[k], w16s[c][li].t(), out=ys[li])
+        fp6_step(0)
+        f16_step(0)
+        torch.cuda.synchronize()
+        t6 = _time_graph(torch, stream, fp6_step, 100)
+        t16 = _time_graph(torch, stream, f16_step, 100)
+        rows.append({"M": M, "fp6_us": round(t6, 2), "fp16_blas_us": round(t16, 2),
+                     "speedup": round(t16 / t6, 3),
+                     "fp6_weight_gbps": round(fp6_bytes / t6 / 1e3, 1)})
+    print(json.dumps({"metric": "decoder-layer linear chain latency (qkv, o, gate_up, down)",
+                      "model_shapes": name, "layers": [[a, n, k] for a, n, k in layers],
+                      "unit": "us", "fp6_weight_bytes": fp6_bytes, "rows": rows,
+                      "data": "synthetic (uniform e3m2 codes)"}), flush=True)
+
+
 def calibrate_copy():
     import torch
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -284,6 +364,9 @@ def main():
         sys.exit(3)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.decoder:
+        decoder_chain(args.decoder)
         return
     import weight_only_fp6_amd as fp6
     from weight_only_fp6_amd import synth
