@@ -160,6 +160,10 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *    13  k-slice: the waves of a workgroup (8 or 16, by K) split
  *        one row block's K, X streamed per half-tile; requires M <= 16,
  *        K <= 12288
+ *    14  streaming, X tiles shared through LDS by the workgroup's 4 waves,
+ *        2 row blocks per wave, ring of 4 tiles
+ *    15  as 14 with 1 row block per wave
+ *    16  as 14 with 8 waves per workgroup
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
  *          (1..K/256; must be 0 or 1 for variant 9).
@@ -173,7 +177,7 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
 
 /*
  * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
- * for (M, N, K) on the current device: *variant (1..13, see fp6_linear_plan)
+ * for (M, N, K) on the current device: *variant (1..16, see fp6_linear_plan)
  * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
  * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
  * >= 1 here), FP6_E_HIP.

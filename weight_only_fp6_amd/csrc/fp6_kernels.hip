@@ -315,6 +315,157 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 }
 
 // ---------------------------------------------------------------------------
+// Streaming kernel with X shared through LDS (memory-bound regime, M <= 16
+// per m-group).  As fp6_gemm_stream, a wave streams A row blocks over a K
+// range through a register ring of D packed tiles, but the NW waves of a
+// workgroup (same K range, different row groups) share X: each X tile
+// (16 rows x 256 k) is loaded once per workgroup into a 3-slot LDS ring
+// (rows XOR-swizzled in 16-byte units, so the B-fragment reads are free of
+// bank conflicts), one barrier per tile.  This cuts X's L2->CU traffic by NW.
+// ---------------------------------------------------------------------------
+template <int A, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
+    int64_t mg_base) {
+  constexpr int kThreads = 64 * NW;
+  constexpr int kChunks = 16 * 32;                      // 16-byte units per X tile
+  constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) half8v xs[3][kChunks];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t ngroups = (nblocks + A - 1) / A;
+  const int64_t gsets = (ngroups + NW - 1) / NW;
+  int64_t b = blockIdx.x;
+  const int split = static_cast<int>(b % splits);
+  b /= splits;
+  const int64_t gs = b % gsets;
+  const int64_t mg = b / gsets + mg_base;
+  const int64_t rg_raw = gs * NW + wave;
+  const bool wave_active = rg_raw < ngroups;
+  const int64_t rg = wave_active ? rg_raw : ngroups - 1;  // idle waves still join barriers
+  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int r = lane & 15, g = lane >> 4;
+
+  const u32x4* w[A];
+  half2v s2[A];
+#pragma unroll
+  for (int a = 0; a < A; ++a) {
+    int64_t nb = rg * A + a;
+    if (nb >= nblocks) nb = nblocks - 1;
+    w[a] = wp + (nb * ktiles) * kTileWords + lane;
+    s2[a] = row_scale2(scales, nb * 16 + r);
+  }
+  // X staging: unit q = (row rr = q/32, chunk c = q%32) of the tile; rows
+  // beyond M repeat row M-1 (their accumulator columns are never stored).
+  const _Float16* xsrc[kPerThread];
+  int xdst[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    int q = i * kThreads + tid;
+    if (q >= kChunks) q = kChunks - 1;  // surplus threads duplicate the last unit
+    const int rr = q >> 5, c = q & 31;
+    int64_t m = mg * 16 + rr;
+    if (m >= M) m = M - 1;
+    xsrc[i] = X + m * K + 8 * c;
+    xdst[i] = rr * 32 + (c ^ rr);
+  }
+  half8v xstage[kPerThread];
+  const int64_t klast = kt1 > kt0 ? kt1 - 1 : kt0;
+  auto clampk = [&](int64_t t) { return t < klast ? t : klast; };
+  auto gload_x = [&](int64_t kt) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      xstage[i] = *reinterpret_cast<const half8v*>(xsrc[i] + kt * 256);
+  };
+  auto swrite_x = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) xs[slot][xdst[i]] = xstage[i];
+  };
+
+  float4v acc[A];
+#pragma unroll
+  for (int i = 0; i < A; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  auto load_w = [&](WStage<A, 1>& st, int64_t kt) {
+#pragma unroll
+    for (int a = 0; a < A; ++a) {
+      st.q2[a] = w[a][kt * kTileWords];
+      st.q4a[a] = w[a][kt * kTileWords + 64];
+      st.q4b[a] = w[a][kt * kTileWords + 128];
+    }
+  };
+  auto mac = [&](const WStage<A, 1>& st, int slot) {
+    const half8v* xb = xs[slot];
+#define FP6_XL_STEP(J)                                                                   \
+  {                                                                                      \
+    const half8v bf = xb[r * 32 + ((4 * J + g) ^ r)];                                    \
+    _Pragma("unroll") for (int a = 0; a < A; ++a) acc[a] =                               \
+        __builtin_amdgcn_mfma_f32_16x16x32_f16(                                          \
+            splice_tile_step<J>(st.q2[a], st.q4a[a], st.q4b[a], s2[a]), bf, acc[a], 0, 0, 0); \
+  }
+    FP6_XL_STEP(0) FP6_XL_STEP(1) FP6_XL_STEP(2) FP6_XL_STEP(3)
+    FP6_XL_STEP(4) FP6_XL_STEP(5) FP6_XL_STEP(6) FP6_XL_STEP(7)
+#undef FP6_XL_STEP
+  };
+
+  // Tile i of the split (kt = kt0 + i) uses slot i % 3.  Iteration i writes
+  // X(kt+1) (loaded during iteration i-1) into slot (i+1) % 3, whose last
+  // reader was iteration i-2, loads X(kt+2), consumes the ring stage of tile
+  // kt and refills it, then meets the barrier.  Branch-free steady state
+  // with clamped prefetch indices; the last (< D) tiles run in a tail.
+  WStage<A, 1> ring[D];
+  if (kt0 < kt1) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_w(ring[d], clampk(kt0 + d));
+    gload_x(kt0);
+    swrite_x(0);
+    gload_x(clampk(kt0 + 1));
+    __syncthreads();
+    int64_t kt = kt0;
+    int slot = 0;
+    for (; kt + D <= kt1; kt += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int64_t t = kt + d;
+        const int nslot = slot == 2 ? 0 : slot + 1;
+        swrite_x(nslot);
+        gload_x(clampk(t + 2));
+        mac(ring[d], slot);
+        load_w(ring[d], clampk(t + D));
+        __syncthreads();
+        slot = nslot;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d + 1 < D; ++d) {
+      if (kt + d < kt1) {
+        const int nslot = slot == 2 ? 0 : slot + 1;
+        swrite_x(nslot);
+        gload_x(clampk(kt + d + 2));
+        mac(ring[d], slot);
+        __syncthreads();
+        slot = nslot;
+      }
+    }
+  }
+  if (!wave_active) return;
+
+  if (splits > 1) {
+    const int64_t unit = mg * ngroups + rg;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (A * 256);
+    if (!splitk_fixup<A>(acc, unit_part, counters + unit, split, splits, lane)) return;
+  }
+#pragma unroll
+  for (int a = 0; a < A; ++a) {
+    const int64_t nb = rg * A + a;
+    if (nb >= nblocks) continue;
+    store_y_block(Y, acc[a], mg * 16 + r, M, N, nb * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // K-split persistent kernel (memory-bound regime, M <= 16,
 // K <= kKsWaves*KTW*256).  One workgroup of kKsWaves (8 or 16) waves per CU.
 // Wave w owns the k-tiles [w*KT/W, (w+1)*KT/W) (W = kKsWaves) for the whole
@@ -774,7 +925,7 @@ int check_linear_args(const void* X, const void* W, const void* s, void* Y, int6
 }
 
 // Kernel configurations reachable through fp6_linear_plan's `variant`.
-enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice };
+enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice, kXlds };
 struct KernelCfg {
   Kind kind;
   int a, mb, d;  // stream: row blocks/wave, 16-col blocks/wave, ring depth; tiled: B = mb
@@ -794,6 +945,9 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kTiled, 2, 4, 8},   // 11: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks
     {Kind::kKsplit, 1, 1, 16}, // 12: k-split persistent with 16 waves per workgroup
     {Kind::kKslice, 1, 1, 16}, // 13: k-slice, 16 waves per row block, X streamed
+    {Kind::kXlds, 2, 1, 4},    // 14: streaming + X in LDS, 2 row blocks/wave, ring 4, 4 waves
+    {Kind::kXlds, 1, 1, 4},    // 15: streaming + X in LDS, 1 row block/wave, ring 4, 4 waves
+    {Kind::kXlds, 2, 1, 8},    // 16: streaming + X in LDS, 2 row blocks/wave, ring 4, 8 waves
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -866,6 +1020,32 @@ int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t 
   return FP6_E_VALUE;
 }
 
+template <int A, int D, int NW>
+int launch_xlds(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                int64_t K, int splits, Workspace* ws, hipStream_t stream) {
+  const int64_t ngroups = ceil_div(N >> 4, A), gsets = ceil_div(ngroups, NW);
+  const int64_t mgroups = ceil_div(M, 16);
+  const int64_t per_mg = gsets * splits;
+  int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
+  if (mg_chunk < 1) mg_chunk = 1;
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  float* part = ws ? static_cast<float*>(ws->part) : nullptr;
+  unsigned* cnt = ws ? ws->counters : nullptr;
+  for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
+    const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
+    const dim3 grid(static_cast<unsigned>(nmg * per_mg));
+    int64_t mg_base = mg0;
+    void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_xlds<A, D, NW>), grid, dim3(64 * NW),
+                        args, 0, stream) != hipSuccess)
+      return FP6_E_HIP;
+  }
+  return FP6_OK;
+}
+
 // Work units (each with its own split-K counter) and the number of partial
 // floats per unit and split.
 void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats) {
@@ -883,18 +1063,15 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
   Plan p;
   const int64_t ktiles = K >> 8;
   if (variant == 0) {
-    // Measured on MI355X: with at most one row block per CU the k-slice
-    // kernel is fastest; with more row blocks the k-split kernels win while
-    // each wave holds one k-tile (8 waves up to K = 2048, 16 waves up to
-    // K = 4096); beyond that the 2-row-block streaming kernel (ring depth 4
-    // for M <= 4, 6 for M <= 16) is faster.
+    // Measured on MI355X: up to K = 4096 the k-slice kernel (at most one row
+    // block per CU) or the k-split kernels (8 waves up to K = 2048, else 16)
+    // are fastest; for longer K the streaming kernel with X shared through
+    // LDS (1 row block per wave, 4 waves) is.
     const bool one_rb_per_cu = (N >> 4) <= cus;
-    if (M <= 16 && ktiles <= kKsliceMaxTiles && one_rb_per_cu) p.variant = 13;
+    if (M <= 16 && ktiles <= 16 && one_rb_per_cu) p.variant = 13;
     else if (M <= 16 && ktiles <= 8) p.variant = 9;
     else if (M <= 16 && ktiles <= 16) p.variant = 12;
-    else if (M <= 16 && (N >> 4) < 4 * cus) p.variant = 1;   // few row blocks: 1 per wave
-    else if (M <= 4) p.variant = 3;
-    else if (M <= 16) p.variant = 8;
+    else if (M <= 16) p.variant = 15;
     else if (M <= 64) p.variant = 11;
     else p.variant = 10;
   } else {
@@ -1032,6 +1209,9 @@ int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M,
     case 9: return launch_ksplit<8>(X, W, S, Y, M, N, K, cus, s);
     case 12: return launch_ksplit<16>(X, W, S, Y, M, N, K, cus, s);
     case 13: return launch_kslice(X, W, S, Y, M, N, K, cus, s);
+    case 14: return launch_xlds<2, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 15: return launch_xlds<1, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
+    case 16: return launch_xlds<2, 4, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 10: return launch_tiled<8, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     case 11: return launch_tiled<4, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
     default: return FP6_E_VALUE;
