@@ -8,10 +8,11 @@ CPU-baseline leg of the benchmark may import it; the product path never does.
 
 Contents (all in :mod:`oracle.fp6_oracle`):
 
-* e3m2 decode table (explicit 64 entries) and round-to-nearest-even encoder;
+* decode tables (explicit, one per format: FP6 e3m2 and e2m3, FP5 e2m2, FP4
+  e2m1) and the round-to-nearest-even encoder;
 * per-row quantizer (input preparation: W fp32 -> codes + fp16 row scales);
-* scalar and vectorised unpackers of the packed layout v1, plus a scalar
-  packer used only to pin the unpacker;
+* scalar and vectorised unpackers of the packed layout v1 of every format,
+  plus a scalar packer used only to pin the unpackers;
 * dequantisation ``fp16_RNE(v(c) * s_n)`` and the float64 GEMM
   ``Y_ref = X . Wdq^T``, plus a naive triple loop used to pin it;
 * the acceptance check (per-element and Frobenius tolerances).
@@ -24,6 +25,13 @@ fixtures under ``tests/golden/``.  No function is "parity unpinned".
 
 from .fp6_oracle import (  # noqa: F401
     E3M2_VALUES,
+    E2M3_VALUES,
+    E2M2_VALUES,
+    E2M1_VALUES,
+    FORMATS,
+    tile_bytes,
+    packed_bytes,
+    unpack_tiles,
     decode,
     encode_rne,
     fp16_rne,

@@ -29,6 +29,17 @@ packed layout.  The readings used here (each one stated where it is used):
   [M,K], W is [N,K], Y is [M,N]).
 * Packed layout v1 (the library's private offline format; any bijection is
   correct, this oracle checks the round trip): see :func:`unpack_scalar`.
+
+Other widths (FP6-LLM abstract: one Tensor-Core kernel scheme for float weights
+of several bit widths; TC-FPx explainer, section "redesigning the kernel
+solution": a unified kernel for quantised weights of different widths up to
+6 bits).  The pages name no formats; the reading used here is the plainest set
+of small IEEE-like float formats (sign, exponent with bias 2^(E-1)-1,
+subnormals, no inf/NaN), each with the same per-row fp16 scale, rounding and
+de-quantisation rules as e3m2:
+  e2m3 (6 bits, bias 1, max 7.5; the OCP MX FP6 E2M3 element format),
+  e2m2 (5 bits, bias 1, max 7),
+  e2m1 (4 bits, bias 1, max 6; the OCP MX FP4 E2M1 element format).
 """
 
 from __future__ import annotations
@@ -62,44 +73,121 @@ E3M2_VALUES = (
     -8.0, -10.0, -12.0, -14.0,
     -16.0, -20.0, -24.0, -28.0,
 )
-_TABLE = np.array(E3M2_VALUES, dtype=np.float64)
-_MAGS = _TABLE[:32]                      # ascending, exact dyadics
-_MIDS = (_MAGS[:-1] + _MAGS[1:]) / 2.0   # exact in float64 (short dyadics)
+# e2m3 (OCP MX FP6 E2M3): 1 sign, 2 exponent bits (bias 1), 3 mantissa bits,
+# subnormals, no inf/NaN, max 7.5.  Index = e*8 + m:
+#   e = 0 (subnormal): m / 8;   e >= 1: 2^(e-1) * (1 + m/8).
+E2M3_VALUES = (
+    0.0, 0.125, 0.25, 0.375, 0.5, 0.625, 0.75, 0.875,               # e=0 (subnormal)
+    1.0, 1.125, 1.25, 1.375, 1.5, 1.625, 1.75, 1.875,               # e=1
+    2.0, 2.25, 2.5, 2.75, 3.0, 3.25, 3.5, 3.75,                     # e=2
+    4.0, 4.5, 5.0, 5.5, 6.0, 6.5, 7.0, 7.5,                         # e=3
+    -0.0, -0.125, -0.25, -0.375, -0.5, -0.625, -0.75, -0.875,
+    -1.0, -1.125, -1.25, -1.375, -1.5, -1.625, -1.75, -1.875,
+    -2.0, -2.25, -2.5, -2.75, -3.0, -3.25, -3.5, -3.75,
+    -4.0, -4.5, -5.0, -5.5, -6.0, -6.5, -7.0, -7.5,
+)
+# e2m2 (5 bits): 1 sign, 2 exponent bits (bias 1), 2 mantissa bits, max 7.
+#   e = 0 (subnormal): m / 4;   e >= 1: 2^(e-1) * (1 + m/4).
+E2M2_VALUES = (
+    0.0, 0.25, 0.5, 0.75,            # e=0 (subnormal)
+    1.0, 1.25, 1.5, 1.75,            # e=1
+    2.0, 2.5, 3.0, 3.5,              # e=2
+    4.0, 5.0, 6.0, 7.0,              # e=3
+    -0.0, -0.25, -0.5, -0.75,
+    -1.0, -1.25, -1.5, -1.75,
+    -2.0, -2.5, -3.0, -3.5,
+    -4.0, -5.0, -6.0, -7.0,
+)
+# e2m1 (OCP MX FP4 E2M1): 1 sign, 2 exponent bits (bias 1), 1 mantissa bit,
+# max 6.   e = 0 (subnormal): m / 2;   e >= 1: 2^(e-1) * (1 + m/2).
+E2M1_VALUES = (
+    0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+    -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0,
+)
+
+
+class Format:
+    """One small float weight format.
+
+    bits: code width (sign = top bit); table: value of every code (explicit);
+    max: largest magnitude (the quantiser divides the row maximum by it);
+    scale_limit: rows must have |s| below it (the library's exactness range,
+    see quantize_rows); ebits, mbits, bias: the field widths and exponent bias
+    the table follows.
+    """
+
+    def __init__(self, name, bits, ebits, mbits, bias, values, vmax, scale_limit):
+        self.name = name
+        self.bits = bits
+        self.ebits = ebits
+        self.mbits = mbits
+        self.bias = bias
+        self.table = np.array(values, dtype=np.float64)
+        if self.table.size != 1 << bits:
+            raise AssertionError("table size does not match the code width")
+        self.nmag = 1 << (bits - 1)
+        self.mags = self.table[: self.nmag]
+        self.mids = (self.mags[:-1] + self.mags[1:]) / 2.0   # exact (short dyadics)
+        self.max = vmax
+        self.scale_limit = scale_limit
+
+
+FORMATS = {
+    "e3m2": Format("e3m2", 6, 3, 2, 3, E3M2_VALUES, 28.0, 16.0),
+    "e2m3": Format("e2m3", 6, 2, 3, 1, E2M3_VALUES, 7.5, 4.0),
+    "e2m2": Format("e2m2", 5, 2, 2, 1, E2M2_VALUES, 7.0, 4.0),
+    "e2m1": Format("e2m1", 4, 2, 1, 1, E2M1_VALUES, 6.0, math.inf),
+}
+_TABLE = FORMATS["e3m2"].table
+_MAGS = FORMATS["e3m2"].mags
+_MIDS = FORMATS["e3m2"].mids
 E3M2_MAX = 28.0
 
 
-def decode(codes) -> np.ndarray:
-    """v(c) for an array of 6-bit codes, as float64 (table lookup)."""
+def _fmt(fmt) -> Format:
+    if isinstance(fmt, Format):
+        return fmt
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FORMATS)}")
+    return FORMATS[fmt]
+
+
+def decode(codes, fmt="e3m2") -> np.ndarray:
+    """v(c) for an array of codes of the format, as float64 (table lookup)."""
+    f = _fmt(fmt)
     c = np.asarray(codes)
-    if c.size and (c.min() < 0 or c.max() > 63):
-        raise ValueError("e3m2 codes must lie in 0..63")
-    return _TABLE[c.astype(np.int64)]
+    if c.size and (c.min() < 0 or c.max() >= (1 << f.bits)):
+        raise ValueError(f"{f.bits}-bit codes must lie in 0..{(1 << f.bits) - 1}")
+    return f.table[c.astype(np.int64)]
 
 
-def encode_rne(x) -> np.ndarray:
-    """Nearest e3m2 code for float64 values, ties to the even code.
+def encode_rne(x, fmt="e3m2") -> np.ndarray:
+    """Nearest code for float64 values, ties to the even code.
 
-    The magnitude |x| is mapped to the closest of the 32 magnitudes; an exact
-    midpoint goes to the even code (m0 = 0); |x| >= 28 saturates to code 31.
-    The sign bit is the IEEE sign bit of x, so -0.0 and small negatives that
-    round to zero give code 0x20.  NaN is rejected.
+    The magnitude |x| is mapped to the closest of the format's magnitudes; an
+    exact midpoint goes to the even code (lowest mantissa bit 0); |x| at or
+    beyond the largest magnitude saturates to it.  The sign bit (the code's top
+    bit) is the IEEE sign bit of x, so -0.0 and small negatives that round to
+    zero give the negative-zero code.  NaN is rejected.
     """
+    f = _fmt(fmt)
+    mids = f.mids
     x = np.asarray(x, dtype=np.float64)
     if np.isnan(x).any():
-        raise ValueError("NaN cannot be encoded in e3m2 (no NaN codes)")
+        raise ValueError("NaN cannot be encoded (no NaN codes)")
     a = np.abs(x)
-    # hi = number of midpoints strictly below a  -> candidate index above
-    below = np.searchsorted(_MIDS, a, side="left")   # mids[below-1] < a <= mids[below]
+    # below = number of midpoints strictly below a: mids[below-1] < a <= mids[below]
+    below = np.searchsorted(mids, a, side="left")
     idx = below.copy()
     # exact midpoint: a == mids[below]; choose the even one of (below, below+1)
     at_mid = np.zeros(a.shape, dtype=bool)
-    inb = below < _MIDS.size
-    at_mid[inb] = a[inb] == _MIDS[below[inb]]
+    inb = below < mids.size
+    at_mid[inb] = a[inb] == mids[below[inb]]
     tie_idx = np.where(below % 2 == 0, below, below + 1)
     idx = np.where(at_mid, tie_idx, idx)
-    idx = np.minimum(idx, 31)                         # saturate (also +inf)
+    idx = np.minimum(idx, f.nmag - 1)                 # saturate (also +inf)
     sign = np.signbit(x).astype(np.int64)
-    return ((sign << 5) | idx).astype(np.uint8)
+    return ((sign << (f.bits - 1)) | idx).astype(np.uint8)
 
 
 def fp16_rne(x) -> np.ndarray:
@@ -110,47 +198,51 @@ def fp16_rne(x) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # O2: per-row quantiser (input preparation, not part of the timed path).
 # ---------------------------------------------------------------------------
-def quantize_rows(W) -> tuple[np.ndarray, np.ndarray]:
+def quantize_rows(W, fmt="e3m2") -> tuple[np.ndarray, np.ndarray]:
     """W fp32 [N,K] -> (codes uint8 [N,K], scales fp16 [N]).
 
-    s_n = fp16_RNE(float64(max_k |W[n,k]|) / 28); x = float64(W)/float64(s_n);
-    codes = encode_rne(x).  A row whose scale is 0 gets all-zero codes.
-    Rows whose scale is not finite or has |s| >= 16 are rejected: outside that
-    range s * 2^12 is not an exact fp16, which the fused kernel relies on.
+    s_n = fp16_RNE(float64(max_k |W[n,k]|) / vmax) (vmax: the format's largest
+    magnitude); x = float64(W)/float64(s_n); codes = encode_rne(x).  A row
+    whose scale is 0 gets all-zero codes.  Rows whose scale is not finite or
+    reaches the format's limit are rejected (16 for e3m2, 4 for e2m3 and e2m2:
+    the library folds s * 2^12 or s * 2^14 as one fp16, exact only below it;
+    e2m1 has no limit beyond finiteness).
     """
+    f = _fmt(fmt)
     W = np.asarray(W)
     if W.dtype != np.float32 or W.ndim != 2:
         raise ValueError("W must be a 2-D float32 array")
     if not np.isfinite(W).all():
         raise ValueError("W must be finite")
     amax = np.abs(W).max(axis=1).astype(np.float64) if W.shape[1] else np.zeros(W.shape[0])
-    scales = fp16_rne(amax / 28.0)
+    scales = fp16_rne(amax / f.max)
     s64 = scales.astype(np.float64)
-    if not np.isfinite(s64).all() or (np.abs(s64) >= 16.0).any():
-        raise ValueError("row scale out of the exact range |s| < 16")
+    if not np.isfinite(s64).all() or (np.abs(s64) >= f.scale_limit).any():
+        raise ValueError("row scale out of the exact range")
     codes = np.zeros(W.shape, dtype=np.uint8)
     nz = s64 != 0.0
     if nz.any():
         q = W[nz].astype(np.float64) / s64[nz][:, None]
-        codes[nz] = encode_rne(q)
+        codes[nz] = encode_rne(q, f)
     return codes, scales
 
 
-def quantize_rows_sampled(W_rows) -> tuple[np.ndarray, np.ndarray]:
+def quantize_rows_sampled(W_rows, fmt="e3m2") -> tuple[np.ndarray, np.ndarray]:
     """Quantise a subset of rows (rows are independent); same as quantize_rows."""
-    return quantize_rows(W_rows)
+    return quantize_rows(W_rows, fmt)
 
 
 # ---------------------------------------------------------------------------
 # O3: packed layout v1.
 #
 # Codes c[n][k] with N % 16 == 0 and K % 256 == 0.  The buffer holds
-# N*K*3/4 bytes in tiles of 16 rows x 256 k (3072 bytes each).  Tile
-# (nb, kb) starts at byte (nb*(K/256) + kb) * 3072 (row-block major, k-block
-# minor).  Inside a tile, local row r in 0..15 and local k = 32*j + 8*g + i
-# (j: k-step 0..7, g: lane group 0..3, i: element 0..7) belong to lane
-# L = 16*g + r.  Each code splits into a 2-bit piece (bits s,e2 = c>>4) and a
-# 4-bit piece (bits e1,e0,m1,m0 = c&15).
+# N*K*bits/8 bytes in tiles of 16 rows x 256 k.  Tile (nb, kb) starts at byte
+# (nb*(K/256) + kb) * tile_bytes (row-block major, k-block minor).  Inside a
+# tile, local row r in 0..15 and local k = 32*j + 8*g + i (j: k-step 0..7,
+# g: lane group 0..3, i: element 0..7) belong to lane L = 16*g + r.
+#
+# FP6 e3m2 (tile 3072 bytes).  Each code splits into a 2-bit piece (bits s,e2
+# = c>>4) and a 4-bit piece (bits e1,e0,m1,m0 = c&15).
 #   * 2-bit plane: bytes [0,1024) of the tile.  Lane L owns the 16 bytes at
 #     16*L, as 4 little-endian 32-bit words; word j//2 holds k-steps j and
 #     j+1.  With pair p = 4*(j%2) + i//2 and half h = i%2, bit e2 sits at
@@ -159,10 +251,30 @@ def quantize_rows_sampled(W_rows) -> tuple[np.ndarray, np.ndarray]:
 #     [2048,3072); lane L owns 16 bytes at 16*L in each half, word j%4 is
 #     k-step j.  Element i occupies nibble slot (i//2) + 4*(i%2), i.e. bits
 #     4*slot .. 4*slot+3 (slots hold elements 0,2,4,6,1,3,5,7).
+# FP6 e2m3 (tile 3072 bytes): as e3m2 (2-bit piece = s,e1; 4-bit piece =
+#   e0,m2,m1,m0), except the 2-bit plane positions: with b = [0,1,2,3,8,9,10,
+#   11][p], bit e1 sits at b + 16*h and bit s at b + 4 + 16*h.
+# FP5 e2m2 (tile 2560 bytes): 4-bit piece (e1,e0,m1,m0 = c&15) in a 4-bit
+#   plane at bytes [0,2048) laid out as the FP6 one; the sign (c>>4) in a
+#   1-bit plane at [2048,2560): lane L owns the 8 bytes at 2048 + 8*L as two
+#   words; word j//4 holds k-steps 4*(j//4)..+3, with P = 4*(j%4) + i//2 the
+#   sign sits at bit P + 16*h.
+# FP4 e2m1 (tile 2048 bytes): one 4-bit plane at [0,2048) laid out as the FP6
+#   one, holding the whole code, element i in nibble slot i (natural order).
 # ---------------------------------------------------------------------------
 TILE_N = 16
 TILE_K = 256
 TILE_BYTES = 3072
+_E2M3_BASE = (0, 1, 2, 3, 8, 9, 10, 11)
+
+
+def tile_bytes(fmt="e3m2") -> int:
+    """Bytes of one 16 x 256 tile: 4096 codes of the format's width."""
+    return 4096 * _fmt(fmt).bits // 8
+
+
+def packed_bytes(N: int, K: int, fmt="e3m2") -> int:
+    return N * K * _fmt(fmt).bits // 8
 
 
 def _check_shape(N: int, K: int) -> None:
@@ -171,7 +283,7 @@ def _check_shape(N: int, K: int) -> None:
 
 
 def _locate(N: int, K: int, n: int, k: int):
-    """Byte offset of the 2-bit word, bit positions, and 4-bit word + shift for (n,k)."""
+    """e3m2: byte offset of the 2-bit word, bit positions, and 4-bit word + shift for (n,k)."""
     nb, r = divmod(n, TILE_N)
     kb, kk = divmod(k, TILE_K)
     j, rem = divmod(kk, 32)
@@ -188,6 +300,40 @@ def _locate(N: int, K: int, n: int, k: int):
     return w2, bit_e2, bit_s, w4, nib
 
 
+def _slots(fmt, N: int, K: int, n: int, k: int):
+    """Where each bit of code (n, k) lives: a list of (byte offset of its
+    little-endian 32-bit word, bit in that word, bit of the code)."""
+    f = _fmt(fmt)
+    nb, r = divmod(n, TILE_N)
+    kb, kk = divmod(k, TILE_K)
+    j, rem = divmod(kk, 32)
+    g, i = divmod(rem, 8)
+    lane = 16 * g + r
+    tb = tile_bytes(f)
+    base = (nb * (K // TILE_K) + kb) * tb
+    p = 4 * (j % 2) + i // 2
+    h = i % 2
+    if f.name == "e3m2":
+        w2, b_e2, b_s, w4, nib = _locate(N, K, n, k)
+        return [(w2, b_e2, 4), (w2, b_s, 5)] + [(w4, nib + b, b) for b in range(4)]
+    if f.name == "e2m3":
+        w2 = base + 16 * lane + 4 * (j // 2)
+        b = _E2M3_BASE[p] + 16 * h
+        w4 = base + 1024 + 1024 * (j // 4) + 16 * lane + 4 * (j % 4)
+        nib = 4 * ((i // 2) + 4 * (i % 2))
+        return [(w2, b, 4), (w2, b + 4, 5)] + [(w4, nib + q, q) for q in range(4)]
+    if f.name == "e2m2":
+        w4 = base + 1024 * (j // 4) + 16 * lane + 4 * (j % 4)
+        nib = 4 * ((i // 2) + 4 * (i % 2))
+        w1 = base + 2048 + 8 * lane + 4 * (j // 4)
+        P = 4 * (j % 4) + i // 2
+        return [(w4, nib + q, q) for q in range(4)] + [(w1, P + 16 * h, 4)]
+    if f.name == "e2m1":
+        w4 = base + 1024 * (j // 4) + 16 * lane + 4 * (j % 4)
+        return [(w4, 4 * i + q, q) for q in range(4)]
+    raise AssertionError(f.name)
+
+
 def _get_word(buf, off: int) -> int:
     return buf[off] | (buf[off + 1] << 8) | (buf[off + 2] << 16) | (buf[off + 3] << 24)
 
@@ -197,47 +343,71 @@ def _set_word(buf, off: int, val: int) -> None:
         buf[off + b] = (val >> (8 * b)) & 0xFF
 
 
-def pack_scalar(codes) -> np.ndarray:
+def pack_scalar(codes, fmt="e3m2") -> np.ndarray:
     """Scalar packer of layout v1 (pure Python; small inputs only).
 
     Used only to pin :func:`unpack_scalar` (bijection checks); the library has
     its own packer.
     """
+    f = _fmt(fmt)
     c = np.asarray(codes, dtype=np.uint8)
     N, K = c.shape
     _check_shape(N, K)
-    if c.max(initial=0) > 63:
-        raise ValueError("codes must lie in 0..63")
-    buf = bytearray(N * K * 3 // 4)
+    if c.max(initial=0) >= (1 << f.bits):
+        raise ValueError(f"codes must lie in 0..{(1 << f.bits) - 1}")
+    buf = bytearray(packed_bytes(N, K, f))
     for n in range(N):
         for k in range(K):
             code = int(c[n, k])
-            w2, b_e2, b_s, w4, nib = _locate(N, K, n, k)
-            v2 = _get_word(buf, w2)
-            v2 |= ((code >> 4) & 1) << b_e2
-            v2 |= ((code >> 5) & 1) << b_s
-            _set_word(buf, w2, v2)
-            v4 = _get_word(buf, w4)
-            v4 |= (code & 0xF) << nib
-            _set_word(buf, w4, v4)
+            for off, wbit, cbit in _slots(f, N, K, n, k):
+                _set_word(buf, off, _get_word(buf, off) | (((code >> cbit) & 1) << wbit))
     return np.frombuffer(bytes(buf), dtype=np.uint8).copy()
 
 
-def unpack_scalar(packed, N: int, K: int) -> np.ndarray:
+def unpack_scalar(packed, N: int, K: int, fmt="e3m2") -> np.ndarray:
     """Scalar unpacker of layout v1 (pure Python loop over every code)."""
+    f = _fmt(fmt)
     _check_shape(N, K)
     buf = bytes(np.asarray(packed, dtype=np.uint8).ravel())
-    if len(buf) != N * K * 3 // 4:
+    if len(buf) != packed_bytes(N, K, f):
         raise ValueError("packed buffer has the wrong size")
     out = np.zeros((N, K), dtype=np.uint8)
     for n in range(N):
         for k in range(K):
-            w2, b_e2, b_s, w4, nib = _locate(N, K, n, k)
-            v2 = _get_word(buf, w2)
-            v4 = _get_word(buf, w4)
-            code = ((v2 >> b_s) & 1) << 5 | ((v2 >> b_e2) & 1) << 4 | ((v4 >> nib) & 0xF)
+            code = 0
+            for off, wbit, cbit in _slots(f, N, K, n, k):
+                code |= ((_get_word(buf, off) >> wbit) & 1) << cbit
             out[n, k] = code
     return out
+
+
+def _tile_map(fmt):
+    """For one tile: byte index and bit in byte of every (row, k, code bit)."""
+    f = _fmt(fmt)
+    byte_idx = np.zeros((f.bits, TILE_N, TILE_K), dtype=np.int64)
+    bit_idx = np.zeros((f.bits, TILE_N, TILE_K), dtype=np.int64)
+    for r in range(TILE_N):
+        for k in range(TILE_K):
+            for off, wbit, cbit in _slots(f, TILE_N, TILE_K, r, k):
+                byte_idx[cbit, r, k] = off + wbit // 8
+                bit_idx[cbit, r, k] = wbit % 8
+    return byte_idx, bit_idx
+
+
+def unpack_tiles(packed, N: int, K: int, fmt="e3m2") -> np.ndarray:
+    """Vectorised unpacker of any format: one tile's bit map applied to all tiles."""
+    f = _fmt(fmt)
+    _check_shape(N, K)
+    p = np.asarray(packed, dtype=np.uint8).ravel()
+    if p.size != packed_bytes(N, K, f):
+        raise ValueError("packed buffer has the wrong size")
+    nbk, kbk = N // TILE_N, K // TILE_K
+    tiles = p.reshape(nbk, kbk, tile_bytes(f)).astype(np.int64)
+    byte_idx, bit_idx = _tile_map(f)
+    out = np.zeros((nbk, kbk, TILE_N, TILE_K), dtype=np.int64)
+    for b in range(f.bits):
+        out |= ((tiles[:, :, byte_idx[b]] >> bit_idx[b]) & 1) << b
+    return out.transpose(0, 2, 1, 3).reshape(N, K).astype(np.uint8)
 
 
 def unpack_np(packed, N: int, K: int) -> np.ndarray:
@@ -271,9 +441,9 @@ def unpack_np(packed, N: int, K: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # O4: dequantisation.
 # ---------------------------------------------------------------------------
-def dequant_ref(codes, scales) -> np.ndarray:
+def dequant_ref(codes, scales, fmt="e3m2") -> np.ndarray:
     """Wdq[n,k] = fp16_RNE(v(c[n,k]) * s_n), product exact in float64, one rounding."""
-    v = decode(codes)
+    v = decode(codes, fmt)
     s = np.asarray(scales, dtype=np.float16).astype(np.float64)
     if v.ndim != 2 or s.shape != (v.shape[0],):
         raise ValueError("codes [N,K] and scales [N] expected")

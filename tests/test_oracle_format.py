@@ -151,14 +151,14 @@ def test_fp16_rne_is_single_rounding():
 def test_pins_catch_planted_table_mistakes(monkeypatch, mutation):
     # Plant a plausible mistake in the oracle's table and check that the
     # IEEE-embedding pin rejects it.
-    t = fo._TABLE.copy()
+    t = fo.FORMATS["e3m2"].table.copy()
     if mutation == "swap":
         t[[9, 10]] = t[[10, 9]]
     elif mutation == "sign":
         t[40] = -t[40]
     else:
         t[2] = 0.0625 * 3
-    monkeypatch.setattr(fo, "_TABLE", t)
+    monkeypatch.setattr(fo.FORMATS["e3m2"], "table", t)
     bits = ((ALL.astype(np.uint16) >> 5) << 15) | ((ALL.astype(np.uint16) & 31) << 8)
     h = bits.view(np.float16).astype(np.float64) * 4096.0
     assert not np.array_equal(h, fo.decode(ALL))
