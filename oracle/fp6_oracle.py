@@ -191,8 +191,10 @@ def encode_rne(x, fmt="e3m2") -> np.ndarray:
 
 
 def fp16_rne(x) -> np.ndarray:
-    """Round float64 values once to IEEE binary16 (RNE, subnormals kept)."""
-    return np.asarray(x, dtype=np.float64).astype(np.float16)
+    """Round float64 values once to IEEE binary16 (RNE, subnormals kept;
+    magnitudes beyond the largest binary16 round to infinity, as IEEE does)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float16)
 
 
 # ---------------------------------------------------------------------------

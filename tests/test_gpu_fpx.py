@@ -1,0 +1,158 @@
+"""GPU parity of the other weight formats (FP6 e2m3, FP5 e2m2, FP4 e2m1)
+against the CPU oracle, through the fpx_* entry points (needs an MI355X).
+
+Same bars as the FP6 e3m2 tests: de-quantisation bit-exact, fused linear
+within |Y - Y_ref| <= 2e-3 (|Y_ref| + rms) per element and relative Frobenius
+<= 5e-4, one-hot activations reproducing Wdq exactly, for every kernel
+configuration on small ragged shapes and for the automatic plan at workload
+shapes (sampled output columns for the large layers).
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_only_fp6_amd import synth
+
+from _workloads import Prepared, prepare_shape
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import weight_only_fp6_amd as fp6  # noqa: E402
+
+DEV = torch.device("cuda:0")
+FMTS = ("e2m3", "e2m2", "e2m1")
+ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16)
+SMALL_M_VARIANTS = (9, 12, 13)
+
+
+def _bits16(t):
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def _assert_tol(y_dev, y_ref, what=""):
+    rep = oracle.tolerance_report(y_dev.detach().cpu().numpy().astype(np.float64), y_ref)
+    assert rep["ok"], (what, rep)
+
+
+def _dequant_dev(codes, scales, fmt):
+    N, K = codes.shape
+    packed = torch.from_numpy(fp6.prepack(codes, scales, fmt)).to(DEV)
+    s = torch.from_numpy(np.ascontiguousarray(scales, np.float16)).to(DEV)
+    out = fp6.dequant(packed, s, N, K, fmt=fmt)
+    torch.cuda.synchronize()
+    return _bits16(out)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequant_all_codes_unit_scale(fmt):
+    N, K = 64, 512
+    ncode = 1 << fp6.bits(fmt)
+    codes = ((np.arange(N)[:, None] * 7 + np.arange(K)[None, :]) % ncode).astype(np.uint8)
+    scales = np.ones(N, np.float16)
+    assert np.array_equal(_dequant_dev(codes, scales, fmt), oracle.dequant_ref(codes, scales, fmt).view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequant_power_of_two_subnormal_and_random_scales(fmt):
+    rng = np.random.default_rng(7)
+    js = list(range(-24, 2))
+    ncode = 1 << fp6.bits(fmt)
+    N, K = 16 * len(js) + 512, 256
+    codes = rng.integers(0, ncode, (N, K)).astype(np.uint8)
+    lim = 0x4400 if fmt != "e2m1" else 0x7BFF          # |s| < 4, or any finite fp16
+    sb = rng.integers(1, lim, 512).astype(np.uint16) | (rng.integers(0, 2, 512).astype(np.uint16) << 15)
+    scales = np.concatenate([np.repeat(np.array([2.0 ** j for j in js], np.float16), 16), sb.view(np.float16)])
+    ref = oracle.dequant_ref(codes, scales, fmt).view(np.uint16)
+    assert np.array_equal(_dequant_dev(codes, scales, fmt), ref)
+    assert (ref[:16 * 10] & 0x7C00 == 0).any()     # fp16 subnormal weights survive
+
+
+@functools.lru_cache(maxsize=2)
+def _prep(name, sample, fmt):
+    return prepare_shape(synth.SHAPES[name], sample=sample, fmt=fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", ["small_8x1024x1024", "llama7b_attn_1x4096x4096",
+                                  "llama7b_mlp_down_16x4096x11008", "llama70b_mlp_16x28672x8192",
+                                  "opt30b_qkv_128x21504x7168"])
+def test_linear_workloads(fmt, name):
+    shp = synth.SHAPES[name]
+    sample = None if shp.N * shp.K <= 48 * 2**20 else 384
+    p = _prep(name, sample, fmt)
+    X, packed, s = p.to_device()
+    Y = fp6.linear(X, packed, s, shp.N, shp.K, fmt=fmt)
+    torch.cuda.synchronize()
+    _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(fmt, name))
+    if sample is None:
+        W16 = fp6.dequant(packed, s, shp.N, shp.K, fmt=fmt)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits16(W16), p.wdq_ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 64, 100])
+@pytest.mark.parametrize("NK", [(16, 256), (80, 2816)])
+def test_linear_small_shapes_every_variant(fmt, M, NK):
+    N, K = NK
+    p = Prepared(M, N, K, seed_w=N * 5 + K, seed_x=M * 13 + 2, fmt=fmt)
+    X, packed, s = p.to_device()
+    for variant in ALL_VARIANTS + (SMALL_M_VARIANTS if M <= 16 else ()):
+        Y = fp6.linear_plan(X, packed, s, N, K, variant=variant, fmt=fmt)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(fmt, M, N, K, variant))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_linear_forced_splits_and_k_coverage(fmt):
+    shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
+    p = _prep(shp.name, None, fmt)
+    X, packed, s = p.to_device()
+    for variant, splits in [(1, 7), (3, 43), (5, 3), (10, 4), (11, 2), (14, 8), (15, 5), (16, 2)]:
+        Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=variant, splits=splits, fmt=fmt)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(fmt, variant, splits))
+    for K in (512, 1280, 4096, 8192):
+        q = Prepared(4, 16 * 300, K, seed_w=K + 9, seed_x=K + 10, sample=64, fmt=fmt)
+        Xq, pq, sq = q.to_device()
+        for variant in SMALL_M_VARIANTS:
+            Y = fp6.linear_plan(Xq, pq, sq, q.N, K, variant=variant, fmt=fmt)
+            torch.cuda.synchronize()
+            _assert_tol(Y[:, torch.from_numpy(q.rows).to(DEV)], q.y_ref, what=(fmt, K, variant))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_linear_one_hot_reproduces_wdq_exactly(fmt):
+    N, K = 64, 1024
+    p = Prepared(16, N, K, seed_w=97, seed_x=3, fmt=fmt)
+    ks = np.array([0, 1, 7, 8, 255, 256, 300, 511, 512, 777, 1000, 1023, 31, 32, 33, 600])
+    X = np.zeros((16, K), np.float16)
+    X[np.arange(16), ks] = 1.0
+    Xd = torch.from_numpy(X).to(DEV)
+    _, packed, s = p.to_device()
+    want = p.wdq_ref[:, ks].T.astype(np.float64)
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 3), (5, 3), (6, 1), (8, 1), (9, 0), (12, 0),
+                            (13, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2)]:
+        Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits, fmt=fmt)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (fmt, variant, splits)
+
+
+def test_fpx_format0_matches_fp6_bitwise():
+    shp = synth.SHAPES["llama7b_attn_1x4096x4096"]
+    p = prepare_shape(shp, sample=64)
+    X, packed, s = p.to_device()
+    a = fp6.linear(X, packed, s, shp.N, shp.K)
+    b = torch.empty_like(a)
+    st = fp6.lib.fpx_linear(0, X.data_ptr(), packed.data_ptr(), s.data_ptr(), b.data_ptr(),
+                            shp.M, shp.N, shp.K, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

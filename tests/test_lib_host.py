@@ -22,7 +22,7 @@ def _declared_functions():
         if fn.endswith(".h"):
             txt = open(os.path.join(ROOT, "include", fn)).read()
             txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-            names += re.findall(r"\b(fp6_\w+)\s*\(", txt)
+            names += re.findall(r"\b(fp[6x]_\w+)\s*\(", txt)
     return sorted(set(names))
 
 
@@ -172,3 +172,133 @@ def test_linear_and_dequant_argument_errors_before_any_hip_call():
     assert L.fp6_dequant(A, A, A, 16, 100, None) == 2
     assert L.fp6_dequant(None, A, A, 16, 256, None) == 1
     assert L.fp6_dequant(A, A, A + 8, 16, 256, None) == 3
+
+
+# ---------------------------------------------------------------------------
+# Other weight formats (fpx_* entry points).
+# ---------------------------------------------------------------------------
+FPX = ("e2m3", "e2m2", "e2m1")
+
+
+def test_fpx_sizes_and_bits():
+    assert [fp6.bits(f) for f in ("e3m2",) + FPX] == [6, 6, 5, 4]
+    assert fp6.lib.fpx_bits(4) == 0 and fp6.lib.fpx_bits(-1) == 0
+    for f, tb in (("e3m2", 3072), ("e2m3", 3072), ("e2m2", 2560), ("e2m1", 2048)):
+        assert fp6.packed_bytes(16, 256, f) == tb == oracle.tile_bytes(f)
+        assert fp6.packed_bytes(28672, 8192, f) == oracle.packed_bytes(28672, 8192, f)
+        assert fp6.packed_bytes(16, 100, f) == 0
+    assert fp6.lib.fpx_packed_bytes(7, 16, 256) == 0
+    with pytest.raises(ValueError):
+        fp6.packed_bytes(16, 256, "e5m2")
+
+
+def test_fpx_format0_is_fp6():
+    W = synth.weights(48, 768, seed=3)
+    c0, s0 = fp6.quantize_rows(W)
+    codes = np.empty((48, 768), np.uint8)
+    scales = np.empty(48, np.uint16)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert fp6.lib.fpx_quantize_rows(0, p(W), 48, 768, p(codes), p(scales)) == 0
+    assert np.array_equal(codes, c0) and np.array_equal(scales, s0.view(np.uint16))
+    out = np.empty(fp6.packed_bytes(48, 768), np.uint8)
+    assert fp6.lib.fpx_prepack(0, p(codes), p(scales), 48, 768, p(out), out.size) == 0
+    assert np.array_equal(out, fp6.prepack(c0, s0))
+
+
+@pytest.mark.parametrize("fmt", FPX)
+@pytest.mark.parametrize("shape", [(5, 7), (16, 256), (37, 1000)])
+def test_fpx_quantizer_matches_oracle_random(fmt, shape):
+    W = synth.weights(*shape, seed=11 + shape[0])
+    c_lib, s_lib = fp6.quantize_rows(W, fmt)
+    c_ref, s_ref = oracle.quantize_rows(W, fmt)
+    assert np.array_equal(s_lib.view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(c_lib, c_ref)
+
+
+@pytest.mark.parametrize("fmt", FPX)
+def test_fpx_quantizer_matches_oracle_adversarial(fmt):
+    f = oracle.FORMATS[fmt]
+    s = 2.0 ** -6
+    mags = f.mags.tolist()
+    mids = [(a + b) / 2 for a, b in zip(mags[:-1], mags[1:])]
+    rng = np.random.default_rng(6)
+    rows = [
+        np.array([f.max * s] + [m * s for m in mids] + [-m * s for m in mids], np.float32),
+        np.zeros(40, np.float32),
+        (rng.standard_normal(40) * 1e-6).astype(np.float32),
+        (rng.standard_normal(40) * 5).astype(np.float32),
+    ]
+    r = np.zeros(40, np.float32)
+    r[3] = -0.0
+    r[4] = np.float32(f.max * (1 + 2.0 ** -11) * 0.01)
+    r[5] = -1e-9
+    rows.append(r)
+    width = max(len(x) for x in rows)
+    W = np.zeros((len(rows), width), np.float32)
+    for i, x in enumerate(rows):
+        W[i, : len(x)] = x
+    c_lib, s_lib = fp6.quantize_rows(W, fmt)
+    c_ref, s_ref = oracle.quantize_rows(W, fmt)
+    assert np.array_equal(s_lib.view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(c_lib, c_ref)
+
+
+@pytest.mark.parametrize("fmt", FPX)
+@pytest.mark.parametrize("shape", [(16, 256), (32, 512)])
+def test_fpx_prepack_matches_oracle_packer_bytewise(fmt, shape):
+    rng = np.random.default_rng(shape[1])
+    codes = rng.integers(0, 1 << fp6.bits(fmt), shape).astype(np.uint8)
+    got = fp6.prepack(codes, np.ones(shape[0], np.float16), fmt)
+    assert np.array_equal(got, oracle.pack_scalar(codes, fmt))
+
+
+@pytest.mark.parametrize("fmt", FPX)
+def test_fpx_prepack_round_trip_llama_shape(fmt):
+    for N, K in [(64, 8192), (32, 11008)]:
+        W = synth.weights(N, K, seed=N + K + 1)
+        codes, scales = fp6.quantize_rows(W, fmt)
+        packed = fp6.prepack(codes, scales, fmt)
+        assert np.array_equal(oracle.unpack_tiles(packed, N, K, fmt), codes)
+
+
+@pytest.mark.parametrize("fmt", FPX)
+def test_fpx_errors(fmt):
+    b = fp6.bits(fmt)
+    codes = np.zeros((16, 256), np.uint8)
+    ones = np.ones(16, np.float16)
+    bad = codes.copy()
+    bad[2, 9] = 1 << b
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.prepack(bad, ones, fmt)
+    assert e.value.name == "FP6_E_CODE"
+    bad[2, 9] = (1 << b) - 1
+    fp6.prepack(bad, ones, fmt)
+    limit = oracle.FORMATS[fmt].scale_limit
+    for sv in [np.nan, np.inf] + ([limit, -limit] if np.isfinite(limit) else []):
+        s = ones.copy()
+        s[5] = sv
+        with pytest.raises(fp6.FP6Error) as e:
+            fp6.prepack(codes, s, fmt)
+        assert e.value.name == "FP6_E_SCALE"
+    if not np.isfinite(limit):
+        s = ones.copy()
+        s[5] = 60000.0
+        fp6.prepack(codes, s, fmt)   # FP4 accepts any finite scale
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.quantize_rows(np.full((1, 4), 1e6 if np.isfinite(limit) else 1e30, np.float32), fmt)
+    assert e.value.name == "FP6_E_SCALE"
+    L = fp6.lib
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    out = np.zeros(fp6.packed_bytes(16, 256, fmt), np.uint8)
+    f = fp6.FORMATS[fmt]
+    assert L.fpx_prepack(f, p(codes), p(ones), 16, 256, p(out), out.size + 1) == 6
+    assert L.fpx_prepack(9, p(codes), p(ones), 16, 256, p(out), out.size) == 8
+    assert L.fpx_quantize_rows(9, p(np.zeros((1, 4), np.float32)), 1, 4, p(codes), p(ones)) == 8
+    A = 1 << 20
+    assert L.fpx_linear(9, A, A, A, A, 4, 16, 256, None) == 8
+    assert L.fpx_linear(f, A, A, A, A, 4, 16, 200, None) == 2
+    assert L.fpx_linear(f, None, None, None, None, 0, 16, 256, None) == 0
+    assert L.fpx_linear(f, A + 8, A, A, A, 4, 16, 256, None) == 3
+    assert L.fpx_linear_plan(f, A, A, A, A, 4, 16, 256, 99, 0, None) == 8
+    assert L.fpx_dequant(9, A, A, A, 16, 256, None) == 8
+    assert L.fpx_dequant(f, A, A, A, 16, 100, None) == 2

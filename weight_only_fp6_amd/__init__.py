@@ -1,15 +1,17 @@
-"""Thin Python binding of the MI355X FP6 (e3m2) weight-only linear library.
+"""Thin Python binding of the MI355X FPx weight-only linear library.
 
 Argument marshalling only: every step runs in ``libfp6amd.so`` (host packer
 and quantiser in C++, de-quantisation and the fused GEMM in HIP kernels for
 gfx950).  Host arrays are NumPy; device buffers are torch CUDA (ROCm) tensors
 used purely as memory, with the current torch stream passed to the library.
 
-The names follow the C ABI in ``include/fp6.h``:
+The names follow the C ABI in ``include/fp6.h`` and ``include/fpx.h``; every
+call takes ``fmt`` ("e3m2" -- the default, FP6 -- "e2m3", "e2m2" or "e2m1"):
+"e3m2" goes through the fp6_* entry points, the others through fpx_*.
 
-* :func:`packed_bytes`, :func:`pack_version`
+* :func:`packed_bytes`, :func:`pack_version`, :func:`bits`
 * :func:`quantize_rows` (host) -> ``(codes uint8 [N,K], scales fp16 [N])``
-* :func:`prepack` (host) -> ``uint8 [N*K*3/4]`` packed layout v1
+* :func:`prepack` (host) -> ``uint8 [N*K*bits/8]`` packed layout v1
 * :func:`linear` (device) -> ``Y fp16 [M,N] = X . dequant(W)^T``
 * :func:`linear_plan` (device, forced schedule), :func:`dequant` (device export)
 
@@ -35,8 +37,10 @@ STATUS_NAMES = {
 EXPORTED = (
     "fp6_pack_version", "fp6_status_string", "fp6_packed_bytes", "fp6_quantize_rows",
     "fp6_prepack", "fp6_linear", "fp6_linear_plan", "fp6_linear_plan_query", "fp6_dequant",
-    "fp6_release",
+    "fp6_release", "fpx_bits", "fpx_packed_bytes", "fpx_quantize_rows", "fpx_prepack",
+    "fpx_linear", "fpx_linear_plan", "fpx_dequant",
 )
+FORMATS = {"e3m2": 0, "e2m3": 1, "e2m2": 2, "e2m1": 3}
 
 
 class FP6Error(RuntimeError):
@@ -71,6 +75,13 @@ def _load() -> ctypes.CDLL:
         "fp6_linear_plan_query": ([i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "fp6_dequant": ([vp, vp, vp, i64, i64, vp], i32),
         "fp6_release": ([], i32),
+        "fpx_bits": ([i32], i32),
+        "fpx_packed_bytes": ([i32, i64, i64], sz),
+        "fpx_quantize_rows": ([i32, vp, i64, i64, vp, vp], i32),
+        "fpx_prepack": ([i32, vp, vp, i64, i64, vp, sz], i32),
+        "fpx_linear": ([i32, vp, vp, vp, vp, i64, i64, i64, vp], i32),
+        "fpx_linear_plan": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp], i32),
+        "fpx_dequant": ([i32, vp, vp, vp, i64, i64, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -88,40 +99,62 @@ def _check(func: str, status: int) -> None:
         raise FP6Error(func, status)
 
 
+def _fmt_id(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown weight format {fmt!r}; expected one of {sorted(FORMATS)}")
+    return FORMATS[fmt]
+
+
 def pack_version() -> int:
     return int(_lib.fp6_pack_version())
 
 
-def packed_bytes(N: int, K: int) -> int:
-    return int(_lib.fp6_packed_bytes(N, K))
+def bits(fmt: str = "e3m2") -> int:
+    return int(_lib.fpx_bits(_fmt_id(fmt)))
+
+
+def packed_bytes(N: int, K: int, fmt: str = "e3m2") -> int:
+    if fmt == "e3m2":
+        return int(_lib.fp6_packed_bytes(N, K))
+    return int(_lib.fpx_packed_bytes(_fmt_id(fmt), N, K))
 
 
 def _host_ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def quantize_rows(W: np.ndarray):
+def quantize_rows(W: np.ndarray, fmt: str = "e3m2"):
     """Host quantiser: float32 [N,K] -> (codes uint8 [N,K], scales float16 [N])."""
+    f = _fmt_id(fmt)
     W = np.ascontiguousarray(W, dtype=np.float32)
     if W.ndim != 2:
         raise ValueError("W must be 2-D")
     N, K = W.shape
     codes = np.empty((N, K), dtype=np.uint8)
     scales = np.empty(N, dtype=np.uint16)
-    _check("fp6_quantize_rows", _lib.fp6_quantize_rows(_host_ptr(W), N, K, _host_ptr(codes), _host_ptr(scales)))
+    if fmt == "e3m2":
+        st = _lib.fp6_quantize_rows(_host_ptr(W), N, K, _host_ptr(codes), _host_ptr(scales))
+    else:
+        st = _lib.fpx_quantize_rows(f, _host_ptr(W), N, K, _host_ptr(codes), _host_ptr(scales))
+    _check("quantize_rows", st)
     return codes, scales.view(np.float16)
 
 
-def prepack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Host packer: codes uint8 [N,K] + scales fp16 [N] -> packed uint8 [N*K*3/4]."""
+def prepack(codes: np.ndarray, scales: np.ndarray, fmt: str = "e3m2") -> np.ndarray:
+    """Host packer: codes uint8 [N,K] + scales fp16 [N] -> packed uint8 [N*K*bits/8]."""
+    f = _fmt_id(fmt)
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float16).view(np.uint16)
     if codes.ndim != 2 or scales.shape != (codes.shape[0],):
         raise ValueError("codes [N,K] and scales [N] expected")
     N, K = codes.shape
-    nbytes = packed_bytes(N, K)
+    nbytes = packed_bytes(N, K, fmt)
     out = np.empty(max(nbytes, 1), dtype=np.uint8)
-    _check("fp6_prepack", _lib.fp6_prepack(_host_ptr(codes), _host_ptr(scales), N, K, _host_ptr(out), nbytes))
+    if fmt == "e3m2":
+        st = _lib.fp6_prepack(_host_ptr(codes), _host_ptr(scales), N, K, _host_ptr(out), nbytes)
+    else:
+        st = _lib.fpx_prepack(f, _host_ptr(codes), _host_ptr(scales), N, K, _host_ptr(out), nbytes)
+    _check("prepack", st)
     return out[:nbytes]
 
 
@@ -135,14 +168,15 @@ def _dev_ptr(t) -> int:
     return int(t.data_ptr()) if t is not None else 0
 
 
-def linear(X, packed, scales, N: int, K: int, out=None, stream=None):
+def linear(X, packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e3m2"):
     """Y[M,N] fp16 = X[M,K] . dequant(W)^T on the GPU (asynchronous)."""
-    return linear_plan(X, packed, scales, N, K, variant=0, splits=0, out=out, stream=stream)
+    return linear_plan(X, packed, scales, N, K, variant=0, splits=0, out=out, stream=stream, fmt=fmt)
 
 
 def linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int = 0,
-                out=None, stream=None):
+                out=None, stream=None, fmt: str = "e3m2"):
     import torch
+    f = _fmt_id(fmt)
     if X.dtype != torch.float16 or X.dim() != 2 or X.shape[1] != K or not X.is_contiguous():
         raise ValueError("X must be a contiguous fp16 [M,K] tensor")
     M = X.shape[0]
@@ -150,13 +184,14 @@ def linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
     elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp16 [M,N] tensor")
-    if packed.numel() != packed_bytes(N, K) or packed.dtype != torch.uint8:
-        raise ValueError("packed must be the uint8 output of prepack for (N, K)")
+    if packed.numel() != packed_bytes(N, K, fmt) or packed.dtype != torch.uint8:
+        raise ValueError("packed must be the uint8 output of prepack for (N, K) and this format")
     if scales.dtype != torch.float16 or scales.numel() != N:
         raise ValueError("scales must be fp16 [N]")
-    st = _lib.fp6_linear_plan(_dev_ptr(X), _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out),
-                              M, N, K, variant, splits, _stream_handle(stream))
-    _check("fp6_linear_plan", st)
+    args = (_dev_ptr(X), _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), M, N, K, variant, splits,
+            _stream_handle(stream))
+    st = _lib.fp6_linear_plan(*args) if fmt == "e3m2" else _lib.fpx_linear_plan(f, *args)
+    _check("linear_plan", st)
     return out
 
 
@@ -177,13 +212,15 @@ def plan_query(M: int, N: int, K: int):
     return v.value, s.value
 
 
-def dequant(packed, scales, N: int, K: int, out=None, stream=None):
+def dequant(packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e3m2"):
     """Wdq fp16 [N,K] from the packed weights (same device splice as linear)."""
     import torch
+    f = _fmt_id(fmt)
     if out is None:
         out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
-    st = _lib.fp6_dequant(_dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), N, K, _stream_handle(stream))
-    _check("fp6_dequant", st)
+    args = (_dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), N, K, _stream_handle(stream))
+    st = _lib.fp6_dequant(*args) if fmt == "e3m2" else _lib.fpx_dequant(f, *args)
+    _check("dequant", st)
     return out
 
 

@@ -1,9 +1,11 @@
 """Build the HIP library ``libfp6amd.so`` in-tree for gfx950.
 
-Host code (fp6_host.cpp) is compiled with g++ and the kernels plus device
-entry points (fp6_kernels.hip) with hipcc; both are linked into one shared
-library next to this file.  Run ``python weight_only_fp6_amd/build_lib.py`` (by
-path, so the package -- which loads the library -- is not imported first).
+Host code (fp6_host.cpp) is compiled with g++; the host dispatch and device
+entry points (fpx_linear.hip) and the kernels, one translation unit per
+weight format (fpx_kern_*.hip, compiled in parallel), with hipcc; all are
+linked into one shared library next to this file.  Run
+``python weight_only_fp6_amd/build_lib.py`` (by path, so the package -- which
+loads the library -- is not imported first).
 """
 
 from __future__ import annotations
@@ -45,16 +47,40 @@ def _run(cmd, verbose):
     return res
 
 
+HIP_SOURCES = ["fpx_linear.hip", "fpx_kern_e3m2.hip", "fpx_kern_e2m3.hip", "fpx_kern_e2m2.hip",
+               "fpx_kern_e2m1.hip"]
+
+
+def _run_parallel(cmds, verbose):
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = None
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0 and failed is None:
+            sys.stderr.write(out)
+            failed = cmd
+    if failed:
+        raise RuntimeError(f"build step failed: {' '.join(failed[:3])} ...")
+
+
 def build(verbose: bool = False) -> str:
     """Compile and link the library; returns its path.  Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", CSRC]
     host_o = os.path.join(BUILD, "fp6_host.o")
-    kern_o = os.path.join(BUILD, "fp6_kernels.o")
-    _run(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "fp6_host.cpp"), "-o", host_o], verbose)
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "fp6_kernels.hip"), "-o", kern_o], verbose)
+    objs = [host_o]
+    cmds = [["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "fp6_host.cpp"), "-o", host_o]]
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+    _run_parallel(cmds, verbose)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, host_o, kern_o], verbose)
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     shutil.move(tmp, LIB)
     # Bandwidth probe used only by the benchmark's roofline measurement.
     probe_tmp = PROBE_LIB + ".tmp"

@@ -1,5 +1,5 @@
-// Host side of the FP6 (e3m2) weight-only linear layer: status strings,
-// size rules, the row quantiser and the offline packer (layout v1).
+// Host side of the FPx weight-only linear layer: status strings, size rules,
+// the row quantiser and the offline packer (layout v1) of every format.
 //
 // Plain C++17, no HIP calls: everything here runs on the CPU.
 //
@@ -10,10 +10,12 @@
 // are this library's own design for 64-lane wavefronts (see fp6.h).
 
 #include "fp6.h"
+#include "fpx.h"
 #include "fp6_limits.h"
 
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <vector>
 
 namespace {
@@ -55,26 +57,112 @@ uint16_t double_to_half_rne(double x) {
   return sign | static_cast<uint16_t>((field << 10) | (static_cast<int>(r) - 1024));
 }
 
-// Nearest e3m2 magnitude index (0..31) of q >= 0, ties to the even index,
-// saturating at 28.  e3m2 value = 2^(e-3) * (1 + m/4) for e >= 1 and
-// m * 2^-4 for e == 0; the index is e*4 + m.
-int e3m2_magnitude_index(double q) {
-  if (!(q < 28.0)) return 31;               // also +inf
-  if (q < 0.25) {                           // subnormal grid, spacing 2^-4
-    return static_cast<int>(std::nearbyint(q * 16.0));  // 4 -> 0.25, the first normal
+// Weight formats: code width, mantissa bits, exponent bias, largest
+// magnitude, and the bound on |scale| (the kernels fold s * 2^12 or s * 2^14
+// into one fp16, exact only below it; FP4 multiplies by s itself).
+struct FormatInfo {
+  int bits, mbits, bias;
+  double vmax, scale_limit;
+};
+constexpr double kInf = std::numeric_limits<double>::infinity();
+constexpr FormatInfo kFormats[] = {
+    {6, 2, 3, 28.0, 16.0},  // FPX_E3M2
+    {6, 3, 1, 7.5, 4.0},    // FPX_E2M3
+    {5, 2, 1, 7.0, 4.0},    // FPX_E2M2
+    {4, 1, 1, 6.0, kInf},   // FPX_E2M1
+};
+constexpr int kNumFormats = sizeof(kFormats) / sizeof(kFormats[0]);
+
+const FormatInfo* format_info(int format) {
+  return format >= 0 && format < kNumFormats ? &kFormats[format] : nullptr;
+}
+
+// Nearest magnitude index of q >= 0 (index = e * 2^M + m), ties to the even
+// index, saturating at the largest magnitude.  Values: m * 2^(1-bias-M) for
+// e == 0 (subnormal), 2^(e-bias) * (1 + m / 2^M) for e >= 1.
+int magnitude_index(const FormatInfo& f, double q) {
+  const int nmag = 1 << (f.bits - 1);
+  if (!(q < f.vmax)) return nmag - 1;        // also +inf
+  if (q < std::ldexp(1.0, 1 - f.bias)) {     // subnormal grid
+    // the first normal comes out as index 2^M, its own code
+    return static_cast<int>(std::nearbyint(std::ldexp(q, f.bias - 1 + f.mbits)));
   }
   int E;
-  const double f = std::frexp(q, &E);       // q = f * 2^E, f in [0.5, 1)
-  double r = std::nearbyint(f * 8.0);       // 3 significant bits: r in 4..8
-  if (r == 8.0) { r = 4.0; ++E; }
-  // value = r/8 * 2^E = (4 + m)/4 * 2^(e-3)  =>  e = E + 2, m = r - 4
-  const int idx = (E + 2) * 4 + (static_cast<int>(r) - 4);
-  return idx > 31 ? 31 : idx;
+  const double fr = std::frexp(q, &E);       // q = fr * 2^E, fr in [0.5, 1)
+  const double top = std::ldexp(1.0, f.mbits + 1);
+  double r = std::nearbyint(fr * top);       // M+1 significant bits
+  if (r == top) { r = top / 2; ++E; }
+  // value = r / 2^(M+1) * 2^E = (2^M + m) / 2^M * 2^(E-1)  =>  e = E - 1 + bias
+  const int idx = (E - 1 + f.bias) * (1 << f.mbits) + (static_cast<int>(r) - (1 << f.mbits));
+  return idx > nmag - 1 ? nmag - 1 : idx;
 }
 
 bool shape_ok(int64_t N, int64_t K) {
   return N >= fp6::kTileN && K >= fp6::kTileK && N <= fp6::kMaxDim && K <= fp6::kMaxDim &&
          N % fp6::kTileN == 0 && K % fp6::kTileK == 0 && N * K <= fp6::kMaxNK;
+}
+
+// One 16 x 256 tile of codes (rows of `src` K apart) into packed layout v1.
+// Lane L = 16g + r owns row r, k = 32j + 8g + i (k-step j, element i).
+void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
+  // Per lane: 4-bit words w4[j/4][lane][j%4]; 6-bit formats add 2-bit words
+  // w2[lane][j/2], FP5 adds 1-bit words w1[lane][j/4].
+  uint32_t w4[2][64][4];
+  uint32_t w2[64][4];
+  uint32_t w1[64][2];
+  std::memset(w4, 0, sizeof(w4));
+  std::memset(w2, 0, sizeof(w2));
+  std::memset(w1, 0, sizeof(w1));
+  static const int kE2M3Base[8] = {0, 1, 2, 3, 8, 9, 10, 11};
+  for (int lane = 0; lane < 64; ++lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const uint8_t* row = src + r * K;
+    for (int j = 0; j < 8; ++j) {
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t c = row[32 * j + 8 * g + i];
+        const int p = 4 * (j & 1) + (i >> 1);  // 6-bit formats: pair in the 2-bit word
+        const int h = i & 1;                   // even / odd element of the pair
+        const int slot = (i >> 1) + 4 * (i & 1);
+        uint32_t& d4 = w4[j >> 2][lane][j & 3];
+        switch (format) {
+          case FPX_E3M2:
+            w2[lane][j >> 1] |= ((c >> 4) & 1u) << ((12 + 16 * h + 2 * p) & 31);
+            w2[lane][j >> 1] |= ((c >> 5) & 1u) << ((15 + 16 * h + 2 * p) & 31);
+            d4 |= (c & 0xFu) << (4 * slot);
+            break;
+          case FPX_E2M3: {
+            const int b = kE2M3Base[p] + 16 * h;
+            w2[lane][j >> 1] |= ((c >> 4) & 1u) << b;
+            w2[lane][j >> 1] |= ((c >> 5) & 1u) << (b + 4);
+            d4 |= (c & 0xFu) << (4 * slot);
+            break;
+          }
+          case FPX_E2M2:
+            w1[lane][j >> 2] |= ((c >> 4) & 1u) << (4 * (j & 3) + (i >> 1) + 16 * h);
+            d4 |= (c & 0xFu) << (4 * slot);
+            break;
+          default:  // FPX_E2M1: whole code, natural nibble order
+            d4 |= (c & 0xFu) << (4 * i);
+            break;
+        }
+      }
+    }
+  }
+  // Little-endian words: x86-64 hosts store them in the required byte order.
+  switch (format) {
+    case FPX_E3M2:
+    case FPX_E2M3:
+      std::memcpy(tile, w2, sizeof(w2));
+      std::memcpy(tile + 1024, w4, sizeof(w4));
+      break;
+    case FPX_E2M2:
+      std::memcpy(tile, w4, sizeof(w4));
+      std::memcpy(tile + 2048, w1, sizeof(w1));
+      break;
+    default:
+      std::memcpy(tile, w4, sizeof(w4));
+      break;
+  }
 }
 
 }  // namespace
@@ -89,8 +177,8 @@ const char* fp6_status_string(int status) {
     case FP6_E_NULL: return "a required pointer is NULL";
     case FP6_E_SHAPE: return "shape outside the supported range (N%16, K%256, limits)";
     case FP6_E_ALIGN: return "a device pointer is misaligned";
-    case FP6_E_CODE: return "a weight code is larger than 63";
-    case FP6_E_SCALE: return "a scale is not finite or has |s| >= 16";
+    case FP6_E_CODE: return "a weight code does not fit the format's width";
+    case FP6_E_SCALE: return "a scale is not finite or outside the format's range";
     case FP6_E_SIZE: return "a buffer size does not match";
     case FP6_E_HIP: return "a HIP runtime call or kernel launch failed";
     case FP6_E_VALUE: return "an input value or plan parameter is invalid";
@@ -98,15 +186,27 @@ const char* fp6_status_string(int status) {
   }
 }
 
-size_t fp6_packed_bytes(int64_t N, int64_t K) {
-  if (!shape_ok(N, K)) return 0;
-  return static_cast<size_t>(N) * static_cast<size_t>(K) / 4 * 3;
+int fpx_bits(int format) {
+  const FormatInfo* f = format_info(format);
+  return f ? f->bits : 0;
 }
 
-int fp6_quantize_rows(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+size_t fpx_packed_bytes(int format, int64_t N, int64_t K) {
+  const FormatInfo* f = format_info(format);
+  if (!f || !shape_ok(N, K)) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K) / 8 * static_cast<size_t>(f->bits);
+}
+
+size_t fp6_packed_bytes(int64_t N, int64_t K) { return fpx_packed_bytes(FPX_E3M2, N, K); }
+
+int fpx_quantize_rows(int format, const float* W, int64_t N, int64_t K, uint8_t* codes,
+                      uint16_t* scales) {
+  const FormatInfo* f = format_info(format);
+  if (!f) return FP6_E_VALUE;
   if (!W || !codes || !scales) return FP6_E_NULL;
   if (N < 1 || K < 1 || N > fp6::kMaxDim || K > fp6::kMaxDim || N * K > fp6::kMaxNK)
     return FP6_E_SHAPE;
+  const int sign_shift = f->bits - 1;
   for (int64_t n = 0; n < N; ++n) {
     const float* row = W + n * K;
     float amax = 0.0f;
@@ -115,9 +215,9 @@ int fp6_quantize_rows(const float* W, int64_t N, int64_t K, uint8_t* codes, uint
       const float a = std::fabs(row[k]);
       if (a > amax) amax = a;
     }
-    const uint16_t sb = double_to_half_rne(static_cast<double>(amax) / 28.0);
+    const uint16_t sb = double_to_half_rne(static_cast<double>(amax) / f->vmax);
     const double s = half_bits_to_double(sb);
-    if (!std::isfinite(s) || std::fabs(s) >= 16.0) return FP6_E_SCALE;
+    if (!std::isfinite(s) || std::fabs(s) >= f->scale_limit) return FP6_E_SCALE;
     scales[n] = sb;
     uint8_t* out = codes + n * K;
     if (s == 0.0) {
@@ -127,58 +227,45 @@ int fp6_quantize_rows(const float* W, int64_t N, int64_t K, uint8_t* codes, uint
     for (int64_t k = 0; k < K; ++k) {
       const double q = static_cast<double>(row[k]) / s;
       const int sign = std::signbit(row[k]) ? 1 : 0;
-      out[k] = static_cast<uint8_t>((sign << 5) | e3m2_magnitude_index(std::fabs(q)));
+      out[k] = static_cast<uint8_t>((sign << sign_shift) | magnitude_index(*f, std::fabs(q)));
     }
   }
   return FP6_OK;
 }
 
-int fp6_prepack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+int fp6_quantize_rows(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+  return fpx_quantize_rows(FPX_E3M2, W, N, K, codes, scales);
+}
+
+int fpx_prepack(int format, const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                 void* packed, size_t packed_bytes) {
+  const FormatInfo* f = format_info(format);
+  if (!f) return FP6_E_VALUE;
   if (!codes || !scales || !packed) return FP6_E_NULL;
   if (!shape_ok(N, K)) return FP6_E_SHAPE;
-  if (packed_bytes != fp6_packed_bytes(N, K)) return FP6_E_SIZE;
+  if (packed_bytes != fpx_packed_bytes(format, N, K)) return FP6_E_SIZE;
   for (int64_t n = 0; n < N; ++n) {
     const double s = half_bits_to_double(scales[n]);
-    if (!std::isfinite(s) || std::fabs(s) >= 16.0) return FP6_E_SCALE;
+    if (!std::isfinite(s) || std::fabs(s) >= f->scale_limit) return FP6_E_SCALE;
   }
   const size_t total = static_cast<size_t>(N) * static_cast<size_t>(K);
+  const uint32_t code_end = 1u << f->bits;
   for (size_t i = 0; i < total; ++i)
-    if (codes[i] > 63) return FP6_E_CODE;
+    if (codes[i] >= code_end) return FP6_E_CODE;
 
   uint8_t* out = static_cast<uint8_t*>(packed);
   const int64_t kblocks = K / fp6::kTileK;
-  // One tile = 16 rows x 256 k -> 64 lanes x (4 two-bit words + 8 four-bit words).
-  for (int64_t nb = 0; nb < N / fp6::kTileN; ++nb) {
-    for (int64_t kb = 0; kb < kblocks; ++kb) {
-      uint32_t w2[64][4];
-      uint32_t w4[2][64][4];
-      std::memset(w2, 0, sizeof(w2));
-      std::memset(w4, 0, sizeof(w4));
-      for (int lane = 0; lane < 64; ++lane) {
-        const int r = lane & 15, g = lane >> 4;
-        const uint8_t* src = codes + (nb * fp6::kTileN + r) * K + kb * fp6::kTileK;
-        for (int j = 0; j < 8; ++j) {
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t c = src[32 * j + 8 * g + i];
-            const int p = 4 * (j & 1) + (i >> 1);
-            const int h = i & 1;
-            const int pos_e2 = (12 + 16 * h + 2 * p) & 31;
-            const int pos_s = (15 + 16 * h + 2 * p) & 31;
-            w2[lane][j >> 1] |= ((c >> 4) & 1u) << pos_e2;
-            w2[lane][j >> 1] |= ((c >> 5) & 1u) << pos_s;
-            const int slot = (i >> 1) + 4 * (i & 1);
-            w4[j >> 2][lane][j & 3] |= (c & 0xFu) << (4 * slot);
-          }
-        }
-      }
-      uint8_t* tile = out + (nb * kblocks + kb) * fp6::kTileBytes;
-      // Little-endian words: x86-64 hosts store them in the required byte order.
-      std::memcpy(tile, w2, sizeof(w2));
-      std::memcpy(tile + 1024, w4, sizeof(w4));
-    }
-  }
+  const int64_t tile_bytes = 4096 / 8 * f->bits;
+  for (int64_t nb = 0; nb < N / fp6::kTileN; ++nb)
+    for (int64_t kb = 0; kb < kblocks; ++kb)
+      pack_tile(format, codes + nb * fp6::kTileN * K + kb * fp6::kTileK, K,
+                out + (nb * kblocks + kb) * tile_bytes);
   return FP6_OK;
+}
+
+int fp6_prepack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                void* packed, size_t packed_bytes) {
+  return fpx_prepack(FPX_E3M2, codes, scales, N, K, packed, packed_bytes);
 }
 
 }  // extern "C"

@@ -1,43 +1,49 @@
-// Fused FP6 (e3m2) weight-only linear layer for gfx950 (MI355X): kernels,
-// schedule choice and the device entry points of the C ABI.
+// Kernels of the fused FPx weight-only linear layer for gfx950 (MI355X),
+// templated on the weight format, plus their host-side launchers.  Included
+// by one translation unit per format (fpx_kern_<format>.hip).
 //
 // FP6-LLM (arXiv 2401.14112), abstract: the two costs of FP6 weights on GPUs
-// are irregular-width memory access and de-quantisation overhead.  TC-FPx
+// are irregular-width memory access and de-quantisation overhead, and one
+// kernel scheme should serve float weights of several widths.  TC-FPx
 // explainer (duicuo.cn), section "redesigning the kernel solution": one
 // kernel de-quantises in registers and feeds FP16 matrix units; weights are
-// pre-split into 2-bit and 4-bit pieces so the splice is a few bit operations.
+// pre-split into power-of-two pieces so the splice is a few bit operations.
 //
-// gfx950 design (this file):
+// gfx950 design:
 //  * A wave owns 16 weight rows (one 16x16x32 MFMA A-operand row block) and a
-//    range of 256-wide k-tiles.  Per tile it issues three coalesced 16-byte
-//    loads per lane (1 KiB per wave instruction): one 2-bit word quad and two
-//    4-bit word quads, exactly the bits of its 64 codes.
-//  * Splice: for the fp16 pair (2r, 2r+1) of k-step j,
+//    range of 256-wide k-tiles.  Per tile it issues two or three coalesced
+//    loads per lane (1 KiB per wave instruction for a 16-byte load), exactly
+//    the bits of its 64 codes.
+//  * Splice (FP6 e3m2): for the fp16 pair (2r, 2r+1) of k-step j,
 //      bits = ((d4 shifted into bits 8..11 / 24..27) & 0x0F000F00)
 //           | (rotr(d2, 2p) & 0x90009000),      p = 4*(j%2) + r
 //    which is the fp16 pattern of v(c) * 2^-12 (sign at bit 15, e2 at bit 12,
-//    e1 e0 m1 m0 at bits 11..8; e3m2 subnormals become fp16 subnormals).
-//  * Scale fold: one v_pk_mul_f16 by s_n * 2^12, an exact fp16 for |s| < 16,
-//    so the single rounding gives fp16_RNE(v * s_n) bit for bit.
+//    e1 e0 m1 m0 at bits 11..8; e3m2 subnormals become fp16 subnormals).  The
+//    other formats use the same scheme with their own masks and rotations.
+//  * Scale fold: one v_pk_mul_f16 by s_n * 2^12 (e3m2), an exact fp16 for
+//    |s| < 16, so the single rounding gives fp16_RNE(v * s_n) bit for bit.
 //  * fp32 MFMA accumulation (v_mfma_f32_16x16x32_f16), A = weights (rows n),
 //    B = X^T (columns m), so the accumulator tile is Y^T.
 //  * Split-K for the memory-bound small-M regime: each split writes an fp32
 //    partial tile; the last split to arrive (agent-scope counter) sums the
 //    partials in split order and stores fp16 Y, then resets the counter.
+#pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
 #include <type_traits>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "fp6.h"
 #include "fp6_limits.h"
+#include "fpx_launch.h"
 
 namespace {
+
+using fpx::kKsMaxTiles;
+using fpx::kKsliceMaxTiles;
+
+inline int64_t fpx_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
@@ -46,21 +52,60 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
-constexpr int kTileWords = 192;  // 3072 bytes / 16 bytes per lane-quad
 
 // ---------------------------------------------------------------------------
-// Splice + scale of one k-step: 8 fp16 weights of this lane (elements
-// 8g..8g+7 of the k-step, row r), from the 2-bit word d2 (covering k-steps
-// 2*(j/2) and 2*(j/2)+1) and the 4-bit word d4 (k-step j).
+// Weight formats.  Every format packs a 16-row x 256-k tile so that wave lane
+// L = 16g + r holds the codes of row r at k = 32j + 8g + i (k-step j, element
+// i): the A-operand order of v_mfma_f32_16x16x32_f16.  A lane rebuilds each
+// pair of fp16 weights with a few bit operations (FP4: the gfx950 FP4
+// conversion instruction) and one v_pk_mul_f16 by its row's scale.
+//   FP6 e3m2: fp16 pattern (s<<15)|(c&31)<<8 = v * 2^-12; scale factor s*2^12
+//   FP6 e2m3: (s<<15)|(c&31)<<7 = v * 2^-14;            scale factor s*2^14
+//   FP5 e2m2: (s<<15)|(c&15)<<8 = v * 2^-14;            scale factor s*2^14
+//   FP4 e2m1: converted exactly to v;                    scale factor s
+// Each scale factor is an exact fp16 for the scales fp6_prepack/fpx_prepack
+// accept, so the one rounding of the multiply gives fp16_RNE(v * s).
 // ---------------------------------------------------------------------------
-template <int JODD>
-__device__ __forceinline__ half8v splice_kstep(uint32_t d2, uint32_t d4, half2v s2) {
-  constexpr uint32_t kM4 = 0x0F000F00u, kM2 = 0x90009000u;
-  constexpr int sh = 8 * JODD;  // 2*p for pair 0 of this k-step
-  const uint32_t t0 = ((d4 << 8) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 0) & kM2);
-  const uint32_t t1 = ((d4 << 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 2) & kM2);
-  const uint32_t t2 = (d4 & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 4) & kM2);
-  const uint32_t t3 = ((d4 >> 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 6) & kM2);
+enum : int { kE3M2 = 0, kE2M3 = 1, kE2M2 = 2, kE2M1 = 3 };
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Packed registers of one tile (8 k-steps) and one half-tile (4 k-steps) of
+// one row block, per lane.
+struct TileFp6 { u32x4 q2, q4a, q4b; };   // 2-bit words (2 k-steps each), 4-bit words
+struct HalfFp6 { u32x2 q2; u32x4 q4; };
+struct TileFp5 { u32x4 q4a, q4b; u32x2 q1; };  // 4-bit words, 1-bit words (4 k-steps each)
+struct HalfFp5 { uint32_t q1; u32x4 q4; };
+struct TileFp4 { u32x4 q4a, q4b; };
+struct HalfFp4 { u32x4 q4; };
+
+// 6-bit formats, one k-step: 8 fp16 weights (elements 8g..8g+7 of row r)
+// from the 2-bit word d2 (k-steps 2*(j/2), +1) and the 4-bit word d4.
+//   e3m2: pair p = 4*(j%2)+q has e2,s at bits 12+2p, 15+2p (+16 for the odd
+//         element); rotr(d2, 2p) lands them on fp16 bits 12 and 15.
+//   e2m3: pair p has e1,s at bits b, b+4 (+16), b = [0,1,2,3,8,9,10,11][p];
+//         rotr(d2, (b-11) mod 32) lands them on fp16 bits 11 and 15.
+// The 4-bit word holds element i in nibble slot i/2 + 4*(i%2), so one shift
+// per pair q moves elements 2q and 2q+1 onto both fp16 halves.
+template <int F, int JODD>
+__device__ __forceinline__ half8v splice6(uint32_t d2, uint32_t d4, half2v s2) {
+  uint32_t t0, t1, t2, t3;
+  if constexpr (F == kE3M2) {
+    constexpr uint32_t kM4 = 0x0F000F00u, kM2 = 0x90009000u;
+    constexpr int sh = 8 * JODD;  // 2*p for pair 0 of this k-step
+    t0 = ((d4 << 8) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 0) & kM2);
+    t1 = ((d4 << 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 2) & kM2);
+    t2 = (d4 & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 4) & kM2);
+    t3 = ((d4 >> 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 6) & kM2);
+  } else {
+    static_assert(F == kE2M3, "6-bit formats: e3m2, e2m3");
+    constexpr uint32_t kM4 = 0x07800780u, kM2 = 0x88008800u;
+    constexpr int r0 = JODD ? 29 : 21;  // (b - 11) mod 32 for pair 0 of this k-step
+    t0 = ((d4 << 7) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, r0) & kM2);
+    t1 = ((d4 << 3) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, r0 + 1) & kM2);
+    t2 = ((d4 >> 1) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, r0 + 2) & kM2);
+    t3 = ((d4 >> 5) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, (r0 + 3) & 31) & kM2);
+  }
   const half2v h0 = __builtin_bit_cast(half2v, t0) * s2;
   const half2v h1 = __builtin_bit_cast(half2v, t1) * s2;
   const half2v h2 = __builtin_bit_cast(half2v, t2) * s2;
@@ -71,16 +116,124 @@ __device__ __forceinline__ half8v splice_kstep(uint32_t d2, uint32_t d4, half2v 
   return a;
 }
 
-template <int J>
-__device__ __forceinline__ half8v splice_tile_step(const u32x4& q2, const u32x4& q4a,
-                                                   const u32x4& q4b, half2v s2) {
-  const uint32_t d2 = q2[J >> 1];
-  const uint32_t d4 = (J < 4) ? q4a[J & 3] : q4b[J & 3];
-  return splice_kstep<J & 1>(d2, d4, s2);
+// FP5 e2m2, k-step j: the 4-bit word d4 as for FP6 (magnitude e1 e0 m1 m0 to
+// fp16 bits 11..8), the sign from the 1-bit word d1 (k-steps 4*(j/4)..+3):
+// pair P = 4*(j%4)+q has its signs at bits P and P+16; rotr(d1, (P-15) mod 32)
+// lands them on fp16 bits 15 and 31.
+template <int JM4>
+__device__ __forceinline__ half8v splice5(uint32_t d1, uint32_t d4, half2v s2) {
+  constexpr uint32_t kM4 = 0x0F000F00u, kM1 = 0x80008000u;
+  constexpr int r0 = (4 * JM4 + 17) & 31;  // (P - 15) mod 32 for pair 0 of this k-step
+  const uint32_t t0 = ((d4 << 8) & kM4) | (__builtin_amdgcn_alignbit(d1, d1, r0) & kM1);
+  const uint32_t t1 = ((d4 << 4) & kM4) | (__builtin_amdgcn_alignbit(d1, d1, (r0 + 1) & 31) & kM1);
+  const uint32_t t2 = (d4 & kM4) | (__builtin_amdgcn_alignbit(d1, d1, (r0 + 2) & 31) & kM1);
+  const uint32_t t3 = ((d4 >> 4) & kM4) | (__builtin_amdgcn_alignbit(d1, d1, (r0 + 3) & 31) & kM1);
+  const half2v h0 = __builtin_bit_cast(half2v, t0) * s2;
+  const half2v h1 = __builtin_bit_cast(half2v, t1) * s2;
+  const half2v h2 = __builtin_bit_cast(half2v, t2) * s2;
+  const half2v h3 = __builtin_bit_cast(half2v, t3) * s2;
+  half8v a;
+  a[0] = h0[0]; a[1] = h0[1]; a[2] = h1[0]; a[3] = h1[1];
+  a[4] = h2[0]; a[5] = h2[1]; a[6] = h3[0]; a[7] = h3[1];
+  return a;
 }
 
+// FP4 e2m1, one k-step: byte q of the 4-bit word holds elements 2q (low
+// nibble) and 2q+1; v_cvt_scalef32_pk_f16_fp4 with scale 1 converts them
+// exactly (it applies only the exponent of its scale operand).
+__device__ __forceinline__ half8v splice4(uint32_t d4, half2v s2) {
+  const half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4, 1.0f, 0) * s2;
+  const half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4, 1.0f, 1) * s2;
+  const half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4, 1.0f, 2) * s2;
+  const half2v h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d4, 1.0f, 3) * s2;
+  half8v a;
+  a[0] = h0[0]; a[1] = h0[1]; a[2] = h1[0]; a[3] = h1[1];
+  a[4] = h2[0]; a[5] = h2[1]; a[6] = h3[0]; a[7] = h3[1];
+  return a;
+}
+
+// Format traits.  kTileQuads: 16-byte units per packed tile; kHalfLoads:
+// load instructions per half-tile (the tiled kernel's wait count depends on
+// it).  load/load_half take the lane's pointer into the tile (tile + lane,
+// in 16-byte units) and the lane index.
+template <int F> struct Fmt;
+
+template <int F>
+struct Fp6Fmt {
+  static constexpr int kTileQuads = 192;
+  static constexpr int kHalfLoads = 2;
+  static constexpr float kScaleFactor = F == kE3M2 ? 4096.0f : 16384.0f;
+  using Tile = TileFp6;
+  using Half = HalfFp6;
+  __device__ static void load(Tile& t, const u32x4* p, int) { t.q2 = p[0]; t.q4a = p[64]; t.q4b = p[128]; }
+  __device__ static void load_half(Half& h, const u32x4* p, int hh, int) {
+    h.q2 = reinterpret_cast<const u32x2*>(p)[hh];
+    h.q4 = p[64 + 64 * hh];
+  }
+  template <int J>
+  __device__ static half8v step(const Tile& t, half2v s2) {
+    return splice6<F, J & 1>(t.q2[J >> 1], J < 4 ? t.q4a[J & 3] : t.q4b[J & 3], s2);
+  }
+  template <int JJ>
+  __device__ static half8v half_step(const Half& h, half2v s2) {
+    return splice6<F, JJ & 1>(h.q2[JJ >> 1], h.q4[JJ], s2);
+  }
+};
+template <> struct Fmt<kE3M2> : Fp6Fmt<kE3M2> {};
+template <> struct Fmt<kE2M3> : Fp6Fmt<kE2M3> {};
+
+template <>
+struct Fmt<kE2M2> {
+  static constexpr int kTileQuads = 160;
+  static constexpr int kHalfLoads = 2;
+  static constexpr float kScaleFactor = 16384.0f;
+  using Tile = TileFp5;
+  using Half = HalfFp5;
+  // 4-bit plane in 16-byte units 0..127 of the tile, 1-bit plane as 8 bytes
+  // per lane from byte 2048.
+  __device__ static const u32x2* plane1(const u32x4* p, int lane) {
+    return reinterpret_cast<const u32x2*>(p) - lane + 256;
+  }
+  __device__ static void load(Tile& t, const u32x4* p, int lane) {
+    t.q4a = p[0]; t.q4b = p[64]; t.q1 = plane1(p, lane)[0];
+  }
+  __device__ static void load_half(Half& h, const u32x4* p, int hh, int lane) {
+    h.q1 = reinterpret_cast<const uint32_t*>(plane1(p, lane))[hh];
+    h.q4 = p[64 * hh];
+  }
+  template <int J>
+  __device__ static half8v step(const Tile& t, half2v s2) {
+    return splice5<J & 3>(t.q1[J >> 2], J < 4 ? t.q4a[J & 3] : t.q4b[J & 3], s2);
+  }
+  template <int JJ>
+  __device__ static half8v half_step(const Half& h, half2v s2) {
+    return splice5<JJ>(h.q1, h.q4[JJ], s2);
+  }
+};
+
+template <>
+struct Fmt<kE2M1> {
+  static constexpr int kTileQuads = 128;
+  static constexpr int kHalfLoads = 1;
+  static constexpr float kScaleFactor = 1.0f;
+  using Tile = TileFp4;
+  using Half = HalfFp4;
+  __device__ static void load(Tile& t, const u32x4* p, int) { t.q4a = p[0]; t.q4b = p[64]; }
+  __device__ static void load_half(Half& h, const u32x4* p, int hh, int) { h.q4 = p[64 * hh]; }
+  template <int J>
+  __device__ static half8v step(const Tile& t, half2v s2) {
+    return splice4(J < 4 ? t.q4a[J & 3] : t.q4b[J & 3], s2);
+  }
+  template <int JJ>
+  __device__ static half8v half_step(const Half& h, half2v s2) {
+    return splice4(h.q4[JJ], s2);
+  }
+};
+
+template <int F>
 __device__ __forceinline__ half2v row_scale2(const _Float16* scales, int64_t n) {
-  const _Float16 s = scales[n] * static_cast<_Float16>(4096.0f);  // exact for |s| < 16
+  _Float16 s = scales[n];
+  if constexpr (Fmt<F>::kScaleFactor != 1.0f) s = s * static_cast<_Float16>(Fmt<F>::kScaleFactor);
   half2v s2;
   s2[0] = s;
   s2[1] = s;
@@ -90,6 +243,7 @@ __device__ __forceinline__ half2v row_scale2(const _Float16* scales, int64_t n) 
 // ---------------------------------------------------------------------------
 // De-quantisation export: one wave per tile, Wdq fp16 [N][K] row-major.
 // ---------------------------------------------------------------------------
+template <int F>
 __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restrict__ wp,
                                                           const _Float16* __restrict__ scales,
                                                           _Float16* __restrict__ w16,
@@ -100,19 +254,19 @@ __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restric
   if (tile >= (N >> 4) * ktiles) return;
   const int64_t nb = tile / ktiles, kt = tile % ktiles;
   const int r = lane & 15, g = lane >> 4;
-  const u32x4* t = wp + tile * kTileWords + lane;
-  const u32x4 q2 = t[0], q4a = t[64], q4b = t[128];
+  typename Fmt<F>::Tile t;
+  Fmt<F>::load(t, wp + tile * Fmt<F>::kTileQuads + lane, lane);
   const int64_t n = nb * 16 + r;
-  const half2v s2 = row_scale2(scales, n);
+  const half2v s2 = row_scale2<F>(scales, n);
   half8v* out = reinterpret_cast<half8v*>(w16 + n * K + kt * 256 + 8 * g);
-  out[0] = splice_tile_step<0>(q2, q4a, q4b, s2);
-  out[4] = splice_tile_step<1>(q2, q4a, q4b, s2);
-  out[8] = splice_tile_step<2>(q2, q4a, q4b, s2);
-  out[12] = splice_tile_step<3>(q2, q4a, q4b, s2);
-  out[16] = splice_tile_step<4>(q2, q4a, q4b, s2);
-  out[20] = splice_tile_step<5>(q2, q4a, q4b, s2);
-  out[24] = splice_tile_step<6>(q2, q4a, q4b, s2);
-  out[28] = splice_tile_step<7>(q2, q4a, q4b, s2);
+  out[0] = Fmt<F>::template step<0>(t, s2);
+  out[4] = Fmt<F>::template step<1>(t, s2);
+  out[8] = Fmt<F>::template step<2>(t, s2);
+  out[12] = Fmt<F>::template step<3>(t, s2);
+  out[16] = Fmt<F>::template step<4>(t, s2);
+  out[20] = Fmt<F>::template step<5>(t, s2);
+  out[24] = Fmt<F>::template step<6>(t, s2);
+  out[28] = Fmt<F>::template step<7>(t, s2);
 }
 
 // ---------------------------------------------------------------------------
@@ -184,9 +338,9 @@ __device__ __forceinline__ void store_y_block(_Float16* __restrict__ Y, const fl
 // and the X fragments of the next tile, splices each k-step once and reuses
 // it for MB MFMAs; each X fragment is reused for A row blocks.
 // ---------------------------------------------------------------------------
-template <int A, int MB>
+template <int F, int A>
 struct WStage {
-  u32x4 q2[A], q4a[A], q4b[A];
+  typename Fmt<F>::Tile t[A];
 };
 
 template <int MB>
@@ -194,7 +348,7 @@ struct XStage {
   half8v b[8][MB];
 };
 
-template <int A, int MB, int D>
+template <int F, int A, int MB, int D>
 __global__ __launch_bounds__(256) void fp6_gemm_stream(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
@@ -223,8 +377,8 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
   for (int a = 0; a < A; ++a) {
     int64_t nb = rg * A + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * kTileWords + lane;
-    s2[a] = row_scale2(scales, nb * 16 + r);
+    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    s2[a] = row_scale2<F>(scales, nb * 16 + r);
   }
   // B operand rows m = (mg*MB + mb)*16 + r; rows >= M read row M-1 (their
   // accumulator columns are never stored).
@@ -240,12 +394,10 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 #pragma unroll
   for (int i = 0; i < A * MB; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  auto load_w = [&](WStage<A, MB>& st, int64_t kt) {
+  auto load_w = [&](WStage<F, A>& st, int64_t kt) {
 #pragma unroll
     for (int a = 0; a < A; ++a) {
-      st.q2[a] = w[a][kt * kTileWords];
-      st.q4a[a] = w[a][kt * kTileWords + 64];
-      st.q4b[a] = w[a][kt * kTileWords + 128];
+      Fmt<F>::load(st.t[a], w[a] + kt * Fmt<F>::kTileQuads, lane);
     }
   };
   auto load_x = [&](XStage<MB>& xs, int64_t kt) {
@@ -255,10 +407,10 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
       for (int mb = 0; mb < MB; ++mb)
         xs.b[j][mb] = *reinterpret_cast<const half8v*>(xrow[mb] + kt * 256 + 32 * j);
   };
-  auto mac = [&](const WStage<A, MB>& st, const XStage<MB>& xs) {
+  auto mac = [&](const WStage<F, A>& st, const XStage<MB>& xs) {
 #define FP6_STEP(J)                                                                   \
   _Pragma("unroll") for (int a = 0; a < A; ++a) {                                     \
-    const half8v av = splice_tile_step<J>(st.q2[a], st.q4a[a], st.q4b[a], s2[a]);     \
+    const half8v av = Fmt<F>::template step<J>(st.t[a], s2[a]);     \
     _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) acc[a * MB + mb] =              \
         __builtin_amdgcn_mfma_f32_16x16x32_f16(av, xs.b[J][mb], acc[a * MB + mb], 0, 0, 0); \
   }
@@ -272,7 +424,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
   // few extra loads at the end hit in cache).  The loads in flight are then
   // the same on every path, so the in-order vmcnt waits only ever wait for
   // the stage being consumed.  The last (< D) tiles run in an explicit tail.
-  WStage<A, MB> ring[D];
+  WStage<F, A> ring[D];
   XStage<MB> xs[2];
   const int64_t klast = kt1 > kt0 ? kt1 - 1 : kt0;
   auto clampk = [&](int64_t t) { return t < klast ? t : klast; };
@@ -323,7 +475,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 // (rows XOR-swizzled in 16-byte units, so the B-fragment reads are free of
 // bank conflicts), one barrier per tile.  This cuts X's L2->CU traffic by NW.
 // ---------------------------------------------------------------------------
-template <int A, int D, int NW>
+template <int F, int A, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
@@ -355,8 +507,8 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
   for (int a = 0; a < A; ++a) {
     int64_t nb = rg * A + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * kTileWords + lane;
-    s2[a] = row_scale2(scales, nb * 16 + r);
+    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    s2[a] = row_scale2<F>(scales, nb * 16 + r);
   }
   // X staging: unit q = (row rr = q/32, chunk c = q%32) of the tile; rows
   // beyond M repeat row M-1 (their accumulator columns are never stored).
@@ -388,22 +540,20 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
   float4v acc[A];
 #pragma unroll
   for (int i = 0; i < A; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
-  auto load_w = [&](WStage<A, 1>& st, int64_t kt) {
+  auto load_w = [&](WStage<F, A>& st, int64_t kt) {
 #pragma unroll
     for (int a = 0; a < A; ++a) {
-      st.q2[a] = w[a][kt * kTileWords];
-      st.q4a[a] = w[a][kt * kTileWords + 64];
-      st.q4b[a] = w[a][kt * kTileWords + 128];
+      Fmt<F>::load(st.t[a], w[a] + kt * Fmt<F>::kTileQuads, lane);
     }
   };
-  auto mac = [&](const WStage<A, 1>& st, int slot) {
+  auto mac = [&](const WStage<F, A>& st, int slot) {
     const half8v* xb = xs[slot];
 #define FP6_XL_STEP(J)                                                                   \
   {                                                                                      \
     const half8v bf = xb[r * 32 + ((4 * J + g) ^ r)];                                    \
     _Pragma("unroll") for (int a = 0; a < A; ++a) acc[a] =                               \
         __builtin_amdgcn_mfma_f32_16x16x32_f16(                                          \
-            splice_tile_step<J>(st.q2[a], st.q4a[a], st.q4b[a], s2[a]), bf, acc[a], 0, 0, 0); \
+            Fmt<F>::template step<J>(st.t[a], s2[a]), bf, acc[a], 0, 0, 0); \
   }
     FP6_XL_STEP(0) FP6_XL_STEP(1) FP6_XL_STEP(2) FP6_XL_STEP(3)
     FP6_XL_STEP(4) FP6_XL_STEP(5) FP6_XL_STEP(6) FP6_XL_STEP(7)
@@ -415,7 +565,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
   // reader was iteration i-2, loads X(kt+2), consumes the ring stage of tile
   // kt and refills it, then meets the barrier.  Branch-free steady state
   // with clamped prefetch indices; the last (< D) tiles run in a tail.
-  WStage<A, 1> ring[D];
+  WStage<F, A> ring[D];
   if (kt0 < kt1) {
 #pragma unroll
     for (int d = 0; d < D; ++d) load_w(ring[d], clampk(kt0 + d));
@@ -477,7 +627,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 // (deterministic) by wave 0, which stores fp16 Y.  No global workspace, no
 // X re-reads, all k-slices of a row block stream concurrently.
 // ---------------------------------------------------------------------------
-template <int KTW, int kKsWaves>
+template <int F, int KTW, int kKsWaves>
 __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
@@ -505,26 +655,21 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     for (int j = 0; j < 8; ++j)
       xf[t][j] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 256 + 32 * j + 8 * g);
 
-  WStage<1, 1> wst[2][KTW];
-  auto load_rb = [&](WStage<1, 1> (&st)[KTW], int64_t nb) {
-    const u32x4* base = wp + (nb * ktiles) * kTileWords + lane;
+  WStage<F, 1> wst[2][KTW];
+  auto load_rb = [&](WStage<F, 1> (&st)[KTW], int64_t nb) {
+    const u32x4* base = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) {
-      const int64_t kt = tile_of(t);
-      st[t].q2[0] = base[kt * kTileWords];
-      st[t].q4a[0] = base[kt * kTileWords + 64];
-      st[t].q4b[0] = base[kt * kTileWords + 128];
-    }
+    for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * Fmt<F>::kTileQuads, lane);
   };
-  auto rb_mac = [&](const WStage<1, 1> (&st)[KTW], int64_t nb) {
-    const half2v s2 = row_scale2(scales, nb * 16 + r);
+  auto rb_mac = [&](const WStage<F, 1> (&st)[KTW], int64_t nb) {
+    const half2v s2 = row_scale2<F>(scales, nb * 16 + r);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < KTW; ++t) {
       if (t < ktw) {
 #define FP6_KS_STEP(J)                                                                     \
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                            \
-      splice_tile_step<J>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[t][J], acc, 0, 0, 0);
+      Fmt<F>::template step<J>(st[t].t[0], s2), xf[t][J], acc, 0, 0, 0);
         FP6_KS_STEP(0) FP6_KS_STEP(1) FP6_KS_STEP(2) FP6_KS_STEP(3)
         FP6_KS_STEP(4) FP6_KS_STEP(5) FP6_KS_STEP(6) FP6_KS_STEP(7)
 #undef FP6_KS_STEP
@@ -572,7 +717,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 // workgroup per row block: meant for N/16 <= CUs, where X is used once per CU
 // anyway.
 // ---------------------------------------------------------------------------
-template <int KTW, int WK>
+template <int F, int KTW, int WK>
 __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
@@ -603,16 +748,11 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     // loads (they do not depend on the row block) and keep them all live.
     const int64_t nb = blockIdx.x;
     if (nb >= nblocks) return;  // uniform for the workgroup
-    const u32x4* base = wp + (nb * ktiles) * kTileWords + lane;
-    WStage<1, 1> st[KTW];
+    const u32x4* base = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    WStage<F, 1> st[KTW];
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) {
-      const int64_t kt = tile_of(t);
-      st[t].q2[0] = base[kt * kTileWords];
-      st[t].q4a[0] = base[kt * kTileWords + 64];
-      st[t].q4b[0] = base[kt * kTileWords + 128];
-    }
-    const half2v s2 = row_scale2(scales, nb * 16 + r);
+    for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * Fmt<F>::kTileQuads, lane);
+    const half2v s2 = row_scale2<F>(scales, nb * 16 + r);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KTW == 1) {
       // One tile per wave: all of its X fragments are loaded at once.
@@ -623,7 +763,7 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
       if (ktw > 0) {
 #define FP6_KX1(J)                                                                          \
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                             \
-      splice_tile_step<J>(st[0].q2[0], st[0].q4a[0], st[0].q4b[0], s2), xf[J], acc, 0, 0, 0);
+      Fmt<F>::template step<J>(st[0].t[0], s2), xf[J], acc, 0, 0, 0);
         FP6_KX1(0) FP6_KX1(1) FP6_KX1(2) FP6_KX1(3) FP6_KX1(4) FP6_KX1(5) FP6_KX1(6) FP6_KX1(7)
 #undef FP6_KX1
       }
@@ -638,15 +778,15 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
       if (t < ktw) {
         const half8v* xf = xr[hh % 3];
         if (hh & 1) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<4>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[0], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<5>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[1], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<6>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[2], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<7>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[3], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<4>(st[t].t[0], s2), xf[0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<5>(st[t].t[0], s2), xf[1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<6>(st[t].t[0], s2), xf[2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<7>(st[t].t[0], s2), xf[3], acc, 0, 0, 0);
         } else {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<0>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[0], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<1>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[1], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<2>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[2], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(splice_tile_step<3>(st[t].q2[0], st[t].q4a[0], st[t].q4b[0], s2), xf[3], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<0>(st[t].t[0], s2), xf[0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<1>(st[t].t[0], s2), xf[1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<2>(st[t].t[0], s2), xf[2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<3>(st[t].t[0], s2), xf[3], acc, 0, 0, 0);
         }
       }
       // Keep the X prefetch two half-tiles ahead: without this fence the
@@ -684,22 +824,19 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
 //   * each wave waits for its own direct loads, then one barrier.
 // ---------------------------------------------------------------------------
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int TA>
+template <int F, int TA>
 struct WHalf {           // packed words of one half-tile for TA row blocks
-  u32x2 q2[TA];          // 2-bit words for k-steps 4h'..4h'+3 (two words)
-  u32x4 q4[TA];          // 4-bit words, one per k-step
+  typename Fmt<F>::Half h[TA];
 };
 
-template <int JJ, int TA>
-__device__ __forceinline__ void splice_half(half8v (&dst)[TA], const WHalf<TA>& w, const half2v (&s2)[TA]) {
+template <int F, int JJ, int TA>
+__device__ __forceinline__ void splice_half(half8v (&dst)[TA], const WHalf<F, TA>& w, const half2v (&s2)[TA]) {
 #pragma unroll
-  for (int a = 0; a < TA; ++a) dst[a] = splice_kstep<JJ & 1>(w.q2[a][JJ >> 1], w.q4[a][JJ], s2[a]);
+  for (int a = 0; a < TA; ++a) dst[a] = Fmt<F>::template half_step<JJ>(w.h[a], s2[a]);
 }
 
 // TA row blocks per wave, NW waves per workgroup, TA * NW = 16 (256 rows).
-template <int B, int TA, int NW>
+template <int F, int B, int TA, int NW>
 __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
@@ -733,16 +870,15 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
   for (int a = 0; a < kTA; ++a) {
     int64_t nb = nt * 16 + wave * kTA + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * kTileWords + lane;
-    s2[a] = row_scale2(scales, nb * 16 + r);
+    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    s2[a] = row_scale2<F>(scales, nb * 16 + r);
   }
-  auto load_wh = [&](WHalf<TA>& st, int64_t h) {  // half-tile h: k-tile h>>1, half h&1
+  auto load_wh = [&](WHalf<F, TA>& st, int64_t h) {  // half-tile h: k-tile h>>1, half h&1
     const int64_t kt = h >> 1;
     const int hh = static_cast<int>(h & 1);
 #pragma unroll
     for (int a = 0; a < kTA; ++a) {
-      st.q2[a] = reinterpret_cast<const u32x2*>(w[a] + kt * kTileWords)[hh];
-      st.q4[a] = w[a][kt * kTileWords + 64 + 64 * hh];
+      Fmt<F>::load_half(st.h[a], w[a] + kt * Fmt<F>::kTileQuads, hh, lane);
     }
   };
 
@@ -802,22 +938,22 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
   // Wait for this wave's direct LDS loads of the next half-tile (issued
   // before the kTA*2 weight loads of that half-tile), then the barrier makes
   // every wave's copy visible.
-  constexpr int kWLoads = kTA * 2;
+  constexpr int kWLoads = kTA * Fmt<F>::kHalfLoads;
   constexpr int kWaitDma = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (7 << 4) | (15 << 8);
 
   // One half-tile: k-steps 0..3 from buffer `cur`; prefetch X(h+1) into
   // `nxt` and the weights of h+1 into `wn`; overlap the last k-step with the
   // splice of h+1's first k-step.
-  auto half_step = [&](half8v* cur, half8v* nxt, const WHalf<TA>& wc, WHalf<TA>& wn, int64_t hnext) {
+  auto half_step = [&](half8v* cur, half8v* nxt, const WHalf<F, TA>& wc, WHalf<F, TA>& wn, int64_t hnext) {
     dma_x(nxt, hnext);
     __builtin_amdgcn_sched_barrier(0);
     load_wh(wn, hnext);
     __builtin_amdgcn_sched_barrier(0);
     read_b(bfr[0], cur, 0);
-    read_b(bfr[1], cur, 1); splice_half<1, TA>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
-    read_b(bfr[0], cur, 2); splice_half<2, TA>(afr[0], wc, s2); mfmas(afr[1], bfr[1]); interleave(IB{});
-    read_b(bfr[1], cur, 3); splice_half<3, TA>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
-                            splice_half<0, TA>(afr[0], wn, s2); mfmas(afr[1], bfr[1]); interleave(I0{});
+    read_b(bfr[1], cur, 1); splice_half<F, 1, TA>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
+    read_b(bfr[0], cur, 2); splice_half<F, 2, TA>(afr[0], wc, s2); mfmas(afr[1], bfr[1]); interleave(IB{});
+    read_b(bfr[1], cur, 3); splice_half<F, 3, TA>(afr[1], wc, s2); mfmas(afr[0], bfr[0]); interleave(IB{});
+                            splice_half<F, 0, TA>(afr[0], wn, s2); mfmas(afr[1], bfr[1]); interleave(I0{});
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitDma);
     __syncthreads();
@@ -828,12 +964,12 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
     // Branch-free steady state: prefetch indices are clamped to the split's
     // last half-tile, so every path has the same loads in flight.
     auto clamph = [&](int64_t h) { return h < h1 - 1 ? h : h1 - 1; };
-    WHalf<TA> wa, wb;
+    WHalf<F, TA> wa, wb;
     dma_x(xbuf0, h0);
     load_wh(wa, h0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    splice_half<0, TA>(afr[0], wa, s2);
+    splice_half<F, 0, TA>(afr[0], wa, s2);
     for (int64_t h = h0; h < h1; h += 2) {
       half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));
       half_step(xbuf1, xbuf0, wb, wa, clamph(h + 2));
@@ -856,111 +992,9 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
 }
 
 // ---------------------------------------------------------------------------
-// Host: workspace per (device, stream), CU count per device.
+// Launchers (host code), one instantiation per format.
 // ---------------------------------------------------------------------------
-struct Workspace {
-  void* part = nullptr;
-  size_t part_bytes = 0;
-  unsigned* counters = nullptr;
-  size_t counter_count = 0;
-};
-
-std::mutex g_mu;
-std::map<std::pair<int, void*>, Workspace> g_ws;
-std::map<int, int> g_cus;
-
-int device_cus(int dev) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_cus.find(dev);
-  if (it != g_cus.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  g_cus[dev] = cus;
-  return cus;
-}
-
-// Ensure the (device, stream) workspace holds at least the given sizes.
-int get_workspace(int dev, void* stream, size_t part_bytes, size_t counter_count, Workspace** out) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  Workspace& ws = g_ws[{dev, stream}];
-  if (ws.part_bytes < part_bytes || ws.counter_count < counter_count) {
-    if (ws.part || ws.counters) {
-      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return FP6_E_HIP;
-      if (ws.part) (void)hipFree(ws.part);
-      if (ws.counters) (void)hipFree(ws.counters);
-      ws = Workspace{};
-    }
-    const size_t pb = part_bytes > ws.part_bytes ? part_bytes : ws.part_bytes;
-    const size_t cc = counter_count > ws.counter_count ? counter_count : ws.counter_count;
-    if (hipMalloc(&ws.part, pb) != hipSuccess) { ws = Workspace{}; return FP6_E_HIP; }
-    if (hipMalloc(reinterpret_cast<void**>(&ws.counters), cc * sizeof(unsigned)) != hipSuccess) {
-      (void)hipFree(ws.part);
-      ws = Workspace{};
-      return FP6_E_HIP;
-    }
-    if (hipMemset(ws.counters, 0, cc * sizeof(unsigned)) != hipSuccess) return FP6_E_HIP;
-    ws.part_bytes = pb;
-    ws.counter_count = cc;
-  }
-  *out = &ws;
-  return FP6_OK;
-}
-
-bool shape_ok(int64_t N, int64_t K) {
-  return N >= fp6::kTileN && K >= fp6::kTileK && N <= fp6::kMaxDim && K <= fp6::kMaxDim &&
-         N % fp6::kTileN == 0 && K % fp6::kTileK == 0 && N * K <= fp6::kMaxNK;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int check_linear_args(const void* X, const void* W, const void* s, void* Y, int64_t M, int64_t N,
-                      int64_t K) {
-  if (!shape_ok(N, K) || M < 0 || M > fp6::kMaxDim) return FP6_E_SHAPE;
-  if (M == 0) return FP6_OK;
-  if (!X || !W || !s || !Y) return FP6_E_NULL;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || (reinterpret_cast<uintptr_t>(s) & 1u))
-    return FP6_E_ALIGN;
-  return FP6_OK;
-}
-
-// Kernel configurations reachable through fp6_linear_plan's `variant`.
-enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice, kXlds };
-struct KernelCfg {
-  Kind kind;
-  int a, mb, d;  // stream: row blocks/wave, 16-col blocks/wave, ring depth; tiled: B = mb
-};
-constexpr KernelCfg kCfgs[] = {
-    {Kind::kAuto, 0, 0, 0},    // 0: automatic
-    {Kind::kStream, 1, 1, 4},  // 1: streaming, 1 row block per wave, 16 columns, ring depth 4
-    {Kind::kStream, 1, 4, 2},  // 2: streaming, 1 row block per wave, 64 columns, ring depth 2
-    {Kind::kStream, 2, 1, 4},  // 3: streaming, 2 row blocks per wave, 16 columns, ring depth 4
-    {Kind::kStream, 4, 1, 2},  // 4: streaming, 4 row blocks per wave, 16 columns, ring depth 2
-    {Kind::kTiled, 4, 4, 4},   // 5: tiled, 256 rows x 64 columns, 4 waves x 4 row blocks
-    {Kind::kTiled, 4, 8, 4},   // 6: tiled, 256 rows x 128 columns, 4 waves x 4 row blocks
-    {Kind::kStream, 1, 1, 8},  // 7: streaming, 1 row block per wave, 16 columns, ring depth 8
-    {Kind::kStream, 2, 1, 6},  // 8: streaming, 2 row blocks per wave, 16 columns, ring depth 6
-    {Kind::kKsplit, 1, 1, 8},  // 9: k-split persistent, M <= 16, K <= 8192 (X in registers)
-    {Kind::kTiled, 2, 8, 8},   // 10: tiled, 256 rows x 128 columns, 8 waves x 2 row blocks
-    {Kind::kTiled, 2, 4, 8},   // 11: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks
-    {Kind::kKsplit, 1, 1, 16}, // 12: k-split persistent with 16 waves per workgroup
-    {Kind::kKslice, 1, 1, 16}, // 13: k-slice, 16 waves per row block, X streamed
-    {Kind::kXlds, 2, 1, 4},    // 14: streaming + X in LDS, 2 row blocks/wave, ring 4, 4 waves
-    {Kind::kXlds, 1, 1, 4},    // 15: streaming + X in LDS, 1 row block/wave, ring 4, 4 waves
-    {Kind::kXlds, 2, 1, 8},    // 16: streaming + X in LDS, 2 row blocks/wave, ring 4, 8 waves
-};
-constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
-
-struct Plan {
-  int variant;
-  int splits;
-};
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-constexpr int kKsMaxTiles = 32;  // k-split kernels: K <= 8192
-
-template <int KTW, int WK>
+template <int F, int KTW, int WK>
 int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                     int64_t K, int cus, hipStream_t stream) {
   const int64_t nblocks = N >> 4;
@@ -970,30 +1004,28 @@ int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
   void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_ksplit<KTW, WK>), grid,
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK>), grid,
                          dim3(64 * WK), args, 0, stream) == hipSuccess
              ? FP6_OK
              : FP6_E_HIP;
 }
 
 // WK waves per workgroup; each wave holds ceil(K/256 / WK) k-tiles.
-template <int WK>
+template <int F, int WK>
 int launch_ksplit(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                   int64_t K, int cus, hipStream_t stream) {
-  switch (ceil_div(K >> 8, WK)) {
-    case 1: return launch_ksplit_t<1, WK>(X, W, S, Y, M, N, K, cus, stream);
-    case 2: return launch_ksplit_t<2, WK>(X, W, S, Y, M, N, K, cus, stream);
-    case 3: if constexpr (WK == 8) return launch_ksplit_t<3, WK>(X, W, S, Y, M, N, K, cus, stream);
+  switch (fpx_ceil_div(K >> 8, WK)) {
+    case 1: return launch_ksplit_t<F, 1, WK>(X, W, S, Y, M, N, K, cus, stream);
+    case 2: return launch_ksplit_t<F, 2, WK>(X, W, S, Y, M, N, K, cus, stream);
+    case 3: if constexpr (WK == 8) return launch_ksplit_t<F, 3, WK>(X, W, S, Y, M, N, K, cus, stream);
             return FP6_E_VALUE;
-    case 4: if constexpr (WK == 8) return launch_ksplit_t<4, WK>(X, W, S, Y, M, N, K, cus, stream);
+    case 4: if constexpr (WK == 8) return launch_ksplit_t<F, 4, WK>(X, W, S, Y, M, N, K, cus, stream);
             return FP6_E_VALUE;
     default: return FP6_E_VALUE;
   }
 }
 
-constexpr int kKsliceMaxTiles = 48;  // k-slice kernels: K <= 12288
-
-template <int KTW, int WK>
+template <int F, int KTW, int WK>
 int launch_kslice_t(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                     int64_t K, int cus, hipStream_t stream) {
   (void)cus;
@@ -1003,28 +1035,29 @@ int launch_kslice_t(const void* X, const void* W, const void* S, void* Y, int64_
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
   void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_kslice<KTW, WK>), grid, dim3(64 * WK),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_kslice<F, KTW, WK>), grid, dim3(64 * WK),
                          args, 0, stream) == hipSuccess
              ? FP6_OK
              : FP6_E_HIP;
 }
 
 // 8 waves up to K = 2048, else 16 waves with up to 3 k-tiles each.
+template <int F>
 int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                   int64_t K, int cus, hipStream_t stream) {
   const int64_t kt = K >> 8;
-  if (kt <= 8) return launch_kslice_t<1, 8>(X, W, S, Y, M, N, K, cus, stream);
-  if (kt <= 16) return launch_kslice_t<1, 16>(X, W, S, Y, M, N, K, cus, stream);
-  if (kt <= 32) return launch_kslice_t<2, 16>(X, W, S, Y, M, N, K, cus, stream);
-  if (kt <= 48) return launch_kslice_t<3, 16>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 8) return launch_kslice_t<F, 1, 8>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 16) return launch_kslice_t<F, 1, 16>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 32) return launch_kslice_t<F, 2, 16>(X, W, S, Y, M, N, K, cus, stream);
+  if (kt <= 48) return launch_kslice_t<F, 3, 16>(X, W, S, Y, M, N, K, cus, stream);
   return FP6_E_VALUE;
 }
 
-template <int A, int D, int NW>
+template <int F, int A, int D, int NW>
 int launch_xlds(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                int64_t K, int splits, Workspace* ws, hipStream_t stream) {
-  const int64_t ngroups = ceil_div(N >> 4, A), gsets = ceil_div(ngroups, NW);
-  const int64_t mgroups = ceil_div(M, 16);
+                int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
+  const int64_t ngroups = fpx_ceil_div(N >> 4, A), gsets = fpx_ceil_div(ngroups, NW);
+  const int64_t mgroups = fpx_ceil_div(M, 16);
   const int64_t per_mg = gsets * splits;
   int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
   if (mg_chunk < 1) mg_chunk = 1;
@@ -1032,87 +1065,23 @@ int launch_xlds(const void* X, const void* W, const void* S, void* Y, int64_t M,
   const u32x4* w = static_cast<const u32x4*>(W);
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
-  float* part = ws ? static_cast<float*>(ws->part) : nullptr;
-  unsigned* cnt = ws ? ws->counters : nullptr;
   for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
     const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
     int64_t mg_base = mg0;
     void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_xlds<A, D, NW>), grid, dim3(64 * NW),
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_xlds<F, A, D, NW>), grid, dim3(64 * NW),
                         args, 0, stream) != hipSuccess)
       return FP6_E_HIP;
   }
   return FP6_OK;
 }
 
-// Work units (each with its own split-K counter) and the number of partial
-// floats per unit and split.
-void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats) {
-  if (c.kind == Kind::kTiled) {
-    // c.a = row blocks per wave, c.d = waves per workgroup (c.a * c.d = 16)
-    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16) * c.d;
-    *floats = static_cast<int64_t>(c.a) * c.mb * 256;
-  } else {
-    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
-    *floats = static_cast<int64_t>(c.a) * c.mb * 256;
-  }
-}
-
-Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
-  Plan p;
-  const int64_t ktiles = K >> 8;
-  if (variant == 0) {
-    // Measured on MI355X: up to K = 4096 the k-slice kernel (at most one row
-    // block per CU) or the k-split kernels (8 waves up to K = 2048, else 16)
-    // are fastest; for longer K the streaming kernel with X shared through
-    // LDS (1 row block per wave, 4 waves) is.
-    const bool one_rb_per_cu = (N >> 4) <= cus;
-    if (M <= 16 && ktiles <= 16 && one_rb_per_cu) p.variant = 13;
-    else if (M <= 16 && ktiles <= 8) p.variant = 9;
-    else if (M <= 16 && ktiles <= 16) p.variant = 12;
-    else if (M <= 16) p.variant = 15;
-    else if (M <= 64) p.variant = 11;
-    else p.variant = 10;
-  } else {
-    p.variant = variant;
-  }
-  const KernelCfg& c = kCfgs[p.variant];
-  if (c.kind == Kind::kKsplit || c.kind == Kind::kKslice) {
-    p.splits = 1;
-    return p;
-  }
-  if (splits > 0) {
-    p.splits = splits;
-    return p;
-  }
-  int64_t s;
-  if (c.kind == Kind::kTiled) {
-    // One workgroup per CU: split K while a whole extra round of workgroups
-    // fits on the CUs (rounding down: a partial second round costs more than
-    // it gains), keeping at least 2 k-tiles per split.
-    const int64_t wgs = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16);
-    s = cus / wgs;
-    if (s > ktiles / 2) s = ktiles / 2;
-  } else {
-    // No split once there are two waves per CU; otherwise split K towards
-    // ~4 waves per CU (measured: more splits cost more in the fix-up than
-    // they add in loads in flight).
-    const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
-    s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
-    if (s > ktiles / 2) s = ktiles / 2;
-  }
-  if (s > 64) s = 64;
-  if (s < 1) s = 1;
-  p.splits = static_cast<int>(s);
-  return p;
-}
-
-template <int A, int MB, int D>
+template <int F, int A, int MB, int D>
 int launch_stream(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                  int64_t K, int splits, Workspace* ws, hipStream_t stream) {
-  const int64_t ngroups = ceil_div(N >> 4, A), gquads = ceil_div(ngroups, 4);
-  const int64_t mgroups = ceil_div(M, 16 * MB);
+                  int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
+  const int64_t ngroups = fpx_ceil_div(N >> 4, A), gquads = fpx_ceil_div(ngroups, 4);
+  const int64_t mgroups = fpx_ceil_div(M, 16 * MB);
   // Keep each launch below 2^24 workgroups.
   const int64_t per_mg = gquads * splits;
   int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
@@ -1121,26 +1090,24 @@ int launch_stream(const void* X, const void* W, const void* S, void* Y, int64_t 
   const u32x4* w = static_cast<const u32x4*>(W);
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
-  float* part = ws ? static_cast<float*>(ws->part) : nullptr;
-  unsigned* cnt = ws ? ws->counters : nullptr;
   for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
     const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
     int64_t mg_base = mg0;
     void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
     // The launch's own status (not the thread's sticky last error).
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_stream<A, MB, D>), grid, dim3(256),
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_stream<F, A, MB, D>), grid, dim3(256),
                         args, 0, stream) != hipSuccess)
       return FP6_E_HIP;
   }
   return FP6_OK;
 }
 
-template <int B, int TA, int NW>
+template <int F, int B, int TA, int NW>
 int launch_tiled(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                 int64_t K, int splits, Workspace* ws, hipStream_t stream) {
-  const int64_t ntiles = ceil_div(N >> 4, 16);
-  const int64_t mgroups = ceil_div(M, 16 * B);
+                 int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
+  const int64_t ntiles = fpx_ceil_div(N >> 4, 16);
+  const int64_t mgroups = fpx_ceil_div(M, 16 * B);
   const int64_t per_mg = ntiles * splits;
   int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
   if (mg_chunk < 1) mg_chunk = 1;
@@ -1148,134 +1115,74 @@ int launch_tiled(const void* X, const void* W, const void* S, void* Y, int64_t M
   const u32x4* w = static_cast<const u32x4*>(W);
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
-  float* part = ws ? static_cast<float*>(ws->part) : nullptr;
-  unsigned* cnt = ws ? ws->counters : nullptr;
   for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
     const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
     int64_t mg_base = mg0;
     void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_tiled<B, TA, NW>), grid, dim3(64 * NW),
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_tiled<F, B, TA, NW>), grid, dim3(64 * NW),
                         args, 0, stream) != hipSuccess)
       return FP6_E_HIP;
   }
   return FP6_OK;
 }
 
-int linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                int64_t K, int variant, int splits, void* stream) {
-  int st = check_linear_args(X, W, S, Y, M, N, K);
-  if (st != FP6_OK || M == 0) return st;
-  if (variant < 0 || variant >= kNumVariants || splits < 0 || splits > (K >> 8) || splits > 4096)
-    return FP6_E_VALUE;
-  // One launch covers at least one m-group: its workgroup count must stay
-  // below 2^24 (so that blocks x 256 threads fits in 32 bits).  Automatic
-  // plans only split when there are fewer units than ~8 waves per CU, far
-  // inside this bound.
-  if (splits > 0 && ceil_div(N >> 4, 4) * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
-    return FP6_E_VALUE;
-  // The k-split kernel keeps each wave's X slice in registers: M <= 16 and
-  // at most K = 8192 (and a per-wave tile count it is instantiated for); it
-  // never splits across workgroups.
-  if (variant > 0 && kCfgs[variant].kind == Kind::kKsplit &&
-      (M > 16 || (K >> 8) > kKsMaxTiles || splits > 1))
-    return FP6_E_VALUE;
-  if (variant > 0 && kCfgs[variant].kind == Kind::kKslice &&
-      (M > 16 || (K >> 8) > kKsliceMaxTiles || splits > 1))
-    return FP6_E_VALUE;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
-  const int cus = device_cus(dev);
-  const Plan p = choose_plan(M, N, K, cus, variant, splits);
-  const KernelCfg& c = kCfgs[p.variant];
-  Workspace* ws = nullptr;
-  if (p.splits > 1) {
-    int64_t units = 0, floats = 0;
-    plan_units(c, M, N, &units, &floats);
-    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
-    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
-    if (st != FP6_OK) return st;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (p.variant) {
-    case 1: return launch_stream<1, 1, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 2: return launch_stream<1, 4, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 3: return launch_stream<2, 1, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 4: return launch_stream<4, 1, 2>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 5: return launch_tiled<4, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 6: return launch_tiled<8, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 7: return launch_stream<1, 1, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 8: return launch_stream<2, 1, 6>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 9: return launch_ksplit<8>(X, W, S, Y, M, N, K, cus, s);
-    case 12: return launch_ksplit<16>(X, W, S, Y, M, N, K, cus, s);
-    case 13: return launch_kslice(X, W, S, Y, M, N, K, cus, s);
-    case 14: return launch_xlds<2, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 15: return launch_xlds<1, 4, 4>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 16: return launch_xlds<2, 4, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 10: return launch_tiled<8, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
-    case 11: return launch_tiled<4, 2, 8>(X, W, S, Y, M, N, K, p.splits, ws, s);
+
+// The planned launch of one format.
+template <int F>
+int launch_variant(const fpx::LaunchCtx& c) {
+  const void *X = c.X, *W = c.W, *S = c.S;
+  void* Y = c.Y;
+  const int64_t M = c.M, N = c.N, K = c.K;
+  const int sp = c.splits;
+  float* pt = c.part;
+  unsigned* ct = c.counters;
+  hipStream_t s = c.stream;
+  switch (c.variant) {
+    case 1: return launch_stream<F, 1, 1, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 2: return launch_stream<F, 1, 4, 2>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 3: return launch_stream<F, 2, 1, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 4: return launch_stream<F, 4, 1, 2>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 5: return launch_tiled<F, 4, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 6: return launch_tiled<F, 8, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 7: return launch_stream<F, 1, 1, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 8: return launch_stream<F, 2, 1, 6>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 9: return launch_ksplit<F, 8>(X, W, S, Y, M, N, K, c.cus, s);
+    case 10: return launch_tiled<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 11: return launch_tiled<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 12: return launch_ksplit<F, 16>(X, W, S, Y, M, N, K, c.cus, s);
+    case 13: return launch_kslice<F>(X, W, S, Y, M, N, K, c.cus, s);
+    case 14: return launch_xlds<F, 2, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 15: return launch_xlds<F, 1, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 16: return launch_xlds<F, 2, 4, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     default: return FP6_E_VALUE;
   }
 }
 
-}  // namespace
-
-extern "C" {
-
-int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
-               int64_t N, int64_t K, void* stream) {
-  return linear_impl(X, packed_W, scales, Y, M, N, K, 0, 0, stream);
-}
-
-int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
-                    int64_t N, int64_t K, int variant, int splits, void* stream) {
-  return linear_impl(X, packed_W, scales, Y, M, N, K, variant, splits, stream);
-}
-
-int fp6_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits) {
-  if (!variant || !splits) return FP6_E_NULL;
-  if (!shape_ok(N, K) || M < 1 || M > fp6::kMaxDim) return FP6_E_SHAPE;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
-  const Plan p = choose_plan(M, N, K, device_cus(dev), 0, 0);
-  *variant = p.variant;
-  *splits = p.splits;
-  return FP6_OK;
-}
-
-int fp6_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, int64_t K,
-                void* stream) {
-  if (!shape_ok(N, K)) return FP6_E_SHAPE;
-  if (!packed_W || !scales || !W16) return FP6_E_NULL;
-  if (!aligned16(packed_W) || !aligned16(W16) || (reinterpret_cast<uintptr_t>(scales) & 1u))
-    return FP6_E_ALIGN;
+// De-quantisation export: one wave per tile, 4 waves per workgroup.
+template <int F>
+int launch_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, int64_t K,
+                   hipStream_t stream) {
   const int64_t tiles = (N >> 4) * (K >> 8);
   const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
   const u32x4* w = static_cast<const u32x4*>(packed_W);
   const _Float16* sc = static_cast<const _Float16*>(scales);
   _Float16* out = static_cast<_Float16*>(W16);
   void* args[] = {&w, &sc, &out, &N, &K};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_dequant_kernel), grid, dim3(256), args, 0,
-                         static_cast<hipStream_t>(stream)) == hipSuccess
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_dequant_kernel<F>), grid, dim3(256), args, 0,
+                         stream) == hipSuccess
              ? FP6_OK
              : FP6_E_HIP;
 }
 
-int fp6_release(void) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (g_ws.empty()) return FP6_OK;
-  if (hipDeviceSynchronize() != hipSuccess) return FP6_E_HIP;
-  int st = FP6_OK;
-  for (auto& kv : g_ws) {
-    int cur = 0;
-    (void)hipGetDevice(&cur);
-    (void)hipSetDevice(kv.first.first);
-    if (kv.second.part && hipFree(kv.second.part) != hipSuccess) st = FP6_E_HIP;
-    if (kv.second.counters && hipFree(kv.second.counters) != hipSuccess) st = FP6_E_HIP;
-    (void)hipSetDevice(cur);
-  }
-  g_ws.clear();
-  return st;
-}
+}  // namespace
 
-}  // extern "C"
+// Instantiates the launch entry points of one format inside namespace fpx.
+#define FPX_DEFINE_FORMAT(NAME, F)                                                          \
+  namespace fpx {                                                                           \
+  int launch_##NAME(const LaunchCtx& c) { return launch_variant<F>(c); }                   \
+  int dequant_##NAME(const void* W, const void* S, void* W16, int64_t N, int64_t K,         \
+                     hipStream_t s) {                                                       \
+    return launch_dequant<F>(W, S, W16, N, K, s);                                           \
+  }                                                                                         \
+  }

@@ -1,0 +1,308 @@
+// Host dispatch of the fused FPx weight-only linear layer: argument checks,
+// schedule choice, the split-K workspace and the device entry points of the
+// C ABI (fp6_* for FP6 e3m2, fpx_* for every format).  The kernels live in
+// the per-format translation units fpx_kern_<format>.hip.
+//
+// FP6-LLM (arXiv 2401.14112), abstract: one kernel scheme with Tensor-Core
+// support for float weights of several bit widths.  TC-FPx explainer
+// (duicuo.cn), section "redesigning the kernel solution": a unified kernel
+// for quantised weights of different widths, de-quantisation fused with the
+// matrix multiply.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "fp6.h"
+#include "fpx.h"
+#include "fp6_limits.h"
+#include "fpx_launch.h"
+
+namespace {
+
+using fpx::Kind;
+using fpx::KernelCfg;
+using fpx::kCfgs;
+using fpx::kNumVariants;
+
+// ---------------------------------------------------------------------------
+// Workspace per (device, stream), CU count per device.
+// ---------------------------------------------------------------------------
+struct Workspace {
+  void* part = nullptr;
+  size_t part_bytes = 0;
+  unsigned* counters = nullptr;
+  size_t counter_count = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+std::map<int, int> g_cus;
+
+int device_cus(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  g_cus[dev] = cus;
+  return cus;
+}
+
+// Ensure the (device, stream) workspace holds at least the given sizes.
+int get_workspace(int dev, void* stream, size_t part_bytes, size_t counter_count, Workspace** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& ws = g_ws[{dev, stream}];
+  if (ws.part_bytes < part_bytes || ws.counter_count < counter_count) {
+    if (ws.part || ws.counters) {
+      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return FP6_E_HIP;
+      if (ws.part) (void)hipFree(ws.part);
+      if (ws.counters) (void)hipFree(ws.counters);
+      ws = Workspace{};
+    }
+    const size_t pb = part_bytes > ws.part_bytes ? part_bytes : ws.part_bytes;
+    const size_t cc = counter_count > ws.counter_count ? counter_count : ws.counter_count;
+    if (hipMalloc(&ws.part, pb) != hipSuccess) { ws = Workspace{}; return FP6_E_HIP; }
+    if (hipMalloc(reinterpret_cast<void**>(&ws.counters), cc * sizeof(unsigned)) != hipSuccess) {
+      (void)hipFree(ws.part);
+      ws = Workspace{};
+      return FP6_E_HIP;
+    }
+    if (hipMemset(ws.counters, 0, cc * sizeof(unsigned)) != hipSuccess) return FP6_E_HIP;
+    ws.part_bytes = pb;
+    ws.counter_count = cc;
+  }
+  *out = &ws;
+  return FP6_OK;
+}
+
+bool shape_ok(int64_t N, int64_t K) {
+  return N >= fp6::kTileN && K >= fp6::kTileK && N <= fp6::kMaxDim && K <= fp6::kMaxDim &&
+         N % fp6::kTileN == 0 && K % fp6::kTileK == 0 && N * K <= fp6::kMaxNK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool format_ok(int format) { return format >= 0 && format < fpx::kNumFormats; }
+
+int check_linear_args(const void* X, const void* W, const void* s, void* Y, int64_t M, int64_t N,
+                      int64_t K) {
+  if (!shape_ok(N, K) || M < 0 || M > fp6::kMaxDim) return FP6_E_SHAPE;
+  if (M == 0) return FP6_OK;
+  if (!X || !W || !s || !Y) return FP6_E_NULL;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || (reinterpret_cast<uintptr_t>(s) & 1u))
+    return FP6_E_ALIGN;
+  return FP6_OK;
+}
+
+struct Plan {
+  int variant;
+  int splits;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Work units (each with its own split-K counter) and the number of partial
+// floats per unit and split.
+void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats) {
+  if (c.kind == Kind::kTiled) {
+    // c.a = row blocks per wave, c.d = waves per workgroup (c.a * c.d = 16)
+    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16) * c.d;
+    *floats = static_cast<int64_t>(c.a) * c.mb * 256;
+  } else {
+    *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
+    *floats = static_cast<int64_t>(c.a) * c.mb * 256;
+  }
+}
+
+// The schedule depends on the shape only: the narrower formats read fewer
+// bytes per tile but run the same kernels with the same work units.
+Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
+  Plan p;
+  const int64_t ktiles = K >> 8;
+  if (variant == 0) {
+    // Measured on MI355X: up to K = 4096 the k-slice kernel (at most one row
+    // block per CU) or the k-split kernels (8 waves up to K = 2048, else 16)
+    // are fastest; for longer K the streaming kernel with X shared through
+    // LDS (1 row block per wave, 4 waves) is.
+    const bool one_rb_per_cu = (N >> 4) <= cus;
+    if (M <= 16 && ktiles <= 16 && one_rb_per_cu) p.variant = 13;
+    else if (M <= 16 && ktiles <= 8) p.variant = 9;
+    else if (M <= 16 && ktiles <= 16) p.variant = 12;
+    else if (M <= 16) p.variant = 15;
+    else if (M <= 64) p.variant = 11;
+    else p.variant = 10;
+  } else {
+    p.variant = variant;
+  }
+  const KernelCfg& c = kCfgs[p.variant];
+  if (c.kind == Kind::kKsplit || c.kind == Kind::kKslice) {
+    p.splits = 1;
+    return p;
+  }
+  if (splits > 0) {
+    p.splits = splits;
+    return p;
+  }
+  int64_t s;
+  if (c.kind == Kind::kTiled) {
+    // One workgroup per CU: split K while a whole extra round of workgroups
+    // fits on the CUs (rounding down: a partial second round costs more than
+    // it gains), keeping at least 2 k-tiles per split.
+    const int64_t wgs = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16);
+    s = cus / wgs;
+    if (s > ktiles / 2) s = ktiles / 2;
+  } else {
+    // No split once there are two waves per CU; otherwise split K towards
+    // ~4 waves per CU (measured: more splits cost more in the fix-up than
+    // they add in loads in flight).
+    const int64_t units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, c.a);
+    s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
+    if (s > ktiles / 2) s = ktiles / 2;
+  }
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  p.splits = static_cast<int>(s);
+  return p;
+}
+
+int launch_format(int format, const fpx::LaunchCtx& c) {
+  switch (format) {
+    case fpx::kFmtE3M2: return fpx::launch_e3m2(c);
+    case fpx::kFmtE2M3: return fpx::launch_e2m3(c);
+    case fpx::kFmtE2M2: return fpx::launch_e2m2(c);
+    case fpx::kFmtE2M1: return fpx::launch_e2m1(c);
+    default: return FP6_E_VALUE;
+  }
+}
+
+int linear_impl(int format, const void* X, const void* W, const void* S, void* Y, int64_t M,
+                int64_t N, int64_t K, int variant, int splits, void* stream) {
+  if (!format_ok(format)) return FP6_E_VALUE;
+  int st = check_linear_args(X, W, S, Y, M, N, K);
+  if (st != FP6_OK || M == 0) return st;
+  if (variant < 0 || variant >= kNumVariants || splits < 0 || splits > (K >> 8) || splits > 4096)
+    return FP6_E_VALUE;
+  // One launch covers at least one m-group: its workgroup count must stay
+  // below 2^24 (so that blocks x 256 threads fits in 32 bits).  Automatic
+  // plans only split when there are fewer units than ~8 waves per CU, far
+  // inside this bound.
+  if (splits > 0 && ceil_div(N >> 4, 4) * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
+    return FP6_E_VALUE;
+  // The k-split kernel keeps each wave's X slice in registers: M <= 16 and
+  // at most K = 8192 (and a per-wave tile count it is instantiated for); it
+  // never splits across workgroups.
+  if (variant > 0 && kCfgs[variant].kind == Kind::kKsplit &&
+      (M > 16 || (K >> 8) > fpx::kKsMaxTiles || splits > 1))
+    return FP6_E_VALUE;
+  if (variant > 0 && kCfgs[variant].kind == Kind::kKslice &&
+      (M > 16 || (K >> 8) > fpx::kKsliceMaxTiles || splits > 1))
+    return FP6_E_VALUE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
+  const int cus = device_cus(dev);
+  const Plan p = choose_plan(M, N, K, cus, variant, splits);
+  const KernelCfg& c = kCfgs[p.variant];
+  Workspace* ws = nullptr;
+  if (p.splits > 1) {
+    int64_t units = 0, floats = 0;
+    plan_units(c, M, N, &units, &floats);
+    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
+    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
+    if (st != FP6_OK) return st;
+  }
+  fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits,
+                     ws ? static_cast<float*>(ws->part) : nullptr, ws ? ws->counters : nullptr, cus,
+                     static_cast<hipStream_t>(stream)};
+  return launch_format(format, ctx);
+}
+
+int plan_query_impl(int format, int64_t M, int64_t N, int64_t K, int* variant, int* splits) {
+  if (!variant || !splits) return FP6_E_NULL;
+  if (!format_ok(format)) return FP6_E_VALUE;
+  if (!shape_ok(N, K) || M < 1 || M > fp6::kMaxDim) return FP6_E_SHAPE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
+  const Plan p = choose_plan(M, N, K, device_cus(dev), 0, 0);
+  *variant = p.variant;
+  *splits = p.splits;
+  return FP6_OK;
+}
+
+int dequant_impl(int format, const void* packed_W, const void* scales, void* W16, int64_t N,
+                 int64_t K, void* stream) {
+  if (!format_ok(format)) return FP6_E_VALUE;
+  if (!shape_ok(N, K)) return FP6_E_SHAPE;
+  if (!packed_W || !scales || !W16) return FP6_E_NULL;
+  if (!aligned16(packed_W) || !aligned16(W16) || (reinterpret_cast<uintptr_t>(scales) & 1u))
+    return FP6_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (format) {
+    case fpx::kFmtE3M2: return fpx::dequant_e3m2(packed_W, scales, W16, N, K, s);
+    case fpx::kFmtE2M3: return fpx::dequant_e2m3(packed_W, scales, W16, N, K, s);
+    case fpx::kFmtE2M2: return fpx::dequant_e2m2(packed_W, scales, W16, N, K, s);
+    case fpx::kFmtE2M1: return fpx::dequant_e2m1(packed_W, scales, W16, N, K, s);
+    default: return FP6_E_VALUE;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
+               int64_t N, int64_t K, void* stream) {
+  return linear_impl(fpx::kFmtE3M2, X, packed_W, scales, Y, M, N, K, 0, 0, stream);
+}
+
+int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
+                    int64_t N, int64_t K, int variant, int splits, void* stream) {
+  return linear_impl(fpx::kFmtE3M2, X, packed_W, scales, Y, M, N, K, variant, splits, stream);
+}
+
+int fp6_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits) {
+  return plan_query_impl(fpx::kFmtE3M2, M, N, K, variant, splits);
+}
+
+int fp6_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, int64_t K,
+                void* stream) {
+  return dequant_impl(fpx::kFmtE3M2, packed_W, scales, W16, N, K, stream);
+}
+
+int fpx_linear(int format, const void* X, const void* packed_W, const void* scales, void* Y,
+               int64_t M, int64_t N, int64_t K, void* stream) {
+  return linear_impl(format, X, packed_W, scales, Y, M, N, K, 0, 0, stream);
+}
+
+int fpx_linear_plan(int format, const void* X, const void* packed_W, const void* scales, void* Y,
+                    int64_t M, int64_t N, int64_t K, int variant, int splits, void* stream) {
+  return linear_impl(format, X, packed_W, scales, Y, M, N, K, variant, splits, stream);
+}
+
+int fpx_dequant(int format, const void* packed_W, const void* scales, void* W16, int64_t N,
+                int64_t K, void* stream) {
+  return dequant_impl(format, packed_W, scales, W16, N, K, stream);
+}
+
+int fp6_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_ws.empty()) return FP6_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return FP6_E_HIP;
+  int st = FP6_OK;
+  for (auto& kv : g_ws) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(kv.first.first);
+    if (kv.second.part && hipFree(kv.second.part) != hipSuccess) st = FP6_E_HIP;
+    if (kv.second.counters && hipFree(kv.second.counters) != hipSuccess) st = FP6_E_HIP;
+    (void)hipSetDevice(cur);
+  }
+  g_ws.clear();
+  return st;
+}
+
+}  // extern "C"
