@@ -11,7 +11,9 @@ the average launch duration.
 
 Default workload: the Llama-7B attention projection, M=1 (decode GEMV),
 N=4096, K=4096.  ``--workload`` selects another shape of
-weight_only_fp6_amd.synth.SHAPES.  Prints ONE JSON line.
+weight_only_fp6_amd.synth.SHAPES and ``--format`` another weight format
+(e2m3, e2m2, e2m1 through ``fpx_linear``; default e3m2).  Prints ONE JSON
+line.
 
 Also reported, as context:
 * ``cpu_baseline``: the plain NumPy oracle timed on this host on a bounded
@@ -49,7 +51,10 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
 ROT_BYTES = 1 << 30             # >= 1 GiB of rotated copies (> 256 MB Infinity Cache)
 COPY_BYTES = 1 << 30            # --calibrate-copy: bytes read (and written) per copy
-KERNEL_SRC = os.path.join(ROOT, "weight_only_fp6_amd", "csrc", "fp6_kernels.hip")
+CSRC = os.path.join(ROOT, "weight_only_fp6_amd", "csrc")
+KERNEL_SRCS = ("fpx_device.h", "fpx_launch.h", "fpx_linear.hip", "fpx_kern_e3m2.hip",
+               "fpx_kern_e2m3.hip", "fpx_kern_e2m2.hip", "fpx_kern_e2m1.hip")
+FORMAT_BITS = {"e3m2": 6, "e2m3": 6, "e2m2": 5, "e2m1": 4}
 
 
 # Linear layers of one decoder layer, (name, N, K) with the projections that
@@ -69,6 +74,8 @@ def _parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--format", default="e3m2", choices=sorted(FORMAT_BITS),
+                    help="weight format (e3m2 = FP6 through fp6_linear; others through fpx_linear)")
     ap.add_argument("--no-graph", action="store_true", help="time direct launches instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the fp16 BLAS and read-probe context numbers")
@@ -84,29 +91,41 @@ def _parse():
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(M, N, K):
+def weight_bytes(N, K, fmt="e3m2"):
+    return N * K * FORMAT_BITS[fmt] // 8
+
+
+def algorithmic_bytes(M, N, K, fmt="e3m2"):
     """Bytes one call must move at least: packed weights, scales, X, Y."""
-    return N * K * 3 // 4 + 2 * N + 2 * M * K + 2 * M * N
+    return weight_bytes(N, K, fmt) + 2 * N + 2 * M * K + 2 * M * N
 
 
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, untuned, on a bounded row sample.
 # ---------------------------------------------------------------------------
-def cpu_baseline(shape, packed, scales, X, budget_s=20.0):
+def cpu_baseline(shape, packed, scales, X, budget_s=20.0, fmt="e3m2"):
     import oracle
     from threadpoolctl import threadpool_limits
     with threadpool_limits(limits=1):
         M, N, K = shape.M, shape.N, shape.K
-        row_bytes = 16 * K * 3 // 4                     # one packed row block
+        row_bytes = weight_bytes(16, K, fmt)            # one packed row block
+
+        def unpack(buf, n):
+            if fmt == "e3m2":
+                return oracle.unpack_np(buf, n, K)
+            return oracle.unpack_tiles(buf, n, K, fmt)
 
         def run(nblk):
             t0 = time.perf_counter()
-            codes = oracle.unpack_np(packed[: nblk * row_bytes], 16 * nblk, K)
-            wdq = oracle.dequant_ref(codes, scales[: 16 * nblk])
+            codes = unpack(packed[: nblk * row_bytes], 16 * nblk)
+            wdq = oracle.dequant_ref(codes, scales[: 16 * nblk], fmt)
             oracle.gemm_ref(X, wdq)
             return time.perf_counter() - t0
         nblk = max(1, min(N // 16, (4 * 2**20) // row_bytes))
@@ -115,13 +134,13 @@ def cpu_baseline(shape, packed, scales, X, budget_s=20.0):
         ts = sorted(run(nblk) for _ in range(3))
         tmed = ts[1]
     nrows = 16 * nblk
-    wbytes = nrows * K * 3 // 4
+    wbytes = weight_bytes(nrows, K, fmt)
     return {
         "value": round(wbytes / tmed / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{nrows} of {N} weight rows x K={K}, M={M}: oracle.unpack_np + dequant_ref + gemm_ref "
+        "sample": f"{nrows} of {N} weight rows x K={K}, M={M}, {fmt}: oracle unpack + dequant_ref + gemm_ref "
                   f"(float64), median of 3 runs of {tmed:.2f} s, single thread (BLAS limited to 1)",
         "tflops": round(2.0 * M * nrows * K / tmed / 1e12, 6),
     }
@@ -131,8 +150,12 @@ def cpu_baseline(shape, packed, scales, X, budget_s=20.0):
 # Traffic from committed counter summaries (only while the kernel source is
 # the one the counters were taken with).
 # ---------------------------------------------------------------------------
-def committed_traffic(workload):
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+def traffic_name(workload, fmt="e3m2"):
+    return f"traffic_{workload}.txt" if fmt == "e3m2" else f"traffic_{workload}_{fmt}.txt"
+
+
+def committed_traffic(workload, fmt="e3m2"):
+    path = os.path.join(ROOT, "profiles", traffic_name(workload, fmt))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -167,9 +190,9 @@ def _time_graph(torch, stream, launch, n):
     return e0.elapsed_time(e1) * 1e3 / n   # microseconds per launch
 
 
-def fp16_blas_context(torch, fp6, stream, pk, sc, x, M, N, K):
+def fp16_blas_context(torch, fp6, stream, pk, sc, x, M, N, K, fmt="e3m2"):
     """fp16 torch linear (hipBLASLt) on the de-quantised weights, cold copies."""
-    W16 = fp6.dequant(pk, sc, N, K, stream=stream)
+    W16 = fp6.dequant(pk, sc, N, K, stream=stream, fmt=fmt)
     torch.cuda.synchronize()
     R = int(min(32, max(2, math.ceil(ROT_BYTES / (2 * N * K)))))
     ws = [W16.clone() for _ in range(R)]
@@ -271,11 +294,12 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
     print(f"hbm_bytes_per_launch = {fetch + write:.0f}")
 
 
-def decoder_chain(name):
-    """One decoder layer's four linears at M = 1, 2, 4, 8, 16: FP6 path vs the
-    same chain in fp16 (hipBLASLt) on the de-quantised weights.  Codes are
-    uniform over all 64 e3m2 values (timing does not depend on them); enough
-    layer copies rotate to keep the weights out of the 256 MB Infinity Cache."""
+def decoder_chain(name, fmt="e3m2"):
+    """One decoder layer's four linears at M = 1, 2, 4, 8, 16: the fused path
+    vs the same chain in fp16 (hipBLASLt) on the de-quantised weights.  Codes
+    are uniform over all codes of the format (timing does not depend on them);
+    enough layer copies rotate to keep the weights out of the 256 MB Infinity
+    Cache."""
     import torch
     import weight_only_fp6_amd as fp6
     from weight_only_fp6_amd import synth
@@ -283,20 +307,22 @@ def decoder_chain(name):
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
-    fp6_bytes = sum(n * k * 3 // 4 for _, n, k in layers)
+    fp6_bytes = sum(weight_bytes(n, k, fmt) for _, n, k in layers)
+    ncode = 1 << FORMAT_BITS[fmt]
+    fid = fp6.FORMATS[fmt]
     copies = int(max(1, math.ceil(ROT_BYTES / fp6_bytes)))
     packed, scales, w16 = [], [], []
     for ci in range(copies):
         pc, sc, wc = [], [], []
         for li, (_, n, k) in enumerate(layers):
-            codes = synth.codes_uniform(n, k, seed=100 * ci + li)
+            codes = synth.codes_uniform(n, k, seed=100 * ci + li) % ncode
             s_ = np.full(n, 0.003, dtype=np.float16)
-            pk = torch.from_numpy(fp6.prepack(codes, s_)).to(dev)
+            pk = torch.from_numpy(fp6.prepack(codes, s_, fmt)).to(dev)
             st = torch.from_numpy(s_).to(dev)
             pc.append(pk)
             sc.append(st)
             if ci == 0:
-                wc.append(fp6.dequant(pk, st, n, k, stream=stream))
+                wc.append(fp6.dequant(pk, st, n, k, stream=stream, fmt=fmt))
         packed.append(pc)
         scales.append(sc)
         if ci == 0:
@@ -313,10 +339,10 @@ def decoder_chain(name):
         def fp6_step(i):
             c = i % copies
             for li, (_, n, k) in enumerate(layers):
-                st = L.fp6_linear(xs[k].data_ptr(), packed[c][li].data_ptr(), scales[c][li].data_ptr(),
+                st = L.fpx_linear(fid, xs[k].data_ptr(), packed[c][li].data_ptr(), scales[c][li].data_ptr(),
                                   ys[li].data_ptr(), M, n, k, stream.cuda_stream)
                 if st:
-                    raise fp6.FP6Error("fp6_linear", st)
+                    raise fp6.FP6Error("fpx_linear", st)
 
         def f16_step(i):
             c = i % w16_copies
@@ -333,7 +359,7 @@ def decoder_chain(name):
     print(json.dumps({"metric": "decoder-layer linear chain latency (qkv, o, gate_up, down)",
                       "model_shapes": name, "layers": [[a, n, k] for a, n, k in layers],
                       "unit": "us", "fp6_weight_bytes": fp6_bytes, "rows": rows,
-                      "data": "synthetic (uniform e3m2 codes)"}), flush=True)
+                      "format": fmt, "data": f"synthetic (uniform {fmt} codes)"}), flush=True)
 
 
 def calibrate_copy():
@@ -352,7 +378,8 @@ def main():
         summarize(args.summarize)
         return
     if args.traffic:
-        traffic_summary(args.workload, *args.traffic)
+        traffic_summary(args.workload if args.format == "e3m2" else f"{args.workload} ({args.format})",
+                        *args.traffic)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -366,7 +393,7 @@ def main():
         calibrate_copy()
         return
     if args.decoder:
-        decoder_chain(args.decoder)
+        decoder_chain(args.decoder, args.format)
         return
     import weight_only_fp6_amd as fp6
     from weight_only_fp6_amd import synth
@@ -379,10 +406,11 @@ def main():
     dev = torch.device("cuda:0")
 
     # ---- inputs: host quantise + prepack, then R rotated device copies ----
+    fmt = args.format
     W = synth.weights(N, K, shape.seed_w)
-    codes, scales = fp6.quantize_rows(W)
+    codes, scales = fp6.quantize_rows(W, fmt)
     del W
-    packed = fp6.prepack(codes, scales)
+    packed = fp6.prepack(codes, scales, fmt)
     del codes
     X = synth.activations(M, K, shape.seed_x)
     R = int(min(64, max(2, math.ceil(ROT_BYTES / packed.nbytes))))
@@ -402,11 +430,16 @@ def main():
     else:
         variant, splits = fp6.plan_query(M, N, K)
 
+    fid = fp6.FORMATS[fmt]
+
     def launch(i):
         x, w, s, y = ptrs[i % R]
-        st = L.fp6_linear_plan(x, w, s, y, M, N, K, args.variant, args.splits, sh)
+        if fmt == "e3m2":
+            st = L.fp6_linear_plan(x, w, s, y, M, N, K, args.variant, args.splits, sh)
+        else:
+            st = L.fpx_linear_plan(fid, x, w, s, y, M, N, K, args.variant, args.splits, sh)
         if st != 0:
-            raise fp6.FP6Error("fp6_linear_plan", st)
+            raise fp6.FP6Error("linear_plan", st)
 
     launch(0)                       # allocates the split-K workspace if the plan needs one
     torch.cuda.synchronize()
@@ -445,15 +478,16 @@ def main():
     wall_s = t1 - t0
     per_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
 
-    wbytes = N * K * 3 // 4
-    abytes = algorithmic_bytes(M, N, K)
+    wbytes = weight_bytes(N, K, fmt)
+    abytes = algorithmic_bytes(M, N, K, fmt)
     flops = 2.0 * M * N * K
     weight_gbs = wbytes * args.steps / wall_s / 1e9
     tflops = flops * args.steps / wall_s / 1e12
     # Ridge: 2500 TFLOP/s / 8 TB/s = 312.5 flop/byte; per packed weight byte the
-    # layer does 2*M*N*K / (0.75*N*K) = 2.67*M flop, so M < 117 is HBM-bound.
-    traffic = committed_traffic(args.workload) if not args.variant else None
-    if M < 117:
+    # layer does 2*M*N*K / (bits/8*N*K) = 16*M/bits flop, so FP6 is HBM-bound
+    # for M < 117 (FP5 98, FP4 78).
+    traffic = committed_traffic(args.workload, fmt) if not args.variant else None
+    if M < 312.5 * FORMAT_BITS[fmt] / 16:
         achieved = abytes / per_launch_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -485,8 +519,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
-                   "weights": "fp6 e3m2 + fp16 row scale (packed layout v1)",
+        "config": {"workload": args.workload if fmt == "e3m2" else f"{args.workload}_{fmt}",
+                   "M": M, "N": N, "K": K,
+                   "weights": f"fp{FORMAT_BITS[fmt]} {fmt} + fp16 row scale (packed layout v1)",
                    "activations": "fp16", "accumulate": "fp32",
                    "rotated_weight_copies": R, "graph": not args.no_graph},
         "weight_gbps": round(weight_gbs, 1),
@@ -496,7 +531,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_context:
-        blas_us = fp16_blas_context(torch, fp6, stream, pk_d[0], sc_d[0], x_d[0], M, N, K)
+        blas_us = fp16_blas_context(torch, fp6, stream, pk_d[0], sc_d[0], x_d[0], M, N, K, fmt)
         out["fp16_blas"] = {"kind": "torch.matmul fp16 (hipBLASLt), de-quantised weights, cold copies",
                             "us": round(blas_us, 3),
                             "fp6_speedup": round(blas_us / (per_launch_s * 1e6), 3)}
@@ -504,7 +539,7 @@ def main():
         out["read_ceiling_gbs"] = round(ceil_gbs, 1)
         out["weight_frac_of_read_ceiling"] = round(wbytes / per_launch_s / 1e9 / ceil_gbs, 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, packed, scales, X)
+        out["cpu_baseline"] = cpu_baseline(shape, packed, scales, X, fmt=fmt)
     print(json.dumps(out), flush=True)
 
 
