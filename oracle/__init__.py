@@ -17,7 +17,12 @@ Contents (all in :mod:`oracle.fp6_oracle`):
   ``Y_ref = X . Wdq^T``, plus a naive triple loop used to pin it;
 * the acceptance check (per-element and Frobenius tolerances).
 
-Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+:mod:`oracle.sparse24` adds the 2:4-sparse FP6 layer: magnitude pruning, the
+compressed (code, position) form, its packed layout and the dense
+de-quantised weights (built on the FP6 functions above).
+
+Parity status: every function here (and in :mod:`oracle.sparse24`) is pinned
+by ``tests/test_oracle_*.py``
 against closed forms, IEEE fp16 decoding, torch's float8_e5m2 rounding,
 exact (math.fsum) sums, brute force on tiny inputs and hand-derived packed-byte
 fixtures under ``tests/golden/``.  No function is "parity unpinned".
