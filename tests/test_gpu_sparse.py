@@ -1,0 +1,140 @@
+"""GPU parity of the 2:4-sparse FP6 path (fp6s_*) against the CPU oracle
+(oracle/sparse24.py), needs an MI355X.
+
+* De-quantisation export: dense Wdq (zeros at pruned positions) bit-exact.
+* Fused sparse linear: |Y - Y_ref| <= 2e-3 (|Y_ref| + rms) per element and
+  relative Frobenius <= 5e-4, every kernel configuration on small ragged
+  shapes, the automatic plan at the workload shapes whose K is a multiple of
+  512 (sampled output columns for the large layers); one-hot activations
+  reproduce Wdq exactly.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import sparse24
+from weight_only_fp6_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import weight_only_fp6_amd as fp6  # noqa: E402
+
+DEV = torch.device("cuda:0")
+VARIANTS = (0, 2, 3)     # any M; 1 (k-slice) only for M <= 16
+KSLICE = 1
+
+
+class SpPrepared:
+    def __init__(self, M, N, K, seed_w, seed_x, sample=None):
+        self.M, self.N, self.K = M, N, K
+        W = synth.weights(N, K, seed_w)
+        self.X = synth.activations(M, K, seed_x)
+        c, p, s = fp6.prune_quantize(W)
+        self.scales = s
+        self.packed = fp6.sparse_prepack(c, p, s, K)
+        self.rows = np.arange(N) if sample is None else synth.sample_rows(N, sample, seed_w + 17)
+        oc, op, osc = sparse24.quantize_sparse(W[self.rows])
+        self.wdq_ref = sparse24.dequant_ref(oc, op, osc, K)
+        self.y_ref = oracle.gemm_ref(self.X, self.wdq_ref)
+
+    def to_device(self):
+        return (torch.from_numpy(self.X).to(DEV), torch.from_numpy(self.packed).to(DEV),
+                torch.from_numpy(self.scales.copy()).to(DEV))
+
+
+def _assert_tol(y_dev, y_ref, what=""):
+    rep = oracle.tolerance_report(y_dev.detach().cpu().numpy().astype(np.float64), y_ref)
+    assert rep["ok"], (what, rep)
+
+
+def test_dequant_all_codes_and_position_pairs():
+    N, K = 48, 1024
+    rng = np.random.default_rng(61)
+    codes = rng.integers(0, 64, (N, K // 2)).astype(np.uint8)
+    pairs = np.array([(a, b) for a in range(4) for b in range(a + 1, 4)], np.uint8)   # all 6
+    pos = pairs[rng.integers(0, 6, (N, K // 4))].reshape(N, K // 2)
+    sb = rng.integers(1, 0x4C00, N).astype(np.uint16) | (rng.integers(0, 2, N).astype(np.uint16) << 15)
+    scales = sb.view(np.float16)
+    scales[:16] = np.array([2.0 ** j for j in range(-24, -8)], np.float16)     # subnormal weights
+    packed = torch.from_numpy(fp6.sparse_prepack(codes, pos, scales, K)).to(DEV)
+    s = torch.from_numpy(scales.copy()).to(DEV)
+    out = fp6.sparse_dequant(packed, s, N, K)
+    torch.cuda.synchronize()
+    ref = sparse24.dequant_ref(codes, pos, scales, K)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 64])
+@pytest.mark.parametrize("NK", [(16, 512), (80, 1536), (48, 4608)])
+def test_linear_small_shapes_every_variant(M, NK):
+    N, K = NK
+    p = SpPrepared(M, N, K, seed_w=N * 3 + K, seed_x=M * 7 + 5)
+    X, packed, s = p.to_device()
+    for variant in VARIANTS + ((KSLICE,) if M <= 16 else ()):
+        Y = fp6.sparse_linear_plan(X, packed, s, N, K, variant=variant)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
+
+
+def test_linear_forced_splits():
+    p = SpPrepared(16, 4096, 8192, seed_w=71, seed_x=72, sample=256)
+    X, packed, s = p.to_device()
+    cols = torch.from_numpy(p.rows).to(DEV)
+    for variant in (2, 3):
+        for splits in (1, 2, 3, 5, 16):
+            Y = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits)
+            torch.cuda.synchronize()
+            _assert_tol(Y[:, cols], p.y_ref, what=(variant, splits))
+
+
+@functools.lru_cache(maxsize=1)
+def _prep(name, sample):
+    shp = synth.SHAPES[name]
+    return SpPrepared(shp.M, shp.N, shp.K, shp.seed_w, shp.seed_x, sample=sample)
+
+
+@pytest.mark.parametrize("name", ["llama7b_attn_1x4096x4096", "llama7b_mlp_up_16x11008x4096",
+                                  "llama70b_mlp_1x28672x8192", "llama70b_mlp_16x28672x8192",
+                                  "opt30b_qkv_64x21504x7168"])
+def test_linear_workloads(name):
+    shp = synth.SHAPES[name]
+    sample = None if shp.N * shp.K <= 48 * 2**20 else 384
+    p = _prep(name, sample)
+    X, packed, s = p.to_device()
+    Y = fp6.sparse_linear(X, packed, s, shp.N, shp.K)
+    torch.cuda.synchronize()
+    _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=name)
+
+
+def test_linear_one_hot_reproduces_wdq_exactly():
+    N, K = 64, 2048
+    p = SpPrepared(16, N, K, seed_w=81, seed_x=82)
+    ks = np.array([0, 1, 2, 3, 4, 63, 64, 100, 511, 512, 700, 1023, 1024, 1500, 2000, 2047])
+    X = np.zeros((16, K), np.float16)
+    X[np.arange(16), ks] = 1.0
+    Xd = torch.from_numpy(X).to(DEV)
+    _, packed, s = p.to_device()
+    want = p.wdq_ref[:, ks].T.astype(np.float64)
+    for variant, splits in [(0, 0), (1, 0), (2, 1), (2, 3), (3, 1), (3, 2)]:
+        Y = fp6.sparse_linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (variant, splits)
+
+
+def test_linear_is_deterministic_and_m_zero():
+    p = SpPrepared(16, 4096, 4096, seed_w=91, seed_x=92, sample=32)
+    X, packed, s = p.to_device()
+    a = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=2, splits=4).clone()
+    b = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=2, splits=4).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    Y = fp6.sparse_linear(torch.zeros((0, p.K), dtype=torch.float16, device=DEV), packed, s, p.N, p.K)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, p.N)

@@ -22,7 +22,7 @@ def _declared_functions():
         if fn.endswith(".h"):
             txt = open(os.path.join(ROOT, "include", fn)).read()
             txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-            names += re.findall(r"\b(fp[6x]_\w+)\s*\(", txt)
+            names += re.findall(r"\b(fp(?:6s|6|x)_\w+)\s*\(", txt)
     return sorted(set(names))
 
 
@@ -302,3 +302,90 @@ def test_fpx_errors(fmt):
     assert L.fpx_linear_plan(f, A, A, A, A, 4, 16, 256, 99, 0, None) == 8
     assert L.fpx_dequant(9, A, A, A, 16, 256, None) == 8
     assert L.fpx_dequant(f, A, A, A, 16, 100, None) == 2
+
+
+# ---------------------------------------------------------------------------
+# 2:4-sparse FP6 (fp6s_* entry points).
+# ---------------------------------------------------------------------------
+from oracle import sparse24  # noqa: E402
+
+
+@pytest.mark.parametrize("shape", [(3, 8), (16, 512), (37, 1024)])
+def test_sparse_prune_quantize_matches_oracle(shape):
+    W = synth.weights(*shape, seed=21 + shape[0])
+    c, p, s = fp6.prune_quantize(W)
+    oc, op, osc = sparse24.quantize_sparse(W)
+    assert np.array_equal(s.view(np.uint16), osc.view(np.uint16))
+    assert np.array_equal(p, op) and np.array_equal(c, oc)
+
+
+def test_sparse_prune_quantize_ties_and_zeros():
+    rng = np.random.default_rng(8)
+    W = (rng.integers(-2, 3, (16, 256)) * 0.25).astype(np.float32)   # many equal magnitudes and zeros
+    W[3] = 0.0
+    W[4, :4] = [-0.0, 0.0, -0.0, 0.0]
+    c, p, s = fp6.prune_quantize(W)
+    oc, op, osc = sparse24.quantize_sparse(W)
+    assert np.array_equal(s.view(np.uint16), osc.view(np.uint16))
+    assert np.array_equal(p, op) and np.array_equal(c, oc)
+
+
+@pytest.mark.parametrize("shape", [(16, 512), (32, 1024)])
+def test_sparse_prepack_matches_oracle_packer_bytewise(shape):
+    N, K = shape
+    W = synth.weights(N, K, seed=K + 3)
+    c, p, s = fp6.prune_quantize(W)
+    got = fp6.sparse_prepack(c, p, s, K)
+    assert got.size == N * K // 2
+    assert np.array_equal(got, sparse24.pack_scalar(c, p, K))
+
+
+def test_sparse_prepack_round_trip_large():
+    for N, K in [(64, 8192), (32, 7168)]:
+        W = synth.weights(N, K, seed=N + K + 2)
+        c, p, s = fp6.prune_quantize(W)
+        cc, pp = sparse24.unpack_tiles(fp6.sparse_prepack(c, p, s, K), N, K)
+        assert np.array_equal(cc, c) and np.array_equal(pp, p)
+
+
+def test_sparse_errors():
+    assert fp6.sparse_packed_bytes(16, 512) == 4096
+    assert fp6.sparse_packed_bytes(16, 768) == 0 and fp6.sparse_packed_bytes(8, 512) == 0
+    N, K = 16, 512
+    c = np.zeros((N, K // 2), np.uint8)
+    p = np.tile(np.array([0, 1], np.uint8), (N, K // 4))
+    s = np.ones(N, np.float16)
+    fp6.sparse_prepack(c, p, s, K)
+    for bad_p in ([1, 1], [2, 1], [0, 4]):
+        q = p.copy()
+        q[5, 10:12] = bad_p
+        with pytest.raises(fp6.FP6Error) as e:
+            fp6.sparse_prepack(c, q, s, K)
+        assert e.value.name == "FP6_E_VALUE"
+    cb = c.copy()
+    cb[0, 0] = 64
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.sparse_prepack(cb, p, s, K)
+    assert e.value.name == "FP6_E_CODE"
+    sb = s.copy()
+    sb[2] = 16.0
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.sparse_prepack(c, p, sb, K)
+    assert e.value.name == "FP6_E_SCALE"
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.prune_quantize(np.zeros((2, 6), np.float32))
+    assert e.value.name == "FP6_E_SHAPE"
+    with pytest.raises(fp6.FP6Error) as e:
+        fp6.prune_quantize(np.array([[1.0, np.nan, 0.0, 0.0]], np.float32))
+    assert e.value.name == "FP6_E_VALUE"
+    L = fp6.lib
+    A = 1 << 20
+    assert L.fp6s_linear(A, A, A, A, 4, 16, 768, None) == 2          # K % 512
+    assert L.fp6s_linear(None, None, None, None, 0, 16, 512, None) == 0
+    assert L.fp6s_linear(A + 8, A, A, A, 4, 16, 512, None) == 3
+    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 9, 0, None) == 8
+    assert L.fp6s_linear_plan(A, A, A, A, 17, 16, 512, 1, 0, None) == 8    # k-slice: M <= 16
+    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512 * 17, 1, 0, None) == 8  # k-slice: K <= 8192
+    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 2, 2, None) == 8    # 2 splits > 1 tile
+    assert L.fp6s_dequant(A, A, A, 16, 768, None) == 2
+    assert L.fp6s_dequant(None, A, A, 16, 512, None) == 1

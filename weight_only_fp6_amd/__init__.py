@@ -14,6 +14,9 @@ call takes ``fmt`` ("e3m2" -- the default, FP6 -- "e2m3", "e2m2" or "e2m1"):
 * :func:`prepack` (host) -> ``uint8 [N*K*bits/8]`` packed layout v1
 * :func:`linear` (device) -> ``Y fp16 [M,N] = X . dequant(W)^T``
 * :func:`linear_plan` (device, forced schedule), :func:`dequant` (device export)
+* 2:4-sparse FP6 (``include/fp6s.h``): :func:`sparse_packed_bytes`,
+  :func:`prune_quantize`, :func:`sparse_prepack`, :func:`sparse_linear`,
+  :func:`sparse_linear_plan`, :func:`sparse_dequant`
 
 There is no fallback: if the shared library is missing or fails to load,
 importing this package raises.
@@ -38,7 +41,8 @@ EXPORTED = (
     "fp6_pack_version", "fp6_status_string", "fp6_packed_bytes", "fp6_quantize_rows",
     "fp6_prepack", "fp6_linear", "fp6_linear_plan", "fp6_linear_plan_query", "fp6_dequant",
     "fp6_release", "fpx_bits", "fpx_packed_bytes", "fpx_quantize_rows", "fpx_prepack",
-    "fpx_linear", "fpx_linear_plan", "fpx_dequant",
+    "fpx_linear", "fpx_linear_plan", "fpx_dequant", "fp6s_packed_bytes", "fp6s_prune_quantize",
+    "fp6s_prepack", "fp6s_linear", "fp6s_linear_plan", "fp6s_dequant",
 )
 FORMATS = {"e3m2": 0, "e2m3": 1, "e2m2": 2, "e2m1": 3}
 
@@ -82,6 +86,12 @@ def _load() -> ctypes.CDLL:
         "fpx_linear": ([i32, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fpx_linear_plan": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp], i32),
         "fpx_dequant": ([i32, vp, vp, vp, i64, i64, vp], i32),
+        "fp6s_packed_bytes": ([i64, i64], sz),
+        "fp6s_prune_quantize": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp6s_prepack": ([vp, vp, vp, i64, i64, vp, sz], i32),
+        "fp6s_linear": ([vp, vp, vp, vp, i64, i64, i64, vp], i32),
+        "fp6s_linear_plan": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp], i32),
+        "fp6s_dequant": ([vp, vp, vp, i64, i64, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -221,6 +231,81 @@ def dequant(packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e
     args = (_dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), N, K, _stream_handle(stream))
     st = _lib.fp6_dequant(*args) if fmt == "e3m2" else _lib.fpx_dequant(f, *args)
     _check("dequant", st)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 2:4-sparse FP6
+# ---------------------------------------------------------------------------
+SPARSE_KERNEL_NAMES = {1: "sp_gemm_kslice", 2: "sp_gemm_xlds<1,4,4>", 3: "sp_gemm_xlds<2,4,4>"}
+
+
+def sparse_packed_bytes(N: int, K: int) -> int:
+    return int(_lib.fp6s_packed_bytes(N, K))
+
+
+def prune_quantize(W: np.ndarray):
+    """Host 2:4 magnitude pruning + quantisation: float32 [N,K] ->
+    (codes uint8 [N,K/2], pos uint8 [N,K/2], scales float16 [N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    N, K = W.shape
+    codes = np.empty((N, max(K // 2, 1)), dtype=np.uint8)
+    pos = np.empty((N, max(K // 2, 1)), dtype=np.uint8)
+    scales = np.empty(N, dtype=np.uint16)
+    _check("fp6s_prune_quantize",
+           _lib.fp6s_prune_quantize(_host_ptr(W), N, K, _host_ptr(codes), _host_ptr(pos), _host_ptr(scales)))
+    return codes, pos, scales.view(np.float16)
+
+
+def sparse_prepack(codes: np.ndarray, pos: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+    """Host packer: compressed (codes, pos) [N,K/2] + scales fp16 [N] -> packed uint8 [N*K/2]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    pos = np.ascontiguousarray(pos, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float16).view(np.uint16)
+    N = codes.shape[0]
+    if codes.shape != (N, K // 2) or pos.shape != (N, K // 2) or scales.shape != (N,):
+        raise ValueError("codes, pos [N,K/2] and scales [N] expected")
+    nbytes = sparse_packed_bytes(N, K)
+    out = np.empty(max(nbytes, 1), dtype=np.uint8)
+    _check("fp6s_prepack", _lib.fp6s_prepack(_host_ptr(codes), _host_ptr(pos), _host_ptr(scales), N, K,
+                                             _host_ptr(out), nbytes))
+    return out[:nbytes]
+
+
+def sparse_linear(X, packed, scales, N: int, K: int, out=None, stream=None):
+    """Y[M,N] fp16 = X[M,K] . Wdq^T for 2:4-sparse packed FP6 weights."""
+    return sparse_linear_plan(X, packed, scales, N, K, 0, 0, out=out, stream=stream)
+
+
+def sparse_linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int = 0,
+                       out=None, stream=None):
+    import torch
+    if X.dtype != torch.float16 or X.dim() != 2 or X.shape[1] != K or not X.is_contiguous():
+        raise ValueError("X must be a contiguous fp16 [M,K] tensor")
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp16 [M,N] tensor")
+    if packed.numel() != sparse_packed_bytes(N, K) or packed.dtype != torch.uint8:
+        raise ValueError("packed must be the uint8 output of sparse_prepack for (N, K)")
+    if scales.dtype != torch.float16 or scales.numel() != N:
+        raise ValueError("scales must be fp16 [N]")
+    st = _lib.fp6s_linear_plan(_dev_ptr(X), _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), M, N, K,
+                               variant, splits, _stream_handle(stream))
+    _check("fp6s_linear_plan", st)
+    return out
+
+
+def sparse_dequant(packed, scales, N: int, K: int, out=None, stream=None):
+    """Dense Wdq fp16 [N,K] (zeros at pruned positions) from packed 2:4 weights."""
+    import torch
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    st = _lib.fp6s_dequant(_dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), N, K, _stream_handle(stream))
+    _check("fp6s_dequant", st)
     return out
 
 

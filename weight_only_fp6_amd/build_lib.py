@@ -48,7 +48,7 @@ def _run(cmd, verbose):
 
 
 HIP_SOURCES = ["fpx_linear.hip", "fpx_kern_e3m2.hip", "fpx_kern_e2m3.hip", "fpx_kern_e2m2.hip",
-               "fpx_kern_e2m1.hip"]
+               "fpx_kern_e2m1.hip", "fpx_sparse.hip"]
 
 
 def _run_parallel(cmds, verbose):

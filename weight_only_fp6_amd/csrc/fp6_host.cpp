@@ -10,6 +10,7 @@
 // are this library's own design for 64-lane wavefronts (see fp6.h).
 
 #include "fp6.h"
+#include "fp6s.h"
 #include "fpx.h"
 #include "fp6_limits.h"
 
@@ -165,6 +166,36 @@ void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
   }
 }
 
+
+// 2:4-sparse FP6: one tile = 16 rows x 512 dense k (4096 bytes).  For k-step
+// j (64 dense k) and lane L = 16g + r, element i is kept weight i%2 of the
+// dense group at offset 64j + 32(g%2) + 16(i/4) + 8(g/2) + 4((i%4)/2): the
+// A-operand order of v_smfmac_f32_16x16x64_f16.  The 6-bit codes fill bytes
+// [0, 3072) exactly as packed layout v1 fills an FP6 tile (lane, k-step j,
+// element i); the 2-bit positions fill [3072, 4096): lane L's word j/2 at
+// 3072 + 16L, bits 16(j%2) + 2i.
+void pack_sparse_tile(const uint8_t* codes, const uint8_t* pos, int64_t half_k, uint8_t* tile) {
+  uint8_t fp6[16 * 256];  // codes in (row, 32j + 8g + i) order, one FP6 tile
+  uint32_t wp[64][4];
+  std::memset(wp, 0, sizeof(wp));
+  for (int r = 0; r < 16; ++r) {
+    for (int j = 0; j < 8; ++j) {
+      for (int g = 0; g < 4; ++g) {
+        for (int i = 0; i < 8; ++i) {
+          const int off = 64 * j + 32 * (g & 1) + 16 * (i >> 2) + 8 * (g >> 1) + 4 * ((i & 3) >> 1);
+          const int64_t t2 = 2 * (off / 4) + (i & 1);     // kept index inside the tile's row
+          const uint8_t c = codes[r * half_k + t2];
+          const uint32_t p = pos[r * half_k + t2];
+          fp6[r * 256 + 32 * j + 8 * g + i] = c;
+          wp[16 * g + r][j >> 1] |= p << (16 * (j & 1) + 2 * i);
+        }
+      }
+    }
+  }
+  pack_tile(FPX_E3M2, fp6, 256, tile);
+  std::memcpy(tile + 3072, wp, sizeof(wp));
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,6 +297,83 @@ int fpx_prepack(int format, const uint8_t* codes, const uint16_t* scales, int64_
 int fp6_prepack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                 void* packed, size_t packed_bytes) {
   return fpx_prepack(FPX_E3M2, codes, scales, N, K, packed, packed_bytes);
+}
+
+// ---------------------------------------------------------------------------
+// 2:4-sparse FP6 (fp6s_*).
+// ---------------------------------------------------------------------------
+size_t fp6s_packed_bytes(int64_t N, int64_t K) {
+  if (!shape_ok(N, K) || K % 512) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K) / 2;
+}
+
+int fp6s_prune_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, uint8_t* pos,
+                        uint16_t* scales) {
+  if (!W || !codes || !pos || !scales) return FP6_E_NULL;
+  if (N < 1 || K < 4 || K % 4 || N > fp6::kMaxDim || K > fp6::kMaxDim || N * K > fp6::kMaxNK)
+    return FP6_E_SHAPE;
+  const FormatInfo& f = kFormats[FPX_E3M2];
+  std::vector<float> kept(static_cast<size_t>(K / 2));
+  for (int64_t n = 0; n < N; ++n) {
+    const float* row = W + n * K;
+    uint8_t* prow = pos + n * (K / 2);
+    float amax = 0.0f;
+    for (int64_t t = 0; t < K / 4; ++t) {
+      const float* w = row + 4 * t;
+      for (int q = 0; q < 4; ++q)
+        if (!std::isfinite(w[q])) return FP6_E_VALUE;
+      // the two largest magnitudes, the lower index first among equals
+      int a = 0;
+      for (int q = 1; q < 4; ++q)
+        if (std::fabs(w[q]) > std::fabs(w[a])) a = q;
+      int b = a == 0 ? 1 : 0;
+      for (int q = 0; q < 4; ++q)
+        if (q != a && std::fabs(w[q]) > std::fabs(w[b])) b = q;
+      const int lo = a < b ? a : b, hi = a < b ? b : a;
+      prow[2 * t] = static_cast<uint8_t>(lo);
+      prow[2 * t + 1] = static_cast<uint8_t>(hi);
+      kept[2 * t] = w[lo];
+      kept[2 * t + 1] = w[hi];
+      amax = std::fmax(amax, std::fmax(std::fabs(w[lo]), std::fabs(w[hi])));
+    }
+    const uint16_t sb = double_to_half_rne(static_cast<double>(amax) / f.vmax);
+    const double s = half_bits_to_double(sb);
+    if (!std::isfinite(s) || std::fabs(s) >= f.scale_limit) return FP6_E_SCALE;
+    scales[n] = sb;
+    uint8_t* out = codes + n * (K / 2);
+    for (int64_t k = 0; k < K / 2; ++k) {
+      if (s == 0.0) { out[k] = 0; continue; }
+      const double q = static_cast<double>(kept[k]) / s;
+      const int sign = std::signbit(kept[k]) ? 1 : 0;
+      out[k] = static_cast<uint8_t>((sign << 5) | magnitude_index(f, std::fabs(q)));
+    }
+  }
+  return FP6_OK;
+}
+
+int fp6s_prepack(const uint8_t* codes, const uint8_t* pos, const uint16_t* scales, int64_t N,
+                 int64_t K, void* packed, size_t packed_bytes) {
+  if (!codes || !pos || !scales || !packed) return FP6_E_NULL;
+  if (!shape_ok(N, K) || K % 512) return FP6_E_SHAPE;
+  if (packed_bytes != fp6s_packed_bytes(N, K)) return FP6_E_SIZE;
+  const FormatInfo& f = kFormats[FPX_E3M2];
+  for (int64_t n = 0; n < N; ++n) {
+    const double s = half_bits_to_double(scales[n]);
+    if (!std::isfinite(s) || std::fabs(s) >= f.scale_limit) return FP6_E_SCALE;
+  }
+  const size_t half = static_cast<size_t>(N) * static_cast<size_t>(K / 2);
+  for (size_t i = 0; i < half; ++i)
+    if (codes[i] > 63) return FP6_E_CODE;
+  for (size_t i = 0; i < half; i += 2)
+    if (pos[i] >= pos[i + 1] || pos[i + 1] > 3) return FP6_E_VALUE;
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  const int64_t kblocks = K / 512;
+  for (int64_t nb = 0; nb < N / 16; ++nb)
+    for (int64_t kb = 0; kb < kblocks; ++kb) {
+      const int64_t off = nb * 16 * (K / 2) + kb * 256;
+      pack_sparse_tile(codes + off, pos + off, K / 2, out + (nb * kblocks + kb) * 4096);
+    }
+  return FP6_OK;
 }
 
 }  // extern "C"

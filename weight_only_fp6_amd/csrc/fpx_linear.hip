@@ -17,6 +17,7 @@
 #include <utility>
 
 #include "fp6.h"
+#include "fp6s.h"
 #include "fpx.h"
 #include "fp6_limits.h"
 #include "fpx_launch.h"
@@ -250,9 +251,89 @@ int dequant_impl(int format, const void* packed_W, const void* scales, void* W16
   }
 }
 
+// 2:4-sparse FP6: k-slice while every row block has its own CU and K fits
+// one 512-k tile per wave; otherwise the streaming kernel with X in LDS,
+// split across workgroups towards ~4 waves per CU like the dense one.
+Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
+  Plan p;
+  const int64_t ktiles = K >> 9;
+  if (variant == fpx::kSpAuto) {
+    p.variant = (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles) ? fpx::kSpKslice
+                                                                                : fpx::kSpXlds1;
+  } else {
+    p.variant = variant;
+  }
+  if (p.variant == fpx::kSpKslice) {
+    p.splits = 1;
+    return p;
+  }
+  if (splits > 0) {
+    p.splits = splits;
+    return p;
+  }
+  const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
+  const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, a);
+  int64_t s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
+  if (s > ktiles / 2) s = ktiles / 2;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  p.splits = static_cast<int>(s);
+  return p;
+}
+
+int sparse_linear_impl(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                       int64_t K, int variant, int splits, void* stream) {
+  int st = check_linear_args(X, W, S, Y, M, N, K);
+  if (st != FP6_OK) return st;
+  if (K % 512) return FP6_E_SHAPE;
+  if (M == 0) return FP6_OK;
+  if (variant < 0 || variant >= fpx::kNumSpVariants || splits < 0 || splits > (K >> 9) || splits > 4096)
+    return FP6_E_VALUE;
+  if (splits > 0 && ceil_div(N >> 4, 4) * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
+    return FP6_E_VALUE;
+  if (variant == fpx::kSpKslice && (M > 16 || (K >> 9) > fpx::kSpKsliceMaxTiles || splits > 1))
+    return FP6_E_VALUE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
+  const int cus = device_cus(dev);
+  const Plan p = choose_sparse_plan(M, N, K, cus, variant, splits);
+  Workspace* ws = nullptr;
+  if (p.splits > 1) {
+    const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
+    const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, a);
+    const size_t part_bytes = static_cast<size_t>(units) * p.splits * a * 256 * sizeof(float);
+    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
+    if (st != FP6_OK) return st;
+  }
+  fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits,
+                     ws ? static_cast<float*>(ws->part) : nullptr, ws ? ws->counters : nullptr, cus,
+                     static_cast<hipStream_t>(stream)};
+  return fpx::launch_sparse(ctx);
+}
+
 }  // namespace
 
 extern "C" {
+
+int fp6s_linear(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
+                int64_t N, int64_t K, void* stream) {
+  return sparse_linear_impl(X, packed_W, scales, Y, M, N, K, 0, 0, stream);
+}
+
+int fp6s_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
+                     int64_t N, int64_t K, int variant, int splits, void* stream) {
+  return sparse_linear_impl(X, packed_W, scales, Y, M, N, K, variant, splits, stream);
+}
+
+int fp6s_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, int64_t K,
+                 void* stream) {
+  if (!shape_ok(N, K) || K % 512) return FP6_E_SHAPE;
+  if (!packed_W || !scales || !W16) return FP6_E_NULL;
+  if (!aligned16(packed_W) || !aligned16(W16) || (reinterpret_cast<uintptr_t>(scales) & 1u))
+    return FP6_E_ALIGN;
+  return fpx::dequant_sparse(packed_W, scales, W16, N, K, static_cast<hipStream_t>(stream));
+}
+
 
 int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
                int64_t N, int64_t K, void* stream) {

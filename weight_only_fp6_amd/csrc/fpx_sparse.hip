@@ -1,0 +1,353 @@
+// Kernels of the 2:4-sparse FP6 (e3m2) weight-only linear layer on gfx950
+// sparse matrix cores.
+//
+// Sparse-Marlin (first page, post on quantised-weight kernels, points on 2:4
+// sparsity): quantised weights that are also 2:4 structured-sparse, on sparse
+// matrix units, with values, metadata and scales laid out together.
+//
+// gfx950 design:
+//  * v_smfmac_f32_16x16x64_f16 multiplies a 16x64 A operand of which 2 of
+//    every 4 k are kept (8 fp16 per lane, plus 2-bit positions in an index
+//    VGPR) by a dense 64x16 B operand (16 fp16 per lane: lane 16g+r holds
+//    column r, k = 16g..16g+15).  Lane 16g+r's A element i is kept weight i%2
+//    of the dense group at k-offset 32(g%2) + 16(i/4) + 8(g/2) + 4((i%4)/2),
+//    its position taken from bits 16*abid + 2i of the index VGPR.
+//  * A packed tile covers 16 rows x 512 dense k (4096 bytes): the kept codes
+//    in the FP6 packed layout v1 (so the FP6 splice and row-scale fold are
+//    reused unchanged) and one 16-byte quad of positions per lane, whose word
+//    j/2 is the index operand of k-steps j (abid 0) and j+1 (abid 1).  A wave
+//    reads a tile with four coalesced 16-byte loads per lane.
+//  * 0.5 bytes per dense weight instead of 0.75, and one sparse MFMA per 64
+//    dense k instead of two dense ones.
+#include "fpx_device.h"
+
+namespace {
+
+typedef _Float16 half16v __attribute__((ext_vector_type(16)));
+
+constexpr int kSpTileQuads = 256;  // 16-byte units per 16 x 512 tile
+
+struct SpTile {
+  TileFp6 w;   // kept codes, FP6 layout
+  u32x4 idx;   // positions: word j/2 = k-steps j (bits 0..15) and j+1 (16..31)
+};
+
+__device__ __forceinline__ void sp_load(SpTile& t, const u32x4* p, int lane) {
+  Fmt<kE3M2>::load(t.w, p, lane);
+  t.idx = p[192];
+}
+
+template <int J>
+__device__ __forceinline__ float4v sp_mac(const SpTile& t, half2v s2, const half16v& b, float4v acc) {
+  const half8v a = Fmt<kE3M2>::template step<J>(t.w, s2);
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, acc, static_cast<int>(t.idx[J >> 1]), 0, J & 1);
+}
+
+// ---------------------------------------------------------------------------
+// K-slice kernel (M <= 16, few row blocks): one workgroup per row block, its
+// WK waves take one sparse tile each (K <= WK*512), reduce through LDS.
+// ---------------------------------------------------------------------------
+template <int WK>
+__global__ __launch_bounds__(64 * WK) void sp_gemm_kslice(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
+    int64_t K) {
+  __shared__ float4v red[WK][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nblocks = N >> 4, ktiles = K >> 9;
+  const int64_t nb = blockIdx.x;
+  if (nb >= nblocks) return;  // uniform for the workgroup
+  const int64_t kw0 = wave * ktiles / WK, kw1 = (wave + 1) * ktiles / WK;  // at most one tile
+  const bool active = kw1 > kw0;
+  const int64_t kt = active ? kw0 : 0;
+  SpTile st;
+  sp_load(st, wp + (nb * ktiles + kt) * kSpTileQuads + lane, lane);
+  // B operand rows m = r; rows >= M read row M-1 (their columns are never stored)
+  const int64_t m = r < M ? r : M - 1;
+  const _Float16* xrow = X + m * K + kt * 512 + 16 * g;
+  half16v xf[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) xf[j] = *reinterpret_cast<const half16v*>(xrow + 64 * j);
+  const half2v s2 = row_scale2<kE3M2>(scales, nb * 16 + r);
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    acc = sp_mac<0>(st, s2, xf[0], acc);
+    acc = sp_mac<1>(st, s2, xf[1], acc);
+    acc = sp_mac<2>(st, s2, xf[2], acc);
+    acc = sp_mac<3>(st, s2, xf[3], acc);
+    acc = sp_mac<4>(st, s2, xf[4], acc);
+    acc = sp_mac<5>(st, s2, xf[5], acc);
+    acc = sp_mac<6>(st, s2, xf[6], acc);
+    acc = sp_mac<7>(st, s2, xf[7], acc);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    float4v sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < WK; ++w) sum += red[w][lane];
+    store_y_block(Y, sum, r, M, N, nb * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming kernel with X shared through LDS (any M, in m-groups of 16).  A
+// wave streams A row blocks over a K range through a register ring of D
+// tiles; the NW waves of a workgroup share each X tile (16 rows x 512 k,
+// 16 KB) through a 3-slot LDS ring, rows XOR-swizzled in 16-byte units; one
+// barrier per tile.  Split-K fix-up as for the dense kernels.
+// ---------------------------------------------------------------------------
+template <int A, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
+    int64_t mg_base) {
+  constexpr int kThreads = 64 * NW;
+  constexpr int kChunks = 16 * 64;  // 16-byte units per X tile
+  constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) half8v xs[3][kChunks];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nblocks = N >> 4, ktiles = K >> 9;
+  const int64_t ngroups = (nblocks + A - 1) / A;
+  const int64_t gsets = (ngroups + NW - 1) / NW;
+  int64_t b = blockIdx.x;
+  const int split = static_cast<int>(b % splits);
+  b /= splits;
+  const int64_t gs = b % gsets;
+  const int64_t mg = b / gsets + mg_base;
+  const int64_t rg_raw = gs * NW + wave;
+  const bool wave_active = rg_raw < ngroups;
+  const int64_t rg = wave_active ? rg_raw : ngroups - 1;  // idle waves still join barriers
+  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int r = lane & 15, g = lane >> 4;
+
+  const u32x4* w[A];
+  half2v s2[A];
+#pragma unroll
+  for (int a = 0; a < A; ++a) {
+    int64_t nb = rg * A + a;
+    if (nb >= nblocks) nb = nblocks - 1;
+    w[a] = wp + (nb * ktiles) * kSpTileQuads + lane;
+    s2[a] = row_scale2<kE3M2>(scales, nb * 16 + r);
+  }
+  // X staging: unit q = (row rr = q/64, chunk c = q%64) of the tile; rows
+  // beyond M repeat row M-1 (their accumulator columns are never stored).
+  const _Float16* xsrc[kPerThread];
+  int xdst[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    int q = i * kThreads + tid;
+    if (q >= kChunks) q = kChunks - 1;  // surplus threads duplicate the last unit
+    const int rr = q >> 6, c = q & 63;
+    int64_t m = mg * 16 + rr;
+    if (m >= M) m = M - 1;
+    xsrc[i] = X + m * K + 8 * c;
+    xdst[i] = rr * 64 + (c ^ rr);
+  }
+  half8v xstage[kPerThread];
+  const int64_t klast = kt1 > kt0 ? kt1 - 1 : kt0;
+  auto clampk = [&](int64_t t) { return t < klast ? t : klast; };
+  auto gload_x = [&](int64_t kt) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      xstage[i] = *reinterpret_cast<const half8v*>(xsrc[i] + kt * 512);
+  };
+  auto swrite_x = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) xs[slot][xdst[i]] = xstage[i];
+  };
+
+  float4v acc[A];
+#pragma unroll
+  for (int i = 0; i < A; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  struct Stage {
+    SpTile t[A];
+  };
+  auto load_w = [&](Stage& st, int64_t kt) {
+#pragma unroll
+    for (int a = 0; a < A; ++a) sp_load(st.t[a], w[a] + kt * kSpTileQuads, lane);
+  };
+  auto mac = [&](const Stage& st, int slot) {
+    const half8v* xb = xs[slot];
+#define FP6S_XL_STEP(J)                                                                  \
+  {                                                                                      \
+    const int c0 = (8 * J + 2 * g) ^ r;                                                  \
+    const half8v lo = xb[r * 64 + c0], hi = xb[r * 64 + (c0 ^ 1)];                       \
+    const half16v bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, \
+                                               11, 12, 13, 14, 15);                      \
+    _Pragma("unroll") for (int a = 0; a < A; ++a) acc[a] = sp_mac<J>(st.t[a], s2[a], bf, acc[a]); \
+  }
+    FP6S_XL_STEP(0) FP6S_XL_STEP(1) FP6S_XL_STEP(2) FP6S_XL_STEP(3)
+    FP6S_XL_STEP(4) FP6S_XL_STEP(5) FP6S_XL_STEP(6) FP6S_XL_STEP(7)
+#undef FP6S_XL_STEP
+  };
+
+  // Tile i of the split uses slot i % 3 (see the dense streaming kernel with
+  // X in LDS): branch-free steady state with clamped prefetch indices, the
+  // last (< D) tiles in a tail.
+  Stage ring[D];
+  if (kt0 < kt1) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_w(ring[d], clampk(kt0 + d));
+    gload_x(kt0);
+    swrite_x(0);
+    gload_x(clampk(kt0 + 1));
+    __syncthreads();
+    int64_t kt = kt0;
+    int slot = 0;
+    for (; kt + D <= kt1; kt += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int64_t t = kt + d;
+        const int nslot = slot == 2 ? 0 : slot + 1;
+        swrite_x(nslot);
+        gload_x(clampk(t + 2));
+        mac(ring[d], slot);
+        load_w(ring[d], clampk(t + D));
+        __syncthreads();
+        slot = nslot;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d + 1 < D; ++d) {
+      if (kt + d < kt1) {
+        const int nslot = slot == 2 ? 0 : slot + 1;
+        swrite_x(nslot);
+        gload_x(clampk(kt + d + 2));
+        mac(ring[d], slot);
+        __syncthreads();
+        slot = nslot;
+      }
+    }
+  }
+  if (!wave_active) return;
+
+  if (splits > 1) {
+    const int64_t unit = mg * ngroups + rg;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (A * 256);
+    if (!splitk_fixup<A>(acc, unit_part, counters + unit, split, splits, lane)) return;
+  }
+#pragma unroll
+  for (int a = 0; a < A; ++a) {
+    const int64_t nb = rg * A + a;
+    if (nb >= nblocks) continue;
+    store_y_block(Y, acc[a], mg * 16 + r, M, N, nb * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// De-quantisation export: one wave per tile; lane 16g+r writes, for each
+// k-step, its 4 dense groups of row r (kept values at their positions, zeros
+// elsewhere), so the 64 lanes cover the tile's 16 x 512 dense weights.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sp_dequant_kernel(const u32x4* __restrict__ wp,
+                                                         const _Float16* __restrict__ scales,
+                                                         _Float16* __restrict__ w16, int64_t N,
+                                                         int64_t K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ktiles = K >> 9;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (tile >= (N >> 4) * ktiles) return;
+  const int64_t nb = tile / ktiles, kt = tile % ktiles;
+  const int r = lane & 15, g = lane >> 4;
+  SpTile st;
+  sp_load(st, wp + tile * kSpTileQuads + lane, lane);
+  const int64_t n = nb * 16 + r;
+  const half2v s2 = row_scale2<kE3M2>(scales, n);
+  _Float16* row = w16 + n * K + kt * 512;
+  auto put = [&](auto JC, const half8v& a) {
+    constexpr int j = decltype(JC)::value;
+    const uint32_t iw = st.idx[j >> 1] >> (16 * (j & 1));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // the lane's groups: elements 2q, 2q+1
+      const int off = 64 * j + 32 * (g & 1) + 16 * (q >> 1) + 8 * (g >> 1) + 4 * (q & 1);
+      const int p0 = (iw >> (4 * q)) & 3, p1 = (iw >> (4 * q + 2)) & 3;
+      half4v h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        h[e] = p0 == e ? a[2 * q] : (p1 == e ? a[2 * q + 1] : static_cast<_Float16>(0.0f));
+      *reinterpret_cast<half4v*>(row + off) = h;
+    }
+  };
+  put(std::integral_constant<int, 0>{}, Fmt<kE3M2>::template step<0>(st.w, s2));
+  put(std::integral_constant<int, 1>{}, Fmt<kE3M2>::template step<1>(st.w, s2));
+  put(std::integral_constant<int, 2>{}, Fmt<kE3M2>::template step<2>(st.w, s2));
+  put(std::integral_constant<int, 3>{}, Fmt<kE3M2>::template step<3>(st.w, s2));
+  put(std::integral_constant<int, 4>{}, Fmt<kE3M2>::template step<4>(st.w, s2));
+  put(std::integral_constant<int, 5>{}, Fmt<kE3M2>::template step<5>(st.w, s2));
+  put(std::integral_constant<int, 6>{}, Fmt<kE3M2>::template step<6>(st.w, s2));
+  put(std::integral_constant<int, 7>{}, Fmt<kE3M2>::template step<7>(st.w, s2));
+}
+
+template <int WK>
+int launch_sp_kslice(const fpx::LaunchCtx& c) {
+  const dim3 grid(static_cast<unsigned>(c.N >> 4));  // one workgroup per row block
+  const _Float16* x = static_cast<const _Float16*>(c.X);
+  const u32x4* w = static_cast<const u32x4*>(c.W);
+  const _Float16* sc = static_cast<const _Float16*>(c.S);
+  _Float16* y = static_cast<_Float16*>(c.Y);
+  int64_t M = c.M, N = c.N, K = c.K;
+  void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&sp_gemm_kslice<WK>), grid, dim3(64 * WK), args,
+                         0, c.stream) == hipSuccess
+             ? FP6_OK
+             : FP6_E_HIP;
+}
+
+template <int A, int D, int NW>
+int launch_sp_xlds(const fpx::LaunchCtx& c) {
+  const int64_t ngroups = fpx_ceil_div(c.N >> 4, A), gsets = fpx_ceil_div(ngroups, NW);
+  const int64_t mgroups = fpx_ceil_div(c.M, 16);
+  const int64_t per_mg = gsets * c.splits;
+  int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
+  if (mg_chunk < 1) mg_chunk = 1;
+  const _Float16* x = static_cast<const _Float16*>(c.X);
+  const u32x4* w = static_cast<const u32x4*>(c.W);
+  const _Float16* sc = static_cast<const _Float16*>(c.S);
+  _Float16* y = static_cast<_Float16*>(c.Y);
+  float* part = c.part;
+  unsigned* cnt = c.counters;
+  int64_t M = c.M, N = c.N, K = c.K;
+  int splits = c.splits;
+  for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
+    const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
+    const dim3 grid(static_cast<unsigned>(nmg * per_mg));
+    int64_t mg_base = mg0;
+    void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&sp_gemm_xlds<A, D, NW>), grid, dim3(64 * NW),
+                        args, 0, c.stream) != hipSuccess)
+      return FP6_E_HIP;
+  }
+  return FP6_OK;
+}
+
+}  // namespace
+
+namespace fpx {
+
+int launch_sparse(const LaunchCtx& c) {
+  switch (c.variant) {
+    case kSpKslice: return (c.K >> 9) <= 8 ? launch_sp_kslice<8>(c) : launch_sp_kslice<16>(c);
+    case kSpXlds1: return launch_sp_xlds<1, 4, 4>(c);
+    case kSpXlds2: return launch_sp_xlds<2, 4, 4>(c);
+    default: return FP6_E_VALUE;
+  }
+}
+
+int dequant_sparse(const void* W, const void* S, void* W16, int64_t N, int64_t K, hipStream_t s) {
+  const int64_t tiles = (N >> 4) * (K >> 9);
+  const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* out = static_cast<_Float16*>(W16);
+  void* args[] = {&w, &sc, &out, &N, &K};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&sp_dequant_kernel), grid, dim3(256), args, 0, s) ==
+                 hipSuccess
+             ? FP6_OK
+             : FP6_E_HIP;
+}
+
+}  // namespace fpx
