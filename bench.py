@@ -76,6 +76,8 @@ def _parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--format", default="e3m2", choices=sorted(FORMAT_BITS),
                     help="weight format (e3m2 = FP6 through fp6_linear; others through fpx_linear)")
+    ap.add_argument("--sparse", action="store_true",
+                    help="2:4-sparse FP6 e3m2 weights through fp6s_linear (K % 512 == 0)")
     ap.add_argument("--no-graph", action="store_true", help="time direct launches instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the fp16 BLAS and read-probe context numbers")
@@ -99,6 +101,8 @@ def kernel_source_hash() -> str:
 
 
 def weight_bytes(N, K, fmt="e3m2"):
+    if fmt == "sparse24":
+        return N * K // 2
     return N * K * FORMAT_BITS[fmt] // 8
 
 
@@ -122,10 +126,16 @@ def cpu_baseline(shape, packed, scales, X, budget_s=20.0, fmt="e3m2"):
                 return oracle.unpack_np(buf, n, K)
             return oracle.unpack_tiles(buf, n, K, fmt)
 
+        def dequant(buf, n):
+            if fmt == "sparse24":
+                from oracle import sparse24
+                codes, pos = sparse24.unpack_tiles(buf, n, K)
+                return sparse24.dequant_ref(codes, pos, scales[:n], K)
+            return oracle.dequant_ref(unpack(buf, n), scales[:n], fmt)
+
         def run(nblk):
             t0 = time.perf_counter()
-            codes = unpack(packed[: nblk * row_bytes], 16 * nblk)
-            wdq = oracle.dequant_ref(codes, scales[: 16 * nblk], fmt)
+            wdq = dequant(packed[: nblk * row_bytes], 16 * nblk)
             oracle.gemm_ref(X, wdq)
             return time.perf_counter() - t0
         nblk = max(1, min(N // 16, (4 * 2**20) // row_bytes))
@@ -192,7 +202,10 @@ def _time_graph(torch, stream, launch, n):
 
 def fp16_blas_context(torch, fp6, stream, pk, sc, x, M, N, K, fmt="e3m2"):
     """fp16 torch linear (hipBLASLt) on the de-quantised weights, cold copies."""
-    W16 = fp6.dequant(pk, sc, N, K, stream=stream, fmt=fmt)
+    if fmt == "sparse24":
+        W16 = fp6.sparse_dequant(pk, sc, N, K, stream=stream)
+    else:
+        W16 = fp6.dequant(pk, sc, N, K, stream=stream, fmt=fmt)
     torch.cuda.synchronize()
     R = int(min(32, max(2, math.ceil(ROT_BYTES / (2 * N * K)))))
     ws = [W16.clone() for _ in range(R)]
@@ -378,8 +391,8 @@ def main():
         summarize(args.summarize)
         return
     if args.traffic:
-        traffic_summary(args.workload if args.format == "e3m2" else f"{args.workload} ({args.format})",
-                        *args.traffic)
+        fmt = "sparse24" if args.sparse else args.format
+        traffic_summary(args.workload if fmt == "e3m2" else f"{args.workload} ({fmt})", *args.traffic)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -406,11 +419,19 @@ def main():
     dev = torch.device("cuda:0")
 
     # ---- inputs: host quantise + prepack, then R rotated device copies ----
-    fmt = args.format
+    fmt = "sparse24" if args.sparse else args.format
+    if args.sparse and args.format != "e3m2":
+        print("--sparse uses FP6 e3m2 weights", file=sys.stderr)
+        sys.exit(2)
     W = synth.weights(N, K, shape.seed_w)
-    codes, scales = fp6.quantize_rows(W, fmt)
+    if args.sparse:
+        codes, pos, scales = fp6.prune_quantize(W)
+        packed = fp6.sparse_prepack(codes, pos, scales, K)
+        del pos
+    else:
+        codes, scales = fp6.quantize_rows(W, fmt)
+        packed = fp6.prepack(codes, scales, fmt)
     del W
-    packed = fp6.prepack(codes, scales, fmt)
     del codes
     X = synth.activations(M, K, shape.seed_x)
     R = int(min(64, max(2, math.ceil(ROT_BYTES / packed.nbytes))))
@@ -427,14 +448,17 @@ def main():
     sh = stream.cuda_stream
     if args.variant:
         variant, splits = args.variant, args.splits
+    elif args.sparse:
+        variant, splits = fp6.sparse_plan_query(M, N, K)
     else:
         variant, splits = fp6.plan_query(M, N, K)
-
-    fid = fp6.FORMATS[fmt]
+    fid = fp6.FORMATS.get(fmt, 0)
 
     def launch(i):
         x, w, s, y = ptrs[i % R]
-        if fmt == "e3m2":
+        if fmt == "sparse24":
+            st = L.fp6s_linear_plan(x, w, s, y, M, N, K, args.variant, args.splits, sh)
+        elif fmt == "e3m2":
             st = L.fp6_linear_plan(x, w, s, y, M, N, K, args.variant, args.splits, sh)
         else:
             st = L.fpx_linear_plan(fid, x, w, s, y, M, N, K, args.variant, args.splits, sh)
@@ -485,9 +509,11 @@ def main():
     tflops = flops * args.steps / wall_s / 1e12
     # Ridge: 2500 TFLOP/s / 8 TB/s = 312.5 flop/byte; per packed weight byte the
     # layer does 2*M*N*K / (bits/8*N*K) = 16*M/bits flop, so FP6 is HBM-bound
-    # for M < 117 (FP5 98, FP4 78).
+    # for M < 117 (FP5 98, FP4 78; 2:4-sparse FP6, 0.5 byte per dense weight,
+    # 78 in dense-equivalent flops).
     traffic = committed_traffic(args.workload, fmt) if not args.variant else None
-    if M < 312.5 * FORMAT_BITS[fmt] / 16:
+    eff_bits = 4 if fmt == "sparse24" else FORMAT_BITS[fmt]
+    if M < 312.5 * eff_bits / 16:
         achieved = abytes / per_launch_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -499,7 +525,10 @@ def main():
                     "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
                     "traffic": round(traffic["bytes_per_launch"]) if traffic else None}
         value, unit = round(tflops, 2), "TFLOP/s"
-    roofline["kernel"] = fp6.KERNEL_NAMES.get(variant, str(variant))
+    if fmt == "sparse24":
+        roofline["kernel"] = fp6.SPARSE_KERNEL_NAMES.get(variant, str(variant))
+    else:
+        roofline["kernel"] = fp6.KERNEL_NAMES.get(variant, str(variant))
     roofline["splits"] = splits
     roofline["per_launch_us"] = round(per_launch_s * 1e6, 3)
     roofline["algorithmic_bytes"] = abytes
@@ -521,7 +550,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload if fmt == "e3m2" else f"{args.workload}_{fmt}",
                    "M": M, "N": N, "K": K,
-                   "weights": f"fp{FORMAT_BITS[fmt]} {fmt} + fp16 row scale (packed layout v1)",
+                   "weights": ("fp6 e3m2, 2:4 sparse (magnitude-pruned), + fp16 row scale (packed 2:4 layout)"
+                               if fmt == "sparse24" else
+                               f"fp{FORMAT_BITS[fmt]} {fmt} + fp16 row scale (packed layout v1)"),
                    "activations": "fp16", "accumulate": "fp32",
                    "rotated_weight_copies": R, "graph": not args.no_graph},
         "weight_gbps": round(weight_gbs, 1),

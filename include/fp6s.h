@@ -79,12 +79,19 @@ int fp6s_linear(const void* X, const void* packed_W, const void* scales, void* Y
  * fp6s_linear_plan -- fp6s_linear with the schedule forced.  variant:
  * 0 = automatic; 1 = k-slice (one workgroup per 16-row block, its waves split
  * K; M <= 16, K <= 8192); 2 = streaming with X shared through LDS, 1 row
- * block per wave; 3 = the same with 2 row blocks per wave.  splits: 0 =
- * automatic, else K-splits across workgroups (1..K/512; variants 2 and 3).
+ * block per wave; 3 = the same with 2 row blocks per wave; 4 = tiled, 256
+ * rows x 64 columns per 8-wave workgroup (X staged in LDS); 5 = tiled, 256
+ * rows x 128 columns.  Variants 2-5 handle any M.  splits: 0 = automatic,
+ * else K-splits across workgroups (1..K/512; variants 2-5).
  * Errors: as fp6_linear_plan.
  */
 int fp6s_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
                      int64_t N, int64_t K, int variant, int splits, void* stream);
+
+/* fp6s_linear_plan_query -- host: the schedule fp6s_linear would use for
+ * (M, N, K) on the current device (*variant 1..5, *splits).  One HIP query.
+ * Errors: FP6_E_NULL, FP6_E_SHAPE (M >= 1, K % 512 == 0), FP6_E_HIP. */
+int fp6s_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits);
 
 /* fp6s_dequant -- device, asynchronous: dense Wdq fp16 [N][K] (zeros at the
  * pruned positions) from the packed 2:4 buffer, with the same device splice

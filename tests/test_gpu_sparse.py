@@ -27,7 +27,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import weight_only_fp6_amd as fp6  # noqa: E402
 
 DEV = torch.device("cuda:0")
-VARIANTS = (0, 2, 3)     # any M; 1 (k-slice) only for M <= 16
+VARIANTS = (0, 2, 3, 4, 5)     # any M; 1 (k-slice) only for M <= 16
 KSLICE = 1
 
 
@@ -71,7 +71,7 @@ def test_dequant_all_codes_and_position_pairs():
     assert np.array_equal(out.cpu().numpy().view(np.uint16), ref.view(np.uint16))
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 17, 64])
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 64, 100, 257])
 @pytest.mark.parametrize("NK", [(16, 512), (80, 1536), (48, 4608)])
 def test_linear_small_shapes_every_variant(M, NK):
     N, K = NK
@@ -87,7 +87,7 @@ def test_linear_forced_splits():
     p = SpPrepared(16, 4096, 8192, seed_w=71, seed_x=72, sample=256)
     X, packed, s = p.to_device()
     cols = torch.from_numpy(p.rows).to(DEV)
-    for variant in (2, 3):
+    for variant in (2, 3, 4, 5):
         for splits in (1, 2, 3, 5, 16):
             Y = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits)
             torch.cuda.synchronize()
@@ -102,7 +102,8 @@ def _prep(name, sample):
 
 @pytest.mark.parametrize("name", ["llama7b_attn_1x4096x4096", "llama7b_mlp_up_16x11008x4096",
                                   "llama70b_mlp_1x28672x8192", "llama70b_mlp_16x28672x8192",
-                                  "opt30b_qkv_64x21504x7168"])
+                                  "opt30b_qkv_64x21504x7168", "opt30b_qkv_128x21504x7168",
+                                  "opt30b_qkv_256x21504x7168"])
 def test_linear_workloads(name):
     shp = synth.SHAPES[name]
     sample = None if shp.N * shp.K <= 48 * 2**20 else 384
@@ -122,7 +123,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
     want = p.wdq_ref[:, ks].T.astype(np.float64)
-    for variant, splits in [(0, 0), (1, 0), (2, 1), (2, 3), (3, 1), (3, 2)]:
+    for variant, splits in [(0, 0), (1, 0), (2, 1), (2, 3), (3, 1), (3, 2), (4, 1), (4, 2), (5, 1), (5, 4)]:
         Y = fp6.sparse_linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (variant, splits)

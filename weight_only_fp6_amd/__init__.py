@@ -42,7 +42,7 @@ EXPORTED = (
     "fp6_prepack", "fp6_linear", "fp6_linear_plan", "fp6_linear_plan_query", "fp6_dequant",
     "fp6_release", "fpx_bits", "fpx_packed_bytes", "fpx_quantize_rows", "fpx_prepack",
     "fpx_linear", "fpx_linear_plan", "fpx_dequant", "fp6s_packed_bytes", "fp6s_prune_quantize",
-    "fp6s_prepack", "fp6s_linear", "fp6s_linear_plan", "fp6s_dequant",
+    "fp6s_prepack", "fp6s_linear", "fp6s_linear_plan", "fp6s_linear_plan_query", "fp6s_dequant",
 )
 FORMATS = {"e3m2": 0, "e2m3": 1, "e2m2": 2, "e2m1": 3}
 
@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "fp6s_prepack": ([vp, vp, vp, i64, i64, vp, sz], i32),
         "fp6s_linear": ([vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp6s_linear_plan": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp], i32),
+        "fp6s_linear_plan_query": ([i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "fp6s_dequant": ([vp, vp, vp, i64, i64, vp], i32),
     }
     for name, (args, res) in sig.items():
@@ -237,7 +238,8 @@ def dequant(packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e
 # ---------------------------------------------------------------------------
 # 2:4-sparse FP6
 # ---------------------------------------------------------------------------
-SPARSE_KERNEL_NAMES = {1: "sp_gemm_kslice", 2: "sp_gemm_xlds<1,4,4>", 3: "sp_gemm_xlds<2,4,4>"}
+SPARSE_KERNEL_NAMES = {1: "sp_gemm_kslice", 2: "sp_gemm_xlds<1,4,4>", 3: "sp_gemm_xlds<2,4,4>",
+                       4: "sp_gemm_tiled<4,2,8>", 5: "sp_gemm_tiled<8,2,8>"}
 
 
 def sparse_packed_bytes(N: int, K: int) -> int:
@@ -297,6 +299,14 @@ def sparse_linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, spli
                                variant, splits, _stream_handle(stream))
     _check("fp6s_linear_plan", st)
     return out
+
+
+def sparse_plan_query(M: int, N: int, K: int):
+    """(variant, splits) that fp6s_linear picks for this shape on the current GPU."""
+    v, s = ctypes.c_int(0), ctypes.c_int(0)
+    _check("fp6s_linear_plan_query",
+           _lib.fp6s_linear_plan_query(M, N, K, ctypes.byref(v), ctypes.byref(s)))
+    return v.value, s.value
 
 
 def sparse_dequant(packed, scales, N: int, K: int, out=None, stream=None):

@@ -251,15 +251,22 @@ int dequant_impl(int format, const void* packed_W, const void* scales, void* W16
   }
 }
 
-// 2:4-sparse FP6: k-slice while every row block has its own CU and K fits
-// one 512-k tile per wave; otherwise the streaming kernel with X in LDS,
-// split across workgroups towards ~4 waves per CU like the dense one.
+// 2:4-sparse FP6.  M <= 16: the k-slice kernel while every row block has its
+// own CU and K fits one 512-k tile per wave, else the streaming kernel with X
+// in LDS, split towards ~4 waves per CU like the dense one.  M > 16: the
+// tiled kernel (64 columns per workgroup up to M = 64, else 128), split
+// across workgroups while a whole extra round fits on the CUs.
+bool sp_tiled(int v) { return v == fpx::kSpTiled4 || v == fpx::kSpTiled8; }
+int sp_tile_b(int v) { return v == fpx::kSpTiled8 ? 8 : 4; }
+
 Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
   Plan p;
   const int64_t ktiles = K >> 9;
   if (variant == fpx::kSpAuto) {
-    p.variant = (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles) ? fpx::kSpKslice
-                                                                                : fpx::kSpXlds1;
+    if (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles) p.variant = fpx::kSpKslice;
+    else if (M <= 16) p.variant = fpx::kSpXlds1;
+    else if (M <= 64) p.variant = fpx::kSpTiled4;
+    else p.variant = fpx::kSpTiled8;
   } else {
     p.variant = variant;
   }
@@ -271,9 +278,15 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
     p.splits = splits;
     return p;
   }
-  const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
-  const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, a);
-  int64_t s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
+  int64_t s;
+  if (sp_tiled(p.variant)) {
+    const int64_t wgs = ceil_div(M, 16 * sp_tile_b(p.variant)) * ceil_div(N >> 4, 16);
+    s = cus / wgs;
+  } else {
+    const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
+    const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, a);
+    s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
+  }
   if (s > ktiles / 2) s = ktiles / 2;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -299,9 +312,16 @@ int sparse_linear_impl(const void* X, const void* W, const void* S, void* Y, int
   const Plan p = choose_sparse_plan(M, N, K, cus, variant, splits);
   Workspace* ws = nullptr;
   if (p.splits > 1) {
-    const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
-    const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, a);
-    const size_t part_bytes = static_cast<size_t>(units) * p.splits * a * 256 * sizeof(float);
+    int64_t units, floats;
+    if (sp_tiled(p.variant)) {  // one unit per wave: 8 waves x 2 row blocks x B column blocks
+      units = ceil_div(M, 16 * sp_tile_b(p.variant)) * ceil_div(N >> 4, 16) * 8;
+      floats = 2 * sp_tile_b(p.variant) * 256;
+    } else {
+      const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
+      units = ceil_div(M, 16) * ceil_div(N >> 4, a);
+      floats = a * 256;
+    }
+    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
     st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
     if (st != FP6_OK) return st;
   }
@@ -323,6 +343,17 @@ int fp6s_linear(const void* X, const void* packed_W, const void* scales, void* Y
 int fp6s_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
                      int64_t N, int64_t K, int variant, int splits, void* stream) {
   return sparse_linear_impl(X, packed_W, scales, Y, M, N, K, variant, splits, stream);
+}
+
+int fp6s_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits) {
+  if (!variant || !splits) return FP6_E_NULL;
+  if (!shape_ok(N, K) || K % 512 || M < 1 || M > fp6::kMaxDim) return FP6_E_SHAPE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
+  const Plan p = choose_sparse_plan(M, N, K, device_cus(dev), 0, 0);
+  *variant = p.variant;
+  *splits = p.splits;
+  return FP6_OK;
 }
 
 int fp6s_dequant(const void* packed_W, const void* scales, void* W16, int64_t N, int64_t K,

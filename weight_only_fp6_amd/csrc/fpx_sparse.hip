@@ -239,6 +239,190 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
 }
 
 // ---------------------------------------------------------------------------
+// Tiled kernel (M > 16): the dense tiled kernel's schedule on sparse tiles.
+// Workgroup = NW waves x TA row blocks = 256 weight rows, BM = 16*B columns
+// of X.  Per half-tile (4 sparse k-steps = 256 dense k): X (BM x 256) is
+// copied global -> LDS with direct LDS loads, XOR-swizzled in 16-byte units;
+// the packed words of the next half-tile (codes and positions) are loaded
+// into registers; each k-step's A fragments are spliced once and reused for
+// B sparse MFMAs while the next k-step is spliced.
+// ---------------------------------------------------------------------------
+struct SpHalf {
+  u32x2 q2;   // 2-bit code words of k-steps 4h'..4h'+3
+  u32x4 q4;   // 4-bit code words, one per k-step
+  u32x2 idx;  // position words: k-steps (4h', 4h'+1) and (4h'+2, 4h'+3)
+};
+
+template <int TA>
+struct SpWHalf {
+  SpHalf h[TA];
+};
+
+template <int B, int TA, int NW>
+__global__ __launch_bounds__(64 * NW) void sp_gemm_tiled(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
+    int64_t mg_base) {
+  constexpr int BM = 16 * B;
+  constexpr int kHalfUnits = BM * 32;             // 16-byte units per X half-tile buffer
+  constexpr int kThreads = 64 * NW;
+  static_assert(TA * NW == 16, "a workgroup covers 16 row blocks");
+  constexpr int kLoadsPerThread = kHalfUnits / kThreads;
+  __shared__ __attribute__((aligned(16))) half8v xbuf0[kHalfUnits];
+  __shared__ __attribute__((aligned(16))) half8v xbuf1[kHalfUnits];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nblocks = N >> 4, ktiles = K >> 9;
+  const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
+  int64_t bidx = blockIdx.x;
+  const int split = static_cast<int>(bidx % splits);
+  bidx /= splits;
+  const int64_t nt = bidx % ntiles;
+  const int64_t mg = bidx / ntiles + mg_base;
+  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t m0 = mg * BM;
+
+  const u32x4* w[TA];
+  half2v s2[TA];
+#pragma unroll
+  for (int a = 0; a < TA; ++a) {
+    int64_t nb = nt * 16 + wave * TA + a;
+    if (nb >= nblocks) nb = nblocks - 1;
+    w[a] = wp + (nb * ktiles) * kSpTileQuads + lane;
+    s2[a] = row_scale2<kE3M2>(scales, nb * 16 + r);
+  }
+  auto load_wh = [&](SpWHalf<TA>& st, int64_t h) {  // half-tile h: tile h>>1, half h&1
+    const int64_t kt = h >> 1;
+    const int hh = static_cast<int>(h & 1);
+#pragma unroll
+    for (int a = 0; a < TA; ++a) {
+      const u32x4* p = w[a] + kt * kSpTileQuads;
+      st.h[a].q2 = reinterpret_cast<const u32x2*>(p)[hh];
+      st.h[a].q4 = p[64 + 64 * hh];
+      st.h[a].idx = reinterpret_cast<const u32x2*>(p + 192)[hh];
+    }
+  };
+
+  // X direct loads: instruction i of this wave fills LDS units
+  // [i*kThreads + wave*64, +64) linearly; unit u = (row mm = u/32, slot
+  // c' = u%32) receives global chunk c = c' ^ (mm & 15) of X row m0+mm.
+  const _Float16* xsrc[kLoadsPerThread];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int u = i * kThreads + tid, mm = u >> 5, c = (u & 31) ^ (mm & 15);
+    int64_t m = m0 + mm;
+    if (m >= M) m = M - 1;
+    xsrc[i] = X + m * K + 8 * c;
+  }
+  auto dma_x = [&](half8v* buf, int64_t h) {
+    const int64_t koff = (h >> 1) * 512 + (h & 1) * 256;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i)
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(xsrc[i] + koff),
+          reinterpret_cast<__attribute__((address_space(3))) void*>(
+              reinterpret_cast<uintptr_t>(buf + i * kThreads + wave * 64)),
+          16, 0, 0);
+  };
+
+  float4v acc[TA * B];
+#pragma unroll
+  for (int i = 0; i < TA * B; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  half8v afr[2][TA];
+  half16v bfr[B];
+  auto read_b = [&](const half8v* buf, int jj) {
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) {
+      const int mm = bi * 16 + r;
+      const int s0 = (8 * jj + 2 * g) ^ (mm & 15);
+      bfr[bi] = __builtin_shufflevector(buf[mm * 32 + s0], buf[mm * 32 + (s0 ^ 1)], 0, 1, 2, 3, 4, 5, 6, 7, 8,
+                                        9, 10, 11, 12, 13, 14, 15);
+    }
+  };
+  auto splice = [&](half8v (&dst)[TA], const SpWHalf<TA>& wh, auto JC) {
+    constexpr int jj = decltype(JC)::value;
+#pragma unroll
+    for (int a = 0; a < TA; ++a) dst[a] = splice6<kE3M2, jj & 1>(wh.h[a].q2[jj >> 1], wh.h[a].q4[jj], s2[a]);
+  };
+  auto mfmas = [&](const half8v (&av)[TA], const SpWHalf<TA>& wh, auto JC) {
+    constexpr int jj = decltype(JC)::value;
+#pragma unroll
+    for (int a = 0; a < TA; ++a)
+#pragma unroll
+      for (int bi = 0; bi < B; ++bi)
+        acc[a * B + bi] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(
+            av[a], bfr[bi], acc[a * B + bi], static_cast<int>(wh.h[a].idx[jj >> 1]), 0, jj & 1);
+  };
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < TA * B; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  };
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
+  // Wait for this wave's direct LDS loads of the next half-tile (issued
+  // before the 3*TA weight loads of that half-tile), then the barrier makes
+  // every wave's copy visible.
+  constexpr int kWLoads = TA * 3;
+  constexpr int kWaitDma = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (7 << 4) | (15 << 8);
+
+  // One half-tile: k-steps 0..3 from buffer `cur`; prefetch X(h+1) into
+  // `nxt` and the words of h+1 into `wn`; the splice of the next k-step
+  // (the last one: of h+1's first) overlaps the current k-step's MFMAs.
+  auto half_step = [&](half8v* cur, half8v* nxt, const SpWHalf<TA>& wc, SpWHalf<TA>& wn, int64_t hnext) {
+    dma_x(nxt, hnext);
+    __builtin_amdgcn_sched_barrier(0);
+    load_wh(wn, hnext);
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(cur, 0); splice(afr[1], wc, J1{}); mfmas(afr[0], wc, J0{}); interleave();
+    read_b(cur, 1); splice(afr[0], wc, J2{}); mfmas(afr[1], wc, J1{}); interleave();
+    read_b(cur, 2); splice(afr[1], wc, J3{}); mfmas(afr[0], wc, J2{}); interleave();
+    read_b(cur, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    splice(afr[0], wn, J0{}); mfmas(afr[1], wc, J3{}); interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitDma);
+    __syncthreads();
+  };
+
+  const int64_t h0 = 2 * kt0, h1 = 2 * kt1;  // half-tiles of this split
+  if (h0 < h1) {
+    auto clamph = [&](int64_t h) { return h < h1 - 1 ? h : h1 - 1; };
+    SpWHalf<TA> wa, wb;
+    dma_x(xbuf0, h0);
+    load_wh(wa, h0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    splice(afr[0], wa, J0{});
+    for (int64_t h = h0; h < h1; h += 2) {
+      half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));
+      half_step(xbuf1, xbuf0, wb, wa, clamph(h + 2));
+    }
+  }
+
+  if (splits > 1) {
+    const int64_t unit = (mg * ntiles + nt) * NW + wave;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (TA * B * 256);
+    if (!splitk_fixup<TA * B>(acc, unit_part, counters + unit, split, splits, lane)) return;
+  }
+#pragma unroll
+  for (int a = 0; a < TA; ++a) {
+    const int64_t nb = nt * 16 + wave * TA + a;
+    if (nb >= nblocks) continue;
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi)
+      store_y_block(Y, acc[a * B + bi], m0 + bi * 16 + r, M, N, nb * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // De-quantisation export: one wave per tile; lane 16g+r writes, for each
 // k-step, its 4 dense groups of row r (kept values at their positions, zeros
 // elsewhere), so the 64 lanes cover the tile's 16 x 512 dense weights.
@@ -324,6 +508,33 @@ int launch_sp_xlds(const fpx::LaunchCtx& c) {
   return FP6_OK;
 }
 
+template <int B, int TA, int NW>
+int launch_sp_tiled(const fpx::LaunchCtx& c) {
+  const int64_t ntiles = fpx_ceil_div(c.N >> 4, 16);
+  const int64_t mgroups = fpx_ceil_div(c.M, 16 * B);
+  const int64_t per_mg = ntiles * c.splits;
+  int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
+  if (mg_chunk < 1) mg_chunk = 1;
+  const _Float16* x = static_cast<const _Float16*>(c.X);
+  const u32x4* w = static_cast<const u32x4*>(c.W);
+  const _Float16* sc = static_cast<const _Float16*>(c.S);
+  _Float16* y = static_cast<_Float16*>(c.Y);
+  float* part = c.part;
+  unsigned* cnt = c.counters;
+  int64_t M = c.M, N = c.N, K = c.K;
+  int splits = c.splits;
+  for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
+    const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
+    const dim3 grid(static_cast<unsigned>(nmg * per_mg));
+    int64_t mg_base = mg0;
+    void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&sp_gemm_tiled<B, TA, NW>), grid, dim3(64 * NW),
+                        args, 0, c.stream) != hipSuccess)
+      return FP6_E_HIP;
+  }
+  return FP6_OK;
+}
+
 }  // namespace
 
 namespace fpx {
@@ -333,6 +544,8 @@ int launch_sparse(const LaunchCtx& c) {
     case kSpKslice: return (c.K >> 9) <= 8 ? launch_sp_kslice<8>(c) : launch_sp_kslice<16>(c);
     case kSpXlds1: return launch_sp_xlds<1, 4, 4>(c);
     case kSpXlds2: return launch_sp_xlds<2, 4, 4>(c);
+    case kSpTiled4: return launch_sp_tiled<4, 2, 8>(c);
+    case kSpTiled8: return launch_sp_tiled<8, 2, 8>(c);
     default: return FP6_E_VALUE;
   }
 }
