@@ -317,25 +317,35 @@ def decoder_chain(name, fmt="e3m2"):
     import weight_only_fp6_amd as fp6
     from weight_only_fp6_amd import synth
     layers = DECODERS[name]
+    sparse = fmt == "sparse24"
+    if sparse and any(k % 512 for _, _, k in layers):
+        print(f"{name}: the 2:4-sparse path needs K % 512 == 0 for every layer", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
     fp6_bytes = sum(weight_bytes(n, k, fmt) for _, n, k in layers)
-    ncode = 1 << FORMAT_BITS[fmt]
-    fid = fp6.FORMATS[fmt]
+    ncode = 64 if sparse else 1 << FORMAT_BITS[fmt]
+    fid = fp6.FORMATS.get(fmt, 0)
     copies = int(max(1, math.ceil(ROT_BYTES / fp6_bytes)))
     packed, scales, w16 = [], [], []
     for ci in range(copies):
         pc, sc, wc = [], [], []
         for li, (_, n, k) in enumerate(layers):
-            codes = synth.codes_uniform(n, k, seed=100 * ci + li) % ncode
             s_ = np.full(n, 0.003, dtype=np.float16)
-            pk = torch.from_numpy(fp6.prepack(codes, s_, fmt)).to(dev)
+            if sparse:
+                codes = synth.codes_uniform(n, k // 2, seed=100 * ci + li)
+                pos = np.tile(np.array([0, 2], np.uint8), (n, k // 4))
+                pk = torch.from_numpy(fp6.sparse_prepack(codes, pos, s_, k)).to(dev)
+            else:
+                codes = synth.codes_uniform(n, k, seed=100 * ci + li) % ncode
+                pk = torch.from_numpy(fp6.prepack(codes, s_, fmt)).to(dev)
             st = torch.from_numpy(s_).to(dev)
             pc.append(pk)
             sc.append(st)
             if ci == 0:
-                wc.append(fp6.dequant(pk, st, n, k, stream=stream, fmt=fmt))
+                wc.append(fp6.sparse_dequant(pk, st, n, k, stream=stream) if sparse else
+                          fp6.dequant(pk, st, n, k, stream=stream, fmt=fmt))
         packed.append(pc)
         scales.append(sc)
         if ci == 0:
@@ -352,10 +362,11 @@ def decoder_chain(name, fmt="e3m2"):
         def fp6_step(i):
             c = i % copies
             for li, (_, n, k) in enumerate(layers):
-                st = L.fpx_linear(fid, xs[k].data_ptr(), packed[c][li].data_ptr(), scales[c][li].data_ptr(),
-                                  ys[li].data_ptr(), M, n, k, stream.cuda_stream)
+                args = (xs[k].data_ptr(), packed[c][li].data_ptr(), scales[c][li].data_ptr(),
+                        ys[li].data_ptr(), M, n, k, stream.cuda_stream)
+                st = L.fp6s_linear(*args) if sparse else L.fpx_linear(fid, *args)
                 if st:
-                    raise fp6.FP6Error("fpx_linear", st)
+                    raise fp6.FP6Error("linear", st)
 
         def f16_step(i):
             c = i % w16_copies
@@ -406,7 +417,7 @@ def main():
         calibrate_copy()
         return
     if args.decoder:
-        decoder_chain(args.decoder, args.format)
+        decoder_chain(args.decoder, "sparse24" if args.sparse else args.format)
         return
     import weight_only_fp6_amd as fp6
     from weight_only_fp6_amd import synth

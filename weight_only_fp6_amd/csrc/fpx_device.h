@@ -329,6 +329,26 @@ __device__ __forceinline__ void store_y_block(_Float16* __restrict__ Y, const fl
   *reinterpret_cast<half4v*>(Y + m * N + n0 + 4 * g) = o;
 }
 
+// Sum of the W partial 16x16 tiles in LDS, in wave order (deterministic).
+// The reads are issued 8 at a time before their adds, so their latencies
+// overlap without holding all W tiles in registers.
+template <int W>
+__device__ __forceinline__ float4v reduce_waves(const float4v (&red)[W][64], int lane) {
+  constexpr int kChunk = W < 8 ? W : 8;
+  static_assert(W % kChunk == 0, "wave count must be a multiple of the chunk");
+  float4v sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w0 = 0; w0 < W; w0 += kChunk) {
+    float4v v[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) v[i] = red[w0 + i][lane];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) sum = (w0 + i == 0) ? v[i] : sum + v[i];
+  }
+  return sum;
+}
+
 // ---------------------------------------------------------------------------
 // Streaming fused kernel (memory-bound regime).
 // Work unit = (m-group of 16*MB columns, row group of A row blocks, K-split).
@@ -680,6 +700,8 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   auto reduce_store = [&](const float4v& acc, int buf, int64_t nb) {
     red[buf][wave][lane] = acc;
     __syncthreads();
+    // A plain loop: this kernel keeps the next row block's tiles and its X
+    // slice in registers, so holding several partial tiles at once spills.
     if (wave == 0) {
       float4v sum = red[buf][0][lane];
 #pragma unroll
@@ -761,11 +783,14 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
       for (int j = 0; j < 8; ++j)
         xf[j] = *reinterpret_cast<const half8v*>(xrow + tile_of(0) * 256 + 32 * j);
       if (ktw > 0) {
-#define FP6_KX1(J)                                                                          \
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                             \
-      Fmt<F>::template step<J>(st[0].t[0], s2), xf[J], acc, 0, 0, 0);
-        FP6_KX1(0) FP6_KX1(1) FP6_KX1(2) FP6_KX1(3) FP6_KX1(4) FP6_KX1(5) FP6_KX1(6) FP6_KX1(7)
+        // Two accumulators halve the MFMA dependency chain.
+        float4v acc1 = {0.f, 0.f, 0.f, 0.f};
+#define FP6_KX1(J, A)                                                                       \
+  A = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<J>(st[0].t[0], s2), xf[J], A, 0, 0, 0);
+        FP6_KX1(0, acc) FP6_KX1(1, acc1) FP6_KX1(2, acc) FP6_KX1(3, acc1)
+        FP6_KX1(4, acc) FP6_KX1(5, acc1) FP6_KX1(6, acc) FP6_KX1(7, acc1)
 #undef FP6_KX1
+        acc += acc1;
       }
     } else {
     half8v xr[3][4];
@@ -797,12 +822,7 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     }
     red[wave][lane] = acc;
     __syncthreads();
-    if (wave == 0) {
-      float4v sum = red[0][lane];
-#pragma unroll
-      for (int w = 1; w < WK; ++w) sum += red[w][lane];
-      store_y_block(Y, sum, r, M, N, nb * 16, g);
-    }
+    if (wave == 0) store_y_block(Y, reduce_waves<WK>(red, lane), r, M, N, nb * 16, g);
   }
 }
 

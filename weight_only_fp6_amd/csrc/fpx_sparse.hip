@@ -83,12 +83,7 @@ __global__ __launch_bounds__(64 * WK) void sp_gemm_kslice(
   }
   red[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0) {
-    float4v sum = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < WK; ++w) sum += red[w][lane];
-    store_y_block(Y, sum, r, M, N, nb * 16, g);
-  }
+  if (wave == 0) store_y_block(Y, reduce_waves<WK>(red, lane), r, M, N, nb * 16, g);
 }
 
 // ---------------------------------------------------------------------------
