@@ -494,9 +494,17 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 // per m-group).  As fp6_gemm_stream, a wave streams A row blocks over a K
 // range through a register ring of D packed tiles, but the NW waves of a
 // workgroup (same K range, different row groups) share X: each X tile
-// (16 rows x 256 k) is loaded once per workgroup into a 3-slot LDS ring
+// (16 rows x 256 k) is loaded once per workgroup into a 2-slot LDS ring
 // (rows XOR-swizzled in 16-byte units, so the B-fragment reads are free of
 // bank conflicts), one barrier per tile.  This cuts X's L2->CU traffic by NW.
+//
+// Vector-memory loads complete in issue order (one vmcnt counter), so a load
+// that is needed soon must not be issued after loads that are needed late:
+// waiting for it would also wait for them.  X therefore travels at the same
+// prefetch distance D as the weights, through a register ring of D stages
+// (X(t+D) is issued just before W(t+D), at the top of iteration t, and is
+// written to LDS in iteration t+D-1).  Every wait then covers D-1 tiles of
+// work instead of one.
 // ---------------------------------------------------------------------------
 template <int F, int A, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
@@ -504,10 +512,11 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
     unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
     int64_t mg_base) {
+  static_assert(D % 2 == 0, "the LDS slot of a tile is its parity");
   constexpr int kThreads = 64 * NW;
   constexpr int kChunks = 16 * 32;                      // 16-byte units per X tile
   constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) half8v xs[3][kChunks];
+  __shared__ __attribute__((aligned(16))) half8v xs[2][kChunks];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
@@ -547,17 +556,19 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     xsrc[i] = X + m * K + 8 * c;
     xdst[i] = rr * 32 + (c ^ rr);
   }
-  half8v xstage[kPerThread];
   const int64_t klast = kt1 > kt0 ? kt1 - 1 : kt0;
   auto clampk = [&](int64_t t) { return t < klast ? t : klast; };
-  auto gload_x = [&](int64_t kt) {
+  struct XRegs {
+    half8v v[kPerThread];
+  };
+  auto gload_x = [&](XRegs& xr, int64_t kt) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i)
-      xstage[i] = *reinterpret_cast<const half8v*>(xsrc[i] + kt * 256);
+      xr.v[i] = *reinterpret_cast<const half8v*>(xsrc[i] + kt * 256);
   };
-  auto swrite_x = [&](int slot) {
+  auto swrite_x = [&](const XRegs& xr, int slot) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) xs[slot][xdst[i]] = xstage[i];
+    for (int i = 0; i < kPerThread; ++i) xs[slot][xdst[i]] = xr.v[i];
   };
 
   float4v acc[A];
@@ -583,43 +594,40 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 #undef FP6_XL_STEP
   };
 
-  // Tile i of the split (kt = kt0 + i) uses slot i % 3.  Iteration i writes
-  // X(kt+1) (loaded during iteration i-1) into slot (i+1) % 3, whose last
-  // reader was iteration i-2, loads X(kt+2), consumes the ring stage of tile
-  // kt and refills it, then meets the barrier.  Branch-free steady state
-  // with clamped prefetch indices; the last (< D) tiles run in a tail.
+  // Tile i of the split (kt = kt0 + i) sits in ring[i % D] and xr[i % D] and
+  // is read from LDS slot i % 2.  Iteration i writes X(i+1) into slot
+  // (i+1) % 2, whose last reader was iteration i-1 (one barrier between),
+  // issues X(i+D) into the freed xr[i % D], consumes ring[i % D], refills it
+  // with W(i+D), then meets the barrier.  Branch-free steady state with
+  // clamped prefetch indices; the last (< D) tiles run in a tail.
   WStage<F, A> ring[D];
+  XRegs xr[D];
   if (kt0 < kt1) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_w(ring[d], clampk(kt0 + d));
-    gload_x(kt0);
-    swrite_x(0);
-    gload_x(clampk(kt0 + 1));
+    for (int d = 0; d < D; ++d) {
+      gload_x(xr[d], clampk(kt0 + d));
+      load_w(ring[d], clampk(kt0 + d));
+    }
+    swrite_x(xr[0], 0);
     __syncthreads();
     int64_t kt = kt0;
-    int slot = 0;
     for (; kt + D <= kt1; kt += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int64_t t = kt + d;
-        const int nslot = slot == 2 ? 0 : slot + 1;
-        swrite_x(nslot);
-        gload_x(clampk(t + 2));
-        mac(ring[d], slot);
+        swrite_x(xr[(d + 1) % D], (d + 1) & 1);
+        gload_x(xr[d], clampk(t + D));
+        mac(ring[d], d & 1);
         load_w(ring[d], clampk(t + D));
         __syncthreads();
-        slot = nslot;
       }
     }
 #pragma unroll
     for (int d = 0; d + 1 < D; ++d) {
       if (kt + d < kt1) {
-        const int nslot = slot == 2 ? 0 : slot + 1;
-        swrite_x(nslot);
-        gload_x(clampk(kt + d + 2));
-        mac(ring[d], slot);
+        swrite_x(xr[(d + 1) % D], (d + 1) & 1);
+        mac(ring[d], d & 1);
         __syncthreads();
-        slot = nslot;
       }
     }
   }
