@@ -855,6 +855,19 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
 //   * each wave waits for its own direct loads, then one barrier.
 // ---------------------------------------------------------------------------
 
+// Workgroup index -> logical tile index, XCD-aware.  Workgroups are handed
+// to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), each XCD with
+// its own L2.  This gives XCD x the contiguous logical range
+// [x*q + min(x, r), ...) (q = G/8, r = G%8, the first r XCDs one more), so
+// workgroups that share operands (the K-splits of a row tile, the row tiles
+// of one column group and their X slice) meet in the same L2.  A bijection
+// on [0, G).
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t b, int64_t G) {
+  constexpr int kXcds = 8;
+  const int64_t x = b % kXcds, j = b / kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + (x < r ? x : r) + j;
+}
+
 template <int F, int TA>
 struct WHalf {           // packed words of one half-tile for TA row blocks
   typename Fmt<F>::Half h[TA];
@@ -885,7 +898,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
-  int64_t bidx = blockIdx.x;
+  int64_t bidx = xcd_logical_block(blockIdx.x, gridDim.x);
   const int split = static_cast<int>(bidx % splits);
   bidx /= splits;
   const int64_t nt = bidx % ntiles;
@@ -1056,7 +1069,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
-  int64_t bidx = blockIdx.x;
+  int64_t bidx = xcd_logical_block(blockIdx.x, gridDim.x);
   const int split = static_cast<int>(bidx % splits);
   bidx /= splits;
   const int64_t nt = bidx % ntiles;
