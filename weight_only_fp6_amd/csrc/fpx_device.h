@@ -274,48 +274,55 @@ __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restric
 
 // ---------------------------------------------------------------------------
 // Split-K fix-up.  Every split of a work unit stores its fp32 accumulators
-// with device-scope (sc1) stores, waits for them to complete, then bumps the
-// unit's counter with a device-scope atomic.  The split that sees count
-// splits-1 is the last one: it reads the other partials with device-scope
-// loads, sums all splits in split order (deterministic), and resets the
-// counter for the next call.  Device-scope accesses keep the partials
-// coherent across the XCDs' L2 caches without any whole-cache write-back or
-// invalidate (which agent-scope fences would issue in every wave).
-// Partial layout: [unit][split][acc i][component c][lane] floats, so each
-// store instruction writes 256 contiguous bytes.
+// with device-scope (sc1) 16-byte stores, waits for them to complete, then
+// bumps the unit's counter with a device-scope atomic.  The split that sees
+// count splits-1 is the last one: it reads the other partials with
+// device-scope 16-byte loads, sums all splits in split order
+// (deterministic), and resets the counter for the next call.  Device-scope
+// accesses keep the partials coherent across the XCDs' L2 caches without
+// any whole-cache write-back or invalidate (which agent-scope fences would
+// issue in every wave).  The accesses go through a buffer resource over the
+// unit's partials (sc1 is a cache-policy bit of buffer instructions), one
+// dwordx4 per lane per accumulator: a quarter of the instructions of
+// per-component stores.  Partial layout: [unit][split][acc i][lane] float4,
+// so each instruction moves 1 KB contiguous.
 // ---------------------------------------------------------------------------
 template <int NACC>
 __device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __restrict__ unit_part,
                                              unsigned* __restrict__ counter, int split, int splits,
                                              int lane) {
-  float* mine = unit_part + static_cast<int64_t>(split) * NACC * 256 + lane;
+  constexpr int kSc1 = 16;                 // cache policy: device scope
+  constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer, gfx9 family
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(unit_part, static_cast<short>(0), splits * NACC * 1024, kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < NACC; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      __hip_atomic_store(mine + (i * 4 + c) * 64, acc[i][c], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i]), rsrc,
+                                           ((split * NACC + i) * 64 + lane) * 16, 0, kSc1);
   __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
   unsigned prev = 0;
   if (lane == 0)
     prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != static_cast<unsigned>(splits - 1)) return false;
+  float4v sum[NACC];
 #pragma unroll
-  for (int i = 0; i < NACC; ++i) {
-    float4v sum = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-      if (s == split) {
-        sum += acc[i];
-      } else {
-        const float* src = unit_part + (static_cast<int64_t>(s) * NACC + i) * 256 + lane;
+  for (int i = 0; i < NACC; ++i) sum[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    if (s == split) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sum[c] += __hip_atomic_load(src + c * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      for (int i = 0; i < NACC; ++i) sum[i] += acc[i];
+    } else {
+      u32x4 v[NACC];
+#pragma unroll
+      for (int i = 0; i < NACC; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((s * NACC + i) * 64 + lane) * 16, 0, kSc1);
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) sum[i] += __builtin_bit_cast(float4v, v[i]);
     }
-    acc[i] = sum;
   }
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) acc[i] = sum[i];
   if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
