@@ -180,9 +180,14 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
 #undef FP6S_XL_STEP
   };
 
-  // Tile i of the split uses slot i % 3 (see the dense streaming kernel with
-  // X in LDS): branch-free steady state with clamped prefetch indices, the
-  // last (< D) tiles in a tail.
+  // Tile i of the split uses slot i % 3.  Iteration i writes X(i+1) (loaded
+  // during iteration i-1) into slot (i+1) % 3, whose last reader was
+  // iteration i-2, loads X(i+2), consumes the ring stage of tile i and
+  // refills it, then meets the barrier.  X stays one tile ahead here (unlike
+  // the dense kernel): X at the ring's distance needs more registers than
+  // two waves per SIMD allow with 16 KB sparse X tiles, and measured slower.
+  // Branch-free steady state with clamped prefetch indices, the last (< D)
+  // tiles in a tail.
   Stage ring[D];
   if (kt0 < kt1) {
 #pragma unroll
