@@ -197,8 +197,10 @@ int fp6_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* sp
 int fp6_dequant(const void* packed_W, const void* scales, void* W16,
                 int64_t N, int64_t K, void* stream);
 
-/* Frees every workspace the library holds (synchronises the device first).
- * Returns FP6_OK or FP6_E_HIP. */
+/* Frees every split-K workspace the library holds, synchronising each device
+ * that holds one first (work still in flight may use it).  Returns FP6_OK, or
+ * FP6_E_HIP if a device could not be synchronised or a buffer freed (the
+ * buffers not freed are kept and a later call retries them). */
 int fp6_release(void);
 
 #ifdef __cplusplus

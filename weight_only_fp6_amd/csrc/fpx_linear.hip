@@ -405,17 +405,22 @@ int fpx_dequant(int format, const void* packed_W, const void* scales, void* W16,
 int fp6_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (g_ws.empty()) return FP6_OK;
-  if (hipDeviceSynchronize() != hipSuccess) return FP6_E_HIP;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FP6_E_HIP;
   int st = FP6_OK;
+  // Each workspace's device is synchronised before its buffers are freed
+  // (work in flight on any stream of that device may still use them).
   for (auto& kv : g_ws) {
-    int cur = 0;
-    (void)hipGetDevice(&cur);
-    (void)hipSetDevice(kv.first.first);
+    if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      st = FP6_E_HIP;
+      continue;
+    }
     if (kv.second.part && hipFree(kv.second.part) != hipSuccess) st = FP6_E_HIP;
     if (kv.second.counters && hipFree(kv.second.counters) != hipSuccess) st = FP6_E_HIP;
-    (void)hipSetDevice(cur);
+    kv.second = Workspace{};
   }
-  g_ws.clear();
+  (void)hipSetDevice(cur);
+  if (st == FP6_OK) g_ws.clear();
   return st;
 }
 
