@@ -275,7 +275,7 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_tiled(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 9;
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
-  int64_t bidx = blockIdx.x;
+  int64_t bidx = xcd_logical_block(blockIdx.x, gridDim.x);
   const int split = static_cast<int>(bidx % splits);
   bidx /= splits;
   const int64_t nt = bidx % ntiles;
