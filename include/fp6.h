@@ -166,6 +166,7 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *    16  as 14 with 8 waves per workgroup
  *    17  tiled, 256 rows x 64 columns per 8-wave workgroup, whole 256-k tiles
  *        per pipeline stage (one barrier per tile)
+ *    18  as 15 with 8 waves per workgroup (each X tile shared by 8 waves)
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
  *          (1..K/256; must be 0 or 1 for variant 9).
@@ -179,7 +180,7 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
 
 /*
  * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
- * for (M, N, K) on the current device: *variant (1..17, see fp6_linear_plan)
+ * for (M, N, K) on the current device: *variant (1..18, see fp6_linear_plan)
  * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
  * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
  * >= 1 here), FP6_E_HIP.

@@ -28,7 +28,7 @@ import weight_only_fp6_amd as fp6  # noqa: E402
 
 DEV = torch.device("cuda:0")
 FMTS = ("e2m3", "e2m2", "e2m1")
-ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17)
+ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18)
 SMALL_M_VARIANTS = (9, 12, 13)
 
 
@@ -115,7 +115,7 @@ def test_linear_forced_splits_and_k_coverage(fmt):
     shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
     p = _prep(shp.name, None, fmt)
     X, packed, s = p.to_device()
-    for variant, splits in [(1, 7), (3, 43), (5, 3), (10, 4), (11, 2), (14, 8), (15, 5), (16, 2), (17, 3)]:
+    for variant, splits in [(1, 7), (3, 43), (5, 3), (10, 4), (11, 2), (14, 8), (15, 5), (16, 2), (17, 3), (18, 1), (18, 4)]:
         Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=variant, splits=splits, fmt=fmt)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(fmt, variant, splits))
@@ -139,7 +139,7 @@ def test_linear_one_hot_reproduces_wdq_exactly(fmt):
     _, packed, s = p.to_device()
     want = p.wdq_ref[:, ks].T.astype(np.float64)
     for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 3), (5, 3), (6, 1), (8, 1), (9, 0), (12, 0),
-                            (13, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3)]:
+                            (13, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits, fmt=fmt)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (fmt, variant, splits)

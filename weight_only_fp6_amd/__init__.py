@@ -212,7 +212,7 @@ KERNEL_NAMES = {
     7: "fp6_gemm_stream<1,1,8>", 8: "fp6_gemm_stream<2,1,6>", 9: "fp6_gemm_ksplit<8 waves>",
     10: "fp6_gemm_tiled<8,2,8>", 11: "fp6_gemm_tiled<4,2,8>", 12: "fp6_gemm_ksplit<16 waves>",
     13: "fp6_gemm_kslice", 14: "fp6_gemm_xlds<2,4,4>", 15: "fp6_gemm_xlds<1,4,4>",
-    16: "fp6_gemm_xlds<2,4,8>", 17: "fp6_gemm_tiledw<4,2,8>",
+    16: "fp6_gemm_xlds<2,4,8>", 17: "fp6_gemm_tiledw<4,2,8>", 18: "fp6_gemm_xlds<1,4,8>",
 }
 
 

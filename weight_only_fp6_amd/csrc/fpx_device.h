@@ -1402,6 +1402,7 @@ int launch_variant(const fpx::LaunchCtx& c) {
     case 15: return launch_xlds<F, 1, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 16: return launch_xlds<F, 2, 4, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 17: return launch_tiledw<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 18: return launch_xlds<F, 1, 4, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     default: return FP6_E_VALUE;
   }
 }

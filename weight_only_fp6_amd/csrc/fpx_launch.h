@@ -38,6 +38,7 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kXlds, 1, 1, 4},    // 15: streaming + X in LDS, 1 row block/wave, ring 4, 4 waves
     {Kind::kXlds, 2, 1, 8},    // 16: streaming + X in LDS, 2 row blocks/wave, ring 4, 8 waves
     {Kind::kTiled, 2, 4, 8},   // 17: tiled, 256 rows x 64 columns, 8 waves, whole-tile stages
+    {Kind::kXlds, 1, 1, 4},    // 18: streaming + X in LDS, 1 row block/wave, ring 4, 8 waves
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kKsMaxTiles = 32;      // k-split kernels: K <= 8192

@@ -129,14 +129,16 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     // Measured on MI355X: up to K = 4096 the k-slice kernel (at most one row
     // block per CU) or the k-split kernels (8 waves up to K = 2048, else 16)
     // are fastest; for longer K the streaming kernel with X shared through
-    // LDS (1 row block per wave, 4 waves) is.  Above M = 16 the tiled
-    // kernels: 64 columns with whole-tile stages up to M = 64, else 128
-    // columns with half-tile stages.
+    // LDS (1 row block per wave): 8 waves per workgroup once there are at
+    // least 7 row blocks per CU (each X tile shared by twice the waves, and
+    // one workgroup per CU instead of a 1-or-2 mix: Llama-70B MLP 38 -> 35
+    // us), else 4.  Above M = 16 the tiled kernels: 64 columns with
+    // whole-tile stages up to M = 64, else 128 columns with half-tile stages.
     const bool one_rb_per_cu = (N >> 4) <= cus;
     if (M <= 16 && ktiles <= 16 && one_rb_per_cu) p.variant = 13;
     else if (M <= 16 && ktiles <= 8) p.variant = 9;
     else if (M <= 16 && ktiles <= 16) p.variant = 12;
-    else if (M <= 16) p.variant = 15;
+    else if (M <= 16) p.variant = (N >> 4) >= 7 * static_cast<int64_t>(cus) ? 18 : 15;
     else if (M <= 64) p.variant = 17;
     else p.variant = 10;
   } else {
