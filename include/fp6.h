@@ -169,10 +169,10 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *    18  as 15 with 8 waves per workgroup (each X tile shared by 8 waves)
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
- *          (1..K/256; must be 0 or 1 for variant 9).
+ *          (1..K/256; must be 0 or 1 for variants 9, 12 and 13).
  * The result equals fp6_linear's up to fp32 summation order.
  * Errors: as fp6_linear, plus FP6_E_VALUE for an unknown variant, a split
- * count out of range, or a shape variant 9 does not cover.
+ * count out of range, or a shape that variant 9, 12 or 13 does not cover.
  */
 int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y,
                     int64_t M, int64_t N, int64_t K, int variant, int splits,
