@@ -238,3 +238,21 @@ def test_linear_on_side_stream_matches_default_stream():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     _assert_tol(b, p.y_ref)
+
+
+def test_release_then_reuse_and_grow_workspace():
+    # The split-K workspace is allocated on first need, grown on demand and
+    # freed by release(); a later split call must allocate it again and give
+    # the same bits.
+    p = Prepared(16, 256, 4096, seed_w=77, seed_x=78)
+    X, packed, s = p.to_device()
+    a = fp6.linear_plan(X, packed, s, p.N, p.K, variant=15, splits=2).clone()
+    fp6.release()
+    b = fp6.linear_plan(X, packed, s, p.N, p.K, variant=15, splits=2).clone()
+    c = fp6.linear_plan(X, packed, s, p.N, p.K, variant=10, splits=16).clone()  # larger workspace
+    fp6.release()
+    fp6.release()  # nothing left to free
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    _assert_tol(a, p.y_ref, what="split 2")
+    _assert_tol(c, p.y_ref, what="split 16")
