@@ -256,3 +256,46 @@ def test_release_then_reuse_and_grow_workspace():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     _assert_tol(a, p.y_ref, what="split 2")
     _assert_tol(c, p.y_ref, what="split 16")
+
+
+def _adversarial_weights(N, K, seed):
+    """Rows that exercise the corners of quantisation and de-quantisation:
+    a zero row (scale 0), a lone outlier over values that quantise to zero or
+    subnormals, a row of negative values below half the smallest subnormal
+    (codes -0) plus one outlier, saturating +-max, exact ties between e3m2
+    magnitudes (scale 2^-4 exactly), a large scale (|s| close to 16), then
+    ordinary N(0, 0.02) rows."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[0] = 0.0
+    W[1] = 1e-6
+    W[1, 5] = 1.0
+    W[2] = -1e-9
+    W[2, 7] = 0.5
+    W[3] = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    mags = np.array(oracle.E3M2_VALUES[:32], dtype=np.float64)
+    mids = (mags[:-1] + mags[1:]) / 2                      # ties between neighbours
+    row = np.resize(np.concatenate([mids, -mids]), K) * 2.0 ** -4
+    row[0] = 28 * 2.0 ** -4                                 # max |W| -> scale exactly 2^-4
+    W[4] = row.astype(np.float32)
+    W[5] = (rng.standard_normal(K) * 100).astype(np.float32)
+    W[5, 3] = 400.0                                         # scale 400/28 ~ 14.3
+    return W
+
+
+@pytest.mark.parametrize("M", [3, 17])
+def test_linear_adversarial_rows(M):
+    N, K = 96, 2816
+    W = _adversarial_weights(N, K, seed=123 + M)
+    X = synth.activations(M, K, 321 + M)
+    X[:, ::7] = 0
+    p = Prepared(M, N, K, seed_w=0, seed_x=0, W=W, X=X)
+    assert np.array_equal(p.codes, p.ocodes) and np.array_equal(p.scales.view(np.uint16), p.oscales.view(np.uint16))
+    Xd, packed, s = p.to_device()
+    assert np.array_equal(_bits16(fp6.dequant(packed, s, N, K)), p.wdq_ref.view(np.uint16))
+    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3)]:
+        Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(M, variant, splits))
+        # the zero row gives exactly zero outputs
+        assert not Y[:, 0].cpu().numpy().astype(np.float64).any(), (M, variant, splits)
