@@ -156,3 +156,48 @@ def test_fpx_format0_matches_fp6_bitwise():
     torch.cuda.synchronize()
     assert st == 0
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _adversarial_weights(N, K, seed, fmt):
+    """As the e3m2 corner rows, per format: a zero row, a lone outlier over
+    values that quantise to zero, negative values below half the smallest
+    subnormal (codes -0) with one outlier, saturating +-max, exact ties
+    between neighbouring magnitudes (power-of-two scale), a scale near the
+    format's limit, then ordinary N(0, 0.02) rows."""
+    f = oracle.FORMATS[fmt]
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[0] = 0.0
+    W[1] = 1e-6
+    W[1, 5] = 1.0
+    W[2] = -1e-9
+    W[2, 7] = 0.5
+    W[3] = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    mags = np.array(f.mags, dtype=np.float64)
+    mids = (mags[:-1] + mags[1:]) / 2
+    row = np.resize(np.concatenate([mids, -mids]), K) * 2.0 ** -4
+    row[0] = f.max * 2.0 ** -4                              # scale exactly 2^-4
+    W[4] = row.astype(np.float32)
+    limit = min(f.scale_limit, 16.0)
+    W[5] = (rng.standard_normal(K) * 0.1).astype(np.float32)
+    W[5, 3] = 0.9 * limit * f.max                           # scale 0.9 of the limit
+    return W
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [3, 17])
+def test_linear_adversarial_rows(fmt, M):
+    N, K = 96, 2816
+    W = _adversarial_weights(N, K, 223 + M, fmt)
+    X = synth.activations(M, K, 421 + M)
+    X[:, ::5] = 0
+    p = Prepared(M, N, K, seed_w=0, seed_x=0, W=W, X=X, fmt=fmt)
+    assert np.array_equal(p.codes, p.ocodes)
+    assert np.array_equal(p.scales.view(np.uint16), p.oscales.view(np.uint16))
+    Xd, packed, s = p.to_device()
+    assert np.array_equal(_bits16(fp6.dequant(packed, s, N, K, fmt=fmt)), p.wdq_ref.view(np.uint16))
+    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3)]:
+        Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits, fmt=fmt)
+        torch.cuda.synchronize()
+        _assert_tol(Y, p.y_ref, what=(fmt, M, variant, splits))
+        assert not Y[:, 0].cpu().numpy().astype(np.float64).any(), (fmt, M, variant, splits)

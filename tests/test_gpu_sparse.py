@@ -139,3 +139,41 @@ def test_linear_is_deterministic_and_m_zero():
     Y = fp6.sparse_linear(torch.zeros((0, p.K), dtype=torch.float16, device=DEV), packed, s, p.N, p.K)
     torch.cuda.synchronize()
     assert Y.shape == (0, p.N)
+
+
+@pytest.mark.parametrize("M", [3, 17])
+def test_sparse_linear_adversarial_rows(M):
+    # Corner rows for pruning and quantisation: a zero row, a lone outlier,
+    # groups with equal magnitudes (ties broken by the lower index), -0
+    # codes, saturation and a scale near 16, over ordinary N(0, 0.02) rows.
+    N, K = 96, 2560
+    rng = np.random.default_rng(500 + M)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[0] = 0.0
+    W[1] = 1e-6
+    W[1, 5] = 1.0
+    W[2] = -1e-9
+    W[2, 7] = 0.5
+    W[3] = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    W[4] = np.resize(np.array([0.25, -0.25, 0.25, -0.25, 0.5, 0.5, 0.5, 0.5], np.float32), K)  # all ties
+    W[5] = (rng.standard_normal(K) * 10).astype(np.float32)
+    W[5, 3] = 400.0
+    X = synth.activations(M, K, 600 + M)
+    X[:, ::3] = 0
+    c, p, s = fp6.prune_quantize(W)
+    oc, op, osc = sparse24.quantize_sparse(W)
+    assert np.array_equal(c, oc) and np.array_equal(p, op)
+    assert np.array_equal(s.view(np.uint16), osc.view(np.uint16))
+    wdq = sparse24.dequant_ref(oc, op, osc, K)
+    y_ref = oracle.gemm_ref(X, wdq)
+    packed = torch.from_numpy(fp6.sparse_prepack(c, p, s, K)).to(DEV)
+    sd = torch.from_numpy(s.copy()).to(DEV)
+    Xd = torch.from_numpy(X).to(DEV)
+    out = fp6.sparse_dequant(packed, sd, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), wdq.view(np.uint16))
+    for variant, splits in [(0, 0), (2, 2), (3, 1), (4, 2), (5, 1)] + ([(KSLICE, 0)] if M <= 16 else []):
+        Y = fp6.sparse_linear_plan(Xd, packed, sd, N, K, variant=variant, splits=splits)
+        torch.cuda.synchronize()
+        _assert_tol(Y, y_ref, what=(M, variant, splits))
+        assert not Y[:, 0].cpu().numpy().astype(np.float64).any(), (M, variant, splits)
