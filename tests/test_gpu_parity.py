@@ -299,3 +299,17 @@ def test_linear_adversarial_rows(M):
         _assert_tol(Y, p.y_ref, what=(M, variant, splits))
         # the zero row gives exactly zero outputs
         assert not Y[:, 0].cpu().numpy().astype(np.float64).any(), (M, variant, splits)
+
+
+@pytest.mark.parametrize("M, N, K", [(1, 1 << 20, 256), (40, 1 << 20, 256), (2, 16, 1 << 22)])
+def test_linear_large_n_or_k(M, N, K):
+    # Far beyond the workloads in one dimension: a million output rows (at
+    # M=1 the persistent k-split kernel walks 256 row blocks per workgroup; at
+    # M=40 the whole-tile tiled kernel launches 4096 workgroups), or K = 4M
+    # with a single row block (the plan splits K 64 ways through the fix-up).
+    # Sampled output columns.
+    p = Prepared(M, N, K, seed_w=N + K + 1, seed_x=M + 2, sample=256)
+    X, packed, s = p.to_device()
+    Y = fp6.linear(X, packed, s, N, K)
+    torch.cuda.synchronize()
+    _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(M, N, K))
