@@ -757,7 +757,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 // workgroup per row block: meant for N/16 <= CUs, where X is used once per CU
 // anyway.
 // ---------------------------------------------------------------------------
-template <int F, int KTW, int WK>
+template <int F, int KTW, int WK, bool M1 = false>
 __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
@@ -789,6 +789,15 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     const int64_t nb = blockIdx.x;
     if (nb >= nblocks) return;  // uniform for the workgroup
     const u32x4* base = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    // M = 1 (KTW = 1): the 16 columns of the B operand all repeat X's single
+    // row, so each lane loads just 8 of the tile's 256 values (one 8-byte
+    // load, issued before the weights so that waiting for it does not wait
+    // for them) into the wave's own LDS slice and reads its fragments back
+    // from there (one address per lane group: an LDS broadcast).  A wave only
+    // reads its own slice, and LDS operations of a wave complete in order,
+    // so no barrier is needed.
+    [[maybe_unused]] half4v x1 = {};
+    if constexpr (M1) x1 = *reinterpret_cast<const half4v*>(X + tile_of(0) * 256 + 4 * lane);
     WStage<F, 1> st[KTW];
 #pragma unroll
     for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * Fmt<F>::kTileQuads, lane);
@@ -797,10 +806,22 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     if constexpr (KTW == 1) {
       // One tile per wave: all of its X fragments are loaded at once.
       half8v xf[8];
+      if constexpr (M1) {
+        static_assert(KTW == 1, "the M = 1 staging covers one tile per wave");
+        __shared__ half8v xw[WK][32];
+        reinterpret_cast<half4v*>(&xw[wave][0])[lane] = x1;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        xf[j] = *reinterpret_cast<const half8v*>(xrow + tile_of(0) * 256 + 32 * j);
-      if (ktw > 0) {
+        for (int j = 0; j < 8; ++j) xf[j] = xw[wave][4 * j + g];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          xf[j] = *reinterpret_cast<const half8v*>(xrow + tile_of(0) * 256 + 32 * j);
+      }
+      // With M1 the MFMAs run unconditionally and an empty k-range (ktw = 0,
+      // tile 0 loaded as a stand-in) is zeroed afterwards: behind a branch
+      // the compiler would sink the weight loads into it, after the X
+      // staging's wait.
+      if (M1 || ktw > 0) {
         // Two accumulators halve the MFMA dependency chain.
         float4v acc1 = {0.f, 0.f, 0.f, 0.f};
 #define FP6_KX1(J, A)                                                                       \
@@ -809,6 +830,7 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
         FP6_KX1(4, acc) FP6_KX1(5, acc1) FP6_KX1(6, acc) FP6_KX1(7, acc1)
 #undef FP6_KX1
         acc += acc1;
+        if (M1 && ktw == 0) acc = float4v{0.f, 0.f, 0.f, 0.f};
       }
     } else {
     half8v xr[3][4];
@@ -1257,8 +1279,11 @@ int launch_kslice_t(const void* X, const void* W, const void* S, void* Y, int64_
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
   void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_kslice<F, KTW, WK>), grid, dim3(64 * WK),
-                         args, 0, stream) == hipSuccess
+  const void* kern = reinterpret_cast<const void*>(&fp6_gemm_kslice<F, KTW, WK>);
+  if constexpr (KTW == 1) {
+    if (M == 1) kern = reinterpret_cast<const void*>(&fp6_gemm_kslice<F, 1, WK, true>);
+  }
+  return hipLaunchKernel(kern, grid, dim3(64 * WK), args, 0, stream) == hipSuccess
              ? FP6_OK
              : FP6_E_HIP;
 }
