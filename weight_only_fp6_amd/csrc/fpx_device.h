@@ -234,13 +234,16 @@ struct Fmt<kE2M1> {
 };
 
 template <int F>
-__device__ __forceinline__ half2v row_scale2(const _Float16* scales, int64_t n) {
-  _Float16 s = scales[n];
+__device__ __forceinline__ half2v scale2_of(_Float16 s) {
   if constexpr (Fmt<F>::kScaleFactor != 1.0f) s = s * static_cast<_Float16>(Fmt<F>::kScaleFactor);
   half2v s2;
   s2[0] = s;
   s2[1] = s;
   return s2;
+}
+template <int F>
+__device__ __forceinline__ half2v row_scale2(const _Float16* scales, int64_t n) {
+  return scale2_of<F>(scales[n]);
 }
 
 // ---------------------------------------------------------------------------
@@ -658,19 +661,22 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 // K <= kKsWaves*KTW*256).  One workgroup of kKsWaves (8 or 16) waves per CU.
 // Wave w owns the k-tiles [w*KT/W, (w+1)*KT/W) (W = kKsWaves) for the whole
 // kernel, so its X fragments (16 columns x
-// at most KTW k-tiles) are loaded once into registers.  The workgroup walks
+// at most KTW k-tiles) are staged once, through LDS, into registers.  The workgroup walks
 // the row blocks nb = blockIdx.x, +gridDim.x, ...; for each, every wave
 // multiplies its k-slice (packed tiles prefetched one row block ahead) and
 // the partial 16x16 tiles are summed through LDS in wave order
 // (deterministic) by wave 0, which stores fp16 Y.  No global workspace, no
 // X re-reads, all k-slices of a row block stream concurrently.
 // ---------------------------------------------------------------------------
-template <int F, int KTW, int kKsWaves>
+template <int F, int KTW, int kKsWaves, bool M1 = false>
 __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
     int64_t K) {
-  __shared__ float4v red[2][kKsWaves][64];
+  // Per wave, one 8 KB LDS region: first the X staging area of its k-tiles,
+  // then (after the wave has read its fragments) its two partial-tile
+  // buffers of 1 KB each.
+  __shared__ __attribute__((aligned(16))) half8v xw[kKsWaves][512];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
@@ -682,25 +688,71 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     if (ktw == 0) return 0;
     return kw0 + (t < ktw ? t : ktw - 1);
   };
+  auto red_at = [&](int buf, int w) { return reinterpret_cast<float4v*>(&xw[w][64 * buf]); };
 
-  // X fragments for this wave's k-slice; rows m >= M read row M-1 (their
-  // accumulator columns are never stored).
-  const int64_t m = r < M ? r : M - 1;
+  // X of this wave's k-slice, loaded coalesced: instruction i covers rows
+  // 2i, 2i+1 (512 B each), lane -> 16-byte unit xc of row xr[i].  Rows
+  // beyond M repeat row M-1 (their accumulator columns are never stored).
+  // Fragment loads straight from global memory touch 16 rows per
+  // instruction, which costs the L1/L2 path several times the bytes.  With
+  // M = 1 all 16 B-operand columns are X's one row: one 8-byte load per lane
+  // covers a tile.
+  const int xc = lane & 31;
+  constexpr int kXLoads = M1 ? 1 : 8;
+  half8v xg[KTW][kXLoads];
+  [[maybe_unused]] half4v xg1[KTW];
+#pragma unroll
+  for (int t = 0; t < KTW; ++t) {
+    if constexpr (M1) {
+      xg1[t] = *reinterpret_cast<const half4v*>(X + tile_of(t) * 256 + 4 * lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kXLoads; ++i) {
+        const int rr = 2 * i + (lane >> 5);
+        const int64_t m = rr < M ? rr : M - 1;
+        xg[t][i] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 256 + 8 * xc);
+      }
+    }
+  }
+  // Unit (rr, c) is stored at column c ^ rr of row rr, so the 16 lanes of a
+  // fragment read (16 rows, same k) hit distinct banks; with M = 1 the row
+  // is stored once and every fragment read is a broadcast.  Only this wave
+  // touches its region, and a wave's LDS operations complete in order, so
+  // a tile's fragments are read before the next tile (or a partial tile)
+  // overwrites them, with no barrier.
   half8v xf[KTW][8];
+  auto stage_x = [&]() {
 #pragma unroll
-  for (int t = 0; t < KTW; ++t)
+    for (int t = 0; t < KTW; ++t) {
+      if constexpr (M1) {
+        reinterpret_cast<half4v*>(&xw[wave][0])[lane] = xg1[t];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      xf[t][j] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 256 + 32 * j + 8 * g);
+        for (int j = 0; j < 8; ++j) xf[t][j] = xw[wave][4 * j + g];
+      } else {
+#pragma unroll
+        for (int i = 0; i < kXLoads; ++i) {
+          const int rr = 2 * i + (lane >> 5);
+          xw[wave][rr * 32 + (xc ^ rr)] = xg[t][i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xf[t][j] = xw[wave][r * 32 + ((4 * j + g) ^ r)];
+      }
+    }
+  };
 
+  // A row block's tiles and its row scale travel together: vector loads
+  // complete in issue order, so a scale requested after the next row
+  // block's tiles would make this one wait for them.
   WStage<F, 1> wst[2][KTW];
-  auto load_rb = [&](WStage<F, 1> (&st)[KTW], int64_t nb) {
+  _Float16 wsc[2];
+  auto load_rb = [&](WStage<F, 1> (&st)[KTW], _Float16& sc, int64_t nb) {
     const u32x4* base = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
 #pragma unroll
     for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * Fmt<F>::kTileQuads, lane);
+    sc = scales[nb * 16 + r];
   };
-  auto rb_mac = [&](const WStage<F, 1> (&st)[KTW], int64_t nb) {
-    const half2v s2 = row_scale2<F>(scales, nb * 16 + r);
+  auto rb_mac = [&](const WStage<F, 1> (&st)[KTW], _Float16 sc) {
+    const half2v s2 = scale2_of<F>(sc);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < KTW; ++t) {
@@ -716,14 +768,14 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     return acc;
   };
   auto reduce_store = [&](const float4v& acc, int buf, int64_t nb) {
-    red[buf][wave][lane] = acc;
+    red_at(buf, wave)[lane] = acc;
     __syncthreads();
     // A plain loop: this kernel keeps the next row block's tiles and its X
     // slice in registers, so holding several partial tiles at once spills.
     if (wave == 0) {
-      float4v sum = red[buf][0][lane];
+      float4v sum = red_at(buf, 0)[lane];
 #pragma unroll
-      for (int w = 1; w < kKsWaves; ++w) sum += red[buf][w][lane];
+      for (int w = 1; w < kKsWaves; ++w) sum += red_at(buf, w)[lane];
       store_y_block(Y, sum, r, M, N, nb * 16, g);
     }
   };
@@ -731,20 +783,25 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   const int64_t stride = gridDim.x;
   int64_t nb = blockIdx.x;
   if (nb >= nblocks) return;  // uniform for the workgroup
-  load_rb(wst[0], nb);
+  // The first two row blocks' tiles are requested before X is staged (whose
+  // LDS writes wait for the X loads, issued first).
+  int64_t nb1 = nb + stride;
+  load_rb(wst[0], wsc[0], nb);
+  load_rb(wst[1], wsc[1], nb1 < nblocks ? nb1 : nb);
+  stage_x();
   // Two row blocks per iteration so the register double buffer is static.
   // The partial-tile buffers alternate too: a buffer is rewritten only after
   // the next barrier, by which time wave 0 has finished reading it.
   while (true) {
-    int64_t nb1 = nb + stride;
-    load_rb(wst[1], nb1 < nblocks ? nb1 : nb);
-    reduce_store(rb_mac(wst[0], nb), 0, nb);
+    reduce_store(rb_mac(wst[0], wsc[0]), 0, nb);
     if (nb1 >= nblocks) break;
-    int64_t nb2 = nb1 + stride;
-    load_rb(wst[0], nb2 < nblocks ? nb2 : nb1);
-    reduce_store(rb_mac(wst[1], nb1), 1, nb1);
+    const int64_t nb2 = nb1 + stride;
+    load_rb(wst[0], wsc[0], nb2 < nblocks ? nb2 : nb1);
+    reduce_store(rb_mac(wst[1], wsc[1]), 1, nb1);
     if (nb2 >= nblocks) break;
     nb = nb2;
+    nb1 = nb + stride;
+    load_rb(wst[1], wsc[1], nb1 < nblocks ? nb1 : nb);
   }
 }
 
@@ -1248,8 +1305,9 @@ int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
   void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK>), grid,
-                         dim3(64 * WK), args, 0, stream) == hipSuccess
+  const void* kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK, true>)
+                            : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK>);
+  return hipLaunchKernel(kern, grid, dim3(64 * WK), args, 0, stream) == hipSuccess
              ? FP6_OK
              : FP6_E_HIP;
 }
