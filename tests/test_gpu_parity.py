@@ -167,6 +167,36 @@ def test_linear_ksplit_k_coverage(M, K):
         _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(M, K, variant))
 
 
+@pytest.mark.parametrize("K", [2048, 4096])
+@pytest.mark.parametrize("per_wg", [2, 3, 4, 5])
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_linear_ksplit_row_blocks_per_workgroup(M, per_wg, K):
+    # The k-split kernels request all row blocks of a workgroup at once when
+    # it has 2-4 of them (a workgroup with one fewer repeats its last) and
+    # loop beyond.  N is sized from the CU count so that the first
+    # workgroups get per_wg row blocks and the rest per_wg - 1; one row of
+    # every row block is checked.  At K = 2048 half of the 16 waves have an
+    # empty k-range.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nblocks = (per_wg - 1) * cus + max(cus // 3, 1)
+    N = 16 * nblocks
+    W = synth.weights(N, K, 900 + per_wg + K)
+    X = synth.activations(M, K, 910 + M)
+    codes, scales = fp6.quantize_rows(W)
+    packed = fp6.prepack(codes, scales)
+    rows = 16 * np.arange(nblocks) + (np.arange(nblocks) * 7) % 16
+    oc, osc = oracle.quantize_rows(W[rows])
+    y_ref = oracle.gemm_ref(X, oracle.dequant_ref(oc, osc))
+    Xd = torch.from_numpy(X).to(DEV)
+    Pd = torch.from_numpy(packed).to(DEV)
+    Sd = torch.from_numpy(scales.copy()).to(DEV)
+    cols = torch.from_numpy(rows).to(DEV)
+    for variant in (KSPLIT, KSPLIT16):
+        Y = fp6.linear_plan(Xd, Pd, Sd, N, K, variant=variant)
+        torch.cuda.synchronize()
+        _assert_tol(Y[:, cols], y_ref, what=(M, per_wg, K, variant))
+
+
 def test_linear_one_hot_reproduces_wdq_exactly():
     N, K = 64, 1024
     p = Prepared(16, N, K, seed_w=99, seed_x=1)

@@ -668,14 +668,14 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 // (deterministic) by wave 0, which stores fp16 Y.  No global workspace, no
 // X re-reads, all k-slices of a row block stream concurrently.
 // ---------------------------------------------------------------------------
-template <int F, int KTW, int kKsWaves, bool M1 = false>
+template <int F, int KTW, int kKsWaves, bool M1 = false, int P = 0>
 __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
     int64_t K) {
   // Per wave, one 8 KB LDS region: first the X staging area of its k-tiles,
-  // then (after the wave has read its fragments) its two partial-tile
-  // buffers of 1 KB each.
+  // then (after the wave has read its fragments) its partial-tile buffers of
+  // 1 KB each (two, or P).
   __shared__ __attribute__((aligned(16))) half8v xw[kKsWaves][512];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -754,9 +754,13 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   auto rb_mac = [&](const WStage<F, 1> (&st)[KTW], _Float16 sc) {
     const half2v s2 = scale2_of<F>(sc);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
+    // With one tile per wave the products run unconditionally and an empty
+    // k-range (tile 0 loaded as a stand-in) is zeroed afterwards: behind a
+    // branch the compiler sinks a row block's loads into it, past earlier
+    // waits.
 #pragma unroll
     for (int t = 0; t < KTW; ++t) {
-      if (t < ktw) {
+      if (KTW == 1 || t < ktw) {
 #define FP6_KS_STEP(J)                                                                     \
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(                                            \
       Fmt<F>::template step<J>(st[t].t[0], s2), xf[t][J], acc, 0, 0, 0);
@@ -765,6 +769,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 #undef FP6_KS_STEP
       }
     }
+    if (KTW == 1 && ktw == 0) acc = float4v{0.f, 0.f, 0.f, 0.f};
     return acc;
   };
   auto reduce_store = [&](const float4v& acc, int buf, int64_t nb) {
@@ -783,6 +788,44 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   const int64_t stride = gridDim.x;
   int64_t nb = blockIdx.x;
   if (nb >= nblocks) return;  // uniform for the workgroup
+  if constexpr (P > 0) {
+    static_assert(P <= 8 && P <= kKsWaves, "P partial tiles per wave region, one summing wave each");
+    // At most P row blocks per workgroup: all of their tiles are requested
+    // at once, in straight-line code.  A workgroup with fewer row blocks
+    // repeats its last one (loads, products and the store of identical
+    // values) instead of branching: behind a branch the compiler sinks the
+    // loads past the X staging's wait, and the waits after it then cover
+    // every row block.
+    WStage<F, 1> ast[P][KTW];
+    _Float16 asc[P];
+    const int64_t nlast = nb + ((nblocks - 1 - nb) / stride) * stride;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int64_t nbi = nb + i * stride;
+      load_rb(ast[i], asc[i], nbi < nlast ? nbi : nlast);
+    }
+    // Fence: left free, the scheduler moves the last row scales down into
+    // the first row block's products, after its waits.
+    __builtin_amdgcn_sched_barrier(0);
+    stage_x();
+    // Every wave multiplies all of its row blocks before the one barrier, so
+    // a wave whose tiles have arrived does not wait for the slowest wave of
+    // each row block in turn.  Wave i then sums and stores row block i.
+    float4v accs[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) accs[i] = rb_mac(ast[i], asc[i]);
+#pragma unroll
+    for (int i = 0; i < P; ++i) red_at(i, wave)[lane] = accs[i];
+    __syncthreads();
+    if (wave < P) {
+      const int64_t nbi = nb + wave * stride;
+      float4v sum = red_at(wave, 0)[lane];
+#pragma unroll
+      for (int w = 1; w < kKsWaves; ++w) sum += red_at(wave, w)[lane];
+      store_y_block(Y, sum, r, M, N, (nbi < nlast ? nbi : nlast) * 16, g);
+    }
+    return;
+  }
   // The first two row blocks' tiles are requested before X is staged (whose
   // LDS writes wait for the X loads, issued first).
   int64_t nb1 = nb + stride;
@@ -1307,6 +1350,17 @@ int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_
   void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
   const void* kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK, true>)
                             : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK>);
+  if constexpr (KTW == 1) {
+    // 2..4 row blocks per workgroup: the straight-line form with all of them
+    // in flight.
+    const int64_t per_wg = fpx_ceil_div(nblocks, static_cast<int64_t>(grid.x));
+    if (per_wg == 2) kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, 2>)
+                                   : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, 2>);
+    if (per_wg == 3) kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, 3>)
+                                   : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, 3>);
+    if (per_wg == 4) kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, 4>)
+                                   : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, 4>);
+  }
   return hipLaunchKernel(kern, grid, dim3(64 * WK), args, 0, stream) == hipSuccess
              ? FP6_OK
              : FP6_E_HIP;
