@@ -168,12 +168,12 @@ def test_linear_ksplit_k_coverage(M, K):
 
 
 @pytest.mark.parametrize("K", [2048, 4096])
-@pytest.mark.parametrize("per_wg", [2, 3, 4, 5])
+@pytest.mark.parametrize("per_wg", [2, 3, 4, 5, 7, 9])
 @pytest.mark.parametrize("M", [1, 5, 16])
 def test_linear_ksplit_row_blocks_per_workgroup(M, per_wg, K):
-    # The k-split kernels request all row blocks of a workgroup at once when
-    # it has 2-4 of them (a workgroup with one fewer repeats its last) and
-    # loop beyond.  N is sized from the CU count so that the first
+    # The k-split kernels run straight-line code for 2-8 row blocks per
+    # workgroup (4 register stages; a workgroup with fewer than the form's
+    # count repeats its last row block) and loop beyond.  N is sized from the CU count so that the first
     # workgroups get per_wg row blocks and the rest per_wg - 1; one row of
     # every row block is checked.  At K = 2048 half of the 16 waves have an
     # empty k-range.

@@ -790,39 +790,42 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   if (nb >= nblocks) return;  // uniform for the workgroup
   if constexpr (P > 0) {
     static_assert(P <= 8 && P <= kKsWaves, "P partial tiles per wave region, one summing wave each");
-    // At most P row blocks per workgroup: all of their tiles are requested
-    // at once, in straight-line code.  A workgroup with fewer row blocks
-    // repeats its last one (loads, products and the store of identical
-    // values) instead of branching: behind a branch the compiler sinks the
-    // loads past the X staging's wait, and the waits after it then cover
-    // every row block.
-    WStage<F, 1> ast[P][KTW];
-    _Float16 asc[P];
+    // At most P row blocks per workgroup, held in S register stages: the
+    // first S are requested at once, and row block i + S into stage i % S
+    // right after row block i's products.  Straight-line code: a workgroup
+    // with fewer row blocks repeats its last one (loads, products and the
+    // store of identical values) instead of branching, since behind a
+    // branch the compiler sinks the loads past the X staging's wait and
+    // the waits after it then cover every row block.
+    constexpr int S = P < 4 ? P : 4;
+    WStage<F, 1> ast[S][KTW];
+    _Float16 asc[S];
     const int64_t nlast = nb + ((nblocks - 1 - nb) / stride) * stride;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
+    auto rb_of = [&](int i) {
       const int64_t nbi = nb + i * stride;
-      load_rb(ast[i], asc[i], nbi < nlast ? nbi : nlast);
-    }
+      return nbi < nlast ? nbi : nlast;
+    };
+#pragma unroll
+    for (int i = 0; i < S; ++i) load_rb(ast[i], asc[i], rb_of(i));
     // Fence: left free, the scheduler moves the last row scales down into
     // the first row block's products, after its waits.
     __builtin_amdgcn_sched_barrier(0);
     stage_x();
-    // Every wave multiplies all of its row blocks before the one barrier, so
-    // a wave whose tiles have arrived does not wait for the slowest wave of
-    // each row block in turn.  Wave i then sums and stores row block i.
-    float4v accs[P];
+    // Every wave multiplies all of its row blocks into its partial-tile
+    // slots before the one barrier, so a wave whose tiles have arrived does
+    // not wait for the slowest wave of each row block in turn.  Wave i then
+    // sums and stores row block i.
 #pragma unroll
-    for (int i = 0; i < P; ++i) accs[i] = rb_mac(ast[i], asc[i]);
-#pragma unroll
-    for (int i = 0; i < P; ++i) red_at(i, wave)[lane] = accs[i];
+    for (int i = 0; i < P; ++i) {
+      red_at(i, wave)[lane] = rb_mac(ast[i % S], asc[i % S]);
+      if (i + S < P) load_rb(ast[i % S], asc[i % S], rb_of(i + S));
+    }
     __syncthreads();
     if (wave < P) {
-      const int64_t nbi = nb + wave * stride;
       float4v sum = red_at(wave, 0)[lane];
 #pragma unroll
       for (int w = 1; w < kKsWaves; ++w) sum += red_at(wave, w)[lane];
-      store_y_block(Y, sum, r, M, N, (nbi < nlast ? nbi : nlast) * 16, g);
+      store_y_block(Y, sum, r, M, N, rb_of(wave) * 16, g);
     }
     return;
   }
@@ -1351,15 +1354,18 @@ int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_
   const void* kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK, true>)
                             : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK>);
   if constexpr (KTW == 1) {
-    // 2..4 row blocks per workgroup: the straight-line form with all of them
-    // in flight.
+    // 2..8 row blocks per workgroup: the straight-line form (P = 6 or 8
+    // covers 5..8, the busiest workgroups setting the count).
     const int64_t per_wg = fpx_ceil_div(nblocks, static_cast<int64_t>(grid.x));
-    if (per_wg == 2) kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, 2>)
-                                   : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, 2>);
-    if (per_wg == 3) kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, 3>)
-                                   : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, 3>);
-    if (per_wg == 4) kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, 4>)
-                                   : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, 4>);
+#define FP6_KS_P(PP)                                                                       \
+  kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, PP>)      \
+                : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, PP>)
+    if (per_wg == 2) FP6_KS_P(2);
+    else if (per_wg == 3) FP6_KS_P(3);
+    else if (per_wg == 4) FP6_KS_P(4);
+    else if (per_wg == 5 || per_wg == 6) FP6_KS_P(6);
+    else if (per_wg == 7 || per_wg == 8) FP6_KS_P(8);
+#undef FP6_KS_P
   }
   return hipLaunchKernel(kern, grid, dim3(64 * WK), args, 0, stream) == hipSuccess
              ? FP6_OK
