@@ -152,7 +152,8 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *     7  streaming, 1 row block per wave, ring of 8 tiles
  *     8  streaming, 2 row blocks per wave, ring of 6 tiles
  *     9  k-split persistent: one 8-wave workgroup per CU, waves split K and
- *        keep their X slice in registers; requires M <= 16, K <= 8192
+ *        keep their X slice in registers; requires M <= 16 and at most
+ *        8192 of K per K-split
  *    10  tiled, 256 rows x 128 columns per 8-wave workgroup (2 row blocks
  *        per wave, two waves per SIMD)
  *    11  tiled, 256 rows x 64 columns per 8-wave workgroup
@@ -169,7 +170,7 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *    18  as 15 with 8 waves per workgroup (each X tile shared by 8 waves)
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
- *          (1..K/256; must be 0 or 1 for variants 9, 12 and 13).
+ *          (1..K/256; must be 0 or 1 for variant 13).
  * The result equals fp6_linear's up to fp32 summation order.
  * Errors: as fp6_linear, plus FP6_E_VALUE for an unknown variant, a split
  * count out of range, or a shape that variant 9, 12 or 13 does not cover.

@@ -197,6 +197,28 @@ def test_linear_ksplit_row_blocks_per_workgroup(M, per_wg, K):
         _assert_tol(Y[:, cols], y_ref, what=(M, per_wg, K, variant))
 
 
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("NK", [(4096, 11008), (1024, 6400), (2048, 2304)])
+def test_linear_ksplit_across_workgroups(M, NK):
+    # The k-split kernels with K split across workgroups (fixed-order
+    # fix-up): straight-line and looping forms, ragged split ranges, idle
+    # waves; bitwise reproducible from run to run.
+    N, K = NK
+    p = Prepared(M, N, K, seed_w=N + K + 5, seed_x=M + 3, sample=192)
+    X, packed, s = p.to_device()
+    cols = torch.from_numpy(p.rows).to(DEV)
+    ktiles = K // 256
+    for variant, wk in ((KSPLIT, 8), (KSPLIT16, 16)):
+        for splits in (2, 3, 4, 7):
+            if splits > ktiles or -(-ktiles // splits) > 32:
+                continue
+            Y = fp6.linear_plan(X, packed, s, N, K, variant=variant, splits=splits).clone()
+            Y2 = fp6.linear_plan(X, packed, s, N, K, variant=variant, splits=splits)
+            torch.cuda.synchronize()
+            _assert_tol(Y[:, cols], p.y_ref, what=(M, N, K, variant, splits))
+            assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, variant, splits)
+
+
 def test_linear_one_hot_reproduces_wdq_exactly():
     N, K = 64, 1024
     p = Prepared(16, N, K, seed_w=99, seed_x=1)

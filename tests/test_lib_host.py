@@ -168,6 +168,7 @@ def test_linear_and_dequant_argument_errors_before_any_hip_call():
     assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 0, -1, None) == 8
     assert L.fp6_linear_plan(A, A, A, A, 17, 16, 256, 9, 0, None) == 8     # k-split: M <= 16
     assert L.fp6_linear_plan(A, A, A, A, 4, 16, 8448, 9, 0, None) == 8     # k-split: K <= 8192
+    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 65 * 256, 12, 2, None) == 8  # <= 8192 of K per split
     # dequant
     assert L.fp6_dequant(A, A, A, 16, 100, None) == 2
     assert L.fp6_dequant(None, A, A, 16, 256, None) == 1

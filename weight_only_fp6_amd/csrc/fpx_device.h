@@ -671,8 +671,8 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 template <int F, int KTW, int kKsWaves, bool M1 = false, int P = 0>
 __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
-    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
-    int64_t K) {
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits) {
   // Per wave, one 8 KB LDS region: first the X staging area of its k-tiles,
   // then (after the wave has read its fragments) its partial-tile buffers of
   // 1 KB each (two, or P).
@@ -680,7 +680,13 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
-  const int64_t kw0 = wave * ktiles / kKsWaves, kw1 = (wave + 1) * ktiles / kKsWaves;
+  // Workgroup b takes K-split b % splits (its k-tiles [kt0, kt1)) of the
+  // row blocks b / splits, + gridDim.x / splits, ...  With splits > 1 the
+  // summed 16x16 tile of a row block goes through the fixed-order split-K
+  // fix-up (the last split to arrive adds the partials in split order).
+  const int split = static_cast<int>(blockIdx.x % splits);
+  const int64_t kt0 = split * ktiles / splits, kts = (split + 1) * ktiles / splits - kt0;
+  const int64_t kw0 = kt0 + wave * kts / kKsWaves, kw1 = kt0 + (wave + 1) * kts / kKsWaves;
   const int ktw = static_cast<int>(kw1 - kw0);  // 0..KTW tiles for this wave
   // Tile indices clamped into the wave's range (or tile 0 for an empty
   // range): clamped slots are loaded but never multiplied.
@@ -772,6 +778,16 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
     if (KTW == 1 && ktw == 0) acc = float4v{0.f, 0.f, 0.f, 0.f};
     return acc;
   };
+  // Row block nb's summed tile: stored, or (with K-splits) handed to the
+  // fix-up, whose last arriver stores.
+  auto finish = [&](float4v sum, int64_t nb) {
+    if (splits > 1) {
+      float4v a1[1] = {sum};
+      if (!splitk_fixup<1>(a1, part + nb * splits * 256, counters + nb, split, splits, lane)) return;
+      sum = a1[0];
+    }
+    store_y_block(Y, sum, r, M, N, nb * 16, g);
+  };
   auto reduce_store = [&](const float4v& acc, int buf, int64_t nb) {
     red_at(buf, wave)[lane] = acc;
     __syncthreads();
@@ -781,12 +797,12 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
       float4v sum = red_at(buf, 0)[lane];
 #pragma unroll
       for (int w = 1; w < kKsWaves; ++w) sum += red_at(buf, w)[lane];
-      store_y_block(Y, sum, r, M, N, nb * 16, g);
+      finish(sum, nb);
     }
   };
 
-  const int64_t stride = gridDim.x;
-  int64_t nb = blockIdx.x;
+  const int64_t stride = gridDim.x / splits;
+  int64_t nb = blockIdx.x / splits;
   if (nb >= nblocks) return;  // uniform for the workgroup
   if constexpr (P > 0) {
     static_assert(P <= 8 && P <= kKsWaves, "P partial tiles per wave region, one summing wave each");
@@ -821,11 +837,11 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
       if (i + S < P) load_rb(ast[i % S], asc[i % S], rb_of(i + S));
     }
     __syncthreads();
-    if (wave < P) {
+    if (wave < P && nb + wave * stride <= nlast) {  // repeated row blocks are not stored again
       float4v sum = red_at(wave, 0)[lane];
 #pragma unroll
       for (int w = 1; w < kKsWaves; ++w) sum += red_at(wave, w)[lane];
-      store_y_block(Y, sum, r, M, N, rb_of(wave) * 16, g);
+      finish(sum, nb + wave * stride);
     }
     return;
   }
@@ -1343,20 +1359,24 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
 // ---------------------------------------------------------------------------
 template <int F, int KTW, int WK>
 int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                    int64_t K, int cus, hipStream_t stream) {
+                    int64_t K, int splits, float* part, unsigned* cnt, int cus, hipStream_t stream) {
   const int64_t nblocks = N >> 4;
-  const dim3 grid(static_cast<unsigned>(nblocks < cus ? nblocks : cus));
+  // Workgroups per split: one per CU in all, at most one per row block.
+  int64_t per_split = cus / splits;
+  if (per_split < 1) per_split = 1;
+  if (per_split > nblocks) per_split = nblocks;
+  const dim3 grid(static_cast<unsigned>(per_split * splits));
   const _Float16* x = static_cast<const _Float16*>(X);
   const u32x4* w = static_cast<const u32x4*>(W);
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
-  void* args[] = {&x, &w, &sc, &y, &M, &N, &K};
+  void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits};
   const void* kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK, true>)
                             : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, KTW, WK>);
   if constexpr (KTW == 1) {
     // 2..8 row blocks per workgroup: the straight-line form (P = 6 or 8
     // covers 5..8, the busiest workgroups setting the count).
-    const int64_t per_wg = fpx_ceil_div(nblocks, static_cast<int64_t>(grid.x));
+    const int64_t per_wg = fpx_ceil_div(nblocks, per_split);
 #define FP6_KS_P(PP)                                                                       \
   kern = M == 1 ? reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, true, PP>)      \
                 : reinterpret_cast<const void*>(&fp6_gemm_ksplit<F, 1, WK, false, PP>)
@@ -1375,13 +1395,15 @@ int launch_ksplit_t(const void* X, const void* W, const void* S, void* Y, int64_
 // WK waves per workgroup; each wave holds ceil(K/256 / WK) k-tiles.
 template <int F, int WK>
 int launch_ksplit(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                  int64_t K, int cus, hipStream_t stream) {
-  switch (fpx_ceil_div(K >> 8, WK)) {
-    case 1: return launch_ksplit_t<F, 1, WK>(X, W, S, Y, M, N, K, cus, stream);
-    case 2: return launch_ksplit_t<F, 2, WK>(X, W, S, Y, M, N, K, cus, stream);
-    case 3: if constexpr (WK == 8) return launch_ksplit_t<F, 3, WK>(X, W, S, Y, M, N, K, cus, stream);
+                  int64_t K, int splits, float* part, unsigned* cnt, int cus, hipStream_t stream) {
+  // Tiles per wave: the longest split's k-tiles over the waves.
+  const int64_t split_tiles = fpx_ceil_div(K >> 8, splits);
+  switch (fpx_ceil_div(split_tiles, WK)) {
+    case 1: return launch_ksplit_t<F, 1, WK>(X, W, S, Y, M, N, K, splits, part, cnt, cus, stream);
+    case 2: return launch_ksplit_t<F, 2, WK>(X, W, S, Y, M, N, K, splits, part, cnt, cus, stream);
+    case 3: if constexpr (WK == 8) return launch_ksplit_t<F, 3, WK>(X, W, S, Y, M, N, K, splits, part, cnt, cus, stream);
             return FP6_E_VALUE;
-    case 4: if constexpr (WK == 8) return launch_ksplit_t<F, 4, WK>(X, W, S, Y, M, N, K, cus, stream);
+    case 4: if constexpr (WK == 8) return launch_ksplit_t<F, 4, WK>(X, W, S, Y, M, N, K, splits, part, cnt, cus, stream);
             return FP6_E_VALUE;
     default: return FP6_E_VALUE;
   }
@@ -1536,10 +1558,10 @@ int launch_variant(const fpx::LaunchCtx& c) {
     case 6: return launch_tiled<F, 8, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 7: return launch_stream<F, 1, 1, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 8: return launch_stream<F, 2, 1, 6>(X, W, S, Y, M, N, K, sp, pt, ct, s);
-    case 9: return launch_ksplit<F, 8>(X, W, S, Y, M, N, K, c.cus, s);
+    case 9: return launch_ksplit<F, 8>(X, W, S, Y, M, N, K, sp, pt, ct, c.cus, s);
     case 10: return launch_tiled<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 11: return launch_tiled<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
-    case 12: return launch_ksplit<F, 16>(X, W, S, Y, M, N, K, c.cus, s);
+    case 12: return launch_ksplit<F, 16>(X, W, S, Y, M, N, K, sp, pt, ct, c.cus, s);
     case 13: return launch_kslice<F>(X, W, S, Y, M, N, K, c.cus, s);
     case 14: return launch_xlds<F, 2, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 15: return launch_xlds<F, 1, 4, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);

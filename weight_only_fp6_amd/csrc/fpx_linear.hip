@@ -128,25 +128,50 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
   if (variant == 0) {
     // Measured on MI355X: up to K = 4096 the k-slice kernel (at most one row
     // block per CU) or the k-split kernels (8 waves up to K = 2048, else 16)
-    // are fastest; for longer K the streaming kernel with X shared through
-    // LDS (1 row block per wave): 8 waves per workgroup once there are at
+    // are fastest; for longer K the k-split kernel split across workgroups
+    // when that leaves few row blocks per workgroup, else the streaming
+    // kernel with X shared through LDS (1 row block per wave): 8 waves per
+    // workgroup once there are at
     // least 7 row blocks per CU (each X tile shared by twice the waves, and
     // one workgroup per CU instead of a 1-or-2 mix: Llama-70B MLP 38 -> 35
     // us), else 4.  Above M = 16 the tiled kernels: 64 columns with
     // whole-tile stages up to M = 64, else 128 columns with half-tile stages.
     const bool one_rb_per_cu = (N >> 4) <= cus;
-    if (M <= 16 && ktiles <= 16 && one_rb_per_cu) p.variant = 13;
-    else if (M <= 16 && ktiles <= 8) p.variant = 9;
-    else if (M <= 16 && ktiles <= 16) p.variant = 12;
-    else if (M <= 16) p.variant = (N >> 4) >= 7 * static_cast<int64_t>(cus) ? 18 : 15;
-    else if (M <= 64) p.variant = 17;
-    else p.variant = 10;
+    // Longer K (split count not forced): the 16-wave k-split kernel with K
+    // split across workgroups (at most 16 k-tiles per split, one per wave)
+    // while its busiest workgroup has at most 6 row blocks, all in flight at
+    // once (Llama-70B attention output 16x8192x8192: 20.0 -> 15.2 us).
+    const int64_t ks_splits = ceil_div(ktiles, 16);
+    const int64_t ks_per_split = cus / ks_splits;
+    const bool ks_fits = splits == 0 && ktiles > 16 && ks_splits <= 8 && ks_per_split >= 1 &&
+                         ceil_div(N >> 4, ks_per_split) <= 6;
+    if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
+      p.variant = 13;
+    } else if (M <= 16 && ktiles <= 8) {
+      p.variant = 9;
+    } else if (M <= 16 && ktiles <= 16) {
+      p.variant = 12;
+    } else if (M <= 16 && ks_fits) {
+      p.variant = 12;
+      p.splits = static_cast<int>(ks_splits);
+      return p;
+    } else if (M <= 16) {
+      p.variant = (N >> 4) >= 7 * static_cast<int64_t>(cus) ? 18 : 15;
+    } else if (M <= 64) {
+      p.variant = 17;
+    } else {
+      p.variant = 10;
+    }
   } else {
     p.variant = variant;
   }
   const KernelCfg& c = kCfgs[p.variant];
-  if (c.kind == Kind::kKsplit || c.kind == Kind::kKslice) {
+  if (c.kind == Kind::kKslice) {
     p.splits = 1;
+    return p;
+  }
+  if (c.kind == Kind::kKsplit) {
+    p.splits = splits > 0 ? splits : 1;
     return p;
   }
   if (splits > 0) {
@@ -199,10 +224,10 @@ int linear_impl(int format, const void* X, const void* W, const void* S, void* Y
   if (splits > 0 && ceil_div(N >> 4, 4) * static_cast<int64_t>(splits) >= (int64_t(1) << 24))
     return FP6_E_VALUE;
   // The k-split kernel keeps each wave's X slice in registers: M <= 16 and
-  // at most K = 8192 (and a per-wave tile count it is instantiated for); it
-  // never splits across workgroups.
+  // at most 8192 of K per split (the per-wave tile counts it is
+  // instantiated for).
   if (variant > 0 && kCfgs[variant].kind == Kind::kKsplit &&
-      (M > 16 || (K >> 8) > fpx::kKsMaxTiles || splits > 1))
+      (M > 16 || ceil_div(K >> 8, splits > 0 ? splits : 1) > fpx::kKsMaxTiles))
     return FP6_E_VALUE;
   if (variant > 0 && kCfgs[variant].kind == Kind::kKslice &&
       (M > 16 || (K >> 8) > fpx::kKsliceMaxTiles || splits > 1))
