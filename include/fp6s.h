@@ -81,15 +81,19 @@ int fp6s_linear(const void* X, const void* packed_W, const void* scales, void* Y
  * K; M <= 16, K <= 8192); 2 = streaming with X shared through LDS, 1 row
  * block per wave; 3 = the same with 2 row blocks per wave; 4 = tiled, 256
  * rows x 64 columns per 8-wave workgroup (X staged in LDS); 5 = tiled, 256
- * rows x 128 columns.  Variants 2-5 handle any M.  splits: 0 = automatic,
- * else K-splits across workgroups (1..K/512; variants 2-5).
- * Errors: as fp6_linear_plan.
+ * rows x 128 columns; 6 = k-split (8-wave workgroups, one 512-k tile per
+ * wave and K-split, each workgroup's row blocks all in flight; M <= 16, at
+ * most K = 4096 per split and 8 row blocks per workgroup, i.e. N/16 <=
+ * 8 * (CUs / splits)).  Variants 2-5 handle any M.  splits: 0 = automatic,
+ * else K-splits across workgroups (1..K/512; variants 2-6).
+ * Errors: as fp6_linear_plan, plus FP6_E_VALUE for a shape variant 1 or 6
+ * does not cover.
  */
 int fp6s_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
                      int64_t N, int64_t K, int variant, int splits, void* stream);
 
 /* fp6s_linear_plan_query -- host: the schedule fp6s_linear would use for
- * (M, N, K) on the current device (*variant 1..5, *splits).  One HIP query.
+ * (M, N, K) on the current device (*variant 1..6, *splits).  One HIP query.
  * Errors: FP6_E_NULL, FP6_E_SHAPE (M >= 1, K % 512 == 0), FP6_E_HIP. */
 int fp6s_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits);
 

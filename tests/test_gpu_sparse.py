@@ -27,8 +27,9 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import weight_only_fp6_amd as fp6  # noqa: E402
 
 DEV = torch.device("cuda:0")
-VARIANTS = (0, 2, 3, 4, 5)     # any M; 1 (k-slice) only for M <= 16
+VARIANTS = (0, 2, 3, 4, 5)     # any M; 1 (k-slice) and 6 (k-split) only for M <= 16
 KSLICE = 1
+KSPLIT = 6
 
 
 class SpPrepared:
@@ -77,7 +78,7 @@ def test_linear_small_shapes_every_variant(M, NK):
     N, K = NK
     p = SpPrepared(M, N, K, seed_w=N * 3 + K, seed_x=M * 7 + 5)
     X, packed, s = p.to_device()
-    for variant in VARIANTS + ((KSLICE,) if M <= 16 else ()):
+    for variant in VARIANTS + ((KSLICE, KSPLIT) if M <= 16 else ()):
         Y = fp6.sparse_linear_plan(X, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
@@ -92,6 +93,10 @@ def test_linear_forced_splits():
             Y = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits)
             torch.cuda.synchronize()
             _assert_tol(Y[:, cols], p.y_ref, what=(variant, splits))
+    for splits in (2, 3, 5):    # k-split: <= 8 tiles per split, <= 8 row blocks per workgroup
+        Y = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=KSPLIT, splits=splits)
+        torch.cuda.synchronize()
+        _assert_tol(Y[:, cols], p.y_ref, what=(KSPLIT, splits))
 
 
 @functools.lru_cache(maxsize=1)
@@ -123,7 +128,8 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
     want = p.wdq_ref[:, ks].T.astype(np.float64)
-    for variant, splits in [(0, 0), (1, 0), (2, 1), (2, 3), (3, 1), (3, 2), (4, 1), (4, 2), (5, 1), (5, 4)]:
+    for variant, splits in [(0, 0), (1, 0), (2, 1), (2, 3), (3, 1), (3, 2), (4, 1), (4, 2), (5, 1), (5, 4),
+                            (6, 0), (6, 2), (6, 4)]:
         Y = fp6.sparse_linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (variant, splits)
@@ -132,10 +138,11 @@ def test_linear_one_hot_reproduces_wdq_exactly():
 def test_linear_is_deterministic_and_m_zero():
     p = SpPrepared(16, 4096, 4096, seed_w=91, seed_x=92, sample=32)
     X, packed, s = p.to_device()
-    a = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=2, splits=4).clone()
-    b = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=2, splits=4).clone()
-    torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for variant, splits in ((2, 4), (KSPLIT, 4)):
+        a = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits).clone()
+        b = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (variant, splits)
     Y = fp6.sparse_linear(torch.zeros((0, p.K), dtype=torch.float16, device=DEV), packed, s, p.N, p.K)
     torch.cuda.synchronize()
     assert Y.shape == (0, p.N)
@@ -172,8 +179,34 @@ def test_sparse_linear_adversarial_rows(M):
     out = fp6.sparse_dequant(packed, sd, N, K)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), wdq.view(np.uint16))
-    for variant, splits in [(0, 0), (2, 2), (3, 1), (4, 2), (5, 1)] + ([(KSLICE, 0)] if M <= 16 else []):
+    for variant, splits in [(0, 0), (2, 2), (3, 1), (4, 2), (5, 1)] + ([(KSLICE, 0), (KSPLIT, 0), (KSPLIT, 3)] if M <= 16 else []):
         Y = fp6.sparse_linear_plan(Xd, packed, sd, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         _assert_tol(Y, y_ref, what=(M, variant, splits))
         assert not Y[:, 0].cpu().numpy().astype(np.float64).any(), (M, variant, splits)
+
+
+@pytest.mark.parametrize("K", [2048, 4096, 6144])
+@pytest.mark.parametrize("per_wg", [1, 2, 3, 4, 5, 7, 8])
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_sparse_ksplit_row_blocks_per_workgroup(M, per_wg, K):
+    # The sparse k-split kernel with 1-8 row blocks per workgroup (a
+    # workgroup with fewer than its form's count repeats its last row
+    # block), K split when it exceeds 8 tiles; N is sized from the CU count
+    # and one row of every row block is checked.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = -(-(K // 512) // 8)
+    per_split = cus // splits
+    nblocks = (per_wg - 1) * per_split + max(per_split // 3, 1)
+    N = 16 * nblocks
+    W = synth.weights(N, K, 950 + per_wg + K)
+    X = synth.activations(M, K, 960 + M)
+    c, pos, sc = fp6.prune_quantize(W)
+    packed = torch.from_numpy(fp6.sparse_prepack(c, pos, sc, K)).to(DEV)
+    rows = 16 * np.arange(nblocks) + (np.arange(nblocks) * 5) % 16
+    oc, op, osc = sparse24.quantize_sparse(W[rows])
+    y_ref = oracle.gemm_ref(X, sparse24.dequant_ref(oc, op, osc, K))
+    Y = fp6.sparse_linear_plan(torch.from_numpy(X).to(DEV), packed, torch.from_numpy(sc.copy()).to(DEV),
+                               N, K, variant=KSPLIT)
+    torch.cuda.synchronize()
+    _assert_tol(Y[:, torch.from_numpy(rows).to(DEV)], y_ref, what=(M, per_wg, K))

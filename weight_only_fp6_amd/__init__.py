@@ -239,7 +239,7 @@ def dequant(packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e
 # 2:4-sparse FP6
 # ---------------------------------------------------------------------------
 SPARSE_KERNEL_NAMES = {1: "sp_gemm_kslice", 2: "sp_gemm_xlds<1,4,4>", 3: "sp_gemm_xlds<2,4,4>",
-                       4: "sp_gemm_tiled<4,2,8>", 5: "sp_gemm_tiled<8,2,8>"}
+                       4: "sp_gemm_tiled<4,2,8>", 5: "sp_gemm_tiled<8,2,8>", 6: "sp_gemm_ksplit"}
 
 
 def sparse_packed_bytes(N: int, K: int) -> int:

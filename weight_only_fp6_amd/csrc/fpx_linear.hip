@@ -281,8 +281,9 @@ int dequant_impl(int format, const void* packed_W, const void* scales, void* W16
 }
 
 // 2:4-sparse FP6.  M <= 16: the k-slice kernel while every row block has its
-// own CU and K fits one 512-k tile per wave, else the streaming kernel with X
-// in LDS, split towards ~4 waves per CU like the dense one.  M > 16: the
+// own CU and K fits one 512-k tile per wave, then the k-split kernel while
+// it has at most 8 row blocks per workgroup, else the streaming kernel with
+// X in LDS, split towards ~4 waves per CU like the dense one.  M > 16: the
 // tiled kernel (64 columns per workgroup up to M = 64, else 128), split
 // across workgroups while a whole extra round fits on the CUs.
 bool sp_tiled(int v) { return v == fpx::kSpTiled4 || v == fpx::kSpTiled8; }
@@ -291,8 +292,14 @@ int sp_tile_b(int v) { return v == fpx::kSpTiled8 ? 8 : 4; }
 Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
   Plan p;
   const int64_t ktiles = K >> 9;
+  // The k-split kernel: at most 8 tiles per K-split (one per wave), as few
+  // splits as that allows, and at most 8 row blocks per workgroup.
+  const int ks_splits = static_cast<int>(ceil_div(ktiles, fpx::kSpKsplitMaxTiles));
+  const bool ks_fits = ks_splits <= 8 &&
+                       fpx::sp_ksplit_rows_per_wg(N, cus, ks_splits) <= fpx::kSpKsplitMaxRows;
   if (variant == fpx::kSpAuto) {
     if (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles) p.variant = fpx::kSpKslice;
+    else if (M <= 16 && splits == 0 && ks_fits) p.variant = fpx::kSpKsplit;
     else if (M <= 16) p.variant = fpx::kSpXlds1;
     else if (M <= 64) p.variant = fpx::kSpTiled4;
     else p.variant = fpx::kSpTiled8;
@@ -301,6 +308,10 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
   }
   if (p.variant == fpx::kSpKslice) {
     p.splits = 1;
+    return p;
+  }
+  if (p.variant == fpx::kSpKsplit) {
+    p.splits = splits > 0 ? splits : ks_splits;
     return p;
   }
   if (splits > 0) {
@@ -335,10 +346,16 @@ int sparse_linear_impl(const void* X, const void* W, const void* S, void* Y, int
     return FP6_E_VALUE;
   if (variant == fpx::kSpKslice && (M > 16 || (K >> 9) > fpx::kSpKsliceMaxTiles || splits > 1))
     return FP6_E_VALUE;
+  // (an automatic split count for it is the smallest that fits)
+  if (variant == fpx::kSpKsplit && (M > 16 || (splits > 0 && ceil_div(K >> 9, splits) > fpx::kSpKsplitMaxTiles)))
+    return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const int cus = device_cus(dev);
   const Plan p = choose_sparse_plan(M, N, K, cus, variant, splits);
+  if (p.variant == fpx::kSpKsplit &&
+      fpx::sp_ksplit_rows_per_wg(N, cus, p.splits) > fpx::kSpKsplitMaxRows)
+    return FP6_E_VALUE;
   Workspace* ws = nullptr;
   if (p.splits > 1) {
     int64_t units, floats;

@@ -87,6 +87,111 @@ __global__ __launch_bounds__(64 * WK) void sp_gemm_kslice(
 }
 
 // ---------------------------------------------------------------------------
+// K-split kernel (M <= 16, at most 8 row blocks per workgroup): the dense
+// k-split kernel's straight-line form on sparse tiles.  A workgroup of 8
+// waves takes K-split blockIdx % splits (at most 8 tiles of 512 k, one per
+// wave) of the row blocks blockIdx / splits, + stride, ... (P of them at
+// most).  Each wave stages its X slice (16 rows x 512 k = 16 KB) once,
+// through its own LDS region with coalesced 1 KB row loads (32-byte units
+// XOR-swizzled by row, so the 16 lanes of a B-fragment read hit distinct
+// banks; at M = 1 one 16-byte load per lane and broadcast reads), keeps up
+// to 4 row blocks' tiles in flight, multiplies every row block into a
+// partial slot of its region, and after one barrier wave i sums row block i
+// (through the fixed-order split-K fix-up when splits > 1).
+// ---------------------------------------------------------------------------
+template <int P, bool M1>
+__global__ __launch_bounds__(512) void sp_gemm_ksplit(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits) {
+  constexpr int WK = 8;
+  static_assert(P >= 1 && P <= WK, "one summing wave per row block");
+  __shared__ __attribute__((aligned(32))) half8v xw[WK][1024];  // 16 KB per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nblocks = N >> 4, ktiles = K >> 9;
+  const int split = static_cast<int>(blockIdx.x % splits);
+  const int64_t kt0 = split * ktiles / splits, kts = (split + 1) * ktiles / splits - kt0;
+  const int64_t kw0 = kt0 + wave * kts / WK, kw1 = kt0 + (wave + 1) * kts / WK;
+  const bool active = kw1 > kw0;  // at most one tile per wave
+  const int64_t kt = active ? kw0 : 0;
+  const int64_t stride = gridDim.x / splits;
+  const int64_t nb = blockIdx.x / splits;
+  if (nb >= nblocks) return;  // uniform for the workgroup
+  const int64_t nlast = nb + ((nblocks - 1 - nb) / stride) * stride;
+  auto rb_of = [&](int i) {
+    const int64_t nbi = nb + i * stride;
+    return nbi < nlast ? nbi : nlast;
+  };
+  auto red_at = [&](int slot, int w) { return reinterpret_cast<float4v*>(&xw[w][64 * slot]); };
+
+  // X loads first (the LDS writes below wait for them, not for the tiles).
+  constexpr int kXLoads = M1 ? 1 : 16;
+  half8v xg[kXLoads];
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int64_t m = i < M ? i : M - 1;
+    xg[i] = *reinterpret_cast<const half8v*>(X + m * K + kt * 512 + 8 * lane);
+  }
+  // Straight-line code throughout: a workgroup with fewer than P row
+  // blocks repeats its last one, and an empty k-range is zeroed after its
+  // products (behind a branch the compiler sinks loads past earlier waits).
+  constexpr int S = P < 4 ? P : 4;
+  SpTile ast[S];
+  _Float16 asc[S];
+  auto load_rb = [&](int st, int64_t rb) {
+    sp_load(ast[st], wp + (rb * ktiles + kt) * kSpTileQuads + lane, lane);
+    asc[st] = scales[rb * 16 + r];
+  };
+#pragma unroll
+  for (int i = 0; i < S; ++i) load_rb(i, rb_of(i));
+  __builtin_amdgcn_sched_barrier(0);
+  // Stage X: row rr's 32-byte unit u sits at unit u ^ rr of the row.
+  half16v xf[8];
+  if constexpr (M1) {
+    xw[wave][lane] = xg[0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xf[j] = *reinterpret_cast<const half16v*>(&xw[wave][2 * (4 * j + g)]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xw[wave][i * 64 + 2 * ((lane >> 1) ^ i) + (lane & 1)] = xg[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      xf[j] = *reinterpret_cast<const half16v*>(&xw[wave][r * 64 + 2 * ((4 * j + g) ^ r)]);
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const SpTile& st = ast[i % S];
+    const half2v s2 = scale2_of<kE3M2>(asc[i % S]);
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    acc = sp_mac<0>(st, s2, xf[0], acc);
+    acc = sp_mac<1>(st, s2, xf[1], acc);
+    acc = sp_mac<2>(st, s2, xf[2], acc);
+    acc = sp_mac<3>(st, s2, xf[3], acc);
+    acc = sp_mac<4>(st, s2, xf[4], acc);
+    acc = sp_mac<5>(st, s2, xf[5], acc);
+    acc = sp_mac<6>(st, s2, xf[6], acc);
+    acc = sp_mac<7>(st, s2, xf[7], acc);
+    if (!active) acc = float4v{0.f, 0.f, 0.f, 0.f};
+    red_at(i, wave)[lane] = acc;
+    if (i + S < P) load_rb(i % S, rb_of(i + S));
+  }
+  __syncthreads();
+  if (wave < P && nb + wave * stride <= nlast) {  // repeated row blocks are not stored again
+    const int64_t rb = nb + wave * stride;
+    float4v sum = red_at(wave, 0)[lane];
+#pragma unroll
+    for (int w = 1; w < WK; ++w) sum += red_at(wave, w)[lane];
+    if (splits > 1) {
+      float4v a1[1] = {sum};
+      if (!splitk_fixup<1>(a1, part + rb * splits * 256, counters + rb, split, splits, lane)) return;
+      sum = a1[0];
+    }
+    store_y_block(Y, sum, r, M, N, rb * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming kernel with X shared through LDS (any M, in m-groups of 16).  A
 // wave streams A row blocks over a K range through a register ring of D
 // tiles; the NW waves of a workgroup share each X tile (16 rows x 512 k,
@@ -481,6 +586,45 @@ int launch_sp_kslice(const fpx::LaunchCtx& c) {
              : FP6_E_HIP;
 }
 
+// Workgroups per K-split and row blocks per workgroup of the sparse k-split
+// kernel (one workgroup per CU in all).
+int64_t sp_ksplit_per_split(int64_t N, int cus, int splits) {
+  int64_t per_split = cus / splits;
+  if (per_split < 1) per_split = 1;
+  if (per_split > (N >> 4)) per_split = N >> 4;
+  return per_split;
+}
+
+int launch_sp_ksplit(const fpx::LaunchCtx& c) {
+  const int64_t per_split = sp_ksplit_per_split(c.N, c.cus, c.splits);
+  const int64_t per_wg = fpx_ceil_div(c.N >> 4, per_split);
+  const dim3 grid(static_cast<unsigned>(per_split * c.splits));
+  const _Float16* x = static_cast<const _Float16*>(c.X);
+  const u32x4* w = static_cast<const u32x4*>(c.W);
+  const _Float16* sc = static_cast<const _Float16*>(c.S);
+  _Float16* y = static_cast<_Float16*>(c.Y);
+  float* part = c.part;
+  unsigned* cnt = c.counters;
+  int64_t M = c.M, N = c.N, K = c.K;
+  int splits = c.splits;
+  const void* kern = nullptr;
+#define FP6_SPKS_P(PP)                                                                        \
+  kern = M == 1 ? reinterpret_cast<const void*>(&sp_gemm_ksplit<PP, true>)                    \
+                : reinterpret_cast<const void*>(&sp_gemm_ksplit<PP, false>)
+  switch (per_wg) {
+    case 1: FP6_SPKS_P(1); break;
+    case 2: FP6_SPKS_P(2); break;
+    case 3: FP6_SPKS_P(3); break;
+    case 4: FP6_SPKS_P(4); break;
+    case 5: case 6: FP6_SPKS_P(6); break;
+    case 7: case 8: FP6_SPKS_P(8); break;
+    default: return FP6_E_VALUE;
+  }
+#undef FP6_SPKS_P
+  void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits};
+  return hipLaunchKernel(kern, grid, dim3(512), args, 0, c.stream) == hipSuccess ? FP6_OK : FP6_E_HIP;
+}
+
 template <int A, int D, int NW>
 int launch_sp_xlds(const fpx::LaunchCtx& c) {
   const int64_t ngroups = fpx_ceil_div(c.N >> 4, A), gsets = fpx_ceil_div(ngroups, NW);
@@ -539,6 +683,10 @@ int launch_sp_tiled(const fpx::LaunchCtx& c) {
 
 namespace fpx {
 
+int64_t sp_ksplit_rows_per_wg(int64_t N, int cus, int splits) {
+  return fpx_ceil_div(N >> 4, sp_ksplit_per_split(N, cus, splits));
+}
+
 int launch_sparse(const LaunchCtx& c) {
   switch (c.variant) {
     case kSpKslice: return (c.K >> 9) <= 8 ? launch_sp_kslice<8>(c) : launch_sp_kslice<16>(c);
@@ -546,6 +694,7 @@ int launch_sparse(const LaunchCtx& c) {
     case kSpXlds2: return launch_sp_xlds<2, 4, 4>(c);
     case kSpTiled4: return launch_sp_tiled<4, 2, 8>(c);
     case kSpTiled8: return launch_sp_tiled<8, 2, 8>(c);
+    case kSpKsplit: return launch_sp_ksplit(c);
     default: return FP6_E_VALUE;
   }
 }
