@@ -168,6 +168,12 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  *    17  tiled, 256 rows x 64 columns per 8-wave workgroup, whole 256-k tiles
  *        per pipeline stage (one barrier per tile)
  *    18  as 15 with 8 waves per workgroup (each X tile shared by 8 waves)
+ *    19  streaming with X in LDS, 8 waves, 2 row blocks x 32 columns per wave
+ *        (each k-step of a row block spliced once for both column groups),
+ *        ring of 2 tiles
+ *    20  as 19 with 64 columns per wave
+ *    21  as 19 with 1 row block per wave and a ring of 4 tiles
+ *    22  as 20 with 1 row block per wave
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
  *          (1..K/256; must be 0 or 1 for variant 13).
@@ -181,7 +187,7 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
 
 /*
  * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
- * for (M, N, K) on the current device: *variant (1..18, see fp6_linear_plan)
+ * for (M, N, K) on the current device: *variant (1..22, see fp6_linear_plan)
  * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
  * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
  * >= 1 here), FP6_E_HIP.

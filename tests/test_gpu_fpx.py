@@ -28,7 +28,7 @@ import weight_only_fp6_amd as fp6  # noqa: E402
 
 DEV = torch.device("cuda:0")
 FMTS = ("e2m3", "e2m2", "e2m1")
-ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18)
+ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18, 19, 20, 21, 22)
 SMALL_M_VARIANTS = (9, 12, 13)
 
 
@@ -139,7 +139,8 @@ def test_linear_one_hot_reproduces_wdq_exactly(fmt):
     _, packed, s = p.to_device()
     want = p.wdq_ref[:, ks].T.astype(np.float64)
     for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 3), (5, 3), (6, 1), (8, 1), (9, 0), (12, 0),
-                            (13, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3)]:
+                            (13, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3),
+                            (19, 2), (20, 1), (21, 3), (22, 2)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits, fmt=fmt)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (fmt, variant, splits)
@@ -196,7 +197,7 @@ def test_linear_adversarial_rows(fmt, M):
     assert np.array_equal(p.scales.view(np.uint16), p.oscales.view(np.uint16))
     Xd, packed, s = p.to_device()
     assert np.array_equal(_bits16(fp6.dequant(packed, s, N, K, fmt=fmt)), p.wdq_ref.view(np.uint16))
-    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3)]:
+    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3), (19, 3), (22, 2)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits, fmt=fmt)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(fmt, M, variant, splits))

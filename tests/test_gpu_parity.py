@@ -28,7 +28,7 @@ import weight_only_fp6_amd as fp6  # noqa: E402
 DEV = torch.device("cuda:0")
 # Kernel configurations of fp6_linear_plan: 0 = automatic, 1-4 and 7-8
 # streaming, 5-6 and 10-11 tiled, 9 k-split persistent (M <= 16, K <= 8192).
-ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18)
+ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18, 19, 20, 21, 22)
 KSPLIT = 9
 KSPLIT16 = 12
 KSLICE = 13
@@ -147,7 +147,7 @@ def test_linear_forced_splits_long_k(splits):
     shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
     p = _prep(shp.name, None)
     X, packed, s = p.to_device()
-    for variant in (1, 3, 5, 6, 10, 11, 14, 16, 17, 18):
+    for variant in (1, 3, 5, 6, 10, 11, 14, 16, 17, 18, 19, 20, 21, 22):
         Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(splits, variant))
@@ -227,7 +227,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     X[np.arange(16), ks] = 1.0
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
-    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (KSLICE, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3)]:
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (KSLICE, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3), (19, 2), (20, 3), (21, 1), (22, 4)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         got = Y.cpu().numpy().astype(np.float64)
@@ -345,7 +345,7 @@ def test_linear_adversarial_rows(M):
     assert np.array_equal(p.codes, p.ocodes) and np.array_equal(p.scales.view(np.uint16), p.oscales.view(np.uint16))
     Xd, packed, s = p.to_device()
     assert np.array_equal(_bits16(fp6.dequant(packed, s, N, K)), p.wdq_ref.view(np.uint16))
-    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3)]:
+    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3), (19, 3), (22, 2)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, variant, splits))

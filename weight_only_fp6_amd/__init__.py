@@ -213,6 +213,8 @@ KERNEL_NAMES = {
     10: "fp6_gemm_tiled<8,2,8>", 11: "fp6_gemm_tiled<4,2,8>", 12: "fp6_gemm_ksplit<16 waves>",
     13: "fp6_gemm_kslice", 14: "fp6_gemm_xlds<2,4,4>", 15: "fp6_gemm_xlds<1,4,4>",
     16: "fp6_gemm_xlds<2,4,8>", 17: "fp6_gemm_tiledw<4,2,8>", 18: "fp6_gemm_xlds<1,4,8>",
+    19: "fp6_gemm_xlds<2,2,8,MB=2>", 20: "fp6_gemm_xlds<2,2,8,MB=4>", 21: "fp6_gemm_xlds<1,4,8,MB=2>",
+    22: "fp6_gemm_xlds<1,2,8,MB=4>",
 }
 
 

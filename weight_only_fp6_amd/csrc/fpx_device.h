@@ -515,8 +515,12 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
 // (X(t+D) is issued just before W(t+D), at the top of iteration t, and is
 // written to LDS in iteration t+D-1).  Every wait then covers D-1 tiles of
 // work instead of one.
+//
+// MB > 1: a workgroup covers MB groups of 16 columns (X tile MB*16 rows);
+// each k-step of a row block is spliced once and feeds MB MFMAs, so the
+// weights are streamed once for up to 16*MB columns.
 // ---------------------------------------------------------------------------
-template <int F, int A, int D, int NW>
+template <int F, int A, int D, int NW, int MB = 1>
 __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     int64_t mg_base) {
   static_assert(D % 2 == 0, "the LDS slot of a tile is its parity");
   constexpr int kThreads = 64 * NW;
-  constexpr int kChunks = 16 * 32;                      // 16-byte units per X tile
+  constexpr int kChunks = MB * 16 * 32;                 // 16-byte units per X tile
   constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) half8v xs[2][kChunks];
 
@@ -561,10 +565,10 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     int q = i * kThreads + tid;
     if (q >= kChunks) q = kChunks - 1;  // surplus threads duplicate the last unit
     const int rr = q >> 5, c = q & 31;
-    int64_t m = mg * 16 + rr;
+    int64_t m = mg * 16 * MB + rr;
     if (m >= M) m = M - 1;
     xsrc[i] = X + m * K + 8 * c;
-    xdst[i] = rr * 32 + (c ^ rr);
+    xdst[i] = rr * 32 + (c ^ (rr & 15));
   }
   const int64_t klast = kt1 > kt0 ? kt1 - 1 : kt0;
   auto clampk = [&](int64_t t) { return t < klast ? t : klast; };
@@ -581,9 +585,9 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     for (int i = 0; i < kPerThread; ++i) xs[slot][xdst[i]] = xr.v[i];
   };
 
-  float4v acc[A];
+  float4v acc[A * MB];  // row block a, column group b: acc[a * MB + b]
 #pragma unroll
-  for (int i = 0; i < A; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < A * MB; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
   auto load_w = [&](WStage<F, A>& st, int64_t kt) {
 #pragma unroll
     for (int a = 0; a < A; ++a) {
@@ -594,10 +598,14 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
     const half8v* xb = xs[slot];
 #define FP6_XL_STEP(J)                                                                   \
   {                                                                                      \
-    const half8v bf = xb[r * 32 + ((4 * J + g) ^ r)];                                    \
-    _Pragma("unroll") for (int a = 0; a < A; ++a) acc[a] =                               \
-        __builtin_amdgcn_mfma_f32_16x16x32_f16(                                          \
-            Fmt<F>::template step<J>(st.t[a], s2[a]), bf, acc[a], 0, 0, 0); \
+    half8v bf[MB];                                                                       \
+    _Pragma("unroll") for (int b = 0; b < MB; ++b) bf[b] =                               \
+        xb[(b * 16 + r) * 32 + ((4 * J + g) ^ r)];                                       \
+    _Pragma("unroll") for (int a = 0; a < A; ++a) {                                      \
+      const half8v wa = Fmt<F>::template step<J>(st.t[a], s2[a]);                        \
+      _Pragma("unroll") for (int b = 0; b < MB; ++b) acc[a * MB + b] =                   \
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, bf[b], acc[a * MB + b], 0, 0, 0);   \
+    }                                                                                    \
   }
     FP6_XL_STEP(0) FP6_XL_STEP(1) FP6_XL_STEP(2) FP6_XL_STEP(3)
     FP6_XL_STEP(4) FP6_XL_STEP(5) FP6_XL_STEP(6) FP6_XL_STEP(7)
@@ -645,14 +653,15 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 
   if (splits > 1) {
     const int64_t unit = mg * ngroups + rg;
-    float* unit_part = part + unit * static_cast<int64_t>(splits) * (A * 256);
-    if (!splitk_fixup<A>(acc, unit_part, counters + unit, split, splits, lane)) return;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (A * MB * 256);
+    if (!splitk_fixup<A * MB>(acc, unit_part, counters + unit, split, splits, lane)) return;
   }
 #pragma unroll
   for (int a = 0; a < A; ++a) {
     const int64_t nb = rg * A + a;
     if (nb >= nblocks) continue;
-    store_y_block(Y, acc[a], mg * 16 + r, M, N, nb * 16, g);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) store_y_block(Y, acc[a * MB + b], (mg * MB + b) * 16 + r, M, N, nb * 16, g);
   }
 }
 
@@ -1440,11 +1449,11 @@ int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t 
   return FP6_E_VALUE;
 }
 
-template <int F, int A, int D, int NW>
+template <int F, int A, int D, int NW, int MB = 1>
 int launch_xlds(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                 int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
   const int64_t ngroups = fpx_ceil_div(N >> 4, A), gsets = fpx_ceil_div(ngroups, NW);
-  const int64_t mgroups = fpx_ceil_div(M, 16);
+  const int64_t mgroups = fpx_ceil_div(M, 16 * MB);
   const int64_t per_mg = gsets * splits;
   int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
   if (mg_chunk < 1) mg_chunk = 1;
@@ -1457,7 +1466,7 @@ int launch_xlds(const void* X, const void* W, const void* S, void* Y, int64_t M,
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
     int64_t mg_base = mg0;
     void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_xlds<F, A, D, NW>), grid, dim3(64 * NW),
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_xlds<F, A, D, NW, MB>), grid, dim3(64 * NW),
                         args, 0, stream) != hipSuccess)
       return FP6_E_HIP;
   }
@@ -1568,6 +1577,10 @@ int launch_variant(const fpx::LaunchCtx& c) {
     case 16: return launch_xlds<F, 2, 4, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 17: return launch_tiledw<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 18: return launch_xlds<F, 1, 4, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 19: return launch_xlds<F, 2, 2, 8, 2>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 20: return launch_xlds<F, 2, 2, 8, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 21: return launch_xlds<F, 1, 4, 8, 2>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 22: return launch_xlds<F, 1, 2, 8, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     default: return FP6_E_VALUE;
   }
 }

@@ -39,6 +39,10 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kXlds, 2, 1, 8},    // 16: streaming + X in LDS, 2 row blocks/wave, ring 4, 8 waves
     {Kind::kTiled, 2, 4, 8},   // 17: tiled, 256 rows x 64 columns, 8 waves, whole-tile stages
     {Kind::kXlds, 1, 1, 4},    // 18: streaming + X in LDS, 1 row block/wave, ring 4, 8 waves
+    {Kind::kXlds, 2, 2, 2},    // 19: streaming + X in LDS, 2 row blocks x 32 columns per wave, ring 2, 8 waves
+    {Kind::kXlds, 2, 4, 2},    // 20: streaming + X in LDS, 2 row blocks x 64 columns per wave, ring 2, 8 waves
+    {Kind::kXlds, 1, 2, 4},    // 21: streaming + X in LDS, 1 row block x 32 columns per wave, ring 4, 8 waves
+    {Kind::kXlds, 1, 4, 2},    // 22: streaming + X in LDS, 1 row block x 64 columns per wave, ring 2, 8 waves
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kKsMaxTiles = 32;      // k-split kernels: K <= 8192

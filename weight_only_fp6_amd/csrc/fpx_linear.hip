@@ -134,8 +134,8 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     // workgroup once there are at
     // least 7 row blocks per CU (each X tile shared by twice the waves, and
     // one workgroup per CU instead of a 1-or-2 mix: Llama-70B MLP 38 -> 35
-    // us), else 4.  Above M = 16 the tiled kernels: 64 columns with
-    // whole-tile stages up to M = 64, else 128 columns with half-tile stages.
+    // us), else 4.  Up to M = 64 the streaming kernel with X in LDS on 32
+    // or 64 columns; above, the tiled kernel (128 columns, half-tile stages).
     const bool one_rb_per_cu = (N >> 4) <= cus;
     // Longer K (split count not forced): the 16-wave k-split kernel with K
     // split across workgroups (at most 16 k-tiles per split, one per wave)
@@ -157,6 +157,22 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
       return p;
     } else if (M <= 16) {
       p.variant = (N >> 4) >= 7 * static_cast<int64_t>(cus) ? 18 : 15;
+    } else if (M <= 64 && splits == 0) {
+      // 17..64 columns: the streaming kernel with X in LDS on 32 (M <= 32)
+      // or 64 columns per workgroup, each k-step spliced once for all of its
+      // column groups; 1 row block per wave while that leaves at most half a
+      // workgroup per CU, else 2; K split while a whole round of workgroups
+      // fits on the CUs, at least 4 k-tiles per split (measured against the
+      // tiled kernels: 32x21504x7168 39.8 -> 30 us, 64x8192x8192 30.3 ->
+      // 22.0 us, OPT-30B QKV M=64 40.9 -> 39.6 us).
+      const int64_t g1 = ceil_div(N >> 4, 8), g2 = ceil_div(ceil_div(N >> 4, 2), 8);
+      const bool one_rb = g1 <= cus / 2;
+      p.variant = M <= 32 ? (one_rb ? 21 : 19) : (one_rb ? 22 : 20);
+      int64_t sp = cus / (one_rb ? g1 : g2);
+      if (sp > ktiles / 4) sp = ktiles / 4;
+      if (sp < 1) sp = 1;
+      p.splits = static_cast<int>(sp);
+      return p;
     } else if (M <= 64) {
       p.variant = 17;
     } else {
