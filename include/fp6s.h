@@ -84,8 +84,11 @@ int fp6s_linear(const void* X, const void* packed_W, const void* scales, void* Y
  * rows x 128 columns; 6 = k-split (8-wave workgroups, one 512-k tile per
  * wave and K-split, each workgroup's row blocks all in flight; M <= 16, at
  * most K = 4096 per split and 8 row blocks per workgroup, i.e. N/16 <=
- * 8 * (CUs / splits)).  Variants 2-5 handle any M.  splits: 0 = automatic,
- * else K-splits across workgroups (1..K/512; variants 2-6).
+ * 8 * (CUs / splits)); 7 = streaming with X shared through LDS, 8 waves,
+ * 1 row block x 32 columns per wave (each spliced k-step feeds both column
+ * groups); 8 = the same with 2 row blocks per wave.  Variants 2-5, 7 and 8
+ * handle any M.  splits: 0 = automatic, else K-splits across workgroups
+ * (1..K/512; variants 2-8).
  * Errors: as fp6_linear_plan, plus FP6_E_VALUE for a shape variant 1 or 6
  * does not cover.
  */
@@ -93,7 +96,7 @@ int fp6s_linear_plan(const void* X, const void* packed_W, const void* scales, vo
                      int64_t N, int64_t K, int variant, int splits, void* stream);
 
 /* fp6s_linear_plan_query -- host: the schedule fp6s_linear would use for
- * (M, N, K) on the current device (*variant 1..6, *splits).  One HIP query.
+ * (M, N, K) on the current device (*variant 1..8, *splits).  One HIP query.
  * Errors: FP6_E_NULL, FP6_E_SHAPE (M >= 1, K % 512 == 0), FP6_E_HIP. */
 int fp6s_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits);
 

@@ -27,7 +27,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import weight_only_fp6_amd as fp6  # noqa: E402
 
 DEV = torch.device("cuda:0")
-VARIANTS = (0, 2, 3, 4, 5)     # any M; 1 (k-slice) and 6 (k-split) only for M <= 16
+VARIANTS = (0, 2, 3, 4, 5, 7, 8)     # any M; 1 (k-slice) and 6 (k-split) only for M <= 16
 KSLICE = 1
 KSPLIT = 6
 
@@ -88,7 +88,7 @@ def test_linear_forced_splits():
     p = SpPrepared(16, 4096, 8192, seed_w=71, seed_x=72, sample=256)
     X, packed, s = p.to_device()
     cols = torch.from_numpy(p.rows).to(DEV)
-    for variant in (2, 3, 4, 5):
+    for variant in (2, 3, 4, 5, 7, 8):
         for splits in (1, 2, 3, 5, 16):
             Y = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits)
             torch.cuda.synchronize()
@@ -129,7 +129,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     _, packed, s = p.to_device()
     want = p.wdq_ref[:, ks].T.astype(np.float64)
     for variant, splits in [(0, 0), (1, 0), (2, 1), (2, 3), (3, 1), (3, 2), (4, 1), (4, 2), (5, 1), (5, 4),
-                            (6, 0), (6, 2), (6, 4)]:
+                            (6, 0), (6, 2), (6, 4), (7, 1), (7, 3), (8, 2)]:
         Y = fp6.sparse_linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (variant, splits)
@@ -179,7 +179,7 @@ def test_sparse_linear_adversarial_rows(M):
     out = fp6.sparse_dequant(packed, sd, N, K)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), wdq.view(np.uint16))
-    for variant, splits in [(0, 0), (2, 2), (3, 1), (4, 2), (5, 1)] + ([(KSLICE, 0), (KSPLIT, 0), (KSPLIT, 3)] if M <= 16 else []):
+    for variant, splits in [(0, 0), (2, 2), (3, 1), (4, 2), (5, 1), (7, 2), (8, 1)] + ([(KSLICE, 0), (KSPLIT, 0), (KSPLIT, 3)] if M <= 16 else []):
         Y = fp6.sparse_linear_plan(Xd, packed, sd, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         _assert_tol(Y, y_ref, what=(M, variant, splits))

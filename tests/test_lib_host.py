@@ -384,7 +384,7 @@ def test_sparse_errors():
     assert L.fp6s_linear(A, A, A, A, 4, 16, 768, None) == 2          # K % 512
     assert L.fp6s_linear(None, None, None, None, 0, 16, 512, None) == 0
     assert L.fp6s_linear(A + 8, A, A, A, 4, 16, 512, None) == 3
-    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 7, 0, None) == 8
+    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 9, 0, None) == 8
     assert L.fp6s_linear_plan(A, A, A, A, 17, 16, 512, 6, 0, None) == 8     # k-split: M <= 16
     assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 9 * 512, 6, 1, None) == 8  # <= 8 tiles per split
     assert L.fp6s_linear_plan(A, A, A, A, 17, 16, 512, 1, 0, None) == 8    # k-slice: M <= 16

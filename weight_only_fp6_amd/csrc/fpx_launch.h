@@ -78,7 +78,7 @@ int dequant_e2m1(const void* W, const void* S, void* W16, int64_t N, int64_t K, 
 // 2:4-sparse FP6 (fp6s_*): kernel configurations of fp6s_linear_plan.
 enum SparseVariant : int {
   kSpAuto = 0, kSpKslice = 1, kSpXlds1 = 2, kSpXlds2 = 3, kSpTiled4 = 4, kSpTiled8 = 5, kSpKsplit = 6,
-  kNumSpVariants = 7
+  kSpXldsMB1 = 7, kSpXldsMB2 = 8, kNumSpVariants = 9
 };
 constexpr int kSpKsliceMaxTiles = 16;  // k-slice: one 512-k tile per wave, 16 waves
 constexpr int kSpKsplitMaxTiles = 8;   // k-split: one 512-k tile per wave and K-split, 8 waves

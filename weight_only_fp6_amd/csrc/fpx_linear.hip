@@ -304,6 +304,10 @@ int dequant_impl(int format, const void* packed_W, const void* scales, void* W16
 // across workgroups while a whole extra round fits on the CUs.
 bool sp_tiled(int v) { return v == fpx::kSpTiled4 || v == fpx::kSpTiled8; }
 int sp_tile_b(int v) { return v == fpx::kSpTiled8 ? 8 : 4; }
+// Streaming (X in LDS) variants: row blocks per wave, 16-column groups per
+// workgroup.
+int sp_xlds_a(int v) { return v == fpx::kSpXlds2 || v == fpx::kSpXldsMB2 ? 2 : 1; }
+int sp_xlds_mb(int v) { return v == fpx::kSpXldsMB1 || v == fpx::kSpXldsMB2 ? 2 : 1; }
 
 Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
   Plan p;
@@ -313,14 +317,30 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
   const int ks_splits = static_cast<int>(ceil_div(ktiles, fpx::kSpKsplitMaxTiles));
   const bool ks_fits = ks_splits <= 8 &&
                        fpx::sp_ksplit_rows_per_wg(N, cus, ks_splits) <= fpx::kSpKsplitMaxRows;
+  // 17 <= M <= 32: the streaming kernel on 32 columns (8 waves), 1 row
+  // block per wave while that leaves at most half a workgroup per CU, else
+  // 2, K split while a whole round of workgroups fits on the CUs (at least
+  // 1024 of K per split), as for the dense kernels.
+  const int64_t g1 = ceil_div(N >> 4, 8), g2 = ceil_div(ceil_div(N >> 4, 2), 8);
+  const bool mb_one_rb = g1 <= cus / 2;
+  auto mb_splits = [&](int v) {
+    int64_t sp = cus / (sp_xlds_a(v) == 1 ? g1 : g2);
+    if (sp > ktiles / 2) sp = ktiles / 2;
+    return static_cast<int>(sp < 1 ? 1 : sp);
+  };
   if (variant == fpx::kSpAuto) {
     if (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles) p.variant = fpx::kSpKslice;
     else if (M <= 16 && splits == 0 && ks_fits) p.variant = fpx::kSpKsplit;
     else if (M <= 16) p.variant = fpx::kSpXlds1;
+    else if (M <= 32) p.variant = mb_one_rb ? fpx::kSpXldsMB1 : fpx::kSpXldsMB2;
     else if (M <= 64) p.variant = fpx::kSpTiled4;
     else p.variant = fpx::kSpTiled8;
   } else {
     p.variant = variant;
+  }
+  if (sp_xlds_mb(p.variant) > 1) {
+    p.splits = splits > 0 ? splits : mb_splits(p.variant);
+    return p;
   }
   if (p.variant == fpx::kSpKslice) {
     p.splits = 1;
@@ -339,8 +359,7 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
     const int64_t wgs = ceil_div(M, 16 * sp_tile_b(p.variant)) * ceil_div(N >> 4, 16);
     s = cus / wgs;
   } else {
-    const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
-    const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, a);
+    const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, sp_xlds_a(p.variant));
     s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
   }
   if (s > ktiles / 2) s = ktiles / 2;
@@ -379,9 +398,9 @@ int sparse_linear_impl(const void* X, const void* W, const void* S, void* Y, int
       units = ceil_div(M, 16 * sp_tile_b(p.variant)) * ceil_div(N >> 4, 16) * 8;
       floats = 2 * sp_tile_b(p.variant) * 256;
     } else {
-      const int a = p.variant == fpx::kSpXlds2 ? 2 : 1;
-      units = ceil_div(M, 16) * ceil_div(N >> 4, a);
-      floats = a * 256;
+      const int a = sp_xlds_a(p.variant), mb = sp_xlds_mb(p.variant);
+      units = ceil_div(M, 16 * mb) * ceil_div(N >> 4, a);
+      floats = a * mb * 256;
     }
     const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
     st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);

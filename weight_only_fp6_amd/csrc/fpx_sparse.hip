@@ -198,14 +198,14 @@ __global__ __launch_bounds__(512) void sp_gemm_ksplit(
 // 16 KB) through a 3-slot LDS ring, rows XOR-swizzled in 16-byte units; one
 // barrier per tile.  Split-K fix-up as for the dense kernels.
 // ---------------------------------------------------------------------------
-template <int A, int D, int NW>
+template <int A, int D, int NW, int MB = 1>
 __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
     unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
     int64_t mg_base) {
   constexpr int kThreads = 64 * NW;
-  constexpr int kChunks = 16 * 64;  // 16-byte units per X tile
+  constexpr int kChunks = MB * 16 * 64;  // 16-byte units per X tile (MB*16 rows x 512 k)
   constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) half8v xs[3][kChunks];
 
@@ -242,10 +242,10 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
     int q = i * kThreads + tid;
     if (q >= kChunks) q = kChunks - 1;  // surplus threads duplicate the last unit
     const int rr = q >> 6, c = q & 63;
-    int64_t m = mg * 16 + rr;
+    int64_t m = mg * 16 * MB + rr;
     if (m >= M) m = M - 1;
     xsrc[i] = X + m * K + 8 * c;
-    xdst[i] = rr * 64 + (c ^ rr);
+    xdst[i] = rr * 64 + (c ^ (rr & 15));
   }
   half8v xstage[kPerThread];
   const int64_t klast = kt1 > kt0 ? kt1 - 1 : kt0;
@@ -260,9 +260,9 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
     for (int i = 0; i < kPerThread; ++i) xs[slot][xdst[i]] = xstage[i];
   };
 
-  float4v acc[A];
+  float4v acc[A * MB];  // row block a, column group b: acc[a * MB + b]
 #pragma unroll
-  for (int i = 0; i < A; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < A * MB; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
   struct Stage {
     SpTile t[A];
   };
@@ -272,6 +272,9 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
   };
   auto mac = [&](const Stage& st, int slot) {
     const half8v* xb = xs[slot];
+    // One column group: one B fragment per k-step (the form measured for
+    // the M <= 16 default); several: each spliced k-step feeds MB MFMAs.
+    if constexpr (MB == 1) {
 #define FP6S_XL_STEP(J)                                                                  \
   {                                                                                      \
     const int c0 = (8 * J + 2 * g) ^ r;                                                  \
@@ -280,8 +283,29 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
                                                11, 12, 13, 14, 15);                      \
     _Pragma("unroll") for (int a = 0; a < A; ++a) acc[a] = sp_mac<J>(st.t[a], s2[a], bf, acc[a]); \
   }
-    FP6S_XL_STEP(0) FP6S_XL_STEP(1) FP6S_XL_STEP(2) FP6S_XL_STEP(3)
-    FP6S_XL_STEP(4) FP6S_XL_STEP(5) FP6S_XL_STEP(6) FP6S_XL_STEP(7)
+      FP6S_XL_STEP(0) FP6S_XL_STEP(1) FP6S_XL_STEP(2) FP6S_XL_STEP(3)
+      FP6S_XL_STEP(4) FP6S_XL_STEP(5) FP6S_XL_STEP(6) FP6S_XL_STEP(7)
+    } else {
+#define FP6S_XL_STEPM(J)                                                                  \
+  {                                                                                      \
+    const int c0 = (8 * J + 2 * g) ^ r;                                                  \
+    half16v bf[MB];                                                                      \
+    _Pragma("unroll") for (int b = 0; b < MB; ++b) {                                     \
+      const half8v lo = xb[(b * 16 + r) * 64 + c0], hi = xb[(b * 16 + r) * 64 + (c0 ^ 1)]; \
+      bf[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, \
+                                      14, 15);                                           \
+    }                                                                                    \
+    _Pragma("unroll") for (int a = 0; a < A; ++a) {                                      \
+      const half8v wa = Fmt<kE3M2>::template step<J>(st.t[a].w, s2[a]);                  \
+      _Pragma("unroll") for (int b = 0; b < MB; ++b) acc[a * MB + b] =                   \
+          __builtin_amdgcn_smfmac_f32_16x16x64_f16(wa, bf[b], acc[a * MB + b],           \
+                                                   static_cast<int>(st.t[a].idx[J >> 1]), 0, J & 1); \
+    }                                                                                    \
+  }
+      FP6S_XL_STEPM(0) FP6S_XL_STEPM(1) FP6S_XL_STEPM(2) FP6S_XL_STEPM(3)
+      FP6S_XL_STEPM(4) FP6S_XL_STEPM(5) FP6S_XL_STEPM(6) FP6S_XL_STEPM(7)
+    }
+#undef FP6S_XL_STEPM
 #undef FP6S_XL_STEP
   };
 
@@ -332,14 +356,15 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
 
   if (splits > 1) {
     const int64_t unit = mg * ngroups + rg;
-    float* unit_part = part + unit * static_cast<int64_t>(splits) * (A * 256);
-    if (!splitk_fixup<A>(acc, unit_part, counters + unit, split, splits, lane)) return;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (A * MB * 256);
+    if (!splitk_fixup<A * MB>(acc, unit_part, counters + unit, split, splits, lane)) return;
   }
 #pragma unroll
   for (int a = 0; a < A; ++a) {
     const int64_t nb = rg * A + a;
     if (nb >= nblocks) continue;
-    store_y_block(Y, acc[a], mg * 16 + r, M, N, nb * 16, g);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) store_y_block(Y, acc[a * MB + b], (mg * MB + b) * 16 + r, M, N, nb * 16, g);
   }
 }
 
@@ -625,10 +650,10 @@ int launch_sp_ksplit(const fpx::LaunchCtx& c) {
   return hipLaunchKernel(kern, grid, dim3(512), args, 0, c.stream) == hipSuccess ? FP6_OK : FP6_E_HIP;
 }
 
-template <int A, int D, int NW>
+template <int A, int D, int NW, int MB = 1>
 int launch_sp_xlds(const fpx::LaunchCtx& c) {
   const int64_t ngroups = fpx_ceil_div(c.N >> 4, A), gsets = fpx_ceil_div(ngroups, NW);
-  const int64_t mgroups = fpx_ceil_div(c.M, 16);
+  const int64_t mgroups = fpx_ceil_div(c.M, 16 * MB);
   const int64_t per_mg = gsets * c.splits;
   int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
   if (mg_chunk < 1) mg_chunk = 1;
@@ -645,7 +670,7 @@ int launch_sp_xlds(const fpx::LaunchCtx& c) {
     const dim3 grid(static_cast<unsigned>(nmg * per_mg));
     int64_t mg_base = mg0;
     void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&sp_gemm_xlds<A, D, NW>), grid, dim3(64 * NW),
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&sp_gemm_xlds<A, D, NW, MB>), grid, dim3(64 * NW),
                         args, 0, c.stream) != hipSuccess)
       return FP6_E_HIP;
   }
@@ -695,6 +720,8 @@ int launch_sparse(const LaunchCtx& c) {
     case kSpTiled4: return launch_sp_tiled<4, 2, 8>(c);
     case kSpTiled8: return launch_sp_tiled<8, 2, 8>(c);
     case kSpKsplit: return launch_sp_ksplit(c);
+    case kSpXldsMB1: return launch_sp_xlds<1, 4, 8, 2>(c);
+    case kSpXldsMB2: return launch_sp_xlds<2, 2, 8, 2>(c);
     default: return FP6_E_VALUE;
   }
 }
