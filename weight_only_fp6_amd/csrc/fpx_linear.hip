@@ -122,6 +122,9 @@ void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_
 
 // The schedule depends on the shape only: the narrower formats read fewer
 // bytes per tile but run the same kernels with the same work units.
+// Waves per workgroup of the X-in-LDS streaming kernels.
+int xlds_waves(int variant) { return variant == 14 || variant == 15 ? 4 : 8; }
+
 Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int splits) {
   Plan p;
   const int64_t ktiles = K >> 8;
@@ -195,7 +198,15 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     return p;
   }
   int64_t s;
-  if (c.kind == Kind::kTiled) {
+  if (c.kind == Kind::kXlds) {
+    // One workgroup per CU: split K while a whole extra round of workgroups
+    // fits (the waves of a workgroup share its X tiles; counting waves
+    // instead left half the CUs idle on the Llama-70B down projection,
+    // 16x8192x28672: 58.4 -> 39.6 us), at least 4 k-tiles per split.
+    const int64_t wgs = ceil_div(M, 16 * c.mb) * ceil_div(ceil_div(N >> 4, c.a), xlds_waves(p.variant));
+    s = cus / wgs;
+    if (s > ktiles / 4) s = ktiles / 4;
+  } else if (c.kind == Kind::kTiled) {
     // One workgroup per CU: split K while a whole extra round of workgroups
     // fits on the CUs (rounding down: a partial second round costs more than
     // it gains), keeping at least 2 k-tiles per split.
@@ -359,8 +370,10 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
     const int64_t wgs = ceil_div(M, 16 * sp_tile_b(p.variant)) * ceil_div(N >> 4, 16);
     s = cus / wgs;
   } else {
-    const int64_t units = ceil_div(M, 16) * ceil_div(N >> 4, sp_xlds_a(p.variant));
-    s = units >= 2 * static_cast<int64_t>(cus) ? 1 : ceil_div(static_cast<int64_t>(cus) * 4, units);
+    // The 4-wave streaming kernel: one workgroup per CU, K split while a
+    // whole extra round of workgroups fits.
+    const int64_t wgs = ceil_div(M, 16) * ceil_div(ceil_div(N >> 4, sp_xlds_a(p.variant)), 4);
+    s = cus / wgs;
   }
   if (s > ktiles / 2) s = ktiles / 2;
   if (s > 64) s = 64;
