@@ -140,14 +140,37 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     // us), else 4.  Up to M = 64 the streaming kernel with X in LDS on 32
     // or 64 columns; above, the tiled kernel (128 columns, half-tile stages).
     const bool one_rb_per_cu = (N >> 4) <= cus;
-    // Longer K (split count not forced): the 16-wave k-split kernel with K
-    // split across workgroups (at most 16 k-tiles per split, one per wave)
-    // while its busiest workgroup has at most 6 row blocks, all in flight at
-    // once (Llama-70B attention output 16x8192x8192: 20.0 -> 15.2 us).
-    const int64_t ks_splits = ceil_div(ktiles, 16);
-    const int64_t ks_per_split = cus / ks_splits;
-    const bool ks_fits = splits == 0 && ktiles > 16 && ks_splits <= 8 && ks_per_split >= 1 &&
-                         ceil_div(N >> 4, ks_per_split) <= 6;
+    // Longer K (split count not forced): the k-split kernel with K split
+    // across workgroups, one k-tile per wave and split, all row blocks of a
+    // workgroup in flight (Llama-70B attention output 16x8192x8192: 20.0 ->
+    // 15.2 us).  Candidates: 16 or 8 waves, the fewest splits that fit and
+    // one more.  A workgroup's work is its straight-line form's row-block
+    // count times its waves (idle waves of a short split still load a
+    // stand-in tile); the cheapest wins, ties to fewer splits, and only up
+    // to 6 row blocks x 16 waves (beyond, the streaming kernel wins).
+    // 16x5120x5120: 8 waves x 3 splits 9.8 us against 16 x 2 11.0 us.
+    int ks_variant = 0;
+    int64_t ks_splits = 0, ks_cost = 0;
+    if (splits == 0 && ktiles > 16) {
+      for (const int wk : {16, 8}) {
+        const int64_t s0 = ceil_div(ktiles, wk);
+        for (int64_t sp = s0; sp <= s0 + 1 && sp <= 8; ++sp) {
+          const int64_t per_split = cus / sp;
+          if (per_split < 1) continue;
+          const int64_t rows = ceil_div(N >> 4, per_split);
+          if (rows > 8) continue;
+          const int64_t form = rows <= 4 ? rows : (rows <= 6 ? 6 : 8);
+          const int64_t cost = form * wk;
+          if (cost > 6 * 16) continue;
+          if (ks_variant == 0 || cost < ks_cost || (cost == ks_cost && sp < ks_splits)) {
+            ks_variant = wk == 16 ? 12 : 9;
+            ks_splits = sp;
+            ks_cost = cost;
+          }
+        }
+      }
+    }
+    const bool ks_fits = ks_variant != 0;
     if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
       p.variant = 13;
     } else if (M <= 16 && ktiles <= 8) {
@@ -155,7 +178,7 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     } else if (M <= 16 && ktiles <= 16) {
       p.variant = 12;
     } else if (M <= 16 && ks_fits) {
-      p.variant = 12;
+      p.variant = ks_variant;
       p.splits = static_cast<int>(ks_splits);
       return p;
     } else if (M <= 16) {
