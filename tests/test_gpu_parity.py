@@ -365,3 +365,42 @@ def test_linear_large_n_or_k(M, N, K):
     Y = fp6.linear(X, packed, s, N, K)
     torch.cuda.synchronize()
     _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(M, N, K))
+
+
+# ----------------------------------------------------------------------------
+# Automatic plans (schedule rules) on a 256-CU MI355X
+# ----------------------------------------------------------------------------
+DENSE_PLANS = [
+    ((1, 4096, 4096), (KSLICE, 1)),      # one row block per CU: k-slice
+    ((16, 4096, 2048), (KSLICE, 1)),
+    ((16, 8192, 2048), (KSPLIT, 1)),     # K <= 2048: 8-wave k-split
+    ((16, 11008, 4096), (KSPLIT16, 1)),  # 3 row blocks per workgroup in flight
+    ((16, 8192, 8192), (KSPLIT16, 2)),   # K split across workgroups
+    ((16, 5120, 5120), (KSPLIT, 3)),     # 8 waves: fewer idle waves on 10-tile splits
+    ((16, 4096, 11008), (KSPLIT16, 3)),
+    ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups
+    ((16, 8192, 28672), (15, 2)),        # split while a whole extra round fits
+    ((32, 21504, 7168), (19, 3)),        # 32 columns per workgroup
+    ((64, 4096, 4096), (22, 4)),         # 64 columns, 1 row block per wave
+    ((64, 21504, 7168), (20, 3)),
+    ((128, 21504, 7168), (10, 3)),       # tiled
+]
+SPARSE_PLANS = [
+    ((1, 4096, 4096), (1, 1)),
+    ((16, 11008, 4096), (6, 1)),
+    ((16, 8192, 8192), (6, 2)),
+    ((16, 28672, 8192), (2, 1)),
+    ((32, 21504, 7168), (8, 3)),
+    ((64, 21504, 7168), (4, 3)),
+]
+
+
+def test_automatic_plans_on_256_cus():
+    # The schedule rules picked from the measurements; the rules depend on
+    # the CU count, so they are pinned for the 256-CU part only.
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("plans pinned for 256 CUs")
+    for (M, N, K), want in DENSE_PLANS:
+        assert fp6.plan_query(M, N, K) == want, (M, N, K)
+    for (M, N, K), want in SPARSE_PLANS:
+        assert fp6.sparse_plan_query(M, N, K) == want, (M, N, K)
