@@ -666,16 +666,21 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 }
 
 // ---------------------------------------------------------------------------
-// K-split persistent kernel (memory-bound regime, M <= 16,
-// K <= kKsWaves*KTW*256).  One workgroup of kKsWaves (8 or 16) waves per CU.
-// Wave w owns the k-tiles [w*KT/W, (w+1)*KT/W) (W = kKsWaves) for the whole
-// kernel, so its X fragments (16 columns x
-// at most KTW k-tiles) are staged once, through LDS, into registers.  The workgroup walks
-// the row blocks nb = blockIdx.x, +gridDim.x, ...; for each, every wave
-// multiplies its k-slice (packed tiles prefetched one row block ahead) and
-// the partial 16x16 tiles are summed through LDS in wave order
-// (deterministic) by wave 0, which stores fp16 Y.  No global workspace, no
-// X re-reads, all k-slices of a row block stream concurrently.
+// K-split persistent kernel (memory-bound regime, M <= 16, at most
+// kKsWaves*KTW k-tiles per K-split).  One workgroup of kKsWaves (8 or 16)
+// waves per CU and K-split.  Wave w owns the k-tiles [w*KT/W, (w+1)*KT/W)
+// of its split (W = kKsWaves) for the whole kernel, so its X fragments (16
+// columns x at most KTW k-tiles) are staged once, through LDS, into
+// registers.  The workgroup walks the row blocks b, b + G, ... (G
+// workgroups per split).  With one tile per wave and 2..8 row blocks per
+// workgroup (P) the code is straight-line: up to 4 row blocks' tiles in
+// flight, every wave multiplies all of its row blocks into partial slots,
+// and after one barrier wave i sums row block i; otherwise a loop
+// prefetches one row block ahead and wave 0 sums each row block after a
+// barrier.  The 16 partial tiles of a row block are summed in wave order
+// (deterministic); with K-splits the sum goes through the fixed-order
+// split-K fix-up.  No X re-reads, all k-slices of a row block stream
+// concurrently.
 // ---------------------------------------------------------------------------
 template <int F, int KTW, int kKsWaves, bool M1 = false, int P = 0>
 __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(

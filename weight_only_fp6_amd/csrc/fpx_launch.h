@@ -29,7 +29,7 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kTiled, 4, 8, 4},   // 6: tiled, 256 rows x 128 columns, 4 waves x 4 row blocks
     {Kind::kStream, 1, 1, 8},  // 7: streaming, 1 row block per wave, 16 columns, ring depth 8
     {Kind::kStream, 2, 1, 6},  // 8: streaming, 2 row blocks per wave, 16 columns, ring depth 6
-    {Kind::kKsplit, 1, 1, 8},  // 9: k-split persistent, M <= 16, K <= 8192 (X in registers)
+    {Kind::kKsplit, 1, 1, 8},  // 9: k-split persistent, M <= 16, K <= 8192 per K-split (X in registers)
     {Kind::kTiled, 2, 8, 8},   // 10: tiled, 256 rows x 128 columns, 8 waves x 2 row blocks
     {Kind::kTiled, 2, 4, 8},   // 11: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks
     {Kind::kKsplit, 1, 1, 16}, // 12: k-split persistent with 16 waves per workgroup
