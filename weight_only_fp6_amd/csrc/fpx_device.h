@@ -711,7 +711,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   auto red_at = [&](int buf, int w) { return reinterpret_cast<float4v*>(&xw[w][64 * buf]); };
 
   // X of this wave's k-slice, loaded coalesced: instruction i covers rows
-  // 2i, 2i+1 (512 B each), lane -> 16-byte unit xc of row xr[i].  Rows
+  // 2i, 2i+1 (512 B each), lane -> 16-byte unit xc of row 2i + lane / 32.  Rows
   // beyond M repeat row M-1 (their accumulator columns are never stored).
   // Fragment loads straight from global memory touch 16 rows per
   // instruction, which costs the L1/L2 path several times the bytes.  With
