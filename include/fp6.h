@@ -135,6 +135,11 @@ int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
  * deterministic: split partials are summed in a fixed order.
  * Concurrent calls on different streams are safe; concurrent calls on the
  * same stream from several host threads are serialised by the stream.
+ * HIP graph capture: nothing is allocated or cleared per call once the
+ * stream's workspace exists, so make one call with the same shape and plan
+ * on the capturing stream before capturing; the captured launch keeps the
+ * workspace's address, so do not grow it (a larger split-K plan on that
+ * stream) while the graph is in use.
  */
 int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
                int64_t M, int64_t N, int64_t K, void* stream);
