@@ -292,6 +292,44 @@ def test_linear_on_side_stream_matches_default_stream():
     _assert_tol(b, p.y_ref)
 
 
+def test_split_k_plans_run_concurrently_on_several_streams():
+    # Each stream has its own split-K workspace: split plans queued on four
+    # streams without synchronisation in between (dense k-split, streaming
+    # and tiled fix-ups, sparse k-split) must each equal their one-stream
+    # result bit for bit.
+    cases = [(16, 8192, 8192, 0, 0, False), (5, 2048, 11008, 15, 3, False),
+             (128, 2048, 7168, 10, 3, False), (16, 8192, 8192, 0, 0, True)]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    prepared = []
+    for i, (M, N, K, v, sp, sparse) in enumerate(cases):
+        W = synth.weights(N, K, 820 + i)
+        X = torch.from_numpy(synth.activations(M, K, 830 + i)).to(DEV)
+        if sparse:
+            c, pos, sc = fp6.prune_quantize(W)
+            P = torch.from_numpy(fp6.sparse_prepack(c, pos, sc, K)).to(DEV)
+            run = fp6.sparse_linear_plan
+        else:
+            c, sc = fp6.quantize_rows(W)
+            P = torch.from_numpy(fp6.prepack(c, sc)).to(DEV)
+            run = fp6.linear_plan
+        S = torch.from_numpy(sc.copy()).to(DEV)
+        want = run(X, P, S, N, K, variant=v, splits=sp).clone()
+        prepared.append((run, X, P, S, N, K, v, sp, want))
+    torch.cuda.synchronize()
+    outs = [[] for _ in cases]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for rep in range(6):
+        for i, (run, X, P, S, N, K, v, sp, want) in enumerate(prepared):
+            st = streams[(i + rep) % len(streams)]
+            with torch.cuda.stream(st):
+                outs[i].append(run(X, P, S, N, K, variant=v, splits=sp, stream=st))
+    torch.cuda.synchronize()
+    for i, (run, X, P, S, N, K, v, sp, want) in enumerate(prepared):
+        for rep, y in enumerate(outs[i]):
+            assert torch.equal(y.view(torch.int16), want.view(torch.int16)), (cases[i], rep)
+
+
 def test_release_then_reuse_and_grow_workspace():
     # The split-K workspace is allocated on first need, grown on demand and
     # freed by release(); a later split call must allocate it again and give
