@@ -417,6 +417,7 @@ DENSE_PLANS = [
     ((16, 5120, 5120), (KSPLIT, 3)),     # 8 waves: fewer idle waves on 10-tile splits
     ((16, 4096, 11008), (KSPLIT16, 3)),
     ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups
+    ((16, 57344, 8192), (16, 1)),        # 2 row blocks per wave: one round instead of 1.75
     ((16, 8192, 28672), (15, 2)),        # split while a whole extra round fits
     ((32, 21504, 7168), (19, 3)),        # 32 columns per workgroup
     ((64, 4096, 4096), (22, 4)),         # 64 columns, 1 row block per wave

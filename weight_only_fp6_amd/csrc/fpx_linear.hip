@@ -182,7 +182,12 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
       p.splits = static_cast<int>(ks_splits);
       return p;
     } else if (M <= 16) {
-      p.variant = (N >> 4) >= 7 * static_cast<int64_t>(cus) ? 18 : 15;
+      // 2 row blocks per wave once that fits one round of 8-wave workgroups
+      // and 1 per wave would take almost two (fused Llama-70B gate/up,
+      // 16x57344x8192: 69.7 -> 67.0 us).
+      const int64_t nb = N >> 4, c = cus;
+      if (nb >= 14 * c && ceil_div(nb, 16) <= c) p.variant = 16;
+      else p.variant = nb >= 7 * c ? 18 : 15;
     } else if (M <= 64 && splits == 0) {
       // 17..64 columns: the streaming kernel with X in LDS on 32 (M <= 32)
       // or 64 columns per workgroup, each k-step spliced once for all of its
