@@ -418,7 +418,7 @@ DENSE_PLANS = [
     ((16, 4096, 11008), (KSPLIT16, 3)),
     ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups
     ((16, 57344, 8192), (16, 1)),        # 2 row blocks per wave: one round instead of 1.75
-    ((16, 8192, 28672), (15, 2)),        # split while a whole extra round fits
+    ((16, 8192, 28672), (14, 4)),        # 2 row blocks per wave, split while a whole round fits
     ((32, 21504, 7168), (19, 3)),        # 32 columns per workgroup
     ((64, 4096, 4096), (22, 4)),         # 64 columns, 1 row block per wave
     ((64, 21504, 7168), (20, 3)),
@@ -429,6 +429,7 @@ SPARSE_PLANS = [
     ((16, 11008, 4096), (6, 1)),
     ((16, 8192, 8192), (6, 2)),
     ((16, 28672, 8192), (2, 1)),
+    ((16, 8192, 28672), (3, 4)),
     ((32, 21504, 7168), (8, 3)),
     ((64, 21504, 7168), (4, 3)),
 ]

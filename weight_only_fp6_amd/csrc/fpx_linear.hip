@@ -185,9 +185,13 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
       // 2 row blocks per wave once that fits one round of 8-wave workgroups
       // and 1 per wave would take almost two (fused Llama-70B gate/up,
       // 16x57344x8192: 69.7 -> 67.0 us).
+      // With at most half a 4-wave workgroup per CU (K split anyway), 2 row
+      // blocks per wave and twice the splits (Llama-70B down projection,
+      // 16x8192x28672: 39.1 -> 37.8 us).
       const int64_t nb = N >> 4, c = cus;
       if (nb >= 14 * c && ceil_div(nb, 16) <= c) p.variant = 16;
-      else p.variant = nb >= 7 * c ? 18 : 15;
+      else if (nb >= 7 * c) p.variant = 18;
+      else p.variant = ceil_div(nb, 4) <= c / 2 ? 14 : 15;
     } else if (M <= 64 && splits == 0) {
       // 17..64 columns: the streaming kernel with X in LDS on 32 (M <= 32)
       // or 64 columns per workgroup, each k-step spliced once for all of its
@@ -338,7 +342,9 @@ int dequant_impl(int format, const void* packed_W, const void* scales, void* W16
 // 2:4-sparse FP6.  M <= 16: the k-slice kernel while every row block has its
 // own CU and K fits one 512-k tile per wave, then the k-split kernel while
 // it has at most 8 row blocks per workgroup, else the streaming kernel with
-// X in LDS, split towards ~4 waves per CU like the dense one.  M > 16: the
+// X in LDS (2 row blocks per wave when 1 would leave at most half a
+// workgroup per CU: Llama-70B down projection 29.2 -> 27.5 us), K split
+// while a whole extra round of workgroups fits.  M > 16: the
 // tiled kernel (64 columns per workgroup up to M = 64, else 128), split
 // across workgroups while a whole extra round fits on the CUs.
 bool sp_tiled(int v) { return v == fpx::kSpTiled4 || v == fpx::kSpTiled8; }
@@ -370,7 +376,7 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
   if (variant == fpx::kSpAuto) {
     if (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles) p.variant = fpx::kSpKslice;
     else if (M <= 16 && splits == 0 && ks_fits) p.variant = fpx::kSpKsplit;
-    else if (M <= 16) p.variant = fpx::kSpXlds1;
+    else if (M <= 16) p.variant = ceil_div(N >> 4, 4) <= cus / 2 ? fpx::kSpXlds2 : fpx::kSpXlds1;
     else if (M <= 32) p.variant = mb_one_rb ? fpx::kSpXldsMB1 : fpx::kSpXldsMB2;
     else if (M <= 64) p.variant = fpx::kSpTiled4;
     else p.variant = fpx::kSpTiled8;
