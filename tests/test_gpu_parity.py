@@ -423,6 +423,8 @@ DENSE_PLANS = [
     ((64, 4096, 4096), (22, 4)),         # 64 columns, 1 row block per wave
     ((64, 21504, 7168), (20, 3)),
     ((128, 21504, 7168), (10, 3)),       # tiled
+    ((128, 8192, 8192), (22, 2)),        # two 64-column passes on a narrower layer
+    ((72, 4096, 11008), (22, 4)),
 ]
 SPARSE_PLANS = [
     ((1, 4096, 4096), (1, 1)),

@@ -137,8 +137,9 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     // workgroup once there are at
     // least 7 row blocks per CU (each X tile shared by twice the waves, and
     // one workgroup per CU instead of a 1-or-2 mix: Llama-70B MLP 38 -> 35
-    // us), else 4.  Up to M = 64 the streaming kernel with X in LDS on 32
-    // or 64 columns; above, the tiled kernel (128 columns, half-tile stages).
+    // us), else 4.  Up to M = 64 (M = 128 on narrower layers) the streaming
+    // kernel with X in LDS on 32 or 64 columns; above, the tiled kernel (128
+    // columns, half-tile stages).
     const bool one_rb_per_cu = (N >> 4) <= cus;
     // Longer K (split count not forced): the k-split kernel with K split
     // across workgroups, one k-tile per wave and split, all row blocks of a
@@ -192,18 +193,22 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
       if (nb >= 14 * c && ceil_div(nb, 16) <= c) p.variant = 16;
       else if (nb >= 7 * c) p.variant = 18;
       else p.variant = ceil_div(nb, 4) <= c / 2 ? 14 : 15;
-    } else if (M <= 64 && splits == 0) {
+    } else if (splits == 0 && (M <= 64 || (M <= 128 && ceil_div(N >> 4, 8) <= cus / 2))) {
       // 17..64 columns: the streaming kernel with X in LDS on 32 (M <= 32)
       // or 64 columns per workgroup, each k-step spliced once for all of its
       // column groups; 1 row block per wave while that leaves at most half a
       // workgroup per CU, else 2; K split while a whole round of workgroups
       // fits on the CUs, at least 4 k-tiles per split (measured against the
       // tiled kernels: 32x21504x7168 39.8 -> 30 us, 64x8192x8192 30.3 ->
-      // 22.0 us, OPT-30B QKV M=64 40.9 -> 39.6 us).
+      // 22.0 us, OPT-30B QKV M=64 40.9 -> 39.6 us).  65..128 columns: two
+      // 64-column passes while 1 row block per wave applies (128x4096x4096
+      // 28.3 -> 16.9 us, 128x8192x8192 40.6 -> 33.1 us); wider layers keep
+      // the tiled kernel.
       const int64_t g1 = ceil_div(N >> 4, 8), g2 = ceil_div(ceil_div(N >> 4, 2), 8);
       const bool one_rb = g1 <= cus / 2;
       p.variant = M <= 32 ? (one_rb ? 21 : 19) : (one_rb ? 22 : 20);
-      int64_t sp = cus / (one_rb ? g1 : g2);
+      const int64_t passes = ceil_div(M, M <= 32 ? 32 : 64);
+      int64_t sp = cus / (passes * (one_rb ? g1 : g2));
       if (sp > ktiles / 4) sp = ktiles / 4;
       if (sp < 1) sp = 1;
       p.splits = static_cast<int>(sp);
