@@ -425,6 +425,8 @@ DENSE_PLANS = [
     ((128, 21504, 7168), (10, 3)),       # tiled
     ((128, 8192, 8192), (22, 2)),        # two 64-column passes on a narrower layer
     ((72, 4096, 11008), (22, 4)),
+    ((256, 4096, 4096), (22, 2)),
+    ((256, 8192, 8192), (10, 4)),        # as many workgroups as CUs: tiled
 ]
 SPARSE_PLANS = [
     ((1, 4096, 4096), (1, 1)),
@@ -434,6 +436,8 @@ SPARSE_PLANS = [
     ((16, 8192, 28672), (3, 4)),
     ((32, 21504, 7168), (8, 3)),
     ((64, 21504, 7168), (4, 3)),
+    ((128, 4096, 4096), (7, 2)),         # 32-column passes on a narrow layer
+    ((48, 11008, 4096), (7, 1)),
 ]
 
 

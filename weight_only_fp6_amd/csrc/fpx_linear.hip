@@ -193,17 +193,20 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
       if (nb >= 14 * c && ceil_div(nb, 16) <= c) p.variant = 16;
       else if (nb >= 7 * c) p.variant = 18;
       else p.variant = ceil_div(nb, 4) <= c / 2 ? 14 : 15;
-    } else if (splits == 0 && (M <= 64 || (M <= 128 && ceil_div(N >> 4, 8) <= cus / 2))) {
+    } else if (splits == 0 &&
+               (M <= 64 || (M <= 256 && ceil_div(N >> 4, 8) <= cus / 2 &&
+                            ceil_div(M, 64) * ceil_div(N >> 4, 8) < cus))) {
       // 17..64 columns: the streaming kernel with X in LDS on 32 (M <= 32)
       // or 64 columns per workgroup, each k-step spliced once for all of its
       // column groups; 1 row block per wave while that leaves at most half a
       // workgroup per CU, else 2; K split while a whole round of workgroups
       // fits on the CUs, at least 4 k-tiles per split (measured against the
       // tiled kernels: 32x21504x7168 39.8 -> 30 us, 64x8192x8192 30.3 ->
-      // 22.0 us, OPT-30B QKV M=64 40.9 -> 39.6 us).  65..128 columns: two
-      // 64-column passes while 1 row block per wave applies (128x4096x4096
-      // 28.3 -> 16.9 us, 128x8192x8192 40.6 -> 33.1 us); wider layers keep
-      // the tiled kernel.
+      // 22.0 us, OPT-30B QKV M=64 40.9 -> 39.6 us).  65..256 columns:
+      // 64-column passes while 1 row block per wave applies and all passes
+      // together make fewer workgroups than CUs (128x4096x4096 28.3 -> 16.9
+      // us, 256x4096x4096 31.9 -> 19.9 us); wider layers keep the tiled
+      // kernel.
       const int64_t g1 = ceil_div(N >> 4, 8), g2 = ceil_div(ceil_div(N >> 4, 2), 8);
       const bool one_rb = g1 <= cus / 2;
       p.variant = M <= 32 ? (one_rb ? 21 : 19) : (one_rb ? 22 : 20);
@@ -374,7 +377,7 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
   const int64_t g1 = ceil_div(N >> 4, 8), g2 = ceil_div(ceil_div(N >> 4, 2), 8);
   const bool mb_one_rb = g1 <= cus / 2;
   auto mb_splits = [&](int v) {
-    int64_t sp = cus / (sp_xlds_a(v) == 1 ? g1 : g2);
+    int64_t sp = cus / (ceil_div(M, 32) * (sp_xlds_a(v) == 1 ? g1 : g2));
     if (sp > ktiles / 2) sp = ktiles / 2;
     return static_cast<int>(sp < 1 ? 1 : sp);
   };
@@ -383,6 +386,10 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
     else if (M <= 16 && splits == 0 && ks_fits) p.variant = fpx::kSpKsplit;
     else if (M <= 16) p.variant = ceil_div(N >> 4, 4) <= cus / 2 ? fpx::kSpXlds2 : fpx::kSpXlds1;
     else if (M <= 32) p.variant = mb_one_rb ? fpx::kSpXldsMB1 : fpx::kSpXldsMB2;
+    // 33..128 columns: 32-column passes on narrower layers, as for dense
+    // (128x4096x4096 24.6 -> 13.6 us, 64x8192x8192 23.9 -> 19.6 us).
+    else if (M <= 128 && splits == 0 && mb_one_rb && ceil_div(M, 32) * g1 < cus)
+      p.variant = fpx::kSpXldsMB1;
     else if (M <= 64) p.variant = fpx::kSpTiled4;
     else p.variant = fpx::kSpTiled8;
   } else {
