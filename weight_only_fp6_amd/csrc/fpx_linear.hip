@@ -368,8 +368,9 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
   // The k-split kernel: at most 8 tiles per K-split (one per wave), as few
   // splits as that allows, and at most 8 row blocks per workgroup.
   const int ks_splits = static_cast<int>(ceil_div(ktiles, fpx::kSpKsplitMaxTiles));
-  const bool ks_fits = ks_splits <= 8 &&
-                       fpx::sp_ksplit_rows_per_wg(N, cus, ks_splits) <= fpx::kSpKsplitMaxRows;
+  // Up to 6 row blocks per workgroup: with 7-8 the streaming kernel wins
+  // (16x13824x5120: 14.9 against 12.0 us).
+  const bool ks_fits = ks_splits <= 8 && fpx::sp_ksplit_rows_per_wg(N, cus, ks_splits) <= 6;
   // 17 <= M <= 32: the streaming kernel on 32 columns (8 waves), 1 row
   // block per wave while that leaves at most half a workgroup per CU, else
   // 2, K split while a whole round of workgroups fits on the CUs (at least
@@ -382,7 +383,12 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
     return static_cast<int>(sp < 1 ? 1 : sp);
   };
   if (variant == fpx::kSpAuto) {
-    if (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles) p.variant = fpx::kSpKslice;
+    // One row block per CU: the k-slice kernel up to M = 11, the k-split
+    // kernel (X staged once per wave with coalesced loads) from M = 12
+    // (M = 16: 4096x4096 6.86 -> 6.27 us, 4096x8192 10.8 -> 8.9 us; M = 8
+    // keeps the k-slice kernel, 5.6 against 5.9 us).
+    if (M <= 16 && (N >> 4) <= cus && ktiles <= fpx::kSpKsliceMaxTiles && (M <= 11 || !ks_fits || splits != 0))
+      p.variant = fpx::kSpKslice;
     else if (M <= 16 && splits == 0 && ks_fits) p.variant = fpx::kSpKsplit;
     else if (M <= 16) p.variant = ceil_div(N >> 4, 4) <= cus / 2 ? fpx::kSpXlds2 : fpx::kSpXlds1;
     else if (M <= 32) p.variant = mb_one_rb ? fpx::kSpXldsMB1 : fpx::kSpXldsMB2;
