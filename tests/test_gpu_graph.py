@@ -29,7 +29,7 @@ DEV = torch.device("cuda:0")
 # without a workspace.
 DENSE = [
     (16, 8192, 8192, 0, 0),      # k-split, 2 K-splits
-    (1, 4096, 11008, 0, 0),      # k-split, 3 K-splits, M = 1 staging
+    (1, 4096, 11008, 12, 3),     # k-split, 3 K-splits, M = 1 staging
     (16, 4096, 11008, 12, 3),
     (16, 11008, 4096, 0, 0),     # k-split, no workspace
     (32, 4096, 4096, 0, 0),      # streaming, 32 columns, K-splits

@@ -416,6 +416,7 @@ DENSE_PLANS = [
     ((16, 8192, 8192), (KSPLIT16, 2)),   # K split across workgroups
     ((16, 5120, 5120), (KSPLIT, 3)),     # 8 waves: fewer idle waves on 10-tile splits
     ((16, 4096, 11008), (KSPLIT16, 3)),
+    ((1, 4096, 11008), (KSLICE, 1)),     # M <= 4, one row block per CU: k-slice up to K = 12288
     ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups
     ((16, 57344, 8192), (16, 1)),        # 2 row blocks per wave: one round instead of 1.75
     ((16, 8192, 28672), (14, 4)),        # 2 row blocks per wave, split while a whole round fits

@@ -174,6 +174,11 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     const bool ks_fits = ks_variant != 0;
     if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
       p.variant = 13;
+    } else if (M <= 4 && ktiles <= fpx::kKsliceMaxTiles && one_rb_per_cu) {
+      // Longer K at M <= 4: the k-slice kernel still beats K-splits (no
+      // fix-up; 1x4096x8192 8.9 -> 7.9 us, 4x4096x8192 9.7 -> 8.2 us); at
+      // M = 16 its X traffic loses (4096x11008: 17.2 against 13.7 us).
+      p.variant = 13;
     } else if (M <= 16 && ktiles <= 8) {
       p.variant = 9;
     } else if (M <= 16 && ktiles <= 16) {
