@@ -83,3 +83,35 @@ def test_graph_replays_match_eager(sparse):
             torch.cuda.synchronize()
             assert torch.equal(again.view(torch.int16), want.view(torch.int16)), (what, rep)
         del g
+
+
+def test_workspace_keeps_the_largest_sizes_for_capture():
+    # Plan A needs many arrival counters and a small partial buffer, plan B
+    # a larger buffer and fewer counters.  After eager calls of A then B on
+    # a stream, both must be capturable there (the workspace only grows, so
+    # neither reallocates during capture) and replay to the eager result.
+    stream = torch.cuda.Stream()
+    cases = [(16, 10240, 2048, 12, 2), (16, 4096, 8192, 14, 8)]
+    runs = []
+    for i, (M, N, K, v, sp) in enumerate(cases):
+        P, S = _prepare(N, K, 900 + i, False)
+        X = torch.from_numpy(synth.activations(M, K, 910 + i)).to(DEV)
+        runs.append((X, P, S, N, K, v, sp))
+    wants = []
+    with torch.cuda.stream(stream):
+        for X, P, S, N, K, v, sp in runs:
+            wants.append(fp6.linear_plan(X, P, S, N, K, variant=v, splits=sp, stream=stream).clone())
+    torch.cuda.synchronize()
+    for (X, P, S, N, K, v, sp), want in zip(runs, wants):
+        out = torch.empty_like(want)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fp6.linear_plan(X, P, S, N, K, variant=v, splits=sp, out=out, stream=stream)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16)), (N, K, v, sp, rep)
+        del g

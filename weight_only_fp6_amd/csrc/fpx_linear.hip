@@ -59,14 +59,18 @@ int get_workspace(int dev, void* stream, size_t part_bytes, size_t counter_count
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace& ws = g_ws[{dev, stream}];
   if (ws.part_bytes < part_bytes || ws.counter_count < counter_count) {
+    // Both sizes only grow: a plan that needs more partial bytes but fewer
+    // counters than an earlier one must not shrink the counters (the earlier
+    // plan would then reallocate on its next call, which is illegal under
+    // graph capture and a synchronisation per call otherwise).
+    const size_t pb = part_bytes > ws.part_bytes ? part_bytes : ws.part_bytes;
+    const size_t cc = counter_count > ws.counter_count ? counter_count : ws.counter_count;
     if (ws.part || ws.counters) {
       if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return FP6_E_HIP;
       if (ws.part) (void)hipFree(ws.part);
       if (ws.counters) (void)hipFree(ws.counters);
       ws = Workspace{};
     }
-    const size_t pb = part_bytes > ws.part_bytes ? part_bytes : ws.part_bytes;
-    const size_t cc = counter_count > ws.counter_count ? counter_count : ws.counter_count;
     if (hipMalloc(&ws.part, pb) != hipSuccess) { ws = Workspace{}; return FP6_E_HIP; }
     if (hipMalloc(reinterpret_cast<void**>(&ws.counters), cc * sizeof(unsigned)) != hipSuccess) {
       (void)hipFree(ws.part);
