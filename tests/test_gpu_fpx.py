@@ -4,11 +4,9 @@ against the CPU oracle, through the fpx_* entry points (needs an MI355X).
 Same bars as the FP6 e3m2 tests: de-quantisation bit-exact, fused linear
 within |Y - Y_ref| <= 2e-3 (|Y_ref| + rms) per element and relative Frobenius
 <= 5e-4, one-hot activations reproducing Wdq exactly, for every kernel
-configuration on small ragged shapes and for the automatic plan at workload
-shapes (sampled output columns for the large layers).
+configuration on small ragged shapes and for the automatic plan on every
+output element of every workload layer at full size.
 """
-
-import functools
 
 import numpy as np
 import pytest
@@ -16,7 +14,7 @@ import pytest
 import oracle
 from weight_only_fp6_amd import synth
 
-from _workloads import Prepared, prepare_shape
+from _workloads import Prepared, dense_weight_set, prepare_shape, workload, y_ref
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -74,27 +72,27 @@ def test_dequant_power_of_two_subnormal_and_random_scales(fmt):
     assert (ref[:16 * 10] & 0x7C00 == 0).any()     # fp16 subnormal weights survive
 
 
-@functools.lru_cache(maxsize=2)
-def _prep(name, sample, fmt):
-    return prepare_shape(synth.SHAPES[name], sample=sample, fmt=fmt)
-
-
-@pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("name", ["small_8x1024x1024", "llama7b_attn_1x4096x4096",
-                                  "llama7b_mlp_down_16x4096x11008", "llama70b_mlp_16x28672x8192",
-                                  "opt30b_qkv_128x21504x7168"])
-def test_linear_workloads(fmt, name):
+def _first_of_weight_set(name):
     shp = synth.SHAPES[name]
-    sample = None if shp.N * shp.K <= 48 * 2**20 else 384
-    p = _prep(name, sample, fmt)
-    X, packed, s = p.to_device()
-    Y = fp6.linear(X, packed, s, shp.N, shp.K, fmt=fmt)
+    return next(n for n, q in synth.SHAPES.items() if (q.N, q.K, q.seed_w) == (shp.N, shp.K, shp.seed_w)) == name
+
+
+@pytest.mark.parametrize("fmt, name", [(f, n) for f in FMTS for n in synth.SHAPES])
+def test_linear_workloads(fmt, name):
+    # Every workload layer at full size: every output element of the
+    # automatic plan, and (once per weight set) the whole de-quantised weight
+    # matrix bit for bit, with the library quantiser equal to the oracle's.
+    shp = synth.SHAPES[name]
+    ws, X, yref = workload(name, fmt)
+    packed, s = ws.to_device()
+    Y = fp6.linear(torch.from_numpy(X).to(DEV), packed, s, shp.N, shp.K, fmt=fmt)
     torch.cuda.synchronize()
-    _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(fmt, name))
-    if sample is None:
+    _assert_tol(Y, yref, what=(fmt, name))
+    if _first_of_weight_set(name):
+        assert ws.codes_match and ws.scales_match, (fmt, name)
         W16 = fp6.dequant(packed, s, shp.N, shp.K, fmt=fmt)
         torch.cuda.synchronize()
-        assert np.array_equal(_bits16(W16), p.wdq_ref.view(np.uint16))
+        assert np.array_equal(_bits16(W16), ws.wdq_ref.view(np.uint16)), (fmt, name)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -111,21 +109,34 @@ def test_linear_small_shapes_every_variant(fmt, M, NK):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_linear_forced_splits_and_k_coverage(fmt):
-    shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
-    p = _prep(shp.name, None, fmt)
-    X, packed, s = p.to_device()
+def test_linear_forced_splits(fmt):
+    name = "llama7b_mlp_down_16x4096x11008"
+    shp = synth.SHAPES[name]
+    ws, X, yref = workload(name, fmt)
+    packed, s = ws.to_device()
+    Xd = torch.from_numpy(X).to(DEV)
     for variant, splits in [(1, 7), (3, 43), (5, 3), (10, 4), (11, 2), (14, 8), (15, 5), (16, 2), (17, 3), (18, 1), (18, 4)]:
-        Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=variant, splits=splits, fmt=fmt)
+        Y = fp6.linear_plan(Xd, packed, s, shp.N, shp.K, variant=variant, splits=splits, fmt=fmt)
         torch.cuda.synchronize()
-        _assert_tol(Y, p.y_ref, what=(fmt, variant, splits))
-    for K in (512, 1280, 4096, 8192):
-        q = Prepared(4, 16 * 300, K, seed_w=K + 9, seed_x=K + 10, sample=64, fmt=fmt)
-        Xq, pq, sq = q.to_device()
-        for variant in SMALL_M_VARIANTS:
-            Y = fp6.linear_plan(Xq, pq, sq, q.N, K, variant=variant, fmt=fmt)
+        _assert_tol(Y, yref, what=(fmt, variant, splits))
+
+
+@pytest.mark.parametrize("fmt, K", [(f, K) for f in FMTS for K in (512, 1280, 4096, 8192, 8448, 11008, 12288)])
+def test_linear_k_coverage(fmt, K):
+    # k-split (up to K = 8192) and k-slice (up to 12288: 1..3 tiles per wave)
+    # kernels and the automatic plan at M = 1, 2, 4 and 16; every output.
+    N = 16 * 300
+    ws = dense_weight_set(N, K, K + 9, fmt)
+    packed, s = ws.to_device()
+    variants = (0,) + (SMALL_M_VARIANTS if K <= 8192 else (13,))
+    for M in (1, 2, 4, 16):
+        X = synth.activations(M, K, K + 10 + M)
+        yref = y_ref(X, ws.wdq_ref)
+        Xd = torch.from_numpy(X).to(DEV)
+        for variant in variants:
+            Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, fmt=fmt)
             torch.cuda.synchronize()
-            _assert_tol(Y[:, torch.from_numpy(q.rows).to(DEV)], q.y_ref, what=(fmt, K, variant))
+            _assert_tol(Y, yref, what=(fmt, M, K, variant))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -148,7 +159,7 @@ def test_linear_one_hot_reproduces_wdq_exactly(fmt):
 
 def test_fpx_format0_matches_fp6_bitwise():
     shp = synth.SHAPES["llama7b_attn_1x4096x4096"]
-    p = prepare_shape(shp, sample=64)
+    p = prepare_shape(shp)
     X, packed, s = p.to_device()
     a = fp6.linear(X, packed, s, shp.N, shp.K)
     b = torch.empty_like(a)

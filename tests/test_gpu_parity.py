@@ -2,12 +2,11 @@
 
 * De-quantisation export: bit-exact against oracle.dequant_ref.
 * Fused linear: |Y - Y_ref| <= 2e-3 (|Y_ref| + rms(Y_ref)) per element and
-  relative Frobenius error <= 5e-4, on every workload shape at full size
-  (sampled output columns for the two largest layers) and on small shapes that
-  span several tiles with ragged M; one-hot inputs must reproduce Wdq exactly.
+  relative Frobenius error <= 5e-4, with rms over the whole output, on every
+  output element of every workload shape at full size and of small shapes
+  that span several tiles with ragged M; one-hot inputs must reproduce Wdq
+  exactly.
 """
-
-import functools
 
 import numpy as np
 import pytest
@@ -15,7 +14,7 @@ import pytest
 import oracle
 from weight_only_fp6_amd import synth
 
-from _workloads import Prepared, prepare_shape  # noqa: F401
+from _workloads import Prepared, dense_weight_set, workload, y_ref
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -89,41 +88,51 @@ def test_dequant_random_scales_full_range():
     assert np.array_equal(got, ref)
 
 
-@functools.lru_cache(maxsize=2)
-def _prep(name, sample):
-    return prepare_shape(synth.SHAPES[name], sample=sample)
+def _weight_set_names():
+    """The first synth.SHAPES entry of every distinct weight set, in order."""
+    seen = {}
+    for name, shp in synth.SHAPES.items():
+        seen.setdefault((shp.N, shp.K, shp.seed_w), name)
+    return list(seen.values())
 
 
-_NK = {}
-for _n, _s in synth.SHAPES.items():
-    _NK.setdefault((_s.N, _s.K, _s.cfg), _n)
-
-
-@pytest.mark.parametrize("name", sorted(_NK.values()))
+@pytest.mark.parametrize("name", _weight_set_names())
 def test_dequant_workload_weights(name):
+    # The whole de-quantised weight matrix of every workload layer (up to
+    # 28672 x 8192), bit for bit; the library quantiser's codes and scales
+    # equal the oracle's on every row.
     shp = synth.SHAPES[name]
-    sample = None if shp.N * shp.K <= 16 * 2**20 else 256
-    p = _prep(name, sample)
-    packed = torch.from_numpy(p.packed).to(DEV)
-    s = torch.from_numpy(p.scales.copy()).to(DEV)
+    ws = dense_weight_set(shp.N, shp.K, shp.seed_w)
+    assert ws.codes_match and ws.scales_match, name
+    packed, s = ws.to_device()
     out = fp6.dequant(packed, s, shp.N, shp.K)
-    got = _bits16(out[torch.from_numpy(p.rows).to(DEV)])
-    assert np.array_equal(got, p.wdq_ref.view(np.uint16))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits16(out), ws.wdq_ref.view(np.uint16)), name
 
 
 # ----------------------------------------------------------------------------
-# Fused linear at the workload shapes (automatic plan = the benchmarked launch)
+# Fused linear at the workload shapes (automatic plan = the benchmarked launch),
+# every output element against Y_ref of the whole layer
 # ----------------------------------------------------------------------------
+class _full:
+    """A whole workload layer on the device with Y_ref of every output."""
+
+    def __init__(self, name):
+        self.ws, self.X, self.y_ref = workload(name)
+
+    def to_device(self):
+        packed, s = self.ws.to_device()
+        return torch.from_numpy(self.X).to(DEV), packed, s
+
+
 @pytest.mark.parametrize("name", list(synth.SHAPES))
 def test_linear_workloads(name):
     shp = synth.SHAPES[name]
-    sample = None if shp.N * shp.K <= 48 * 2**20 else 384
-    p = _prep(name, sample)
-    X, packed, s = p.to_device()
-    Y = fp6.linear(X, packed, s, shp.N, shp.K)
+    ws, X, yref = workload(name)
+    packed, s = ws.to_device()
+    Y = fp6.linear(torch.from_numpy(X).to(DEV), packed, s, shp.N, shp.K)
     torch.cuda.synchronize()
-    ycols = Y[:, torch.from_numpy(p.rows).to(DEV)]
-    _assert_tol(ycols, p.y_ref, what=name)
+    _assert_tol(Y, yref, what=(name, fp6.plan_query(shp.M, shp.N, shp.K)))
 
 
 # ----------------------------------------------------------------------------
@@ -145,7 +154,7 @@ def test_linear_small_shapes_ragged_m(M, NK):
 def test_linear_forced_splits_long_k(splits):
     # Llama-7B MLP down projection: K = 11008 = 43 tiles of 256 (43 is prime)
     shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
-    p = _prep(shp.name, None)
+    p = _full(shp.name)
     X, packed, s = p.to_device()
     for variant in (1, 3, 5, 6, 10, 11, 14, 16, 17, 18, 19, 20, 21, 22):
         Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=variant, splits=splits)
@@ -153,69 +162,102 @@ def test_linear_forced_splits_long_k(splits):
         _assert_tol(Y, p.y_ref, what=(splits, variant))
 
 
-@pytest.mark.parametrize("K", [256, 512, 1280, 2048, 4096, 6144, 8192])
-@pytest.mark.parametrize("M", [1, 4, 16])
-def test_linear_ksplit_k_coverage(M, K):
-    # the k-split and k-slice kernels at every per-wave tile count (1..4,
-    # ragged ranges), with more row blocks than workgroups (N = 16*300 > 256)
+KCOV_K = (256, 512, 1280, 2048, 4096, 6144, 8192, 8448, 11008, 12288)
+
+
+@pytest.mark.parametrize("K, M", [(K, M) for K in KCOV_K for M in (1, 2, 4, 16)])
+def test_linear_ksplit_k_coverage(K, M):
+    # The k-split and k-slice kernels at every per-wave tile count: k-split
+    # 1..4 tiles per wave up to K = 8192; k-slice 1..3 (K = 8448 and 11008
+    # leave ragged 2-or-3-tile ranges, 12288 is 3 tiles in every wave), with
+    # more row blocks than workgroups (N = 16*300 > 256); and the automatic
+    # plan.  Every output element.
     N = 16 * 300
-    p = Prepared(M, N, K, seed_w=K + M, seed_x=K * 3 + M, sample=64)
-    X, packed, s = p.to_device()
-    for variant in (KSPLIT, KSPLIT16, KSLICE):
-        Y = fp6.linear_plan(X, packed, s, N, K, variant=variant)
+    ws = dense_weight_set(N, K, K + 7)
+    X = synth.activations(M, K, K * 3 + M)
+    yref = y_ref(X, ws.wdq_ref)
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
+    variants = (0, KSPLIT, KSPLIT16, KSLICE) if K <= 8192 else (0, KSLICE)
+    for variant in variants:
+        Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
-        _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(M, K, variant))
+        _assert_tol(Y, yref, what=(M, K, variant))
 
 
-@pytest.mark.parametrize("K", [2048, 4096])
-@pytest.mark.parametrize("per_wg", [2, 3, 4, 5, 7, 9])
-@pytest.mark.parametrize("M", [1, 5, 16])
-def test_linear_ksplit_row_blocks_per_workgroup(M, per_wg, K):
+@pytest.mark.parametrize("K", [8448, 11008, 12288])
+def test_kslice_one_hot_third_tile_slot(K):
+    # One-hot activations through the k-slice kernel with 3 tiles per wave:
+    # columns land in each of a wave's three tile slots (and in the k-steps,
+    # lane groups and elements inside a tile), so every output must equal a
+    # de-quantised weight exactly.
+    N, M = 64, 16
+    ws = dense_weight_set(N, K, K + 11)
+    kt = K // 256
+    cols, slots = [], []
+    for m in range(M):
+        w = (5 * m + 3) % 16                        # wave w owns tiles [k0, k1)
+        k0, k1 = w * kt // 16, (w + 1) * kt // 16
+        slot = k1 - k0 - 1 if m % 2 == 0 else (m // 2) % (k1 - k0)
+        slots.append(slot)
+        cols.append((k0 + slot) * 256 + (37 * m + 11) % 256)
+    assert 2 in slots
+    ks = np.array(cols)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
+    want = ws.wdq_ref[:, ks].T.astype(np.float64)
+    for m_used in (1, 2, 4, 16):
+        Y = fp6.linear_plan(Xd[:m_used].contiguous(), packed, s, N, K, variant=KSLICE)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), want[:m_used]), (K, m_used)
+
+
+@pytest.mark.parametrize("K, per_wg, M", [(K, w, M) for K in (2048, 4096) for w in (2, 3, 4, 5, 7, 9)
+                                          for M in (1, 5, 16)])
+def test_linear_ksplit_row_blocks_per_workgroup(K, per_wg, M):
     # The k-split kernels run straight-line code for 2-8 row blocks per
     # workgroup (4 register stages; a workgroup with fewer than the form's
-    # count repeats its last row block) and loop beyond.  N is sized from the CU count so that the first
-    # workgroups get per_wg row blocks and the rest per_wg - 1; one row of
-    # every row block is checked.  At K = 2048 half of the 16 waves have an
-    # empty k-range.
+    # count repeats its last row block) and loop beyond.  N is sized from the
+    # CU count so that the first workgroups get per_wg row blocks and the rest
+    # per_wg - 1.  At K = 2048 half of the 16 waves have an empty k-range.
+    # Every output element.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nblocks = (per_wg - 1) * cus + max(cus // 3, 1)
     N = 16 * nblocks
-    W = synth.weights(N, K, 900 + per_wg + K)
+    ws = dense_weight_set(N, K, 900 + per_wg + K)
     X = synth.activations(M, K, 910 + M)
-    codes, scales = fp6.quantize_rows(W)
-    packed = fp6.prepack(codes, scales)
-    rows = 16 * np.arange(nblocks) + (np.arange(nblocks) * 7) % 16
-    oc, osc = oracle.quantize_rows(W[rows])
-    y_ref = oracle.gemm_ref(X, oracle.dequant_ref(oc, osc))
+    yref = y_ref(X, ws.wdq_ref)
     Xd = torch.from_numpy(X).to(DEV)
-    Pd = torch.from_numpy(packed).to(DEV)
-    Sd = torch.from_numpy(scales.copy()).to(DEV)
-    cols = torch.from_numpy(rows).to(DEV)
+    Pd, Sd = ws.to_device()
     for variant in (KSPLIT, KSPLIT16):
         Y = fp6.linear_plan(Xd, Pd, Sd, N, K, variant=variant)
         torch.cuda.synchronize()
-        _assert_tol(Y[:, cols], y_ref, what=(M, per_wg, K, variant))
+        _assert_tol(Y, yref, what=(M, per_wg, K, variant))
 
 
-@pytest.mark.parametrize("M", [1, 5, 16])
-@pytest.mark.parametrize("NK", [(4096, 11008), (1024, 6400), (2048, 2304)])
-def test_linear_ksplit_across_workgroups(M, NK):
+@pytest.mark.parametrize("NK, M", [(NK, M) for NK in ((4096, 11008), (1024, 6400), (2048, 2304))
+                                   for M in (1, 5, 16)])
+def test_linear_ksplit_across_workgroups(NK, M):
     # The k-split kernels with K split across workgroups (fixed-order
     # fix-up): straight-line and looping forms, ragged split ranges, idle
-    # waves; bitwise reproducible from run to run.
+    # waves; bitwise reproducible from run to run.  Every output element.
     N, K = NK
-    p = Prepared(M, N, K, seed_w=N + K + 5, seed_x=M + 3, sample=192)
-    X, packed, s = p.to_device()
-    cols = torch.from_numpy(p.rows).to(DEV)
+    ws = dense_weight_set(N, K, N + K + 5)
+    X = synth.activations(M, K, M + 3)
+    yref = y_ref(X, ws.wdq_ref)
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
     ktiles = K // 256
     for variant, wk in ((KSPLIT, 8), (KSPLIT16, 16)):
         for splits in (2, 3, 4, 7):
             if splits > ktiles or -(-ktiles // splits) > 32:
                 continue
-            Y = fp6.linear_plan(X, packed, s, N, K, variant=variant, splits=splits).clone()
-            Y2 = fp6.linear_plan(X, packed, s, N, K, variant=variant, splits=splits)
+            Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits).clone()
+            Y2 = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
             torch.cuda.synchronize()
-            _assert_tol(Y[:, cols], p.y_ref, what=(M, N, K, variant, splits))
+            _assert_tol(Y, yref, what=(M, N, K, variant, splits))
             assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, variant, splits)
 
 
@@ -248,7 +290,7 @@ def test_linear_zero_activations_give_zero():
 
 def test_linear_is_deterministic():
     shp = synth.SHAPES["llama7b_mlp_down_16x4096x11008"]
-    p = _prep(shp.name, None)
+    p = _full(shp.name)
     X, packed, s = p.to_device()
     a = fp6.linear(X, packed, s, shp.N, shp.K).clone()
     b = fp6.linear(X, packed, s, shp.N, shp.K).clone()
@@ -280,7 +322,7 @@ def test_linear_m_zero_is_noop():
 
 def test_linear_on_side_stream_matches_default_stream():
     shp = synth.SHAPES["llama7b_attn_1x4096x4096"]
-    p = _prep(shp.name, None)
+    p = _full(shp.name)
     X, packed, s = p.to_device()
     a = fp6.linear(X, packed, s, shp.N, shp.K)
     side = torch.cuda.Stream()
@@ -397,12 +439,14 @@ def test_linear_large_n_or_k(M, N, K):
     # M=1 the persistent k-split kernel walks 256 row blocks per workgroup; at
     # M=40 the whole-tile tiled kernel launches 4096 workgroups), or K = 4M
     # with a single row block (the plan splits K 64 ways through the fix-up).
-    # Sampled output columns.
-    p = Prepared(M, N, K, seed_w=N + K + 1, seed_x=M + 2, sample=256)
-    X, packed, s = p.to_device()
-    Y = fp6.linear(X, packed, s, N, K)
+    # Every output element.
+    ws = dense_weight_set(N, K, N + K + 1)
+    X = synth.activations(M, K, M + 2)
+    yref = y_ref(X, ws.wdq_ref)
+    packed, s = ws.to_device()
+    Y = fp6.linear(torch.from_numpy(X).to(DEV), packed, s, N, K)
     torch.cuda.synchronize()
-    _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=(M, N, K))
+    _assert_tol(Y, yref, what=(M, N, K))
 
 
 # ----------------------------------------------------------------------------

@@ -4,12 +4,10 @@
 * De-quantisation export: dense Wdq (zeros at pruned positions) bit-exact.
 * Fused sparse linear: |Y - Y_ref| <= 2e-3 (|Y_ref| + rms) per element and
   relative Frobenius <= 5e-4, every kernel configuration on small ragged
-  shapes, the automatic plan at the workload shapes whose K is a multiple of
-  512 (sampled output columns for the large layers); one-hot activations
-  reproduce Wdq exactly.
+  shapes, the automatic plan on every output element of the workload layers
+  whose K is a multiple of 512, at full size; one-hot activations reproduce
+  Wdq exactly.
 """
-
-import functools
 
 import numpy as np
 import pytest
@@ -17,6 +15,8 @@ import pytest
 import oracle
 from oracle import sparse24
 from weight_only_fp6_amd import synth
+
+from _workloads import sparse_weight_set, workload, y_ref
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -33,17 +33,15 @@ KSPLIT = 6
 
 
 class SpPrepared:
-    def __init__(self, M, N, K, seed_w, seed_x, sample=None):
+    """A 2:4-sparse layer (synthetic weights pruned and quantised by the
+    library and by the oracle) with Y_ref of every output element."""
+
+    def __init__(self, M, N, K, seed_w, seed_x):
         self.M, self.N, self.K = M, N, K
-        W = synth.weights(N, K, seed_w)
+        self.ws = sparse_weight_set(N, K, seed_w)
         self.X = synth.activations(M, K, seed_x)
-        c, p, s = fp6.prune_quantize(W)
-        self.scales = s
-        self.packed = fp6.sparse_prepack(c, p, s, K)
-        self.rows = np.arange(N) if sample is None else synth.sample_rows(N, sample, seed_w + 17)
-        oc, op, osc = sparse24.quantize_sparse(W[self.rows])
-        self.wdq_ref = sparse24.dequant_ref(oc, op, osc, K)
-        self.y_ref = oracle.gemm_ref(self.X, self.wdq_ref)
+        self.scales, self.packed, self.wdq_ref = self.ws.scales, self.ws.packed, self.ws.wdq_ref
+        self.y_ref = y_ref(self.X, self.wdq_ref)
 
     def to_device(self):
         return (torch.from_numpy(self.X).to(DEV), torch.from_numpy(self.packed).to(DEV),
@@ -85,38 +83,41 @@ def test_linear_small_shapes_every_variant(M, NK):
 
 
 def test_linear_forced_splits():
-    p = SpPrepared(16, 4096, 8192, seed_w=71, seed_x=72, sample=256)
+    p = SpPrepared(16, 4096, 8192, seed_w=71, seed_x=72)
     X, packed, s = p.to_device()
-    cols = torch.from_numpy(p.rows).to(DEV)
     for variant in (2, 3, 4, 5, 7, 8):
         for splits in (1, 2, 3, 5, 16):
             Y = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits)
             torch.cuda.synchronize()
-            _assert_tol(Y[:, cols], p.y_ref, what=(variant, splits))
+            _assert_tol(Y, p.y_ref, what=(variant, splits))
     for splits in (2, 3, 5):    # k-split: <= 8 tiles per split, <= 8 row blocks per workgroup
         Y = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=KSPLIT, splits=splits)
         torch.cuda.synchronize()
-        _assert_tol(Y[:, cols], p.y_ref, what=(KSPLIT, splits))
+        _assert_tol(Y, p.y_ref, what=(KSPLIT, splits))
 
 
-@functools.lru_cache(maxsize=1)
-def _prep(name, sample):
-    shp = synth.SHAPES[name]
-    return SpPrepared(shp.M, shp.N, shp.K, shp.seed_w, shp.seed_x, sample=sample)
+SPARSE_SHAPES = [n for n, q in synth.SHAPES.items() if q.K % 512 == 0]
 
 
-@pytest.mark.parametrize("name", ["llama7b_attn_1x4096x4096", "llama7b_mlp_up_16x11008x4096",
-                                  "llama70b_mlp_1x28672x8192", "llama70b_mlp_16x28672x8192",
-                                  "opt30b_qkv_64x21504x7168", "opt30b_qkv_128x21504x7168",
-                                  "opt30b_qkv_256x21504x7168"])
+@pytest.mark.parametrize("name", SPARSE_SHAPES)
 def test_linear_workloads(name):
+    # Every workload layer whose K is a multiple of 512, at full size: every
+    # output element of the automatic plan, and (once per weight set) the
+    # whole dense de-quantised matrix bit for bit, with the library's pruning
+    # and quantisation equal to the oracle's.
     shp = synth.SHAPES[name]
-    sample = None if shp.N * shp.K <= 48 * 2**20 else 384
-    p = _prep(name, sample)
-    X, packed, s = p.to_device()
-    Y = fp6.sparse_linear(X, packed, s, shp.N, shp.K)
+    ws, X, yref = workload(name, sparse=True)
+    packed, s = ws.to_device()
+    Y = fp6.sparse_linear(torch.from_numpy(X).to(DEV), packed, s, shp.N, shp.K)
     torch.cuda.synchronize()
-    _assert_tol(Y[:, torch.from_numpy(p.rows).to(DEV)], p.y_ref, what=name)
+    _assert_tol(Y, yref, what=(name, fp6.sparse_plan_query(shp.M, shp.N, shp.K)))
+    first = next(n for n in SPARSE_SHAPES if (synth.SHAPES[n].N, synth.SHAPES[n].K, synth.SHAPES[n].seed_w)
+                 == (shp.N, shp.K, shp.seed_w))
+    if first == name:
+        assert ws.codes_match, name
+        W16 = fp6.sparse_dequant(packed, s, shp.N, shp.K)
+        torch.cuda.synchronize()
+        assert np.array_equal(W16.cpu().numpy().view(np.uint16), ws.wdq_ref.view(np.uint16)), name
 
 
 def test_linear_one_hot_reproduces_wdq_exactly():
@@ -136,7 +137,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
 
 
 def test_linear_is_deterministic_and_m_zero():
-    p = SpPrepared(16, 4096, 4096, seed_w=91, seed_x=92, sample=32)
+    p = SpPrepared(16, 4096, 4096, seed_w=91, seed_x=92)
     X, packed, s = p.to_device()
     for variant, splits in ((2, 4), (KSPLIT, 4)):
         a = fp6.sparse_linear_plan(X, packed, s, p.N, p.K, variant=variant, splits=splits).clone()
@@ -186,27 +187,21 @@ def test_sparse_linear_adversarial_rows(M):
         assert not Y[:, 0].cpu().numpy().astype(np.float64).any(), (M, variant, splits)
 
 
-@pytest.mark.parametrize("K", [2048, 4096, 6144])
-@pytest.mark.parametrize("per_wg", [1, 2, 3, 4, 5, 7, 8])
-@pytest.mark.parametrize("M", [1, 5, 16])
-def test_sparse_ksplit_row_blocks_per_workgroup(M, per_wg, K):
+@pytest.mark.parametrize("K, per_wg, M", [(K, w, M) for K in (2048, 4096, 6144) for w in (1, 2, 3, 4, 5, 7, 8)
+                                          for M in (1, 5, 16)])
+def test_sparse_ksplit_row_blocks_per_workgroup(K, per_wg, M):
     # The sparse k-split kernel with 1-8 row blocks per workgroup (a
     # workgroup with fewer than its form's count repeats its last row
-    # block), K split when it exceeds 8 tiles; N is sized from the CU count
-    # and one row of every row block is checked.
+    # block), K split when it exceeds 8 tiles; N is sized from the CU count.
+    # Every output element.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     splits = -(-(K // 512) // 8)
     per_split = cus // splits
     nblocks = (per_wg - 1) * per_split + max(per_split // 3, 1)
     N = 16 * nblocks
-    W = synth.weights(N, K, 950 + per_wg + K)
+    ws = sparse_weight_set(N, K, 950 + per_wg + K)
     X = synth.activations(M, K, 960 + M)
-    c, pos, sc = fp6.prune_quantize(W)
-    packed = torch.from_numpy(fp6.sparse_prepack(c, pos, sc, K)).to(DEV)
-    rows = 16 * np.arange(nblocks) + (np.arange(nblocks) * 5) % 16
-    oc, op, osc = sparse24.quantize_sparse(W[rows])
-    y_ref = oracle.gemm_ref(X, sparse24.dequant_ref(oc, op, osc, K))
-    Y = fp6.sparse_linear_plan(torch.from_numpy(X).to(DEV), packed, torch.from_numpy(sc.copy()).to(DEV),
-                               N, K, variant=KSPLIT)
+    packed, sd = ws.to_device()
+    Y = fp6.sparse_linear_plan(torch.from_numpy(X).to(DEV), packed, sd, N, K, variant=KSPLIT)
     torch.cuda.synchronize()
-    _assert_tol(Y[:, torch.from_numpy(rows).to(DEV)], y_ref, what=(M, per_wg, K))
+    _assert_tol(Y, y_ref(X, ws.wdq_ref), what=(M, per_wg, K))

@@ -69,10 +69,25 @@ def activations(M: int, K: int, seed: int) -> np.ndarray:
     return rng.standard_normal((M, K), dtype=np.float32).astype(np.float16)
 
 
-def codes_uniform(N: int, K: int, seed: int) -> np.ndarray:
-    """uint8 [N,K] uniform over all 64 e3m2 codes (adversarial coverage)."""
+def codes_uniform(N: int, K: int, seed: int, bits: int = 6) -> np.ndarray:
+    """uint8 [N,K] uniform over all 2^bits codes (adversarial coverage)."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    return rng.integers(0, 64, (N, K), dtype=np.uint8)
+    return rng.integers(0, 1 << bits, (N, K), dtype=np.uint8)
+
+
+def row_scales(N: int, seed: int, lo: float = 0.002, hi: float = 0.004) -> np.ndarray:
+    """fp16 [N] drawn uniformly from [lo, hi) (the range that max|row|/28
+    takes for N(0, 0.02) rows of a few thousand weights)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.uniform(lo, hi, N).astype(np.float16)
+
+
+def positions_2of4(N: int, K: int, seed: int) -> np.ndarray:
+    """uint8 [N, K/2]: for every group of 4 along k, two distinct positions
+    (0..3) in ascending order, each of the 6 pairs equally likely."""
+    pairs = np.array([(a, b) for a in range(4) for b in range(a + 1, 4)], np.uint8)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return pairs[rng.integers(0, 6, (N, K // 4))].reshape(N, K // 2)
 
 
 def sample_rows(N: int, count: int, seed: int) -> np.ndarray:
