@@ -392,3 +392,58 @@ def test_sparse_errors():
     assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 2, 2, None) == 8    # 2 splits > 1 tile
     assert L.fp6s_dequant(A, A, A, 16, 768, None) == 2
     assert L.fp6s_dequant(None, A, A, 16, 512, None) == 1
+
+
+def _binding_cases():
+    """(call, expected message fragment) for every device-tensor check of the
+    Python binding; each call has exactly one bad argument and fails before
+    any library call (CPU tensors are rejected last, for being off the GPU)."""
+    import torch
+    N, K, M = 32, 512, 4
+    f16, u8 = torch.float16, torch.uint8
+    nb, snb = fp6.packed_bytes(N, K), fp6.sparse_packed_bytes(N, K)
+    X = torch.zeros((M, K), dtype=f16)
+    P, PS = torch.zeros(nb, dtype=u8), torch.zeros(snb, dtype=u8)
+    S = torch.zeros(N, dtype=f16)
+    Y = torch.zeros((M, N), dtype=f16)
+    W16 = torch.zeros((N, K), dtype=f16)
+    cases = [
+        # dequant: packed size / dtype, scales dtype / count, out shape / dtype / layout
+        (lambda: fp6.dequant(torch.zeros(nb - 1, dtype=u8), S, N, K), "packed"),
+        (lambda: fp6.dequant(torch.zeros(nb, dtype=torch.int8), S, N, K), "packed"),
+        (lambda: fp6.dequant(torch.zeros(fp6.packed_bytes(N, K, "e2m1") + 16, dtype=u8), S, N, K, fmt="e2m1"), "packed"),
+        (lambda: fp6.dequant(P, torch.zeros(N, dtype=torch.float32), N, K), "scales"),
+        (lambda: fp6.dequant(P, torch.zeros(N - 1, dtype=f16), N, K), "scales"),
+        (lambda: fp6.dequant(P, S, N, K, out=torch.zeros((N, K - 1), dtype=f16)), "out"),
+        (lambda: fp6.dequant(P, S, N, K, out=torch.zeros((N, K), dtype=torch.float32)), "out"),
+        (lambda: fp6.dequant(P, S, N, K, out=torch.zeros((K, N), dtype=f16).t()), "out"),
+        (lambda: fp6.dequant(P, S, N, K, out=W16), "GPU"),
+        (lambda: fp6.dequant(P, S, N, K), "GPU"),
+        # sparse_dequant
+        (lambda: fp6.sparse_dequant(torch.zeros(snb + 1, dtype=u8), S, N, K), "packed"),
+        (lambda: fp6.sparse_dequant(P, S, N, K), "packed"),           # dense-sized buffer
+        (lambda: fp6.sparse_dequant(PS, torch.zeros(N, dtype=torch.bfloat16), N, K), "scales"),
+        (lambda: fp6.sparse_dequant(PS, torch.zeros(2 * N, dtype=f16), N, K), "scales"),
+        (lambda: fp6.sparse_dequant(PS, S, N, K, out=torch.zeros((N, K // 2), dtype=f16)), "out"),
+        (lambda: fp6.sparse_dequant(PS, S, N, K, out=torch.zeros((N, K), dtype=u8)), "out"),
+        (lambda: fp6.sparse_dequant(PS, S, N, K, out=W16), "GPU"),
+        # linear / sparse_linear
+        (lambda: fp6.linear(torch.zeros((M, K), dtype=torch.float32), P, S, N, K), "X"),
+        (lambda: fp6.linear(torch.zeros((M, K + 1), dtype=f16), P, S, N, K), "X"),
+        (lambda: fp6.linear(torch.zeros((K, M), dtype=f16).t(), P, S, N, K), "X"),
+        (lambda: fp6.linear(X, P[:-1], S, N, K), "packed"),
+        (lambda: fp6.linear(X, P, S[:-1], N, K), "scales"),
+        (lambda: fp6.linear(X, P, S, N, K, out=torch.zeros((M, N + 1), dtype=f16)), "out"),
+        (lambda: fp6.linear(X, P, S, N, K, out=Y), "GPU"),
+        (lambda: fp6.sparse_linear(X, P, S, N, K), "packed"),
+        (lambda: fp6.sparse_linear(X, PS, S.float(), N, K), "scales"),
+        (lambda: fp6.sparse_linear(X, PS, S, N, K, out=Y), "GPU"),
+    ]
+    return cases
+
+
+def test_binding_rejects_bad_device_tensors():
+    cases = _binding_cases()
+    for i, (call, frag) in enumerate(cases):
+        with pytest.raises(ValueError, match=frag):
+            call()

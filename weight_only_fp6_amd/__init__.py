@@ -179,6 +179,34 @@ def _dev_ptr(t) -> int:
     return int(t.data_ptr()) if t is not None else 0
 
 
+_PACKED = "packed (the prepack output for N, K and this format)"
+_SPARSE_PACKED = "packed (the sparse_prepack output for N, K)"
+
+
+def _check_device_tensors(*specs) -> None:
+    """Each (tensor, dtype, shape or element count, name) must be a contiguous
+    GPU tensor of that dtype and shape, else ValueError -- before anything
+    reaches the library, which takes raw pointers and cannot check buffer
+    sizes.  Dtypes, shapes and layouts are checked for every tensor before
+    devices."""
+    import torch
+    for t, dtype, shape, what in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{what} must be a torch tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+        if isinstance(shape, int):
+            if t.numel() != shape:
+                raise ValueError(f"{what} must hold {shape} elements, got {t.numel()}")
+        elif tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+    for t, _, _, what in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{what} must be on the GPU")
+
+
 def linear(X, packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e3m2"):
     """Y[M,N] fp16 = X[M,K] . dequant(W)^T on the GPU (asynchronous)."""
     return linear_plan(X, packed, scales, N, K, variant=0, splits=0, out=out, stream=stream, fmt=fmt)
@@ -188,17 +216,15 @@ def linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int
                 out=None, stream=None, fmt: str = "e3m2"):
     import torch
     f = _fmt_id(fmt)
-    if X.dtype != torch.float16 or X.dim() != 2 or X.shape[1] != K or not X.is_contiguous():
-        raise ValueError("X must be a contiguous fp16 [M,K] tensor")
+    if not isinstance(X, torch.Tensor) or X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be an fp16 [M,K] tensor")
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous fp16 [M,N] tensor")
-    if packed.numel() != packed_bytes(N, K, fmt) or packed.dtype != torch.uint8:
-        raise ValueError("packed must be the uint8 output of prepack for (N, K) and this format")
-    if scales.dtype != torch.float16 or scales.numel() != N:
-        raise ValueError("scales must be fp16 [N]")
+    _check_device_tensors((X, torch.float16, (M, K), "X"),
+                          (packed, torch.uint8, packed_bytes(N, K, fmt), _PACKED),
+                          (scales, torch.float16, N, "scales"),
+                          (out, torch.float16, (M, N), "out"))
     args = (_dev_ptr(X), _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), M, N, K, variant, splits,
             _stream_handle(stream))
     st = _lib.fp6_linear_plan(*args) if fmt == "e3m2" else _lib.fpx_linear_plan(f, *args)
@@ -231,6 +257,9 @@ def dequant(packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e
     f = _fmt_id(fmt)
     if out is None:
         out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    _check_device_tensors((packed, torch.uint8, packed_bytes(N, K, fmt), _PACKED),
+                          (scales, torch.float16, N, "scales"),
+                          (out, torch.float16, (N, K), "out"))
     args = (_dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), N, K, _stream_handle(stream))
     st = _lib.fp6_dequant(*args) if fmt == "e3m2" else _lib.fpx_dequant(f, *args)
     _check("dequant", st)
@@ -287,17 +316,15 @@ def sparse_linear(X, packed, scales, N: int, K: int, out=None, stream=None):
 def sparse_linear_plan(X, packed, scales, N: int, K: int, variant: int = 0, splits: int = 0,
                        out=None, stream=None):
     import torch
-    if X.dtype != torch.float16 or X.dim() != 2 or X.shape[1] != K or not X.is_contiguous():
-        raise ValueError("X must be a contiguous fp16 [M,K] tensor")
+    if not isinstance(X, torch.Tensor) or X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be an fp16 [M,K] tensor")
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous fp16 [M,N] tensor")
-    if packed.numel() != sparse_packed_bytes(N, K) or packed.dtype != torch.uint8:
-        raise ValueError("packed must be the uint8 output of sparse_prepack for (N, K)")
-    if scales.dtype != torch.float16 or scales.numel() != N:
-        raise ValueError("scales must be fp16 [N]")
+    _check_device_tensors((X, torch.float16, (M, K), "X"),
+                          (packed, torch.uint8, sparse_packed_bytes(N, K), _SPARSE_PACKED),
+                          (scales, torch.float16, N, "scales"),
+                          (out, torch.float16, (M, N), "out"))
     st = _lib.fp6s_linear_plan(_dev_ptr(X), _dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), M, N, K,
                                variant, splits, _stream_handle(stream))
     _check("fp6s_linear_plan", st)
@@ -317,6 +344,9 @@ def sparse_dequant(packed, scales, N: int, K: int, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    _check_device_tensors((packed, torch.uint8, sparse_packed_bytes(N, K), _SPARSE_PACKED),
+                          (scales, torch.float16, N, "scales"),
+                          (out, torch.float16, (N, K), "out"))
     st = _lib.fp6s_dequant(_dev_ptr(packed), _dev_ptr(scales), _dev_ptr(out), N, K, _stream_handle(stream))
     _check("fp6s_dequant", st)
     return out
