@@ -133,13 +133,21 @@ int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
  * (device, stream), allocated with hipMalloc on first need and grown on
  * demand (growing synchronises that stream once).  Results are bitwise
  * deterministic: split partials are summed in a fixed order.
- * Concurrent calls on different streams are safe; concurrent calls on the
- * same stream from several host threads are serialised by the stream.
+ * A workspace is kept for every stream that ran a split plan, until
+ * fp6_release (a process that creates many streams holds one per stream).
+ * Concurrent calls on different streams are safe.  Calls on one stream from
+ * several host threads are safe too: the library holds its lock from the
+ * workspace lookup until the launch is enqueued, and the stream orders the
+ * kernels.
  * HIP graph capture: nothing is allocated or cleared per call once the
  * stream's workspace exists, so make one call with the same shape and plan
  * on the capturing stream before capturing; the captured launch keeps the
  * workspace's address, so do not grow it (a larger split-K plan on that
- * stream) while the graph is in use.
+ * stream) while the graph is in use.  Every graph captured on a stream
+ * shares that stream's one workspace (partial sums and arrival counters):
+ * replay such graphs one after another, never two at once on different
+ * streams and never alongside eager split-K calls on the capturing stream,
+ * or their partial sums mix.
  */
 int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
                int64_t M, int64_t N, int64_t K, void* stream);

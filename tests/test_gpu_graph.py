@@ -90,6 +90,11 @@ def test_workspace_keeps_the_largest_sizes_for_capture():
     # a larger buffer and fewer counters.  After eager calls of A then B on
     # a stream, both must be capturable there (the workspace only grows, so
     # neither reallocates during capture) and replay to the eager result.
+    # torch hands out pooled stream handles, which earlier tests may already
+    # have given a large workspace: release every workspace first so that A
+    # and B grow a fresh one, in that order.
+    torch.cuda.synchronize()
+    fp6.release()
     stream = torch.cuda.Stream()
     cases = [(16, 10240, 2048, 12, 2), (16, 4096, 8192, 14, 8)]
     runs = []

@@ -54,9 +54,14 @@ int device_cus(int dev) {
   return cus;
 }
 
-// Ensure the (device, stream) workspace holds at least the given sizes.
-int get_workspace(int dev, void* stream, size_t part_bytes, size_t counter_count, Workspace** out) {
-  std::lock_guard<std::mutex> lk(g_mu);
+// Ensure the (device, stream) workspace holds at least the given sizes.  The
+// caller holds g_mu and keeps holding it until the launch that uses the
+// buffers is enqueued: another host thread growing the same workspace (or
+// fp6_release) would otherwise free them in between.  Workspaces are kept
+// per stream until fp6_release, so a process that cycles through many
+// streams with split plans holds one per stream.
+int get_workspace_locked(int dev, void* stream, size_t part_bytes, size_t counter_count,
+                         Workspace** out) {
   Workspace& ws = g_ws[{dev, stream}];
   if (ws.part_bytes < part_bytes || ws.counter_count < counter_count) {
     // Both sizes only grow: a plan that needs more partial bytes but fewer
@@ -71,13 +76,19 @@ int get_workspace(int dev, void* stream, size_t part_bytes, size_t counter_count
       if (ws.counters) (void)hipFree(ws.counters);
       ws = Workspace{};
     }
-    if (hipMalloc(&ws.part, pb) != hipSuccess) { ws = Workspace{}; return FP6_E_HIP; }
-    if (hipMalloc(reinterpret_cast<void**>(&ws.counters), cc * sizeof(unsigned)) != hipSuccess) {
-      (void)hipFree(ws.part);
-      ws = Workspace{};
+    void* part = nullptr;
+    unsigned* counters = nullptr;
+    if (hipMalloc(&part, pb) != hipSuccess) return FP6_E_HIP;
+    if (hipMalloc(reinterpret_cast<void**>(&counters), cc * sizeof(unsigned)) != hipSuccess ||
+        hipMemset(counters, 0, cc * sizeof(unsigned)) != hipSuccess) {
+      // Nothing is kept half-made: the entry stays empty and the next call
+      // allocates from scratch.
+      (void)hipFree(part);
+      if (counters) (void)hipFree(counters);
       return FP6_E_HIP;
     }
-    if (hipMemset(ws.counters, 0, cc * sizeof(unsigned)) != hipSuccess) return FP6_E_HIP;
+    ws.part = part;
+    ws.counters = counters;
     ws.part_bytes = pb;
     ws.counter_count = cc;
   }
@@ -313,17 +324,18 @@ int linear_impl(int format, const void* X, const void* W, const void* S, void* Y
   const int cus = device_cus(dev);
   const Plan p = choose_plan(M, N, K, cus, variant, splits);
   const KernelCfg& c = kCfgs[p.variant];
-  Workspace* ws = nullptr;
-  if (p.splits > 1) {
-    int64_t units = 0, floats = 0;
-    plan_units(c, M, N, &units, &floats);
-    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
-    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
-    if (st != FP6_OK) return st;
-  }
-  fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits,
-                     ws ? static_cast<float*>(ws->part) : nullptr, ws ? ws->counters : nullptr, cus,
+  fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus,
                      static_cast<hipStream_t>(stream)};
+  if (p.splits <= 1) return launch_format(format, ctx);
+  int64_t units = 0, floats = 0;
+  plan_units(c, M, N, &units, &floats);
+  const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
+  std::lock_guard<std::mutex> lk(g_mu);  // held until the launch is enqueued
+  Workspace* ws = nullptr;
+  st = get_workspace_locked(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
+  if (st != FP6_OK) return st;
+  ctx.part = static_cast<float*>(ws->part);
+  ctx.counters = ws->counters;
   return launch_format(format, ctx);
 }
 
@@ -465,24 +477,25 @@ int sparse_linear_impl(const void* X, const void* W, const void* S, void* Y, int
   if (p.variant == fpx::kSpKsplit &&
       fpx::sp_ksplit_rows_per_wg(N, cus, p.splits) > fpx::kSpKsplitMaxRows)
     return FP6_E_VALUE;
-  Workspace* ws = nullptr;
-  if (p.splits > 1) {
-    int64_t units, floats;
-    if (sp_tiled(p.variant)) {  // one unit per wave: 8 waves x 2 row blocks x B column blocks
-      units = ceil_div(M, 16 * sp_tile_b(p.variant)) * ceil_div(N >> 4, 16) * 8;
-      floats = 2 * sp_tile_b(p.variant) * 256;
-    } else {
-      const int a = sp_xlds_a(p.variant), mb = sp_xlds_mb(p.variant);
-      units = ceil_div(M, 16 * mb) * ceil_div(N >> 4, a);
-      floats = a * mb * 256;
-    }
-    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
-    st = get_workspace(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
-    if (st != FP6_OK) return st;
-  }
-  fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits,
-                     ws ? static_cast<float*>(ws->part) : nullptr, ws ? ws->counters : nullptr, cus,
+  fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus,
                      static_cast<hipStream_t>(stream)};
+  if (p.splits <= 1) return fpx::launch_sparse(ctx);
+  int64_t units, floats;
+  if (sp_tiled(p.variant)) {  // one unit per wave: 8 waves x 2 row blocks x B column blocks
+    units = ceil_div(M, 16 * sp_tile_b(p.variant)) * ceil_div(N >> 4, 16) * 8;
+    floats = 2 * sp_tile_b(p.variant) * 256;
+  } else {
+    const int a = sp_xlds_a(p.variant), mb = sp_xlds_mb(p.variant);
+    units = ceil_div(M, 16 * mb) * ceil_div(N >> 4, a);
+    floats = a * mb * 256;
+  }
+  const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
+  std::lock_guard<std::mutex> lk(g_mu);  // held until the launch is enqueued
+  Workspace* ws = nullptr;
+  st = get_workspace_locked(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
+  if (st != FP6_OK) return st;
+  ctx.part = static_cast<float*>(ws->part);
+  ctx.counters = ws->counters;
   return fpx::launch_sparse(ctx);
 }
 
