@@ -9,8 +9,8 @@ from a HIP graph captured from plain library launches on a side stream and
 bracketed by torch.cuda.synchronize(); HIP events recorded on that stream give
 the average launch duration.
 
-Default workload: the Llama-7B attention projection, M=1 (decode GEMV),
-N=4096, K=4096.  ``--workload`` selects another shape of
+Default workload: the Llama-70B MLP layer with one GPU's full weights, M=16,
+N=28672, K=8192 (176 MB of packed FP6 weights, the memory-bound regime).  ``--workload`` selects another shape of
 weight_only_fp6_amd.synth.SHAPES and ``--format`` another weight format
 (e2m3, e2m2, e2m1 through ``fpx_linear``; default e3m2).  Prints ONE JSON
 line.
@@ -22,7 +22,13 @@ Also reported, as context:
   de-quantised weights, with rotated cold copies -- the W16A16 reference the
   FP6-LLM pages normalise their kernel speedups to;
 * ``read_ceiling_gbs``: a plain streaming-read probe over a buffer of the
-  packed-weight size (the practical HBM ceiling at this size).
+  packed-weight size (the practical HBM ceiling at this size);
+* ``mfma_ceiling_tflops``: a loop of register-only fp16 MFMAs over the whole
+  GPU (the practical dense fp16 MFMA ceiling).
+
+``value`` and ``ms_per_step`` come from HIP events recorded on the launch
+stream around the K timed steps; ``wall_ms_per_step`` is the host clock
+between the synchronisations that bracket them (it adds the graph launch).
 
 Helper modes for the committed rocprofv3 summaries (see the profile files for
 the exact commands): ``--calibrate-copy`` runs a torch copy of a known size so
@@ -46,7 +52,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "W6A16 GEMM TFLOP/s + weight HBM GB/s (% of peak), Llama-shaped layers M=1..128"
-DEFAULT_WORKLOAD = "llama7b_attn_1x4096x4096"
+DEFAULT_WORKLOAD = "llama70b_mlp_16x28672x8192"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
 ROT_BYTES = 1 << 30             # >= 1 GiB of rotated copies (> 256 MB Infinity Cache)
@@ -114,34 +120,49 @@ def algorithmic_bytes(M, N, K, fmt="e3m2"):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, untuned, on a bounded row sample.
 # ---------------------------------------------------------------------------
+def cpu_cores():
+    """Host cores this process may use (at most 16: a one-GPU machine's share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def cpu_baseline(shape, packed, scales, X, budget_s=20.0, fmt="e3m2"):
+    """The oracle as it stands, on every core of this host's share: its
+    functions (unpack, de-quantise, float64 GEMM) run unchanged on
+    row-block chunks of the sample, one chunk per thread, BLAS limited to one
+    thread per call so that the threads in use equal the cores."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        M, N, K = shape.M, shape.N, shape.K
-        row_bytes = weight_bytes(16, K, fmt)            # one packed row block
+    cores = cpu_cores()
+    M, N, K = shape.M, shape.N, shape.K
+    row_bytes = weight_bytes(16, K, fmt)            # one packed row block
 
-        def unpack(buf, n):
-            if fmt == "e3m2":
-                return oracle.unpack_np(buf, n, K)
-            return oracle.unpack_tiles(buf, n, K, fmt)
+    def unpack(buf, n):
+        if fmt == "e3m2":
+            return oracle.unpack_np(buf, n, K)
+        return oracle.unpack_tiles(buf, n, K, fmt)
 
-        def dequant(buf, n):
-            if fmt == "sparse24":
-                from oracle import sparse24
-                codes, pos = sparse24.unpack_tiles(buf, n, K)
-                return sparse24.dequant_ref(codes, pos, scales[:n], K)
-            return oracle.dequant_ref(unpack(buf, n), scales[:n], fmt)
+    def dequant(buf, n, sc):
+        if fmt == "sparse24":
+            from oracle import sparse24
+            codes, pos = sparse24.unpack_tiles(buf, n, K)
+            return sparse24.dequant_ref(codes, pos, sc, K)
+        return oracle.dequant_ref(unpack(buf, n), sc, fmt)
 
+    def chunk(b0, b1):
+        wdq = dequant(packed[b0 * row_bytes: b1 * row_bytes], 16 * (b1 - b0), scales[16 * b0: 16 * b1])
+        oracle.gemm_ref(X, wdq)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(cores) as ex:
         def run(nblk):
+            step = max(1, -(-nblk // cores))
             t0 = time.perf_counter()
-            wdq = dequant(packed[: nblk * row_bytes], 16 * nblk)
-            oracle.gemm_ref(X, wdq)
+            list(ex.map(lambda b: chunk(b, min(nblk, b + step)), range(0, nblk, step)))
             return time.perf_counter() - t0
         # Size one run to about a third of the budget (capped at the whole
         # layer), then repeat it until the budget is spent (at least 3 runs)
         # and report the median.
-        nblk = max(1, min(N // 16, (4 * 2**20) // row_bytes))
+        nblk = max(cores, min(N // 16, (4 * 2**20) // row_bytes))
         t = run(nblk)
         nblk = int(max(1, min(N // 16, nblk * (budget_s / 3) / max(t, 1e-3))))
         ts = [run(nblk)]
@@ -154,11 +175,11 @@ def cpu_baseline(shape, packed, scales, X, budget_s=20.0, fmt="e3m2"):
     return {
         "value": round(wbytes / tmed / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{nrows} of {N} weight rows x K={K}, M={M}, {fmt}: oracle unpack + dequant_ref + gemm_ref "
-                  f"(float64), median of {len(ts)} runs of {tmed:.2f} s ({sum(ts):.1f} s in all), "
-                  f"single thread (BLAS limited to 1)",
+                  f"(float64) on row-block chunks over {cores} threads (BLAS 1 thread each), median of "
+                  f"{len(ts)} runs of {tmed:.2f} s ({sum(ts):.1f} s in all)",
         "tflops": round(2.0 * M * nrows * K / tmed / 1e12, 6),
     }
 
@@ -249,6 +270,27 @@ def read_ceiling(torch, nbytes, stream):
         best = gbs if best is None else max(best, gbs)
     del bufs
     return best
+
+
+def mfma_ceiling(torch, stream):
+    """Dense fp16 MFMA rate of a register-only MFMA loop over the whole GPU
+    (TFLOP/s): 8 workgroups of 4 waves per CU, each wave 8 independent
+    16x16x32 MFMA chains."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_fp6_amd", "libfp6probe.so"))
+    lib.fp6probe_mfma.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    chains = lib.fp6probe_mfma_chains()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 8 * cus, 4096
+    out = torch.zeros(4, dtype=torch.float32, device="cuda")
+
+    def launch(i):
+        if lib.fp6probe_mfma(iters, blocks, out.data_ptr(), stream.cuda_stream):
+            raise RuntimeError("probe launch failed")
+    launch(0)
+    torch.cuda.synchronize()
+    us = _time_graph(torch, stream, launch, 10)
+    return blocks * 4 * iters * chains * 16384 / us / 1e6
 
 
 # ---------------------------------------------------------------------------
@@ -523,8 +565,8 @@ def main():
     wbytes = weight_bytes(N, K, fmt)
     abytes = algorithmic_bytes(M, N, K, fmt)
     flops = 2.0 * M * N * K
-    weight_gbs = wbytes * args.steps / wall_s / 1e9
-    tflops = flops * args.steps / wall_s / 1e12
+    weight_gbs = wbytes / per_launch_s / 1e9
+    tflops = flops / per_launch_s / 1e12
     # Ridge: 2500 TFLOP/s / 8 TB/s = 312.5 flop/byte; per packed weight byte the
     # layer does 2*M*N*K / (bits/8*N*K) = 16*M/bits flop, so FP6 is HBM-bound
     # for M < 117 (FP5 98, FP4 78; 2:4-sparse FP6, 0.5 byte per dense weight,
@@ -560,7 +602,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_s * 1e3 / args.steps, 6),
+        "ms_per_step": round(per_launch_s * 1e3, 6),
+        "wall_ms_per_step": round(wall_s * 1e3 / args.steps, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -587,6 +630,9 @@ def main():
         ceil_gbs = read_ceiling(torch, wbytes, stream)
         out["read_ceiling_gbs"] = round(ceil_gbs, 1)
         out["weight_frac_of_read_ceiling"] = round(wbytes / per_launch_s / 1e9 / ceil_gbs, 4)
+        mfma_tf = mfma_ceiling(torch, stream)
+        out["mfma_ceiling_tflops"] = round(mfma_tf, 1)
+        out["mfma_frac_of_probe"] = round(tflops / mfma_tf, 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, packed, scales, X, fmt=fmt)
     print(json.dumps(out), flush=True)

@@ -1,4 +1,5 @@
-// Bandwidth probes for the benchmark's roofline (not part of the FP6 path).
+// Bandwidth and MFMA probes for the benchmark's roofline (not part of the FP6
+// path).
 //
 // fp6probe_read: each wave streams `per_wave` contiguous 1 KiB chunks with
 // 16-byte loads per lane, 8 loads in flight, and folds them into a value that
@@ -11,6 +12,8 @@
 
 namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kUnroll = 8;
 
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t nchunks,
@@ -32,6 +35,35 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   }
   if (acc == 0x12345679u) out[0] = acc;
 }
+
+// fp6probe_mfma: every wave issues `iters` rounds of kChains independent
+// v_mfma_f32_16x16x32_f16 (16x16x32, 16384 flops each) on register operands,
+// with no memory traffic in the loop: the practical dense fp16 MFMA ceiling
+// (the vendor's peak is a bound).  The operands depend on the lane and a
+// kernel argument and the sums are stored only if they match an impossible
+// value, so nothing can be folded away.
+constexpr int kChains = 8;
+
+__global__ __launch_bounds__(256) void mfma_kernel(int64_t iters, float seed, float* out) {
+  const int lane = threadIdx.x & 63;
+  half8v a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<_Float16>(seed * static_cast<float>((lane + i) & 7));
+    b[i] = static_cast<_Float16>(seed * static_cast<float>((lane * 3 + i) & 7));
+  }
+  float4v acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (s == 1234.5678f) out[0] = s;
+}
 }  // namespace
 
 extern "C" {
@@ -47,4 +79,18 @@ int fp6probe_read(const void* src, int64_t bytes, int64_t per_wave, void* out, v
   return hipLaunchKernel(reinterpret_cast<const void*>(&read_kernel), dim3((waves + 3) / 4), dim3(256),
                          args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 1;
 }
+
+// `blocks` workgroups of 4 waves, each wave `iters` x 8 MFMAs of 16384 flops;
+// out: device float scratch.  Returns 0, or 1 on bad arguments or a launch
+// failure.
+int fp6probe_mfma(int64_t iters, int64_t blocks, void* out, void* stream) {
+  if (!out || iters < 1 || blocks < 1 || blocks >= (int64_t(1) << 31)) return 1;
+  float seed = 0.25f;
+  float* o = static_cast<float*>(out);
+  void* args[] = {&iters, &seed, &o};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&mfma_kernel), dim3(static_cast<unsigned>(blocks)),
+                         dim3(256), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 1;
+}
+
+int fp6probe_mfma_chains(void) { return kChains; }
 }
