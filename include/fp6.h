@@ -46,7 +46,8 @@ enum fp6_status {
   FP6_E_ALIGN = 3,  /* a device pointer is not 16-byte aligned (scales: 2)  */
   FP6_E_CODE = 4,   /* a weight code is > 63                                */
   FP6_E_SCALE = 5,  /* a scale is not finite or |s| >= 16                   */
-  FP6_E_SIZE = 6,   /* a caller buffer size does not match                  */
+  FP6_E_SIZE = 6,   /* a caller buffer size does not match (fp6_linear_noalloc:
+                       the plan needs more than the static scratch)         */
   FP6_E_HIP = 7,    /* a HIP runtime call or kernel launch failed           */
   FP6_E_VALUE = 8,  /* an input value is invalid (NaN/inf weight) or a plan
                        parameter is out of range                            */
@@ -151,6 +152,27 @@ int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
  */
 int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
                int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * fp6_linear_noalloc -- fp6_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, plan, kernels and result bits as
+ * fp6_linear, but split plans keep their fp32 partial sums and arrival
+ * counters in a static device array of the library (40 MiB, of which the
+ * first 256 KiB are counters; each GPU holds its own copy until the process
+ * ends) instead of a per-stream workspace: the call never calls hipMalloc,
+ * hipFree or any allocating routine.  The first call on a device looks the
+ * array up and clears its counters with a kernel on `stream`; split plans
+ * leave them at zero.
+ * Every call on a GPU shares that GPU's one array: calls that overlap on one
+ * GPU (on different streams, or graphs replayed alongside eager calls) race
+ * and give wrong sums.  Order them on one stream.
+ * Errors: as fp6_linear, plus FP6_E_SIZE when the plan would need more
+ * partial sums or counters than the array holds (no automatic plan does on a
+ * 256-CU MI355X: at most 32 MiB).
+ */
+int fp6_linear_noalloc(const void* X, const void* packed_W, const void* scales, void* Y,
+                       int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * fp6_linear_plan -- fp6_linear with the schedule forced (tuning and tests).

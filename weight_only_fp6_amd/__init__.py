@@ -39,7 +39,7 @@ STATUS_NAMES = {
 }
 EXPORTED = (
     "fp6_pack_version", "fp6_status_string", "fp6_packed_bytes", "fp6_quantize_rows",
-    "fp6_prepack", "fp6_linear", "fp6_linear_plan", "fp6_linear_plan_query", "fp6_dequant",
+    "fp6_prepack", "fp6_linear", "fp6_linear_noalloc", "fp6_linear_plan", "fp6_linear_plan_query", "fp6_dequant",
     "fp6_release", "fpx_bits", "fpx_packed_bytes", "fpx_quantize_rows", "fpx_prepack",
     "fpx_linear", "fpx_linear_plan", "fpx_dequant", "fp6s_packed_bytes", "fp6s_prune_quantize",
     "fp6s_prepack", "fp6s_linear", "fp6s_linear_plan", "fp6s_linear_plan_query", "fp6s_dequant",
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "fp6_quantize_rows": ([vp, i64, i64, vp, vp], i32),
         "fp6_prepack": ([vp, vp, i64, i64, vp, sz], i32),
         "fp6_linear": ([vp, vp, vp, vp, i64, i64, i64, vp], i32),
+        "fp6_linear_noalloc": ([vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp6_linear_plan": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp], i32),
         "fp6_linear_plan_query": ([i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "fp6_dequant": ([vp, vp, vp, i64, i64, vp], i32),

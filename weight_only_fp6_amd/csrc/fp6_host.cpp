@@ -210,7 +210,7 @@ const char* fp6_status_string(int status) {
     case FP6_E_ALIGN: return "a device pointer is misaligned";
     case FP6_E_CODE: return "a weight code does not fit the format's width";
     case FP6_E_SCALE: return "a scale is not finite or outside the format's range";
-    case FP6_E_SIZE: return "a buffer size does not match";
+    case FP6_E_SIZE: return "a buffer size does not match, or the plan needs more than the static scratch";
     case FP6_E_HIP: return "a HIP runtime call or kernel launch failed";
     case FP6_E_VALUE: return "an input value or plan parameter is invalid";
     default: return "unknown status";

@@ -22,6 +22,16 @@
 #include "fp6_limits.h"
 #include "fpx_launch.h"
 
+// Scratch of fp6_linear_noalloc: the split-K arrival counters (the first
+// kScratchCounterBytes) and fp32 partial sums of its plans, in device memory
+// that the library owns, so that the call allocates nothing.  Every GPU the
+// library runs on holds its own copy until the process ends.  Automatic plans
+// on a 256-CU MI355X need at most 32 MiB of partial sums (a split plan puts
+// at most one round of workgroups on the CUs).
+constexpr size_t kScratchBytes = size_t(40) << 20;
+constexpr size_t kScratchCounterBytes = size_t(256) << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 using fpx::Kind;
@@ -93,6 +103,38 @@ int get_workspace_locked(int dev, void* stream, size_t part_bytes, size_t counte
     ws.counter_count = cc;
   }
   *out = &ws;
+  return FP6_OK;
+}
+
+// The scratch array's device address on each GPU (hipGetSymbolAddress on
+// the first fp6_linear_noalloc call with that device current).
+std::map<int, unsigned char*> g_scratch;
+
+__global__ void zero_words(unsigned* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Address of this device's scratch; on the first call for the device it is
+// looked up and its counters are cleared by a kernel on `stream` (split
+// plans leave the counters at zero when they finish, so once is enough).
+int scratch_for_device(int dev, hipStream_t stream, unsigned char** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    *out = it->second;
+    return FP6_OK;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FP6_E_HIP;
+  unsigned* counters = static_cast<unsigned*>(ptr);
+  int64_t words = static_cast<int64_t>(kScratchCounterBytes / sizeof(unsigned));
+  void* args[] = {&counters, &words};
+  if (hipLaunchKernel(reinterpret_cast<const void*>(&zero_words), dim3(static_cast<unsigned>((words + 255) / 256)),
+                      dim3(256), args, 0, stream) != hipSuccess)
+    return FP6_E_HIP;
+  g_scratch[dev] = static_cast<unsigned char*>(ptr);
+  *out = static_cast<unsigned char*>(ptr);
   return FP6_OK;
 }
 
@@ -537,6 +579,32 @@ int fp6s_dequant(const void* packed_W, const void* scales, void* W16, int64_t N,
 int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
                int64_t N, int64_t K, void* stream) {
   return linear_impl(fpx::kFmtE3M2, X, packed_W, scales, Y, M, N, K, 0, 0, stream);
+}
+
+int fp6_linear_noalloc(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
+                       int64_t N, int64_t K, void* stream) {
+  int st = check_linear_args(X, packed_W, scales, Y, M, N, K);
+  if (st != FP6_OK || M == 0) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
+  const int cus = device_cus(dev);
+  const Plan p = choose_plan(M, N, K, cus, 0, 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fpx::LaunchCtx ctx{X, packed_W, scales, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus, s};
+  if (p.splits > 1) {
+    int64_t units = 0, floats = 0;
+    plan_units(kCfgs[p.variant], M, N, &units, &floats);
+    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
+    if (static_cast<size_t>(units) * sizeof(unsigned) > kScratchCounterBytes ||
+        part_bytes > kScratchBytes - kScratchCounterBytes)
+      return FP6_E_SIZE;
+    unsigned char* base = nullptr;
+    st = scratch_for_device(dev, s, &base);
+    if (st != FP6_OK) return st;
+    ctx.counters = reinterpret_cast<unsigned*>(base);
+    ctx.part = reinterpret_cast<float*>(base + kScratchCounterBytes);
+  }
+  return launch_format(fpx::kFmtE3M2, ctx);
 }
 
 int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
