@@ -53,7 +53,7 @@ enum fp6_status {
                        parameter is out of range                            */
 };
 
-/* Version of the packed weight layout produced by fp6_prepack (1). */
+/* Version of the packed weight layout produced by fp6_prepack (2). */
 int fp6_pack_version(void);
 
 /* Static, NUL-terminated text for a status code (never NULL). */
@@ -82,7 +82,7 @@ int fp6_quantize_rows(const float* W, int64_t N, int64_t K,
 
 /*
  * fp6_prepack -- host, synchronous, pure and deterministic (offline step).
- * Re-orders 6-bit codes into packed layout v1 (TC-FPx explainer, section
+ * Re-orders 6-bit codes into packed layout v2 (TC-FPx explainer, section
  * "redesigning the kernel solution": bit-level pre-packing and 2+4 splitting
  * before inference).
  *
@@ -93,22 +93,27 @@ int fp6_quantize_rows(const float* W, int64_t N, int64_t K,
  * packed:  host out, packed_bytes == fp6_packed_bytes(N, K).
  * Errors: FP6_E_NULL, FP6_E_SHAPE, FP6_E_CODE, FP6_E_SCALE, FP6_E_SIZE.
  *
- * Packed layout v1.  Tiles of 16 rows x 256 k, 3072 bytes each; tile
- * (nb, kb) starts at byte (nb*(K/256) + kb)*3072.  Within a tile, local row r
- * (0..15) and local k = 32*j + 8*g + i (k-step j 0..7, lane group g 0..3,
- * element i 0..7) belong to wave lane L = 16*g + r.  Each code c is split into
- * a 2-bit piece (s, e2) = c >> 4 and a 4-bit piece (e1 e0 m1 m0) = c & 15.
+ * Packed layout v2 (fp6_pack_version() == 2).  Tiles of 16 rows x 256 k,
+ * 3072 bytes each; tile (nb, kb) starts at byte (nb*(K/256) + kb)*3072.
+ * Within a tile, local row r (0..15) and local k = 32*j + 8*g + i (k-step j
+ * 0..7, lane group g 0..3, element i 0..7) belong to wave lane L = 16*g + r.
+ * Each code c is split into a 2-bit piece (s, e2) = c >> 4 and a 4-bit piece
+ * (e1 e0 m1 m0) = c & 15.  Element i is in group G = i/4 at byte E = i%4.
  *   bytes [0,1024):    2-bit plane.  Lane L's 16 bytes at 16*L are four
  *                      little-endian words; word j/2 covers k-steps j, j+1.
- *                      With p = 4*(j%2) + i/2 and h = i%2, bit e2 is at
- *                      (12 + 16h + 2p) mod 32 and bit s at (15 + 16h + 2p) mod 32.
+ *                      With rho = 4*(j%2) + 2*G, bit e2 is at
+ *                      (4 + 8E + rho) mod 32 and bit s at (7 + 8E + rho) mod 32.
  *   bytes [1024,3072): 4-bit plane; k-steps 0..3 in the first 1024 bytes,
  *                      4..7 in the second.  Lane L's 16 bytes at 16*L hold
  *                      words j%4; element i is the nibble at bits
- *                      4*(i/2 + 4*(i%2)) .. +3.
+ *                      4*(2E + G) .. +3 (elements 0..3 in the low nibbles).
  * A wave reads one tile with three fully coalesced 16-byte-per-lane loads,
  * and each lane's words hold exactly the 8 k-values per k-step that a
- * 16x16x32 fp16 MFMA A-operand lane consumes.
+ * 16x16x32 fp16 MFMA A-operand lane consumes.  The positions make the fp16
+ * high bytes (s<<7)|(e2<<4)|nibble of four elements one and_or of the
+ * 4-bit word with the rotated 2-bit word, spread onto fp16 pairs by one
+ * byte permute per pair.  (Layout v1, the first version, placed the pieces
+ * per fp16 pair instead; v2 changed only the bit positions.)
  */
 int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
                 int64_t N, int64_t K, void* packed, size_t packed_bytes);

@@ -29,14 +29,15 @@
  * is the same as the matching fp6_* call.  An unknown format gives
  * FP6_E_VALUE (before any HIP call).
  *
- * Packed layout v1 for each format: tiles of 16 rows x 256 k at
+ * Packed layout v2 for each format: tiles of 16 rows x 256 k at
  * (nb*(K/256) + kb) * tile_bytes, tile_bytes = 4096*bits/8; local row r,
  * local k = 32*j + 8*g + i belong to wave lane L = 16*g + r.
  *   e3m2: as described in fp6.h.
- *   e2m3: as e3m2 with 2-bit piece (s, e1) = c >> 4 and 4-bit piece
- *         (e0 m2 m1 m0) = c & 15; in the 2-bit plane, with p = 4*(j%2) + i/2,
- *         h = i%2 and b = [0,1,2,3,8,9,10,11][p], bit e1 is at b + 16h and
- *         bit s at b + 4 + 16h of word j/2 of lane L.
+ *   e2m3: planes placed as e3m2's, with 2-bit piece (s, e1) = c >> 4 and
+ *         4-bit piece (e0 m2 m1 m0) = c & 15; in the 2-bit plane, with
+ *         p = 4*(j%2) + i/2, h = i%2 and b = [0,1,2,3,8,9,10,11][p], bit e1
+ *         is at b + 16h and bit s at b + 4 + 16h of word j/2 of lane L; in
+ *         the 4-bit word j%4 element i is the nibble at slot i/2 + 4*(i%2).
  *   e2m2: 4-bit plane (e1 e0 m1 m0 = c & 15) at tile bytes [0,2048) laid out
  *         like the FP6 one ([0,1024) k-steps 0..3, [1024,2048) k-steps 4..7,
  *         16 bytes per lane, word j%4, nibble slot i/2 + 4*(i%2)); 1-bit
@@ -79,7 +80,7 @@ int fpx_quantize_rows(int format, const float* W, int64_t N, int64_t K, uint8_t*
 
 /*
  * fpx_prepack -- host, synchronous, pure (offline step): codes (host uint8
- * [N][K], each < 2^bits) into packed layout v1 of the format.  scales are
+ * [N][K], each < 2^bits) into packed layout v2 of the format.  scales are
  * only checked against the format's range.  packed_bytes must equal
  * fpx_packed_bytes(format, N, K).  Errors: FP6_E_NULL, FP6_E_SHAPE,
  * FP6_E_CODE, FP6_E_SCALE, FP6_E_SIZE, FP6_E_VALUE (unknown format).

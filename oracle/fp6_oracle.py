@@ -27,7 +27,7 @@ packed layout.  The readings used here (each one stated where it is used):
   gradual underflow, signed zero kept).
 * Y_ref = X . Wdq^T accumulated in float64 (nn.Linear convention: X is
   [M,K], W is [N,K], Y is [M,N]).
-* Packed layout v1 (the library's private offline format; any bijection is
+* Packed layout v2 (the library's private offline format; any bijection is
   correct, this oracle checks the round trip): see :func:`unpack_scalar`.
 
 Other widths (FP6-LLM abstract: one Tensor-Core kernel scheme for float weights
@@ -235,7 +235,7 @@ def quantize_rows_sampled(W_rows, fmt="e3m2") -> tuple[np.ndarray, np.ndarray]:
 
 
 # ---------------------------------------------------------------------------
-# O3: packed layout v1.
+# O3: packed layout v2.
 #
 # Codes c[n][k] with N % 16 == 0 and K % 256 == 0.  The buffer holds
 # N*K*bits/8 bytes in tiles of 16 rows x 256 k.  Tile (nb, kb) starts at byte
@@ -247,17 +247,21 @@ def quantize_rows_sampled(W_rows, fmt="e3m2") -> tuple[np.ndarray, np.ndarray]:
 # = c>>4) and a 4-bit piece (bits e1,e0,m1,m0 = c&15).
 #   * 2-bit plane: bytes [0,1024) of the tile.  Lane L owns the 16 bytes at
 #     16*L, as 4 little-endian 32-bit words; word j//2 holds k-steps j and
-#     j+1.  With pair p = 4*(j%2) + i//2 and half h = i%2, bit e2 sits at
-#     position (12 + 16*h + 2*p) mod 32 and bit s at (15 + 16*h + 2*p) mod 32.
+#     j+1.  Element i of k-step j belongs to group G = i//4 at byte E = i%4;
+#     with rho = 4*(j%2) + 2*G, bit e2 sits at position (4 + 8*E + rho) mod
+#     32 and bit s at (7 + 8*E + rho) mod 32 (the four rho values put the 16
+#     elements of a word on the 16 even and the 16 odd positions).
 #   * 4-bit plane: bytes [1024,3072).  k-steps 0..3 in [1024,2048), 4..7 in
 #     [2048,3072); lane L owns 16 bytes at 16*L in each half, word j%4 is
-#     k-step j.  Element i occupies nibble slot (i//2) + 4*(i%2), i.e. bits
-#     4*slot .. 4*slot+3 (slots hold elements 0,2,4,6,1,3,5,7).
-# FP6 e2m3 (tile 3072 bytes): as e3m2 (2-bit piece = s,e1; 4-bit piece =
-#   e0,m2,m1,m0), except the 2-bit plane positions: with b = [0,1,2,3,8,9,10,
-#   11][p], bit e1 sits at b + 16*h and bit s at b + 4 + 16*h.
+#     k-step j.  Element i occupies nibble slot 2*(i%4) + i//4, i.e. bits
+#     4*slot .. 4*slot+3 (elements 0..3 in the low nibbles of bytes 0..3,
+#     elements 4..7 in the high nibbles).
+# FP6 e2m3 (tile 3072 bytes): 2-bit piece = s,e1; 4-bit piece = e0,m2,m1,m0.
+#   With pair p = 4*(j%2) + i//2 and half h = i%2, b = [0,1,2,3,8,9,10,
+#   11][p]: bit e1 sits at b + 16*h and bit s at b + 4 + 16*h of the 2-bit
+#   word; element i occupies nibble slot (i//2) + 4*(i%2) of the 4-bit word.
 # FP5 e2m2 (tile 2560 bytes): 4-bit piece (e1,e0,m1,m0 = c&15) in a 4-bit
-#   plane at bytes [0,2048) laid out as the FP6 one; the sign (c>>4) in a
+#   plane at bytes [0,2048) laid out as the e2m3 one; the sign (c>>4) in a
 #   1-bit plane at [2048,2560): lane L owns the 8 bytes at 2048 + 8*L as two
 #   words; word j//4 holds k-steps 4*(j//4)..+3, with P = 4*(j%4) + i//2 the
 #   sign sits at bit P + 16*h.
@@ -281,7 +285,7 @@ def packed_bytes(N: int, K: int, fmt="e3m2") -> int:
 
 def _check_shape(N: int, K: int) -> None:
     if N <= 0 or K <= 0 or N % TILE_N or K % TILE_K:
-        raise ValueError("layout v1 needs N % 16 == 0 and K % 256 == 0, both > 0")
+        raise ValueError("layout v2 needs N % 16 == 0 and K % 256 == 0, both > 0")
 
 
 def _locate(N: int, K: int, n: int, k: int):
@@ -292,13 +296,13 @@ def _locate(N: int, K: int, n: int, k: int):
     g, i = divmod(rem, 8)
     lane = 16 * g + r
     base = (nb * (K // TILE_K) + kb) * TILE_BYTES
-    p = 4 * (j % 2) + i // 2
-    h = i % 2
+    grp, e = divmod(i, 4)
+    rho = 4 * (j % 2) + 2 * grp
     w2 = base + 16 * lane + 4 * (j // 2)
-    bit_e2 = (12 + 16 * h + 2 * p) % 32
-    bit_s = (15 + 16 * h + 2 * p) % 32
+    bit_e2 = (4 + 8 * e + rho) % 32
+    bit_s = (7 + 8 * e + rho) % 32
     w4 = base + 1024 + 1024 * (j // 4) + 16 * lane + 4 * (j % 4)
-    nib = 4 * ((i // 2) + 4 * (i % 2))
+    nib = 4 * (2 * e + grp)
     return w2, bit_e2, bit_s, w4, nib
 
 
@@ -346,7 +350,7 @@ def _set_word(buf, off: int, val: int) -> None:
 
 
 def pack_scalar(codes, fmt="e3m2") -> np.ndarray:
-    """Scalar packer of layout v1 (pure Python; small inputs only).
+    """Scalar packer of layout v2 (pure Python; small inputs only).
 
     Used only to pin :func:`unpack_scalar` (bijection checks); the library has
     its own packer.
@@ -367,7 +371,7 @@ def pack_scalar(codes, fmt="e3m2") -> np.ndarray:
 
 
 def unpack_scalar(packed, N: int, K: int, fmt="e3m2") -> np.ndarray:
-    """Scalar unpacker of layout v1 (pure Python loop over every code)."""
+    """Scalar unpacker of layout v2 (pure Python loop over every code)."""
     f = _fmt(fmt)
     _check_shape(N, K)
     buf = bytes(np.asarray(packed, dtype=np.uint8).ravel())
@@ -413,7 +417,7 @@ def unpack_tiles(packed, N: int, K: int, fmt="e3m2") -> np.ndarray:
 
 
 def unpack_np(packed, N: int, K: int) -> np.ndarray:
-    """Vectorised unpacker of layout v1 (same definition, NumPy indexing)."""
+    """Vectorised unpacker of layout v2 (e3m2; same definition, NumPy indexing)."""
     _check_shape(N, K)
     p = np.asarray(packed, dtype=np.uint8).ravel()
     if p.size != N * K * 3 // 4:
@@ -426,11 +430,11 @@ def unpack_np(packed, N: int, K: int) -> np.ndarray:
     out = np.zeros((nbk, kbk, TILE_N, 8, 4, 8), dtype=np.int64)  # [nb,kb,r,j,g,i]
     for j in range(8):
         for i in range(8):
-            p_ = 4 * (j % 2) + i // 2
-            h = i % 2
-            b_e2 = (12 + 16 * h + 2 * p_) % 32
-            b_s = (15 + 16 * h + 2 * p_) % 32
-            nib = 4 * ((i // 2) + 4 * (i % 2))
+            grp, e = divmod(i, 4)
+            rho = 4 * (j % 2) + 2 * grp
+            b_e2 = (4 + 8 * e + rho) % 32
+            b_s = (7 + 8 * e + rho) % 32
+            nib = 4 * (2 * e + grp)
             for g in range(4):
                 lanes = slice(16 * g, 16 * g + 16)
                 v2 = w2[:, :, lanes, j // 2]

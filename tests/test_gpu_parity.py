@@ -31,6 +31,7 @@ ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18, 19, 20, 2
 KSPLIT = 9
 KSPLIT16 = 12
 KSLICE = 13
+SMALL_M = (KSPLIT, KSPLIT16, KSLICE)   # M <= 16 only
 
 
 def _bits16(t):
@@ -144,7 +145,7 @@ def test_linear_small_shapes_ragged_m(M, NK):
     N, K = NK
     p = Prepared(M, N, K, seed_w=N * 7 + K, seed_x=M * 11 + 1)
     X, packed, s = p.to_device()
-    for variant in ALL_VARIANTS + ((KSPLIT, KSPLIT16, KSLICE) if M <= 16 else ()):
+    for variant in ALL_VARIANTS + (SMALL_M if M <= 16 else ()):
         Y = fp6.linear_plan(X, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
@@ -178,7 +179,7 @@ def test_linear_ksplit_k_coverage(K, M):
     yref = y_ref(X, ws.wdq_ref)
     Xd = torch.from_numpy(X).to(DEV)
     packed, s = ws.to_device()
-    variants = (0, KSPLIT, KSPLIT16, KSLICE) if K <= 8192 else (0, KSLICE)
+    variants = (0,) + SMALL_M if K <= 8192 else (0, KSLICE)
     for variant in variants:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()

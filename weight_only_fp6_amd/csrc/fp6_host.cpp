@@ -1,5 +1,5 @@
 // Host side of the FPx weight-only linear layer: status strings, size rules,
-// the row quantiser and the offline packer (layout v1) of every format.
+// the row quantiser and the offline packer (layout v2) of every format.
 //
 // Plain C++17, no HIP calls: everything here runs on the CPU.
 //
@@ -103,7 +103,7 @@ bool shape_ok(int64_t N, int64_t K) {
          N % fp6::kTileN == 0 && K % fp6::kTileK == 0 && N * K <= fp6::kMaxNK;
 }
 
-// One 16 x 256 tile of codes (rows of `src` K apart) into packed layout v1.
+// One 16 x 256 tile of codes (rows of `src` K apart) into packed layout v2.
 // Lane L = 16g + r owns row r, k = 32j + 8g + i (k-step j, element i).
 void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
   // Per lane: 4-bit words w4[j/4][lane][j%4]; 6-bit formats add 2-bit words
@@ -121,16 +121,21 @@ void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
     for (int j = 0; j < 8; ++j) {
       for (int i = 0; i < 8; ++i) {
         const uint32_t c = row[32 * j + 8 * g + i];
-        const int p = 4 * (j & 1) + (i >> 1);  // 6-bit formats: pair in the 2-bit word
+        const int p = 4 * (j & 1) + (i >> 1);  // e2m3: pair in the 2-bit word
         const int h = i & 1;                   // even / odd element of the pair
         const int slot = (i >> 1) + 4 * (i & 1);
         uint32_t& d4 = w4[j >> 2][lane][j & 3];
         switch (format) {
-          case FPX_E3M2:
-            w2[lane][j >> 1] |= ((c >> 4) & 1u) << ((12 + 16 * h + 2 * p) & 31);
-            w2[lane][j >> 1] |= ((c >> 5) & 1u) << ((15 + 16 * h + 2 * p) & 31);
-            d4 |= (c & 0xFu) << (4 * slot);
+          case FPX_E3M2: {
+            // Group G = i/4 at byte E = i%4: e2 and s at bits 4 and 7 of byte
+            // E once the word is rotated right by rho = 4(j%2) + 2G; the
+            // nibble in slot 2E + G (low nibbles: elements 0..3).
+            const int G = i >> 2, E = i & 3, rho = 4 * (j & 1) + 2 * G;
+            w2[lane][j >> 1] |= ((c >> 4) & 1u) << ((4 + 8 * E + rho) & 31);
+            w2[lane][j >> 1] |= ((c >> 5) & 1u) << ((7 + 8 * E + rho) & 31);
+            d4 |= (c & 0xFu) << (4 * (2 * E + G));
             break;
+          }
           case FPX_E2M3: {
             const int b = kE2M3Base[p] + 16 * h;
             w2[lane][j >> 1] |= ((c >> 4) & 1u) << b;
@@ -171,7 +176,7 @@ void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
 // j (64 dense k) and lane L = 16g + r, element i is kept weight i%2 of the
 // dense group at offset 64j + 32(g%2) + 16(i/4) + 8(g/2) + 4((i%4)/2): the
 // A-operand order of v_smfmac_f32_16x16x64_f16.  The 6-bit codes fill bytes
-// [0, 3072) exactly as packed layout v1 fills an FP6 tile (lane, k-step j,
+// [0, 3072) exactly as packed layout v2 fills an FP6 tile (lane, k-step j,
 // element i); the 2-bit positions fill [3072, 4096): lane L's word j/2 at
 // 3072 + 16L, bits 16(j%2) + 2i.
 void pack_sparse_tile(const uint8_t* codes, const uint8_t* pos, int64_t half_k, uint8_t* tile) {
@@ -200,7 +205,7 @@ void pack_sparse_tile(const uint8_t* codes, const uint8_t* pos, int64_t half_k, 
 
 extern "C" {
 
-int fp6_pack_version(void) { return 1; }
+int fp6_pack_version(void) { return 2; }
 
 const char* fp6_status_string(int status) {
   switch (status) {

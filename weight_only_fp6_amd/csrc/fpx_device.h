@@ -81,22 +81,30 @@ struct HalfFp4 { u32x4 q4; };
 
 // 6-bit formats, one k-step: 8 fp16 weights (elements 8g..8g+7 of row r)
 // from the 2-bit word d2 (k-steps 2*(j/2), +1) and the 4-bit word d4.
-//   e3m2: pair p = 4*(j%2)+q has e2,s at bits 12+2p, 15+2p (+16 for the odd
-//         element); rotr(d2, 2p) lands them on fp16 bits 12 and 15.
+//   e3m2: the fp16 pattern of v * 2^-12 has all its bits in the high byte:
+//         (s<<7) | (e2<<4) | (e1 e0 m1 m0).  The 4-bit word holds elements
+//         0..3 in the low nibbles and 4..7 in the high nibbles of its bytes;
+//         for group G (elements 4G..4G+3) the 2-bit word rotated right by
+//         4*(j%2) + 2G has e2 and s of element 4G+E at bits 4 and 7 of byte
+//         E.  So one and_or builds the four high bytes of a group, and one
+//         v_perm_b32 per pair spreads two of them onto the fp16 halves.
 //   e2m3: pair p has e1,s at bits b, b+4 (+16), b = [0,1,2,3,8,9,10,11][p];
-//         rotr(d2, (b-11) mod 32) lands them on fp16 bits 11 and 15.
-// The 4-bit word holds element i in nibble slot i/2 + 4*(i%2), so one shift
-// per pair q moves elements 2q and 2q+1 onto both fp16 halves.
+//         rotr(d2, (b-11) mod 32) lands them on fp16 bits 11 and 15; the
+//         4-bit word holds element i in nibble slot i/2 + 4*(i%2), so one
+//         shift per pair q moves elements 2q and 2q+1 onto both fp16 halves.
 template <int F, int JODD>
 __device__ __forceinline__ half8v splice6(uint32_t d2, uint32_t d4, half2v s2) {
   uint32_t t0, t1, t2, t3;
   if constexpr (F == kE3M2) {
-    constexpr uint32_t kM4 = 0x0F000F00u, kM2 = 0x90009000u;
-    constexpr int sh = 8 * JODD;  // 2*p for pair 0 of this k-step
-    t0 = ((d4 << 8) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 0) & kM2);
-    t1 = ((d4 << 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 2) & kM2);
-    t2 = (d4 & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 4) & kM2);
-    t3 = ((d4 >> 4) & kM4) | (__builtin_amdgcn_alignbit(d2, d2, sh + 6) & kM2);
+    constexpr uint32_t kNib = 0x0F0F0F0Fu, kSE = 0x90909090u;
+    // v_perm_b32 selectors: bytes (1, zero, 0, zero) and (3, zero, 2, zero).
+    constexpr uint32_t kLo = 0x010C000Cu, kHi = 0x030C020Cu;
+    const uint32_t wa = (d4 & kNib) | (__builtin_amdgcn_alignbit(d2, d2, 4 * JODD) & kSE);
+    const uint32_t wb = ((d4 >> 4) & kNib) | (__builtin_amdgcn_alignbit(d2, d2, 4 * JODD + 2) & kSE);
+    t0 = __builtin_amdgcn_perm(wa, wa, kLo);
+    t1 = __builtin_amdgcn_perm(wa, wa, kHi);
+    t2 = __builtin_amdgcn_perm(wb, wb, kLo);
+    t3 = __builtin_amdgcn_perm(wb, wb, kHi);
   } else {
     static_assert(F == kE2M3, "6-bit formats: e3m2, e2m3");
     constexpr uint32_t kM4 = 0x07800780u, kM2 = 0x88008800u;
