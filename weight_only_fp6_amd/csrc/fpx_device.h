@@ -338,6 +338,13 @@ __device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __rest
   return true;
 }
 
+// Workgroup-index arithmetic in 32 bits: every operand (workgroup index,
+// split count, tile and group counts, split * k-tiles) stays below 2^31, and
+// a 64-bit division by a runtime value is a long software sequence that
+// delays a kernel's first loads.  Division by 1 (no K-split) is skipped.
+__device__ __forceinline__ uint32_t udiv32(uint32_t a, uint32_t b) { return b == 1 ? a : a / b; }
+__device__ __forceinline__ uint32_t umod32(uint32_t a, uint32_t b) { return b == 1 ? 0 : a - (a / b) * b; }
+
 // Store one 16x16 accumulator block (Y^T layout: lane holds Y[m][n0+4g .. +3]).
 __device__ __forceinline__ void store_y_block(_Float16* __restrict__ Y, const float4v& v, int64_t m,
                                               int64_t M, int64_t N, int64_t n0, int g) {
@@ -400,14 +407,15 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
   const int64_t ngroups = (nblocks + A - 1) / A;
   const int64_t gquads = (ngroups + 3) >> 2;
-  int64_t b = blockIdx.x;
-  const int split = static_cast<int>(b % splits);
-  b /= splits;
-  const int64_t gq = b % gquads;
-  const int64_t mg = b / gquads + mg_base;
+  const uint32_t b = udiv32(blockIdx.x, splits);
+  const int split = static_cast<int>(umod32(blockIdx.x, splits));
+  const uint32_t bq = udiv32(b, static_cast<uint32_t>(gquads));
+  const int64_t gq = b - bq * static_cast<uint32_t>(gquads);
+  const int64_t mg = bq + mg_base;
   const int64_t rg = gq * 4 + wave;
   if (rg >= ngroups) return;
-  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
   const int r = lane & 15, g = lane >> 4;
 
   // Row blocks of this wave; a ragged last group repeats the last block and
@@ -544,15 +552,16 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
   const int64_t ngroups = (nblocks + A - 1) / A;
   const int64_t gsets = (ngroups + NW - 1) / NW;
-  int64_t b = blockIdx.x;
-  const int split = static_cast<int>(b % splits);
-  b /= splits;
-  const int64_t gs = b % gsets;
-  const int64_t mg = b / gsets + mg_base;
+  const uint32_t b = udiv32(blockIdx.x, splits);
+  const int split = static_cast<int>(umod32(blockIdx.x, splits));
+  const uint32_t bq = udiv32(b, static_cast<uint32_t>(gsets));
+  const int64_t gs = b - bq * static_cast<uint32_t>(gsets);
+  const int64_t mg = bq + mg_base;
   const int64_t rg_raw = gs * NW + wave;
   const bool wave_active = rg_raw < ngroups;
   const int64_t rg = wave_active ? rg_raw : ngroups - 1;  // idle waves still join barriers
-  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
   const int r = lane & 15, g = lane >> 4;
 
   const u32x4* w[A];
@@ -1068,12 +1077,14 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
-  int64_t bidx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int split = static_cast<int>(bidx % splits);
-  bidx /= splits;
-  const int64_t nt = bidx % ntiles;
-  const int64_t mg = bidx / ntiles + mg_base;
-  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const int split = static_cast<int>(umod32(lb, splits));
+  const uint32_t bidx = udiv32(lb, splits);
+  const uint32_t bq = udiv32(bidx, static_cast<uint32_t>(ntiles));
+  const int64_t nt = bidx - bq * static_cast<uint32_t>(ntiles);
+  const int64_t mg = bq + mg_base;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
   const int r = lane & 15, g = lane >> 4;
   const int64_t m0 = mg * BM;
 
@@ -1239,12 +1250,14 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
-  int64_t bidx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int split = static_cast<int>(bidx % splits);
-  bidx /= splits;
-  const int64_t nt = bidx % ntiles;
-  const int64_t mg = bidx / ntiles + mg_base;
-  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const int split = static_cast<int>(umod32(lb, splits));
+  const uint32_t bidx = udiv32(lb, splits);
+  const uint32_t bq = udiv32(bidx, static_cast<uint32_t>(ntiles));
+  const int64_t nt = bidx - bq * static_cast<uint32_t>(ntiles);
+  const int64_t mg = bq + mg_base;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
   const int r = lane & 15, g = lane >> 4;
   const int64_t m0 = mg * BM;
 

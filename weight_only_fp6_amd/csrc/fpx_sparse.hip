@@ -213,15 +213,16 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
   const int64_t nblocks = N >> 4, ktiles = K >> 9;
   const int64_t ngroups = (nblocks + A - 1) / A;
   const int64_t gsets = (ngroups + NW - 1) / NW;
-  int64_t b = blockIdx.x;
-  const int split = static_cast<int>(b % splits);
-  b /= splits;
-  const int64_t gs = b % gsets;
-  const int64_t mg = b / gsets + mg_base;
+  const uint32_t b = udiv32(blockIdx.x, splits);
+  const int split = static_cast<int>(umod32(blockIdx.x, splits));
+  const uint32_t bq = udiv32(b, static_cast<uint32_t>(gsets));
+  const int64_t gs = b - bq * static_cast<uint32_t>(gsets);
+  const int64_t mg = bq + mg_base;
   const int64_t rg_raw = gs * NW + wave;
   const bool wave_active = rg_raw < ngroups;
   const int64_t rg = wave_active ? rg_raw : ngroups - 1;  // idle waves still join barriers
-  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
   const int r = lane & 15, g = lane >> 4;
 
   const u32x4* w[A];
@@ -405,12 +406,14 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_tiled(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 9;
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
-  int64_t bidx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int split = static_cast<int>(bidx % splits);
-  bidx /= splits;
-  const int64_t nt = bidx % ntiles;
-  const int64_t mg = bidx / ntiles + mg_base;
-  const int64_t kt0 = split * ktiles / splits, kt1 = (split + 1) * ktiles / splits;
+  const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const int split = static_cast<int>(umod32(lb, splits));
+  const uint32_t bidx = udiv32(lb, splits);
+  const uint32_t bq = udiv32(bidx, static_cast<uint32_t>(ntiles));
+  const int64_t nt = bidx - bq * static_cast<uint32_t>(ntiles);
+  const int64_t mg = bq + mg_base;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
   const int r = lane & 15, g = lane >> 4;
   const int64_t m0 = mg * BM;
 
