@@ -214,6 +214,9 @@ int fp6_linear_noalloc(const void* X, const void* packed_W, const void* scales, 
  *    20  as 19 with 64 columns per wave
  *    21  as 19 with 1 row block per wave and a ring of 4 tiles
  *    22  as 20 with 1 row block per wave
+ *    23  as 10 with the packed weights staged in LDS: every global load is
+ *        a direct LDS load, the weights four half-tiles deep
+ *    24  as 23 with 64 columns per workgroup
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
  *          (1..K/256; must be 0 or 1 for variant 13).
@@ -227,7 +230,7 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
 
 /*
  * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
- * for (M, N, K) on the current device: *variant (1..22, see fp6_linear_plan)
+ * for (M, N, K) on the current device: *variant (1..24, see fp6_linear_plan)
  * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
  * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
  * >= 1 here), FP6_E_HIP.

@@ -35,6 +35,7 @@ DENSE = [
     (32, 4096, 4096, 0, 0),      # streaming, 32 columns, K-splits
     (5, 2048, 28672, 15, 2),     # streaming, ragged M
     (128, 2048, 7168, 10, 3),    # tiled
+    (128, 2048, 7168, 23, 3),    # tiled, weights staged in LDS (probe-first fix-up)
     (1, 4096, 4096, 0, 0),       # k-slice
 ]
 SPARSE = [

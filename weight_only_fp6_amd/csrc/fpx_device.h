@@ -160,6 +160,16 @@ __device__ __forceinline__ half8v splice4(uint32_t d4, half2v s2) {
   return a;
 }
 
+// Direct global -> LDS load of BYTES (4 or 16) per lane: lane i's bytes land
+// at lds + BYTES*i (lds is wave-uniform).
+template <int BYTES>
+__device__ __forceinline__ void lds_load(const void* src, void* lds) {
+  static_assert(BYTES == 4 || BYTES == 16, "direct LDS loads of 4 or 16 bytes per lane");
+  auto* dst = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds));
+  if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  else __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
 // Format traits.  kTileQuads: 16-byte units per packed tile; kHalfLoads,
 // kTileLoads: load instructions per half-tile and per tile (the tiled
 // kernels' wait counts depend on them).  load/load_half take the lane's pointer into the tile (tile + lane,
@@ -186,6 +196,22 @@ struct Fp6Fmt {
   template <int JJ>
   __device__ static half8v half_step(const Half& h, half2v s2) {
     return splice6<F, JJ & 1>(h.q2[JJ >> 1], h.q4[JJ], s2);
+  }
+  // LDS staging of half hh of one row block's tile (lane pointer p), by
+  // direct LDS loads: the lane's 4-bit words (16 B) at 16*lane, its two
+  // 2-bit words at 1024 + 4*lane and 1280 + 4*lane of the wave-uniform
+  // region `lds` (kStageBytes).
+  static constexpr int kStageBytes = 1536;
+  static constexpr int kStageLoads = 3;
+  __device__ static void stage_half(char* lds, const u32x4* p, int hh, int) {
+    lds_load<16>(p + 64 + 64 * hh, lds);
+    lds_load<4>(reinterpret_cast<const uint32_t*>(p) + 2 * hh, lds + 1024);
+    lds_load<4>(reinterpret_cast<const uint32_t*>(p) + 2 * hh + 1, lds + 1280);
+  }
+  __device__ static void read_half(Half& h, const char* lds, int lane) {
+    h.q4 = reinterpret_cast<const u32x4*>(lds)[lane];
+    h.q2[0] = reinterpret_cast<const uint32_t*>(lds + 1024)[lane];
+    h.q2[1] = reinterpret_cast<const uint32_t*>(lds + 1280)[lane];
   }
 };
 template <> struct Fmt<kE3M2> : Fp6Fmt<kE3M2> {};
@@ -219,6 +245,17 @@ struct Fmt<kE2M2> {
   __device__ static half8v half_step(const Half& h, half2v s2) {
     return splice5<JJ>(h.q1, h.q4[JJ], s2);
   }
+  // LDS staging (see Fp6Fmt): 4-bit words at 16*lane, 1-bit word at 1024 + 4*lane.
+  static constexpr int kStageBytes = 1280;
+  static constexpr int kStageLoads = 2;
+  __device__ static void stage_half(char* lds, const u32x4* p, int hh, int lane) {
+    lds_load<16>(p + 64 * hh, lds);
+    lds_load<4>(reinterpret_cast<const uint32_t*>(plane1(p, lane)) + hh, lds + 1024);
+  }
+  __device__ static void read_half(Half& h, const char* lds, int lane) {
+    h.q4 = reinterpret_cast<const u32x4*>(lds)[lane];
+    h.q1 = reinterpret_cast<const uint32_t*>(lds + 1024)[lane];
+  }
 };
 
 template <>
@@ -238,6 +275,13 @@ struct Fmt<kE2M1> {
   template <int JJ>
   __device__ static half8v half_step(const Half& h, half2v s2) {
     return splice4(h.q4[JJ], s2);
+  }
+  // LDS staging (see Fp6Fmt): 4-bit words at 16*lane.
+  static constexpr int kStageBytes = 1024;
+  static constexpr int kStageLoads = 1;
+  __device__ static void stage_half(char* lds, const u32x4* p, int hh, int) { lds_load<16>(p + 64 * hh, lds); }
+  __device__ static void read_half(Half& h, const char* lds, int lane) {
+    h.q4 = reinterpret_cast<const u32x4*>(lds)[lane];
   }
 };
 
@@ -297,8 +341,16 @@ __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restric
 // dwordx4 per lane per accumulator: a quarter of the instructions of
 // per-component stores.  Partial layout: [unit][split][acc i][lane] float4,
 // so each instruction moves 1 KB contiguous.
+// With kProbeFirst (for kernels whose last split has the most work and so
+// usually finishes last), a split first reads the counter: if every other
+// split has already stored (they count only after their stores complete),
+// it is the last one and goes straight to the sum without storing its own
+// partial or counting.  Otherwise it stores and counts as above.  Exactly
+// one split finishes either way: one that sees splits-1 is the only split
+// that has not counted, and a split whose count returns splits-1 was
+// preceded by the counts of all others.
 // ---------------------------------------------------------------------------
-template <int NACC>
+template <int NACC, bool kProbeFirst = false>
 __device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __restrict__ unit_part,
                                              unsigned* __restrict__ counter, int split, int splits,
                                              int lane) {
@@ -306,16 +358,24 @@ __device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __rest
   constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer, gfx9 family
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(unit_part, static_cast<short>(0), splits * NACC * 1024, kRsrcWord3);
+  bool last = false;
+  if constexpr (kProbeFirst) {
+    const unsigned seen = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    last = seen == static_cast<unsigned>(splits - 1);
+  }
+  if (!last) {
 #pragma unroll
-  for (int i = 0; i < NACC; ++i)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i]), rsrc,
-                                           ((split * NACC + i) * 64 + lane) * 16, 0, kSc1);
-  __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
-  unsigned prev = 0;
-  if (lane == 0)
-    prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  if (prev != static_cast<unsigned>(splits - 1)) return false;
+    for (int i = 0; i < NACC; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i]), rsrc,
+                                             ((split * NACC + i) * 64 + lane) * 16, 0, kSc1);
+    __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
+    unsigned prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != static_cast<unsigned>(splits - 1)) return false;
+  }
   float4v sum[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) sum[i] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -1034,6 +1094,13 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
 //   * each wave waits for its own direct loads, then one barrier.
 // ---------------------------------------------------------------------------
 
+// Workgroup barrier without the release fence of __syncthreads().  The
+// fence makes a wave wait for every direct LDS load it has in flight, so a
+// copy issued several stages ahead would be waited for at once; the callers
+// instead wait (s_waitcnt) for exactly the copies the next stage reads.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
 // Workgroup index -> logical tile index, XCD-aware.  Workgroups are handed
 // to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), each XCD with
 // its own L2.  This gives XCD x the contiguous logical range
@@ -1208,11 +1275,226 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
   if (splits > 1) {
     const int64_t unit = (mg * ntiles + nt) * NW + wave;
     float* unit_part = part + unit * static_cast<int64_t>(splits) * (kTA * B * 256);
-    if (!splitk_fixup<kTA * B>(acc, unit_part, counters + unit, split, splits, lane)) return;
+    if (!splitk_fixup<kTA * B, true>(acc, unit_part, counters + unit, split, splits, lane)) return;
   }
 #pragma unroll
   for (int a = 0; a < kTA; ++a) {
     const int64_t nb = nt * 16 + wave * kTA + a;
+    if (nb >= nblocks) continue;
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi)
+      store_y_block(Y, acc[a * B + bi], m0 + bi * 16 + r, M, N, nb * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel with the packed weights staged in LDS (compute-bound regime,
+// M > 64).  Same tile and MFMA schedule as fp6_gemm_tiled (NW waves x TA
+// row blocks = 256 rows, BM = 16*B columns, half-tile steps), but every
+// global load is a direct LDS load: X(h+1) into a two-stage ring shared by
+// the workgroup, and each wave's own packed words of half-tile h+3 into a
+// four-stage ring, so the weights (from HBM) have three half-tiles of
+// compute to arrive and X (from L2) one.  A wave reads its words back from
+// LDS one half-tile before it splices them.  The waits are explicit vmcnt
+// counts (every load in flight is a direct LDS load, issued in a fixed
+// order), and the barrier carries no release fence, which would wait for
+// every copy in flight.  Each ring stage is its own LDS array so that the
+// compiler, too, tells the copies into one stage from the reads of another.
+// ---------------------------------------------------------------------------
+template <int F, int TA>
+struct WHalfL {
+  typename Fmt<F>::Half h[TA];
+};
+
+template <int F, int B, int TA, int NW>
+__global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledl(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
+    int64_t mg_base) {
+  constexpr int BM = 16 * B;
+  constexpr int kHalfUnits = BM * 16;             // 16-byte units per X half-tile stage
+  constexpr int kThreads = 64 * NW;
+  static_assert(TA * NW == 16, "a workgroup covers 16 row blocks");
+  constexpr int kLoadsPerThread = kHalfUnits / kThreads;
+  constexpr int kStage = Fmt<F>::kStageBytes;
+  constexpr int kWUnits = 16 * kStage / 16;       // 16-byte units per weight stage
+  __shared__ __attribute__((aligned(16))) half8v xb0[kHalfUnits];
+  __shared__ __attribute__((aligned(16))) half8v xb1[kHalfUnits];
+  __shared__ __attribute__((aligned(16))) u32x4 wl0[kWUnits];
+  __shared__ __attribute__((aligned(16))) u32x4 wl1[kWUnits];
+  __shared__ __attribute__((aligned(16))) u32x4 wl2[kWUnits];
+  __shared__ __attribute__((aligned(16))) u32x4 wl3[kWUnits];
+
+  // The wave index is uniform: kept in a scalar register, the LDS addresses
+  // of the direct loads need no per-load conversion.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
+  const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const int split = static_cast<int>(umod32(lb, splits));
+  const uint32_t bidx = udiv32(lb, splits);
+  const uint32_t bq = udiv32(bidx, static_cast<uint32_t>(ntiles));
+  const int64_t nt = bidx - bq * static_cast<uint32_t>(ntiles);
+  const int64_t mg = bq + mg_base;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t m0 = mg * BM;
+
+  // Weights: this wave's TA row blocks (ragged N: repeat the last block).
+  const u32x4* w[TA];
+  half2v s2[TA];
+#pragma unroll
+  for (int a = 0; a < TA; ++a) {
+    int64_t nb = nt * 16 + wave * TA + a;
+    if (nb >= nblocks) nb = nblocks - 1;
+    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    s2[a] = row_scale2<F>(scales, nb * 16 + r);
+  }
+  // This wave's row block a in a weight stage.
+  auto wregion = [&](u32x4* stage, int a) { return reinterpret_cast<char*>(stage) + (wave * TA + a) * kStage; };
+  auto stage_w = [&](u32x4* stage, int64_t h) {
+    const int64_t kt = h >> 1;
+    const int hh = static_cast<int>(h & 1);
+#pragma unroll
+    for (int a = 0; a < TA; ++a) Fmt<F>::stage_half(wregion(stage, a), w[a] + kt * Fmt<F>::kTileQuads, hh, lane);
+  };
+  auto read_w = [&](WHalfL<F, TA>& st, u32x4* stage) {
+#pragma unroll
+    for (int a = 0; a < TA; ++a) Fmt<F>::read_half(st.h[a], wregion(stage, a), lane);
+  };
+
+  // X direct loads as in fp6_gemm_tiled (16-byte units XOR-swizzled per row).
+  const _Float16* xsrc[kLoadsPerThread];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int u = i * kThreads + tid, mm = u >> 4, c = (u & 15) ^ (mm & 15);
+    int64_t m = m0 + mm;
+    if (m >= M) m = M - 1;
+    xsrc[i] = X + m * K + 8 * c;
+  }
+  auto dma_x = [&](half8v* buf, int64_t h) {
+    const int64_t koff = (h >> 1) * 256 + (h & 1) * 128;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) lds_load<16>(xsrc[i] + koff, buf + i * kThreads + wave * 64);
+  };
+
+  float4v acc[TA * B];
+#pragma unroll
+  for (int i = 0; i < TA * B; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  half8v afr[2][TA];
+  half8v bfr[2][B];
+  auto read_b = [&](half8v (&bf)[B], const half8v* buf, int jj) {
+#pragma unroll
+    for (int bi = 0; bi < B; ++bi) {
+      const int mm = bi * 16 + r, c = 4 * jj + g;
+      bf[bi] = buf[mm * 16 + (c ^ (mm & 15))];
+    }
+  };
+  auto splice = [&](half8v (&dst)[TA], const WHalfL<F, TA>& wv, auto JC) {
+    constexpr int jj = decltype(JC)::value;
+#pragma unroll
+    for (int a = 0; a < TA; ++a) dst[a] = Fmt<F>::template half_step<jj>(wv.h[a], s2[a]);
+  };
+  auto mfmas = [&](const half8v (&av)[TA], const half8v (&bf)[B]) {
+#pragma unroll
+    for (int a = 0; a < TA; ++a)
+#pragma unroll
+      for (int bi = 0; bi < B; ++bi)
+        acc[a * B + bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[a], bf[bi], acc[a * B + bi], 0, 0, 0);
+  };
+  auto interleave = [&](auto NDS) {
+    constexpr int nds = decltype(NDS)::value;
+    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);
+#pragma unroll
+    for (int i = 0; i < TA * B; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using IB = std::integral_constant<int, B>;
+  auto vmcnt = [](auto NC) {
+    constexpr int n = decltype(NC)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  };
+  // Loads per step, in issue order: X(h+1) (kLoadsPerThread), then the
+  // words of h+3 (kWLoads).  Before reading the words of h+1 at the end of
+  // step h, the loads issued after them may still be in flight: X(h),
+  // words(h+2), X(h+1), words(h+3).  Before the barrier: words(h+3).
+  constexpr int kWLoads = TA * Fmt<F>::kStageLoads;
+  using WaitW = std::integral_constant<int, 2 * kLoadsPerThread + 2 * kWLoads>;
+  using WaitX = std::integral_constant<int, kWLoads>;
+
+  // One half-tile h: k-steps 0..3 from X buffer `xc` and words `wc`; copy
+  // X(h+1) into `xn` and the words of h+3 into stage `wt`; read the words of
+  // h+1 from stage `wr` into `wn` and splice its first k-step while the
+  // last k-step's MFMAs run.
+  auto step = [&](const half8v* xc, half8v* xn, u32x4* wt, u32x4* wr, const WHalfL<F, TA>& wc,
+                  WHalfL<F, TA>& wn, int64_t hx, int64_t hw) {
+    dma_x(xn, hx);
+    stage_w(wt, hw);
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(bfr[0], xc, 0);
+    read_b(bfr[1], xc, 1); splice(afr[1], wc, I1{}); mfmas(afr[0], bfr[0]); interleave(IB{});
+    read_b(bfr[0], xc, 2); splice(afr[0], wc, I2{}); mfmas(afr[1], bfr[1]); interleave(IB{});
+    __builtin_amdgcn_sched_barrier(0);
+    vmcnt(WaitW{});
+    read_w(wn, wr);
+    read_b(bfr[1], xc, 3); splice(afr[1], wc, I3{}); mfmas(afr[0], bfr[0]); interleave(IB{});
+    __builtin_amdgcn_sched_barrier(0);
+                           splice(afr[0], wn, I0{}); mfmas(afr[1], bfr[1]); interleave(I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    vmcnt(WaitX{});
+    barrier_no_fence();
+  };
+
+  const int64_t h0 = 2 * kt0, h1 = 2 * kt1;  // half-tiles of this split
+  if (h0 < h1) {
+    // Prefetch indices are clamped to the split's last half-tile, so every
+    // step issues the same loads (the wait counts are constants).  The loop
+    // body is four steps (one turn of both rings); the remaining one to
+    // three steps follow it.
+    auto cl = [&](int64_t h) { return h < h1 - 1 ? h : h1 - 1; };
+    // Issue order words(h0), words(h0+1), X(h0), words(h0+2): from the
+    // first step on, the words of h+1 are followed by X(h), words(h+2),
+    // X(h+1), words(h+3), as the wait counts assume.
+    WHalfL<F, TA> wa, wb;
+    stage_w(wl0, h0);
+    stage_w(wl1, cl(h0 + 1));
+    dma_x(xb0, h0);
+    stage_w(wl2, cl(h0 + 2));
+    vmcnt(WaitX{});  // X(h0) and the words of h0 (issued before it) have landed
+    barrier_no_fence();
+    read_w(wa, wl0);
+    splice(afr[0], wa, I0{});
+    int64_t h = h0;
+    for (; h + 4 <= h1; h += 4) {
+      step(xb0, xb1, wl3, wl1, wa, wb, cl(h + 1), cl(h + 3));
+      step(xb1, xb0, wl0, wl2, wb, wa, cl(h + 2), cl(h + 4));
+      step(xb0, xb1, wl1, wl3, wa, wb, cl(h + 3), cl(h + 5));
+      step(xb1, xb0, wl2, wl0, wb, wa, cl(h + 4), cl(h + 6));
+    }
+    if (h < h1) step(xb0, xb1, wl3, wl1, wa, wb, cl(h + 1), cl(h + 3));
+    if (h + 1 < h1) step(xb1, xb0, wl0, wl2, wb, wa, cl(h + 2), cl(h + 4));
+    if (h + 2 < h1) step(xb0, xb1, wl1, wl3, wa, wb, cl(h + 3), cl(h + 5));
+    // No copy into LDS may still be in flight when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  if (splits > 1) {
+    const int64_t unit = (mg * ntiles + nt) * NW + wave;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (TA * B * 256);
+    if (!splitk_fixup<TA * B, true>(acc, unit_part, counters + unit, split, splits, lane)) return;
+  }
+#pragma unroll
+  for (int a = 0; a < TA; ++a) {
+    const int64_t nb = nt * 16 + wave * TA + a;
     if (nb >= nblocks) continue;
 #pragma unroll
     for (int bi = 0; bi < B; ++bi)
@@ -1550,6 +1832,30 @@ int launch_tiledw(const void* X, const void* W, const void* S, void* Y, int64_t 
 }
 
 template <int F, int B, int TA, int NW>
+int launch_tiledl(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                  int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
+  const int64_t ntiles = fpx_ceil_div(N >> 4, 16);
+  const int64_t mgroups = fpx_ceil_div(M, 16 * B);
+  const int64_t per_mg = ntiles * splits;
+  int64_t mg_chunk = ((int64_t(1) << 24) - 1) / per_mg;
+  if (mg_chunk < 1) mg_chunk = 1;
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  for (int64_t mg0 = 0; mg0 < mgroups; mg0 += mg_chunk) {
+    const int64_t nmg = (mgroups - mg0 < mg_chunk) ? (mgroups - mg0) : mg_chunk;
+    const dim3 grid(static_cast<unsigned>(nmg * per_mg));
+    int64_t mg_base = mg0;
+    void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &splits, &mg_base};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_tiledl<F, B, TA, NW>), grid, dim3(64 * NW),
+                        args, 0, stream) != hipSuccess)
+      return FP6_E_HIP;
+  }
+  return FP6_OK;
+}
+
+template <int F, int B, int TA, int NW>
 int launch_tiled(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                  int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
   const int64_t ntiles = fpx_ceil_div(N >> 4, 16);
@@ -1607,6 +1913,8 @@ int launch_variant(const fpx::LaunchCtx& c) {
     case 20: return launch_xlds<F, 2, 2, 8, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 21: return launch_xlds<F, 1, 4, 8, 2>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 22: return launch_xlds<F, 1, 2, 8, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 23: return launch_tiledl<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 24: return launch_tiledl<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     default: return FP6_E_VALUE;
   }
 }
