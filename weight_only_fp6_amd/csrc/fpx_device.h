@@ -1155,15 +1155,17 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
   const int r = lane & 15, g = lane >> 4;
   const int64_t m0 = mg * BM;
 
-  // Weights: this wave's 4 row blocks (ragged N: repeat the last block).
+  // Weights: this wave's TA row blocks (ragged N: repeat the last block).
+  // The row scales are loaded after the first tile's loads are in flight.
   const u32x4* w[kTA];
+  int64_t srow[kTA];
   half2v s2[kTA];
 #pragma unroll
   for (int a = 0; a < kTA; ++a) {
     int64_t nb = nt * 16 + wave * kTA + a;
     if (nb >= nblocks) nb = nblocks - 1;
     w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
-    s2[a] = row_scale2<F>(scales, nb * 16 + r);
+    srow[a] = nb * 16 + r;
   }
   auto load_wh = [&](WHalf<F, TA>& st, int64_t h) {  // half-tile h: k-tile h>>1, half h&1
     const int64_t kt = h >> 1;
@@ -1260,11 +1262,18 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
     // Branch-free steady state: prefetch indices are clamped to the split's
     // last half-tile, so every path has the same loads in flight.
     auto clamph = [&](int64_t h) { return h < h1 - 1 ? h : h1 - 1; };
+    // One round trip: the first half-tile's X and words, then the row
+    // scales, all in flight together; the fences keep the compiler from
+    // starting the first splice (which waits for the words) between them.
     WHalf<F, TA> wa, wb;
     dma_x(xbuf0, h0);
     load_wh(wa, h0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int a = 0; a < kTA; ++a) s2[a] = row_scale2<F>(scales, srow[a]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     splice_half<F, 0, TA>(afr[0], wa, s2);
     for (int64_t h = h0; h < h1; h += 2) {
       half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));
@@ -1544,13 +1553,14 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
   const int64_t m0 = mg * BM;
 
   const u32x4* w[TA];
+  int64_t srow[TA];
   half2v s2[TA];
 #pragma unroll
   for (int a = 0; a < TA; ++a) {
     int64_t nb = nt * 16 + wave * TA + a;
     if (nb >= nblocks) nb = nblocks - 1;
     w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
-    s2[a] = row_scale2<F>(scales, nb * 16 + r);
+    srow[a] = nb * 16 + r;
   }
   auto load_wt = [&](WTile<F, TA>& st, int64_t kt) {
 #pragma unroll
@@ -1645,8 +1655,12 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
     WTile<F, TA> wa, wb;
     dma_x(xbuf0, kt0);
     load_wt(wa, kt0);
+    __builtin_amdgcn_sched_barrier(0);  // first loads, then the row scales, one round trip
+#pragma unroll
+    for (int a = 0; a < TA; ++a) s2[a] = row_scale2<F>(scales, srow[a]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     splice(afr[0], wa, std::integral_constant<int, 0>{});
     int64_t kt = kt0;
     for (; kt + 2 <= kt1; kt += 2) {

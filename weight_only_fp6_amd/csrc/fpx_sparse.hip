@@ -418,13 +418,14 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_tiled(
   const int64_t m0 = mg * BM;
 
   const u32x4* w[TA];
+  int64_t srow[TA];
   half2v s2[TA];
 #pragma unroll
   for (int a = 0; a < TA; ++a) {
     int64_t nb = nt * 16 + wave * TA + a;
     if (nb >= nblocks) nb = nblocks - 1;
     w[a] = wp + (nb * ktiles) * kSpTileQuads + lane;
-    s2[a] = row_scale2<kE3M2>(scales, nb * 16 + r);
+    srow[a] = nb * 16 + r;
   }
   auto load_wh = [&](SpWHalf<TA>& st, int64_t h) {  // half-tile h: tile h>>1, half h&1
     const int64_t kt = h >> 1;
@@ -531,8 +532,12 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_tiled(
     SpWHalf<TA> wa, wb;
     dma_x(xbuf0, h0);
     load_wh(wa, h0);
+    __builtin_amdgcn_sched_barrier(0);  // first loads, then the row scales, one round trip
+#pragma unroll
+    for (int a = 0; a < TA; ++a) s2[a] = row_scale2<kE3M2>(scales, srow[a]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     splice(afr[0], wa, J0{});
     for (int64_t h = h0; h < h1; h += 2) {
       half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));
