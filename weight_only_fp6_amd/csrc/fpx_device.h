@@ -1673,7 +1673,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
   if (splits > 1) {
     const int64_t unit = (mg * ntiles + nt) * NW + wave;
     float* unit_part = part + unit * static_cast<int64_t>(splits) * (TA * B * 256);
-    if (!splitk_fixup<TA * B>(acc, unit_part, counters + unit, split, splits, lane)) return;
+    if (!splitk_fixup<TA * B, true>(acc, unit_part, counters + unit, split, splits, lane)) return;
   }
 #pragma unroll
   for (int a = 0; a < TA; ++a) {
