@@ -163,8 +163,8 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, plan, kernels and result bits as
  * fp6_linear, but split plans keep their fp32 partial sums and arrival
- * counters in a static device array of the library (40 MiB, of which the
- * first 256 KiB are counters; each GPU holds its own copy until the process
+ * counters in a static device array of the library (64 MiB + 256 KiB, of
+ * which the first 256 KiB are counters; each GPU holds its own copy until the process
  * ends) instead of a per-stream workspace: the call never calls hipMalloc,
  * hipFree or any allocating routine.  The first call on a device looks the
  * array up and clears its counters with a kernel on `stream`; split plans
@@ -174,7 +174,7 @@ int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
  * and give wrong sums.  Order them on one stream.
  * Errors: as fp6_linear, plus FP6_E_SIZE when the plan would need more
  * partial sums or counters than the array holds (no automatic plan does on a
- * 256-CU MI355X: at most 32 MiB).
+ * 256-CU MI355X: at most 32 MiB for split-K plans, 64 MiB for stream-K).
  */
 int fp6_linear_noalloc(const void* X, const void* packed_W, const void* scales, void* Y,
                        int64_t M, int64_t N, int64_t K, void* stream);

@@ -36,6 +36,7 @@ DENSE = [
     (5, 2048, 28672, 15, 2),     # streaming, ragged M
     (128, 2048, 7168, 10, 3),    # tiled
     (128, 2048, 7168, 23, 3),    # tiled, weights staged in LDS (probe-first fix-up)
+    (256, 4096, 7168, 25, 0),    # tiled, stream-K
     (1, 4096, 4096, 0, 0),       # k-slice
 ]
 SPARSE = [

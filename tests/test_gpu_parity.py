@@ -27,7 +27,7 @@ import weight_only_fp6_amd as fp6  # noqa: E402
 DEV = torch.device("cuda:0")
 # Kernel configurations of fp6_linear_plan: 0 = automatic, 1-4 and 7-8
 # streaming, 5-6 and 10-11 tiled, 9 k-split persistent (M <= 16, K <= 8192).
-ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24)
+ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25)
 KSPLIT = 9
 KSPLIT16 = 12
 KSLICE = 13
@@ -262,6 +262,41 @@ def test_linear_ksplit_across_workgroups(NK, M):
             assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, variant, splits)
 
 
+STREAM_K = 25
+
+
+@pytest.mark.parametrize("M, N, K", [
+    (128, 21504, 7168),   # OPT-30B QKV: 84 tiles x 56 half-tiles over one workgroup per CU
+    (256, 21504, 7168),   # two column groups, 168 tiles
+    (200, 4096, 4096),    # ragged M: the second column group is part empty
+    (64, 1024, 11008),    # 4 tiles of 86 half-tiles: dozens of pieces per tile
+    (1, 16, 256),         # one tile of 2 half-tiles: most workgroups idle
+    (768, 25600, 256),    # 600 tiles of 2 half-tiles: a workgroup runs tails, whole tiles and heads
+])
+def test_linear_stream_k(M, N, K):
+    # The stream-K tiled kernel: every output element against Y_ref, and
+    # bitwise reproducible from run to run (fixed piece order).
+    # The OPT-30B layer shares the workload tests' weight set (cached).
+    seed = synth.SHAPES["opt30b_qkv_128x21504x7168"].seed_w if (N, K) == (21504, 7168) else 7 * N + K
+    ws = dense_weight_set(N, K, seed)
+    X = synth.activations(M, K, M + 29)
+    yref = y_ref(X, ws.wdq_ref)
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
+    Y = fp6.linear_plan(Xd, packed, s, N, K, variant=STREAM_K).clone()
+    Y2 = fp6.linear_plan(Xd, packed, s, N, K, variant=STREAM_K)
+    torch.cuda.synchronize()
+    _assert_tol(Y, yref, what=(M, N, K))
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K)
+
+
+def test_linear_stream_k_rejects_splits():
+    p = Prepared(128, 64, 512, seed_w=5, seed_x=6)
+    X, packed, s = p.to_device()
+    with pytest.raises(fp6.FP6Error):
+        fp6.linear_plan(X, packed, s, 64, 512, variant=STREAM_K, splits=2)
+
+
 def test_linear_one_hot_reproduces_wdq_exactly():
     N, K = 64, 1024
     p = Prepared(16, N, K, seed_w=99, seed_x=1)
@@ -270,7 +305,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     X[np.arange(16), ks] = 1.0
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
-    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (KSLICE, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3), (19, 2), (20, 3), (21, 1), (22, 4), (23, 1), (23, 3), (24, 2)]:
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (KSLICE, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3), (19, 2), (20, 3), (21, 1), (22, 4), (23, 1), (23, 3), (24, 2), (25, 0)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         got = Y.cpu().numpy().astype(np.float64)
@@ -426,7 +461,7 @@ def test_linear_adversarial_rows(M):
     assert np.array_equal(p.codes, p.ocodes) and np.array_equal(p.scales.view(np.uint16), p.oscales.view(np.uint16))
     Xd, packed, s = p.to_device()
     assert np.array_equal(_bits16(fp6.dequant(packed, s, N, K)), p.wdq_ref.view(np.uint16))
-    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3), (19, 3), (22, 2), (23, 2), (24, 1)]:
+    for variant, splits in [(0, 0), (1, 3), (15, 2), (18, 1), (10, 1), (17, 3), (19, 3), (22, 2), (23, 2), (24, 1), (25, 0)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, variant, splits))
@@ -473,6 +508,8 @@ DENSE_PLANS = [
     ((72, 4096, 11008), (22, 4)),
     ((256, 4096, 4096), (22, 2)),
     ((256, 8192, 8192), (10, 4)),        # as many workgroups as CUs: tiled
+    ((256, 21504, 7168), (25, 256)),     # 168 tiles: stream-K, one workgroup per CU
+    ((512, 21504, 7168), (10, 1)),       # 336 tiles, more than CUs: split-K rounds
 ]
 SPARSE_PLANS = [
     ((1, 4096, 4096), (1, 1)),

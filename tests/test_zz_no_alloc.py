@@ -34,9 +34,10 @@ def _noalloc(X, P, S, N, K, out):
 def test_noalloc_matches_fp6_linear_on_consecutive_calls():
     # OPT-30B QKV M=128: tiled kernel with 3 K-splits (31.5 MiB of partial
     # sums); then the smaller Llama-7B MLP down projection (k-split kernel, 3
-    # K-splits); then the first layer again.  And a plan without K-splits.
+    # K-splits); then M=256, stream-K (53 MiB); then the first layer again.
+    # And a plan without K-splits.
     names = ["opt30b_qkv_128x21504x7168", "llama7b_mlp_down_16x4096x11008",
-             "llama70b_mlp_16x28672x8192"]
+             "llama70b_mlp_16x28672x8192", "opt30b_qkv_256x21504x7168"]
     runs = []
     for name in names:
         ws, X, yref = workload(name)
@@ -46,7 +47,7 @@ def test_noalloc_matches_fp6_linear_on_consecutive_calls():
         runs.append((name, Xd, P, S, ws.N, ws.K, want, yref))
     torch.cuda.synchronize()
     assert fp6.plan_query(128, 21504, 7168)[1] > 1 and fp6.plan_query(16, 4096, 11008)[1] > 1
-    order = [0, 1, 0, 2]
+    order = [0, 1, 3, 0, 2]
     outs = []
     for i in order:
         name, Xd, P, S, N, K, _, _ = runs[i]

@@ -340,7 +340,9 @@ __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restric
 // unit's partials (sc1 is a cache-policy bit of buffer instructions), one
 // dwordx4 per lane per accumulator: a quarter of the instructions of
 // per-component stores.  Partial layout: [unit][split][acc i][lane] float4,
-// so each instruction moves 1 KB contiguous.
+// so each instruction moves 1 KB contiguous; split s starts piece_quads
+// 16-byte units after split s-1 (NACC*64 when a unit's splits are adjacent;
+// larger when other units' slots sit between them).
 // With kProbeFirst (for kernels whose last split has the most work and so
 // usually finishes last), a split first reads the counter: if every other
 // split has already stored (they count only after their stores complete),
@@ -353,11 +355,13 @@ __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restric
 template <int NACC, bool kProbeFirst = false>
 __device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __restrict__ unit_part,
                                              unsigned* __restrict__ counter, int split, int splits,
-                                             int lane) {
+                                             int lane, int piece_quads = NACC * 64) {
   constexpr int kSc1 = 16;                 // cache policy: device scope
   constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer, gfx9 family
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(unit_part, static_cast<short>(0), splits * NACC * 1024, kRsrcWord3);
+  // The buffer spans exactly this unit's splits: the last one ends NACC*1 KB
+  // after its start.
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      unit_part, static_cast<short>(0), ((splits - 1) * piece_quads + NACC * 64) * 16, kRsrcWord3);
   bool last = false;
   if constexpr (kProbeFirst) {
     const unsigned seen = __builtin_amdgcn_readfirstlane(
@@ -368,7 +372,7 @@ __device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __rest
 #pragma unroll
     for (int i = 0; i < NACC; ++i)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i]), rsrc,
-                                             ((split * NACC + i) * 64 + lane) * 16, 0, kSc1);
+                                             (split * piece_quads + i * 64 + lane) * 16, 0, kSc1);
     __builtin_amdgcn_s_waitcnt(0);  // the partial stores have completed
     unsigned prev = 0;
     if (lane == 0)
@@ -387,7 +391,7 @@ __device__ __forceinline__ bool splitk_fixup(float4v (&acc)[NACC], float* __rest
       u32x4 v[NACC];
 #pragma unroll
       for (int i = 0; i < NACC; ++i)
-        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((s * NACC + i) * 64 + lane) * 16, 0, kSc1);
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (s * piece_quads + i * 64 + lane) * 16, 0, kSc1);
 #pragma unroll
       for (int i = 0; i < NACC; ++i) sum[i] += __builtin_bit_cast(float4v, v[i]);
     }
@@ -1125,33 +1129,22 @@ __device__ __forceinline__ void splice_half(half8v (&dst)[TA], const WHalf<F, TA
   for (int a = 0; a < TA; ++a) dst[a] = Fmt<F>::template half_step<JJ>(w.h[a], s2[a]);
 }
 
-// TA row blocks per wave, NW waves per workgroup, TA * NW = 16 (256 rows).
+// One workgroup's pass over half-tiles [h0, h1) of its tile (m-group mg,
+// 256-row tile nt), accumulated into acc.  X half-tiles go through the LDS
+// buffers xbuf0/xbuf1 (distinct __shared__ arrays of the caller).
 template <int F, int B, int TA, int NW>
-__global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
-    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
-    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
-    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
-    int64_t mg_base) {
+__device__ __forceinline__ void tiled_run(const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+                                          const _Float16* __restrict__ scales, int64_t M, int64_t N,
+                                          int64_t K, int64_t mg, int64_t nt, int64_t h0, int64_t h1,
+                                          half8v* xbuf0, half8v* xbuf1, float4v (&acc)[TA * B]) {
   constexpr int BM = 16 * B;
   constexpr int kHalfUnits = BM * 16;             // 16-byte units per X half-tile buffer
   constexpr int kTA = TA;
   constexpr int kThreads = 64 * NW;
   static_assert(TA * NW == 16, "a workgroup covers 16 row blocks");
   constexpr int kLoadsPerThread = kHalfUnits / kThreads;
-  __shared__ __attribute__((aligned(16))) half8v xbuf0[kHalfUnits];
-  __shared__ __attribute__((aligned(16))) half8v xbuf1[kHalfUnits];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
-  const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
-  const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
-  const int split = static_cast<int>(umod32(lb, splits));
-  const uint32_t bidx = udiv32(lb, splits);
-  const uint32_t bq = udiv32(bidx, static_cast<uint32_t>(ntiles));
-  const int64_t nt = bidx - bq * static_cast<uint32_t>(ntiles);
-  const int64_t mg = bq + mg_base;
-  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
-  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
   const int r = lane & 15, g = lane >> 4;
   const int64_t m0 = mg * BM;
 
@@ -1197,10 +1190,6 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
               reinterpret_cast<uintptr_t>(buf + i * kThreads + wave * 64)),
           16, 0, 0);
   };
-
-  float4v acc[kTA * B];
-#pragma unroll
-  for (int i = 0; i < kTA * B; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
 
   half8v afr[2][kTA];
   half8v bfr[2][B];
@@ -1257,7 +1246,6 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
     __syncthreads();
   };
 
-  const int64_t h0 = 2 * kt0, h1 = 2 * kt1;  // half-tiles of this split
   if (h0 < h1) {
     // Branch-free steady state: prefetch indices are clamped to the split's
     // last half-tile, so every path has the same loads in flight.
@@ -1275,24 +1263,121 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     splice_half<F, 0, TA>(afr[0], wa, s2);
-    for (int64_t h = h0; h < h1; h += 2) {
+    int64_t h = h0;
+    for (; h + 2 <= h1; h += 2) {
       half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));
       half_step(xbuf1, xbuf0, wb, wa, clamph(h + 2));
     }
+    if (h < h1) half_step(xbuf0, xbuf1, wa, wb, clamph(h + 1));  // odd count (stream-K segments)
   }
 
-  if (splits > 1) {
-    const int64_t unit = (mg * ntiles + nt) * NW + wave;
-    float* unit_part = part + unit * static_cast<int64_t>(splits) * (kTA * B * 256);
-    if (!splitk_fixup<kTA * B, true>(acc, unit_part, counters + unit, split, splits, lane)) return;
-  }
+}
+
+// Store a tiled workgroup's accumulators (rows of row tile nt, columns of
+// m-group mg); ragged N: the repeated last row block is not stored.
+template <int B, int TA>
+__device__ __forceinline__ void tiled_store(_Float16* __restrict__ Y, const float4v (&acc)[TA * B], int64_t M,
+                                            int64_t N, int64_t mg, int64_t nt, int wave, int lane) {
+  const int64_t nblocks = N >> 4;
+  const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int a = 0; a < kTA; ++a) {
-    const int64_t nb = nt * 16 + wave * kTA + a;
+  for (int a = 0; a < TA; ++a) {
+    const int64_t nb = nt * 16 + wave * TA + a;
     if (nb >= nblocks) continue;
 #pragma unroll
     for (int bi = 0; bi < B; ++bi)
-      store_y_block(Y, acc[a * B + bi], m0 + bi * 16 + r, M, N, nb * 16, g);
+      store_y_block(Y, acc[a * B + bi], mg * 16 * B + bi * 16 + r, M, N, nb * 16, g);
+  }
+}
+
+// TA row blocks per wave, NW waves per workgroup, TA * NW = 16 (256 rows).
+// Split-K: workgroup (tile, split) runs the split's k-tiles.
+template <int F, int B, int TA, int NW>
+__global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int splits,
+    int64_t mg_base) {
+  constexpr int kHalfUnits = 16 * B * 16;
+  __shared__ __attribute__((aligned(16))) half8v xbuf0[kHalfUnits];
+  __shared__ __attribute__((aligned(16))) half8v xbuf1[kHalfUnits];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
+  const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
+  const int split = static_cast<int>(umod32(lb, splits));
+  const uint32_t bidx = udiv32(lb, splits);
+  const uint32_t bq = udiv32(bidx, static_cast<uint32_t>(ntiles));
+  const int64_t nt = bidx - bq * static_cast<uint32_t>(ntiles);
+  const int64_t mg = bq + mg_base;
+  const int64_t kt0 = udiv32(split * static_cast<uint32_t>(ktiles), splits);
+  const int64_t kt1 = udiv32((split + 1) * static_cast<uint32_t>(ktiles), splits);
+
+  float4v acc[TA * B];
+#pragma unroll
+  for (int i = 0; i < TA * B; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  tiled_run<F, B, TA, NW>(X, wp, scales, M, N, K, mg, nt, 2 * kt0, 2 * kt1, xbuf0, xbuf1, acc);
+
+  if (splits > 1) {
+    const int64_t unit = (mg * ntiles + nt) * NW + wave;
+    float* unit_part = part + unit * static_cast<int64_t>(splits) * (TA * B * 256);
+    if (!splitk_fixup<TA * B, true>(acc, unit_part, counters + unit, split, splits, lane)) return;
+  }
+  tiled_store<B, TA>(Y, acc, M, N, mg, nt, wave, lane);
+}
+
+// Stream-K form: the G workgroups (one per CU) split the launch's
+// (tile, half-tile) units into G contiguous, equal ranges in tile-major
+// order, so every CU does the same number of half-tiles (+-1) whatever the
+// tile count.  A range covers the tail of one tile, whole tiles and the head
+// of another; each piece is run as one segment.  A tile's pieces come from
+// workgroups wf..wl (computable from the range bounds) and meet in the
+// fixed-order fix-up (piece order = workgroup order), whose partials sit in
+// slots [wf + tile, wf + tile + pieces) of the workspace (disjoint between
+// tiles, G + tiles slots of NW waves each).  Workgroups process their range
+// in order, so a tile's head piece, run last by its workgroup, is usually
+// the last to arrive: the probe-first fix-up lets it sum without a store.
+template <int F, int B, int TA, int NW>
+__global__ __launch_bounds__(64 * NW) void fp6_gemm_tiled_sk(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int, int64_t) {
+  constexpr int kHalfUnits = 16 * B * 16;
+  constexpr int kAcc = TA * B;
+  __shared__ __attribute__((aligned(16))) half8v xbuf0[kHalfUnits];
+  __shared__ __attribute__((aligned(16))) half8v xbuf1[kHalfUnits];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t w = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t nblocks = N >> 4, htiles = 2 * (K >> 8);
+  const int64_t ntiles = (nblocks + 15) >> 4;
+  const int64_t tiles = ((M + 16 * B - 1) / (16 * B)) * ntiles;
+  const int64_t T = tiles * htiles;
+  // With fewer units than workgroups, only the first T take part (one unit
+  // each): every range is then non-empty, so each workgroup that a tile's
+  // range bounds cover does arrive at its fix-up.
+  const int64_t G = T < static_cast<int64_t>(gridDim.x) ? T : static_cast<int64_t>(gridDim.x);
+  if (w >= G) return;
+  int64_t u = w * T / G;
+  const int64_t u1 = (w + 1) * T / G;
+  while (u < u1) {
+    const int64_t tile = u / htiles, hs = u - tile * htiles;
+    const int64_t he = (u1 - u < htiles - hs) ? hs + (u1 - u) : htiles;
+    const int64_t mg = tile / ntiles, nt = tile - mg * ntiles;
+    float4v acc[kAcc];
+#pragma unroll
+    for (int i = 0; i < kAcc; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+    tiled_run<F, B, TA, NW>(X, wp, scales, M, N, K, mg, nt, hs, he, xbuf0, xbuf1, acc);
+    // Workgroups holding the tile's first and last units.
+    const int64_t wf = ((tile * htiles + 1) * G - 1) / T;
+    const int64_t wl = ((tile + 1) * htiles * G - 1) / T;
+    bool finish = true;
+    if (wl > wf) {
+      float* unit_part = part + ((wf + tile) * NW + wave) * (kAcc * 256);
+      finish = splitk_fixup<kAcc, true>(acc, unit_part, counters + tile * NW + wave, static_cast<int>(w - wf),
+                                         static_cast<int>(wl - wf + 1), lane, NW * kAcc * 64);
+    }
+    if (finish) tiled_store<B, TA>(Y, acc, M, N, mg, nt, wave, lane);
+    u = tile * htiles + he;
   }
 }
 
@@ -1845,6 +1930,24 @@ int launch_tiledw(const void* X, const void* W, const void* S, void* Y, int64_t 
   return FP6_OK;
 }
 
+// Stream-K tiled kernel: one launch, `workgroups` workgroups (splits field
+// of the plan), all m-groups.
+template <int F, int B, int TA, int NW>
+int launch_tiled_sk(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                    int64_t K, int workgroups, float* part, unsigned* cnt, hipStream_t stream) {
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  int unused = 0;
+  int64_t unused64 = 0;
+  void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &unused, &unused64};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fp6_gemm_tiled_sk<F, B, TA, NW>),
+                         dim3(static_cast<unsigned>(workgroups)), dim3(64 * NW), args, 0, stream) == hipSuccess
+             ? FP6_OK
+             : FP6_E_HIP;
+}
+
 template <int F, int B, int TA, int NW>
 int launch_tiledl(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                   int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
@@ -1929,6 +2032,7 @@ int launch_variant(const fpx::LaunchCtx& c) {
     case 22: return launch_xlds<F, 1, 2, 8, 4>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 23: return launch_tiledl<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 24: return launch_tiledl<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 25: return launch_tiled_sk<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     default: return FP6_E_VALUE;
   }
 }

@@ -14,7 +14,7 @@ namespace fpx {
 enum Format : int { kFmtE3M2 = 0, kFmtE2M3 = 1, kFmtE2M2 = 2, kFmtE2M1 = 3, kNumFormats = 4 };
 
 // Kernel configurations reachable through the `variant` argument.
-enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice, kXlds };
+enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice, kXlds, kTiledSk };
 struct KernelCfg {
   Kind kind;
   int a, mb, d;  // stream: row blocks/wave, 16-col blocks/wave, ring depth; tiled: B = mb
@@ -45,6 +45,7 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kXlds, 1, 4, 2},    // 22: streaming + X in LDS, 1 row block x 64 columns per wave, ring 2, 8 waves
     {Kind::kTiled, 2, 8, 8},   // 23: tiled, 256 rows x 128 columns, 8 waves x 2 row blocks, weights staged in LDS
     {Kind::kTiled, 2, 4, 8},   // 24: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks, weights staged in LDS
+    {Kind::kTiledSk, 2, 8, 8}, // 25: tiled (as 10), stream-K: one workgroup per CU, equal (tile, half-tile) ranges
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kKsMaxTiles = 32;      // k-split kernels: K <= 8192

@@ -26,9 +26,10 @@
 // kScratchCounterBytes) and fp32 partial sums of its plans, in device memory
 // that the library owns, so that the call allocates nothing.  Every GPU the
 // library runs on holds its own copy until the process ends.  Automatic plans
-// on a 256-CU MI355X need at most 32 MiB of partial sums (a split plan puts
-// at most one round of workgroups on the CUs).
-constexpr size_t kScratchBytes = size_t(40) << 20;
+// on a 256-CU MI355X need at most 64 MiB of partial sums: a split-K plan puts
+// at most one round of workgroups on the CUs (32 MiB), a stream-K plan keeps
+// CU-count + tile-count slots of 128 KiB with fewer tiles than CUs.
+constexpr size_t kScratchBytes = (size_t(64) << 20) + (size_t(256) << 10);
 constexpr size_t kScratchCounterBytes = size_t(256) << 10;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -164,10 +165,28 @@ struct Plan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats);
+
+// Split-K workspace of a plan: counters (one per unit) and partial bytes.
+// Split-K kernels keep `splits` partial slots per unit.  The stream-K tiled
+// kernel (plan.splits = its workgroup count G) keeps G + tiles slots of one
+// tile's partials, each tile's pieces in slots [wf + tile, wf + tile +
+// pieces) (see fp6_gemm_tiled_sk).
+void workspace_need(const KernelCfg& c, int splits, int64_t M, int64_t N, int64_t* units, size_t* part_bytes) {
+  int64_t floats = 0;
+  plan_units(c, M, N, units, &floats);
+  if (c.kind == Kind::kTiledSk) {
+    const int64_t tiles = *units / c.d;
+    *part_bytes = static_cast<size_t>(splits + tiles) * c.d * floats * sizeof(float);
+  } else {
+    *part_bytes = static_cast<size_t>(*units) * splits * floats * sizeof(float);
+  }
+}
+
 // Work units (each with its own split-K counter) and the number of partial
 // floats per unit and split.
 void plan_units(const KernelCfg& c, int64_t M, int64_t N, int64_t* units, int64_t* floats) {
-  if (c.kind == Kind::kTiled) {
+  if (c.kind == Kind::kTiled || c.kind == Kind::kTiledSk) {
     // c.a = row blocks per wave, c.d = waves per workgroup (c.a * c.d = 16)
     *units = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16) * c.d;
     *floats = static_cast<int64_t>(c.a) * c.mb * 256;
@@ -291,6 +310,10 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     p.splits = 1;
     return p;
   }
+  if (c.kind == Kind::kTiledSk) {  // one workgroup per CU
+    p.splits = cus;
+    return p;
+  }
   if (c.kind == Kind::kKsplit) {
     p.splits = splits > 0 ? splits : 1;
     return p;
@@ -315,6 +338,20 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     const int64_t wgs = ceil_div(M, 16 * c.mb) * ceil_div(N >> 4, 16);
     s = cus / wgs;
     if (s > ktiles / 2) s = ktiles / 2;
+    if (s < 1) s = 1;
+    // The automatic plan's 128-column tiled kernel goes stream-K when the
+    // split-K rounds would leave more than a quarter of their CU slots idle
+    // (OPT-30B QKV 256x21504x7168, 168 tiles: 97.9 -> 94.1 us; M = 160 and
+    // 192: 97.2 -> 91.5 and 97.4 -> 92.2 us); with fuller rounds split-K
+    // is faster (M = 128, 252 workgroups: 55.0 against 58.8 us).
+    // Only with fewer tiles than CUs, which bounds its partial sums (G +
+    // tiles slots) at twice a split-K round's.
+    const int64_t slots = ceil_div(wgs * s, cus) * cus;
+    if (variant == 0 && p.variant == 10 && wgs < cus && 4 * wgs * s < 3 * slots) {
+      p.variant = 25;
+      p.splits = cus;
+      return p;
+    }
   } else {
     // No split once there are two waves per CU; otherwise split K towards
     // ~4 waves per CU (measured: more splits cost more in the fix-up than
@@ -361,6 +398,7 @@ int linear_impl(int format, const void* X, const void* W, const void* S, void* Y
   if (variant > 0 && kCfgs[variant].kind == Kind::kKslice &&
       (M > 16 || (K >> 8) > fpx::kKsliceMaxTiles || splits > 1))
     return FP6_E_VALUE;
+  if (variant > 0 && kCfgs[variant].kind == Kind::kTiledSk && splits != 0) return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const int cus = device_cus(dev);
@@ -369,9 +407,9 @@ int linear_impl(int format, const void* X, const void* W, const void* S, void* Y
   fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus,
                      static_cast<hipStream_t>(stream)};
   if (p.splits <= 1) return launch_format(format, ctx);
-  int64_t units = 0, floats = 0;
-  plan_units(c, M, N, &units, &floats);
-  const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
+  int64_t units = 0;
+  size_t part_bytes = 0;
+  workspace_need(c, p.splits, M, N, &units, &part_bytes);
   std::lock_guard<std::mutex> lk(g_mu);  // held until the launch is enqueued
   Workspace* ws = nullptr;
   st = get_workspace_locked(dev, stream, part_bytes, static_cast<size_t>(units), &ws);
@@ -592,9 +630,9 @@ int fp6_linear_noalloc(const void* X, const void* packed_W, const void* scales, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   fpx::LaunchCtx ctx{X, packed_W, scales, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus, s};
   if (p.splits > 1) {
-    int64_t units = 0, floats = 0;
-    plan_units(kCfgs[p.variant], M, N, &units, &floats);
-    const size_t part_bytes = static_cast<size_t>(units) * p.splits * floats * sizeof(float);
+    int64_t units = 0;
+    size_t part_bytes = 0;
+    workspace_need(kCfgs[p.variant], p.splits, M, N, &units, &part_bytes);
     if (static_cast<size_t>(units) * sizeof(unsigned) > kScratchCounterBytes ||
         part_bytes > kScratchBytes - kScratchCounterBytes)
       return FP6_E_SIZE;
