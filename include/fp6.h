@@ -217,9 +217,12 @@ int fp6_linear_noalloc(const void* X, const void* packed_W, const void* scales, 
  *    23  as 10 with the packed weights staged in LDS: every global load is
  *        a direct LDS load, the weights four half-tiles deep
  *    24  as 23 with 64 columns per workgroup
+ *    25  as 10, stream-K: one workgroup per CU, each running an equal
+ *        contiguous range of (tile, 128-k half-tile) units; a tile's pieces
+ *        meet in the fixed-order fix-up
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
- *          (1..K/256; must be 0 or 1 for variant 13).
+ *          (1..K/256; must be 0 or 1 for variant 13, 0 for variant 25).
  * The result equals fp6_linear's up to fp32 summation order.
  * Errors: as fp6_linear, plus FP6_E_VALUE for an unknown variant, a split
  * count out of range, or a shape that variant 9, 12 or 13 does not cover.
@@ -230,8 +233,9 @@ int fp6_linear_plan(const void* X, const void* packed_W, const void* scales, voi
 
 /*
  * fp6_linear_plan_query -- host; reports the schedule fp6_linear would use
- * for (M, N, K) on the current device: *variant (1..24, see fp6_linear_plan)
- * and *splits (K-splits across workgroups; 1 = none).  Makes one HIP query
+ * for (M, N, K) on the current device: *variant (1..25, see fp6_linear_plan)
+ * and *splits (K-splits across workgroups, 1 = none; for variant 25 the
+ * number of stream-K workgroups).  Makes one HIP query
  * (device id and CU count).  Errors: FP6_E_NULL, FP6_E_SHAPE (M must be
  * >= 1 here), FP6_E_HIP.
  */
