@@ -121,7 +121,7 @@ def algorithmic_bytes(M, N, K, fmt="e3m2"):
 # CPU baseline: the oracle, untuned, on a bounded row sample.
 # ---------------------------------------------------------------------------
 def cpu_cores():
-    """Host cores this process may use (at most 16: a one-GPU machine's share)."""
+    """Host cores this process may use, at most 16 (one GPU's share of a multi-GPU host)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
@@ -455,7 +455,7 @@ def main():
         traffic_summary(args.workload if fmt == "e3m2" else f"{args.workload} ({fmt})", *args.traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -24,7 +24,7 @@ from oracle import sparse24
 import weight_only_fp6_amd as fp6
 from weight_only_fp6_amd import synth
 
-# Worker threads: the host's CPU share (at most 16 on a one-GPU machine).
+# Worker threads: the cores this process may use, at most 16.
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 ROW_CHUNK = 1024
 
