@@ -613,7 +613,7 @@ def main():
                    "M": M, "N": N, "K": K,
                    "weights": ("fp6 e3m2, 2:4 sparse (magnitude-pruned), + fp16 row scale (packed 2:4 layout)"
                                if fmt == "sparse24" else
-                               f"fp{FORMAT_BITS[fmt]} {fmt} + fp16 row scale (packed layout v2)"),
+                               f"fp{FORMAT_BITS[fmt]} {fmt} + fp16 row scale (packed layout v3)"),
                    "activations": "fp16", "accumulate": "fp32",
                    "rotated_weight_copies": R, "graph": not args.no_graph},
         "weight_gbps": round(weight_gbs, 1),

@@ -82,7 +82,7 @@ int fp6_quantize_rows(const float* W, int64_t N, int64_t K,
 
 /*
  * fp6_prepack -- host, synchronous, pure and deterministic (offline step).
- * Re-orders 6-bit codes into packed layout v2 (TC-FPx explainer, section
+ * Re-orders 6-bit codes into packed layout v3 (TC-FPx explainer, section
  * "redesigning the kernel solution": bit-level pre-packing and 2+4 splitting
  * before inference).
  *
@@ -93,8 +93,9 @@ int fp6_quantize_rows(const float* W, int64_t N, int64_t K,
  * packed:  host out, packed_bytes == fp6_packed_bytes(N, K).
  * Errors: FP6_E_NULL, FP6_E_SHAPE, FP6_E_CODE, FP6_E_SCALE, FP6_E_SIZE.
  *
- * Packed layout v2 (fp6_pack_version() == 2).  Tiles of 16 rows x 256 k,
- * 3072 bytes each; tile (nb, kb) starts at byte (nb*(K/256) + kb)*3072.
+ * Packed layout v3 (fp6_pack_version() == 3).  Tiles of 16 rows x 256 k,
+ * 3072 bytes each, k-block major: tile (nb, kb) starts at byte
+ * (kb*(N/16) + nb)*3072, so the row blocks read at one k-block are adjacent.
  * Within a tile, local row r (0..15) and local k = 32*j + 8*g + i (k-step j
  * 0..7, lane group g 0..3, element i 0..7) belong to wave lane L = 16*g + r.
  * Each code c is split into a 2-bit piece (s, e2) = c >> 4 and a 4-bit piece
@@ -113,7 +114,8 @@ int fp6_quantize_rows(const float* W, int64_t N, int64_t K,
  * high bytes (s<<7)|(e2<<4)|nibble of four elements one and_or of the
  * 4-bit word with the rotated 2-bit word, spread onto fp16 pairs by one
  * byte permute per pair.  (Layout v1, the first version, placed the pieces
- * per fp16 pair instead; v2 changed only the bit positions.)
+ * per fp16 pair instead; v2 changed only the bit positions; v3 only the
+ * order of the tiles, which layouts v1 and v2 kept row-block major.)
  */
 int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
                 int64_t N, int64_t K, void* packed, size_t packed_bytes);

@@ -26,7 +26,7 @@
  * (nb*(K/512) + kb)*4096.  For k-step j (64 dense k, one sparse MFMA) and wave
  * lane L = 16g + r (row r), element i (0..7) is kept weight i%2 of the dense
  * group at tile offset 64j + 32(g%2) + 16(i/4) + 8(g/2) + 4((i%4)/2).  Bytes
- * [0, 3072) hold the codes exactly where packed layout v2 (fp6.h) puts lane
+ * [0, 3072) hold the codes exactly where the dense layout (fp6.h) puts lane
  * L, k-step j, element i of an FP6 tile; bytes [3072, 4096) hold the
  * positions: lane L's 16 bytes at 3072 + 16L, word j/2, bits 16(j%2) + 2i.
  */

@@ -29,9 +29,9 @@
  * is the same as the matching fp6_* call.  An unknown format gives
  * FP6_E_VALUE (before any HIP call).
  *
- * Packed layout v2 for each format: tiles of 16 rows x 256 k at
- * (nb*(K/256) + kb) * tile_bytes, tile_bytes = 4096*bits/8; local row r,
- * local k = 32*j + 8*g + i belong to wave lane L = 16*g + r.
+ * Packed layout v3 for each format: tiles of 16 rows x 256 k at
+ * (kb*(N/16) + nb) * tile_bytes (k-block major), tile_bytes = 4096*bits/8;
+ * local row r, local k = 32*j + 8*g + i belong to wave lane L = 16*g + r.
  *   e3m2: as described in fp6.h.
  *   e2m3: planes placed as e3m2's, with 2-bit piece (s, e1) = c >> 4 and
  *         4-bit piece (e0 m2 m1 m0) = c & 15; in the 2-bit plane, with
@@ -80,7 +80,7 @@ int fpx_quantize_rows(int format, const float* W, int64_t N, int64_t K, uint8_t*
 
 /*
  * fpx_prepack -- host, synchronous, pure (offline step): codes (host uint8
- * [N][K], each < 2^bits) into packed layout v2 of the format.  scales are
+ * [N][K], each < 2^bits) into packed layout v3 of the format.  scales are
  * only checked against the format's range.  packed_bytes must equal
  * fpx_packed_bytes(format, N, K).  Errors: FP6_E_NULL, FP6_E_SHAPE,
  * FP6_E_CODE, FP6_E_SCALE, FP6_E_SIZE, FP6_E_VALUE (unknown format).

@@ -11,7 +11,7 @@ Contents (all in :mod:`oracle.fp6_oracle`):
 * decode tables (explicit, one per format: FP6 e3m2 and e2m3, FP5 e2m2, FP4
   e2m1) and the round-to-nearest-even encoder;
 * per-row quantizer (input preparation: W fp32 -> codes + fp16 row scales);
-* scalar and vectorised unpackers of the packed layout v2 of every format,
+* scalar and vectorised unpackers of the packed layout v3 of every format,
   plus a scalar packer used only to pin the unpackers;
 * dequantisation ``fp16_RNE(v(c) * s_n)`` and the float64 GEMM
   ``Y_ref = X . Wdq^T``, plus a naive triple loop used to pin it;

@@ -27,7 +27,7 @@ packed layout.  The readings used here (each one stated where it is used):
   gradual underflow, signed zero kept).
 * Y_ref = X . Wdq^T accumulated in float64 (nn.Linear convention: X is
   [M,K], W is [N,K], Y is [M,N]).
-* Packed layout v2 (the library's private offline format; any bijection is
+* Packed layout v3 (the library's private offline format; any bijection is
   correct, this oracle checks the round trip): see :func:`unpack_scalar`.
 
 Other widths (FP6-LLM abstract: one Tensor-Core kernel scheme for float weights
@@ -235,11 +235,11 @@ def quantize_rows_sampled(W_rows, fmt="e3m2") -> tuple[np.ndarray, np.ndarray]:
 
 
 # ---------------------------------------------------------------------------
-# O3: packed layout v2.
+# O3: packed layout v3.
 #
 # Codes c[n][k] with N % 16 == 0 and K % 256 == 0.  The buffer holds
 # N*K*bits/8 bytes in tiles of 16 rows x 256 k.  Tile (nb, kb) starts at byte
-# (nb*(K/256) + kb) * tile_bytes (row-block major, k-block minor).  Inside a
+# (kb*(N/16) + nb) * tile_bytes (k-block major, row-block minor).  Inside a
 # tile, local row r in 0..15 and local k = 32*j + 8*g + i (j: k-step 0..7,
 # g: lane group 0..3, i: element 0..7) belong to lane L = 16*g + r.
 #
@@ -285,7 +285,7 @@ def packed_bytes(N: int, K: int, fmt="e3m2") -> int:
 
 def _check_shape(N: int, K: int) -> None:
     if N <= 0 or K <= 0 or N % TILE_N or K % TILE_K:
-        raise ValueError("layout v2 needs N % 16 == 0 and K % 256 == 0, both > 0")
+        raise ValueError("layout v3 needs N % 16 == 0 and K % 256 == 0, both > 0")
 
 
 def _locate(N: int, K: int, n: int, k: int):
@@ -295,7 +295,7 @@ def _locate(N: int, K: int, n: int, k: int):
     j, rem = divmod(kk, 32)
     g, i = divmod(rem, 8)
     lane = 16 * g + r
-    base = (nb * (K // TILE_K) + kb) * TILE_BYTES
+    base = (kb * (N // TILE_N) + nb) * TILE_BYTES
     grp, e = divmod(i, 4)
     rho = 4 * (j % 2) + 2 * grp
     w2 = base + 16 * lane + 4 * (j // 2)
@@ -316,7 +316,7 @@ def _slots(fmt, N: int, K: int, n: int, k: int):
     g, i = divmod(rem, 8)
     lane = 16 * g + r
     tb = tile_bytes(f)
-    base = (nb * (K // TILE_K) + kb) * tb
+    base = (kb * (N // TILE_N) + nb) * tb
     p = 4 * (j % 2) + i // 2
     h = i % 2
     if f.name == "e3m2":
@@ -350,7 +350,7 @@ def _set_word(buf, off: int, val: int) -> None:
 
 
 def pack_scalar(codes, fmt="e3m2") -> np.ndarray:
-    """Scalar packer of layout v2 (pure Python; small inputs only).
+    """Scalar packer of layout v3 (pure Python; small inputs only).
 
     Used only to pin :func:`unpack_scalar` (bijection checks); the library has
     its own packer.
@@ -371,7 +371,7 @@ def pack_scalar(codes, fmt="e3m2") -> np.ndarray:
 
 
 def unpack_scalar(packed, N: int, K: int, fmt="e3m2") -> np.ndarray:
-    """Scalar unpacker of layout v2 (pure Python loop over every code)."""
+    """Scalar unpacker of layout v3 (pure Python loop over every code)."""
     f = _fmt(fmt)
     _check_shape(N, K)
     buf = bytes(np.asarray(packed, dtype=np.uint8).ravel())
@@ -408,7 +408,8 @@ def unpack_tiles(packed, N: int, K: int, fmt="e3m2") -> np.ndarray:
     if p.size != packed_bytes(N, K, f):
         raise ValueError("packed buffer has the wrong size")
     nbk, kbk = N // TILE_N, K // TILE_K
-    tiles = p.reshape(nbk, kbk, tile_bytes(f)).astype(np.int64)
+    # the buffer's tiles are in (kb, nb) order
+    tiles = p.reshape(kbk, nbk, tile_bytes(f)).transpose(1, 0, 2).astype(np.int64)
     byte_idx, bit_idx = _tile_map(f)
     out = np.zeros((nbk, kbk, TILE_N, TILE_K), dtype=np.int64)
     for b in range(f.bits):
@@ -417,13 +418,13 @@ def unpack_tiles(packed, N: int, K: int, fmt="e3m2") -> np.ndarray:
 
 
 def unpack_np(packed, N: int, K: int) -> np.ndarray:
-    """Vectorised unpacker of layout v2 (e3m2; same definition, NumPy indexing)."""
+    """Vectorised unpacker of layout v3 (e3m2; same definition, NumPy indexing)."""
     _check_shape(N, K)
     p = np.asarray(packed, dtype=np.uint8).ravel()
     if p.size != N * K * 3 // 4:
         raise ValueError("packed buffer has the wrong size")
     nbk, kbk = N // TILE_N, K // TILE_K
-    tiles = p.reshape(nbk, kbk, TILE_BYTES)
+    tiles = p.reshape(kbk, nbk, TILE_BYTES).transpose(1, 0, 2)  # buffer in (kb, nb) order
     # words: 2-bit plane [nbk,kbk,lane=64,word=4]; 4-bit [nbk,kbk,half=2,lane=64,word=4]
     w2 = tiles[:, :, :1024].copy().view("<u4").reshape(nbk, kbk, 64, 4).astype(np.int64)
     w4 = tiles[:, :, 1024:].copy().view("<u4").reshape(nbk, kbk, 2, 64, 4).astype(np.int64)

@@ -110,7 +110,7 @@ def dequant_ref(codes, pos, scales, K: int) -> np.ndarray:
 # with 2 of every 4 kept).  For step j and wave lane L = 16*g + r (row r),
 # element i (0..7) of the lane is kept weight s = i%2 of the dense group at
 # k-offset 64*j + 32*(g%2) + 16*(i/4) + 8*(g/2) + 4*((i%4)/2) of the tile:
-#   * its 6-bit code sits where packed layout v2 (FP6 e3m2) puts the code of
+#   * its 6-bit code sits where the dense FP6 e3m2 packing puts the code of
 #     lane L, k-step j, element i in bytes [0, 3072) of the tile;
 #   * its position inside the group (0..3) is the 2-bit field at bit
 #     16*(j%2) + 2*i of the little-endian word at byte 3072 + 16*L + 4*(j/2).
@@ -146,7 +146,7 @@ def _sparse_slots(N: int, K: int, n: int, t2: int):
     i = i_base + s
     lane = 16 * g + r
     base = (nb * (K // TILE_K) + kb) * TILE_BYTES
-    # code bits: packed layout v2 positions of (lane, k-step j, element i)
+    # code bits: dense FP6 e3m2 tile positions of (lane, k-step j, element i)
     w2, b_e2, b_s, w4, nib = fo._locate(16, 256, r, 32 * j + 8 * g + i)
     out = [(base + w2, b_e2, ("c", 4)), (base + w2, b_s, ("c", 5))]
     out += [(base + w4, nib + b, ("c", b)) for b in range(4)]

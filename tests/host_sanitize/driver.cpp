@@ -95,7 +95,7 @@ int errors() {
     }
   };
   for (int s = -1; s < 12; ++s) expect(fp6_status_string(s) != nullptr, 1);
-  expect(fp6_pack_version(), 2);
+  expect(fp6_pack_version(), 3);
   expect(fpx_bits(9), 0);
   expect(fpx_bits(-1), 0);
   expect(static_cast<int>(fp6_packed_bytes(16, 256)), 3072);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_sizes_and_status_strings():
-    assert fp6.pack_version() == 2
+    assert fp6.pack_version() == 3
     assert fp6.packed_bytes(16, 256) == 3072
     assert fp6.packed_bytes(28672, 8192) == 176_160_768
     for bad in [(0, 256), (16, 0), (8, 256), (16, 128), (16, 300), (2**25, 256), (2**24, 2**24)]:

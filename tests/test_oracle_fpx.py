@@ -5,7 +5,7 @@ decoding (numpy) of the fp16 embedding of each code, the closed forms in
 tests/golden/fpx_formats.txt, torch's float8 rounding where the grids agree,
 numpy's rint (round-half-even) on a frexp decomposition, exact rational
 arithmetic, brute force, and hand-derived packed-byte images in
-tests/golden/packed_v2_onehot_fpx.txt.
+tests/golden/packed_v3_onehot_fpx.txt.
 """
 
 import os
@@ -226,7 +226,7 @@ def test_quantize_scale_limits():
 # ---------------------------------------------------------------------------
 def _onehot_cases():
     cases = []
-    with open(os.path.join(GOLDEN, "packed_v2_onehot_fpx.txt")) as f:
+    with open(os.path.join(GOLDEN, "packed_v3_onehot_fpx.txt")) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):

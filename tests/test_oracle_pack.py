@@ -1,6 +1,6 @@
-"""Pins of the oracle's packed-layout-v2 unpackers (FP6 e3m2).
+"""Pins of the oracle's packed-layout-v3 unpackers (FP6 e3m2).
 
-The hand-derived one-hot byte images in tests/golden/packed_v2_onehot.txt fix
+The hand-derived one-hot byte images in tests/golden/packed_v3_onehot.txt fix
 the reading of the layout independently of the oracle's code; bijection and
 cross-implementation checks cover every other position.
 """
@@ -18,7 +18,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def _onehot_cases():
     cases = []
-    with open(os.path.join(GOLDEN, "packed_v2_onehot.txt")) as f:
+    with open(os.path.join(GOLDEN, "packed_v3_onehot.txt")) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):

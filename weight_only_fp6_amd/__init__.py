@@ -11,7 +11,7 @@ call takes ``fmt`` ("e3m2" -- the default, FP6 -- "e2m3", "e2m2" or "e2m1"):
 
 * :func:`packed_bytes`, :func:`pack_version`, :func:`bits`
 * :func:`quantize_rows` (host) -> ``(codes uint8 [N,K], scales fp16 [N])``
-* :func:`prepack` (host) -> ``uint8 [N*K*bits/8]`` packed layout v2
+* :func:`prepack` (host) -> ``uint8 [N*K*bits/8]`` packed layout v3
 * :func:`linear` (device) -> ``Y fp16 [M,N] = X . dequant(W)^T``
 * :func:`linear_plan` (device, forced schedule), :func:`dequant` (device export)
 * 2:4-sparse FP6 (``include/fp6s.h``): :func:`sparse_packed_bytes`,

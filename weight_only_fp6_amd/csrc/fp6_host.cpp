@@ -1,5 +1,5 @@
 // Host side of the FPx weight-only linear layer: status strings, size rules,
-// the row quantiser and the offline packer (layout v2) of every format.
+// the row quantiser and the offline packer (layout v3) of every format.
 //
 // Plain C++17, no HIP calls: everything here runs on the CPU.
 //
@@ -103,7 +103,7 @@ bool shape_ok(int64_t N, int64_t K) {
          N % fp6::kTileN == 0 && K % fp6::kTileK == 0 && N * K <= fp6::kMaxNK;
 }
 
-// One 16 x 256 tile of codes (rows of `src` K apart) into packed layout v2.
+// One 16 x 256 tile of codes (rows of `src` K apart) into one packed tile.
 // Lane L = 16g + r owns row r, k = 32j + 8g + i (k-step j, element i).
 void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
   // Per lane: 4-bit words w4[j/4][lane][j%4]; 6-bit formats add 2-bit words
@@ -176,7 +176,7 @@ void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
 // j (64 dense k) and lane L = 16g + r, element i is kept weight i%2 of the
 // dense group at offset 64j + 32(g%2) + 16(i/4) + 8(g/2) + 4((i%4)/2): the
 // A-operand order of v_smfmac_f32_16x16x64_f16.  The 6-bit codes fill bytes
-// [0, 3072) exactly as packed layout v2 fills an FP6 tile (lane, k-step j,
+// [0, 3072) exactly as the dense packer fills an FP6 tile (lane, k-step j,
 // element i); the 2-bit positions fill [3072, 4096): lane L's word j/2 at
 // 3072 + 16L, bits 16(j%2) + 2i.
 void pack_sparse_tile(const uint8_t* codes, const uint8_t* pos, int64_t half_k, uint8_t* tile) {
@@ -205,7 +205,7 @@ void pack_sparse_tile(const uint8_t* codes, const uint8_t* pos, int64_t half_k, 
 
 extern "C" {
 
-int fp6_pack_version(void) { return 2; }
+int fp6_pack_version(void) { return 3; }
 
 const char* fp6_status_string(int status) {
   switch (status) {
@@ -290,12 +290,14 @@ int fpx_prepack(int format, const uint8_t* codes, const uint16_t* scales, int64_
     if (codes[i] >= code_end) return FP6_E_CODE;
 
   uint8_t* out = static_cast<uint8_t*>(packed);
-  const int64_t kblocks = K / fp6::kTileK;
+  // Layout v3 orders the tiles k-tile-major: tile (nb, kb) is tile number
+  // kb * nblocks + nb.
+  const int64_t kblocks = K / fp6::kTileK, nblocks = N / fp6::kTileN;
   const int64_t tile_bytes = 4096 / 8 * f->bits;
-  for (int64_t nb = 0; nb < N / fp6::kTileN; ++nb)
-    for (int64_t kb = 0; kb < kblocks; ++kb)
+  for (int64_t kb = 0; kb < kblocks; ++kb)
+    for (int64_t nb = 0; nb < nblocks; ++nb)
       pack_tile(format, codes + nb * fp6::kTileN * K + kb * fp6::kTileK, K,
-                out + (nb * kblocks + kb) * tile_bytes);
+                out + (kb * nblocks + nb) * tile_bytes);
   return FP6_OK;
 }
 

@@ -1,5 +1,5 @@
 // Tile geometry and size limits shared by the host code and the kernels of
-// the FP6 library (packed layout v2: 16 rows x 256 k per 3072-byte tile).
+// the FP6 library (packed layout v3: 16 rows x 256 k per 3072-byte tile).
 #pragma once
 #include <stdint.h>
 

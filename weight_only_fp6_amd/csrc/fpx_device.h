@@ -65,6 +65,9 @@ constexpr int kWaveSize = 64;
 //   FP4 e2m1: converted exactly to v;                    scale factor s
 // Each scale factor is an exact fp16 for the scales fp6_prepack/fpx_prepack
 // accept, so the one rounding of the multiply gives fp16_RNE(v * s).
+// Tiles follow one another k-tile by k-tile: tile (row block nb, k-tile kt)
+// is tile number kt * (N / 16) + nb, so the row blocks that a wave or a
+// workgroup reads at one k-tile lie side by side in memory.
 // ---------------------------------------------------------------------------
 enum : int { kE3M2 = 0, kE2M3 = 1, kE2M2 = 2, kE2M1 = 3 };
 
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(256) void fp6_dequant_kernel(const u32x4* __restric
   const int64_t ktiles = K >> 8;
   const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (tile >= (N >> 4) * ktiles) return;
-  const int64_t nb = tile / ktiles, kt = tile % ktiles;
+  const int64_t nblocks = N >> 4;
+  const int64_t kt = tile / nblocks, nb = tile - kt * nblocks;  // k-tile-major order
   const int r = lane & 15, g = lane >> 4;
   typename Fmt<F>::Tile t;
   Fmt<F>::load(t, wp + tile * Fmt<F>::kTileQuads + lane, lane);
@@ -469,6 +473,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
   static_assert(D % 2 == 0, "X double buffer indexes by parity");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
   const int64_t ngroups = (nblocks + A - 1) / A;
   const int64_t gquads = (ngroups + 3) >> 2;
   const uint32_t b = udiv32(blockIdx.x, splits);
@@ -490,7 +495,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
   for (int a = 0; a < A; ++a) {
     int64_t nb = rg * A + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    w[a] = wp + nb * Fmt<F>::kTileQuads + lane;
     s2[a] = row_scale2<F>(scales, nb * 16 + r);
   }
   // B operand rows m = (mg*MB + mb)*16 + r; rows >= M read row M-1 (their
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(256) void fp6_gemm_stream(
   auto load_w = [&](WStage<F, A>& st, int64_t kt) {
 #pragma unroll
     for (int a = 0; a < A; ++a) {
-      Fmt<F>::load(st.t[a], w[a] + kt * Fmt<F>::kTileQuads, lane);
+      Fmt<F>::load(st.t[a], w[a] + kt * kstr, lane);
     }
   };
   auto load_x = [&](XStage<MB>& xs, int64_t kt) {
@@ -614,6 +619,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
   const int64_t ngroups = (nblocks + A - 1) / A;
   const int64_t gsets = (ngroups + NW - 1) / NW;
   const uint32_t b = udiv32(blockIdx.x, splits);
@@ -634,7 +640,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
   for (int a = 0; a < A; ++a) {
     int64_t nb = rg * A + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    w[a] = wp + nb * Fmt<F>::kTileQuads + lane;
     s2[a] = row_scale2<F>(scales, nb * 16 + r);
   }
   // X staging: unit q = (row rr = q/32, chunk c = q%32) of the tile; rows
@@ -672,7 +678,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_xlds(
   auto load_w = [&](WStage<F, A>& st, int64_t kt) {
 #pragma unroll
     for (int a = 0; a < A; ++a) {
-      Fmt<F>::load(st.t[a], w[a] + kt * Fmt<F>::kTileQuads, lane);
+      Fmt<F>::load(st.t[a], w[a] + kt * kstr, lane);
     }
   };
   auto mac = [&](const WStage<F, A>& st, int slot) {
@@ -775,6 +781,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
   // Workgroup b takes K-split b % splits (its k-tiles [kt0, kt1)) of the
   // row blocks b / splits, + gridDim.x / splits, ...  With splits > 1 the
   // summed 16x16 tile of a row block goes through the fixed-order split-K
@@ -847,9 +854,9 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
   WStage<F, 1> wst[2][KTW];
   _Float16 wsc[2];
   auto load_rb = [&](WStage<F, 1> (&st)[KTW], _Float16& sc, int64_t nb) {
-    const u32x4* base = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    const u32x4* base = wp + nb * Fmt<F>::kTileQuads + lane;
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * Fmt<F>::kTileQuads, lane);
+    for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * kstr, lane);
     sc = scales[nb * 16 + r];
   };
   auto rb_mac = [&](const WStage<F, 1> (&st)[KTW], _Float16 sc) {
@@ -980,6 +987,7 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
   const int64_t kw0 = wave * ktiles / WK, kw1 = (wave + 1) * ktiles / WK;
   const int ktw = static_cast<int>(kw1 - kw0);
   auto tile_of = [&](int t) -> int64_t {
@@ -1002,7 +1010,7 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     // loads (they do not depend on the row block) and keep them all live.
     const int64_t nb = blockIdx.x;
     if (nb >= nblocks) return;  // uniform for the workgroup
-    const u32x4* base = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    const u32x4* base = wp + nb * Fmt<F>::kTileQuads + lane;
     // M = 1 (KTW = 1): the 16 columns of the B operand all repeat X's single
     // row, so each lane loads just 8 of the tile's 256 values (one 8-byte
     // load, issued before the weights so that waiting for it does not wait
@@ -1014,7 +1022,7 @@ __global__ __launch_bounds__(64 * WK) void fp6_gemm_kslice(
     if constexpr (M1) x1 = *reinterpret_cast<const half4v*>(X + tile_of(0) * 256 + 4 * lane);
     WStage<F, 1> st[KTW];
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * Fmt<F>::kTileQuads, lane);
+    for (int t = 0; t < KTW; ++t) Fmt<F>::load(st[t].t[0], base + tile_of(t) * kstr, lane);
     const half2v s2 = row_scale2<F>(scales, nb * 16 + r);
     float4v acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KTW == 1) {
@@ -1145,6 +1153,7 @@ __device__ __forceinline__ void tiled_run(const _Float16* __restrict__ X, const 
   constexpr int kLoadsPerThread = kHalfUnits / kThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
   const int r = lane & 15, g = lane >> 4;
   const int64_t m0 = mg * BM;
 
@@ -1157,7 +1166,7 @@ __device__ __forceinline__ void tiled_run(const _Float16* __restrict__ X, const 
   for (int a = 0; a < kTA; ++a) {
     int64_t nb = nt * 16 + wave * kTA + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    w[a] = wp + nb * Fmt<F>::kTileQuads + lane;
     srow[a] = nb * 16 + r;
   }
   auto load_wh = [&](WHalf<F, TA>& st, int64_t h) {  // half-tile h: k-tile h>>1, half h&1
@@ -1165,7 +1174,7 @@ __device__ __forceinline__ void tiled_run(const _Float16* __restrict__ X, const 
     const int hh = static_cast<int>(h & 1);
 #pragma unroll
     for (int a = 0; a < kTA; ++a) {
-      Fmt<F>::load_half(st.h[a], w[a] + kt * Fmt<F>::kTileQuads, hh, lane);
+      Fmt<F>::load_half(st.h[a], w[a] + kt * kstr, hh, lane);
     }
   };
 
@@ -1424,6 +1433,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledl(
   // of the direct loads need no per-load conversion.
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
   const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
   const int split = static_cast<int>(umod32(lb, splits));
@@ -1443,7 +1453,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledl(
   for (int a = 0; a < TA; ++a) {
     int64_t nb = nt * 16 + wave * TA + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    w[a] = wp + nb * Fmt<F>::kTileQuads + lane;
     s2[a] = row_scale2<F>(scales, nb * 16 + r);
   }
   // This wave's row block a in a weight stage.
@@ -1452,7 +1462,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledl(
     const int64_t kt = h >> 1;
     const int hh = static_cast<int>(h & 1);
 #pragma unroll
-    for (int a = 0; a < TA; ++a) Fmt<F>::stage_half(wregion(stage, a), w[a] + kt * Fmt<F>::kTileQuads, hh, lane);
+    for (int a = 0; a < TA; ++a) Fmt<F>::stage_half(wregion(stage, a), w[a] + kt * kstr, hh, lane);
   };
   auto read_w = [&](WHalfL<F, TA>& st, u32x4* stage) {
 #pragma unroll
@@ -1625,6 +1635,7 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
   const int64_t ntiles = (nblocks + 15) >> 4;     // 256-row workgroup tiles
   const uint32_t lb = static_cast<uint32_t>(xcd_logical_block(blockIdx.x, gridDim.x));
   const int split = static_cast<int>(umod32(lb, splits));
@@ -1644,12 +1655,12 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledw(
   for (int a = 0; a < TA; ++a) {
     int64_t nb = nt * 16 + wave * TA + a;
     if (nb >= nblocks) nb = nblocks - 1;
-    w[a] = wp + (nb * ktiles) * Fmt<F>::kTileQuads + lane;
+    w[a] = wp + nb * Fmt<F>::kTileQuads + lane;
     srow[a] = nb * 16 + r;
   }
   auto load_wt = [&](WTile<F, TA>& st, int64_t kt) {
 #pragma unroll
-    for (int a = 0; a < TA; ++a) Fmt<F>::load(st.t[a], w[a] + kt * Fmt<F>::kTileQuads, lane);
+    for (int a = 0; a < TA; ++a) Fmt<F>::load(st.t[a], w[a] + kt * kstr, lane);
   };
 
   // X direct loads: instruction i of this wave fills LDS units

@@ -13,7 +13,7 @@
 //    of the dense group at k-offset 32(g%2) + 16(i/4) + 8(g/2) + 4((i%4)/2),
 //    its position taken from bits 16*abid + 2i of the index VGPR.
 //  * A packed tile covers 16 rows x 512 dense k (4096 bytes): the kept codes
-//    in the FP6 packed layout v2 (so the FP6 splice and row-scale fold are
+//    in the order of a dense FP6 tile (so the FP6 splice and row-scale fold are
 //    reused unchanged) and one 16-byte quad of positions per lane, whose word
 //    j/2 is the index operand of k-steps j (abid 0) and j+1 (abid 1).  A wave
 //    reads a tile with four coalesced 16-byte loads per lane.
