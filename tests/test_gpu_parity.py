@@ -493,13 +493,15 @@ DENSE_PLANS = [
     ((16, 4096, 2048), (KSLICE, 1)),
     ((16, 8192, 2048), (KSPLIT, 1)),     # K <= 2048: 8-wave k-split
     ((16, 11008, 4096), (KSPLIT16, 1)),  # 3 row blocks per workgroup in flight
-    ((16, 8192, 8192), (KSPLIT16, 2)),   # K split across workgroups
+    ((16, 8192, 8192), (15, 2)),         # 4 row blocks per k-split workgroup: streaming instead
     ((16, 5120, 5120), (KSPLIT, 3)),     # 8 waves: fewer idle waves on 10-tile splits
-    ((16, 4096, 11008), (KSPLIT16, 3)),
+    ((16, 4096, 11008), (15, 4)),
+    ((16, 2048, 8192), (KSPLIT16, 2)),   # 1 row block per workgroup: K split across workgroups
+    ((16, 3072, 8192), (KSPLIT, 4)),     # 8 waves: 3 row blocks per workgroup
     ((1, 4096, 11008), (KSLICE, 1)),     # M <= 4, one row block per CU: k-slice up to K = 12288
     ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups
     ((16, 57344, 8192), (16, 1)),        # 2 row blocks per wave: one round instead of 1.75
-    ((16, 8192, 28672), (14, 4)),        # 2 row blocks per wave, split while a whole round fits
+    ((16, 8192, 28672), (15, 2)),        # split while a whole round of 4-wave workgroups fits
     ((32, 21504, 7168), (19, 3)),        # 32 columns per workgroup
     ((64, 4096, 4096), (22, 4)),         # 64 columns, 1 row block per wave
     ((64, 21504, 7168), (20, 3)),

@@ -219,13 +219,14 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     const bool one_rb_per_cu = (N >> 4) <= cus;
     // Longer K (split count not forced): the k-split kernel with K split
     // across workgroups, one k-tile per wave and split, all row blocks of a
-    // workgroup in flight (Llama-70B attention output 16x8192x8192: 20.0 ->
-    // 15.2 us).  Candidates: 16 or 8 waves, the fewest splits that fit and
-    // one more.  A workgroup's work is its straight-line form's row-block
-    // count times its waves (idle waves of a short split still load a
-    // stand-in tile); the cheapest wins, ties to fewer splits, and only up
-    // to 6 row blocks x 16 waves (beyond, the streaming kernel wins).
-    // 16x5120x5120: 8 waves x 3 splits 9.8 us against 16 x 2 11.0 us.
+    // workgroup in flight.  Candidates: 16 or 8 waves, the fewest splits
+    // that fit and one more.  A workgroup's work is its straight-line form's
+    // row-block count times its waves (idle waves of a short split still
+    // load a stand-in tile); the cheapest wins, ties to fewer splits, and
+    // only up to 3 row blocks x 16 waves: beyond, the streaming kernel is
+    // faster (16x8192x5120 12.1 -> 10.7 us, 16x4096x11008 13.0 -> 12.2,
+    // 16x5120x13824 17.4 -> 15.0), below it loses (16x2048x8192 8.2 against
+    // 11.8 us).  16x5120x5120: 8 waves x 3 splits 9.8 us against 16 x 2 11.0 us.
     int ks_variant = 0;
     int64_t ks_splits = 0, ks_cost = 0;
     if (splits == 0 && ktiles > 16) {
@@ -238,7 +239,7 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
           if (rows > 8) continue;
           const int64_t form = rows <= 4 ? rows : (rows <= 6 ? 6 : 8);
           const int64_t cost = form * wk;
-          if (cost > 6 * 16) continue;
+          if (cost > 3 * 16) continue;
           if (ks_variant == 0 || cost < ks_cost || (cost == ks_cost && sp < ks_splits)) {
             ks_variant = wk == 16 ? 12 : 9;
             ks_splits = sp;
@@ -266,14 +267,14 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     } else if (M <= 16) {
       // 2 row blocks per wave once that fits one round of 8-wave workgroups
       // and 1 per wave would take almost two (fused Llama-70B gate/up,
-      // 16x57344x8192: 69.7 -> 67.0 us).
-      // With at most half a 4-wave workgroup per CU (K split anyway), 2 row
-      // blocks per wave and twice the splits (Llama-70B down projection,
-      // 16x8192x28672: 39.1 -> 37.8 us).
+      // 16x57344x8192: 69.7 -> 67.0 us).  Below 7 row blocks per CU, 4-wave
+      // workgroups with 1 row block per wave (2 per wave measured slower at
+      // every such shape: Llama-70B down projection 16x8192x28672 37.3 ->
+      // 35.1 us, 16x8192x8192 15.6 against 13.8 us).
       const int64_t nb = N >> 4, c = cus;
       if (nb >= 14 * c && ceil_div(nb, 16) <= c) p.variant = 16;
       else if (nb >= 7 * c) p.variant = 18;
-      else p.variant = ceil_div(nb, 4) <= c / 2 ? 14 : 15;
+      else p.variant = 15;
     } else if (splits == 0 &&
                (M <= 64 || (M <= 256 && ceil_div(N >> 4, 8) <= cus / 2 &&
                             ceil_div(M, 64) * ceil_div(N >> 4, 8) < cus))) {
