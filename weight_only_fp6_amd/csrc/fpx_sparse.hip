@@ -32,9 +32,10 @@ struct SpTile {
   u32x4 idx;   // positions: word j/2 = k-steps j (bits 0..15) and j+1 (16..31)
 };
 
+template <bool NT = false>
 __device__ __forceinline__ void sp_load(SpTile& t, const u32x4* p, int lane) {
-  Fmt<kE3M2>::load(t.w, p, lane);
-  t.idx = p[192];
+  Fmt<kE3M2>::template load<NT>(t.w, p, lane);
+  t.idx = ldw<NT>(p + 192);
 }
 
 template <int J>
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(64 * WK) void sp_gemm_kslice(
   const bool active = kw1 > kw0;
   const int64_t kt = active ? kw0 : 0;
   SpTile st;
-  sp_load(st, wp + (nb * ktiles + kt) * kSpTileQuads + lane, lane);
+  sp_load<true>(st, wp + (nb * ktiles + kt) * kSpTileQuads + lane, lane);
   // B operand rows m = r; rows >= M read row M-1 (their columns are never stored)
   const int64_t m = r < M ? r : M - 1;
   const _Float16* xrow = X + m * K + kt * 512 + 16 * g;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(512) void sp_gemm_ksplit(
   SpTile ast[S];
   _Float16 asc[S];
   auto load_rb = [&](int st, int64_t rb) {
-    sp_load(ast[st], wp + (rb * ktiles + kt) * kSpTileQuads + lane, lane);
+    sp_load<true>(ast[st], wp + (rb * ktiles + kt) * kSpTileQuads + lane, lane);
     asc[st] = scales[rb * 16 + r];
   };
 #pragma unroll
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_xlds(
   };
   auto load_w = [&](Stage& st, int64_t kt) {
 #pragma unroll
-    for (int a = 0; a < A; ++a) sp_load(st.t[a], w[a] + kt * kSpTileQuads, lane);
+    for (int a = 0; a < A; ++a) sp_load<MB == 1>(st.t[a], w[a] + kt * kSpTileQuads, lane);
   };
   auto mac = [&](const Stage& st, int slot) {
     const half8v* xb = xs[slot];
