@@ -53,7 +53,9 @@ enum fp6_status {
                        parameter is out of range                            */
 };
 
-/* Version of the packed weight layout produced by fp6_prepack (2). */
+/* Version of the packed weight layout produced by fp6_prepack (3).  The
+ * kernels read this version only: a buffer packed by an earlier version is
+ * packed again from its codes (fp6_prepack is deterministic). */
 int fp6_pack_version(void);
 
 /* Static, NUL-terminated text for a status code (never NULL). */

@@ -39,10 +39,12 @@
  *         is at b + 16h and bit s at b + 4 + 16h of word j/2 of lane L; in
  *         the 4-bit word j%4 element i is the nibble at slot i/2 + 4*(i%2).
  *   e2m2: 4-bit plane (e1 e0 m1 m0 = c & 15) at tile bytes [0,2048) laid out
- *         like the FP6 one ([0,1024) k-steps 0..3, [1024,2048) k-steps 4..7,
- *         16 bytes per lane, word j%4, nibble slot i/2 + 4*(i%2)); 1-bit
+ *         like the e3m2 one ([0,1024) k-steps 0..3, [1024,2048) k-steps 4..7,
+ *         16 bytes per lane, word j%4, nibble slot 2*(i%4) + i/4); 1-bit
  *         plane (s = c >> 4) at [2048,2560): lane L's 8 bytes at 2048 + 8L,
- *         word j/4, bit 4*(j%4) + i/2 + 16*(i%2).
+ *         word j/4, bit (7 + 8*(i%4) + 2*(j%4) + i/4) mod 32 (layout v3;
+ *         v1 and v2 had bit 4*(j%4) + i/2 + 16*(i%2), nibble slot
+ *         i/2 + 4*(i%2)).
  *   e2m1: one 4-bit plane at [0,2048) laid out like the FP6 one but holding
  *         the whole code, element i in nibble slot i.
  */

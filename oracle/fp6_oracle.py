@@ -261,10 +261,12 @@ def quantize_rows_sampled(W_rows, fmt="e3m2") -> tuple[np.ndarray, np.ndarray]:
 #   11][p]: bit e1 sits at b + 16*h and bit s at b + 4 + 16*h of the 2-bit
 #   word; element i occupies nibble slot (i//2) + 4*(i%2) of the 4-bit word.
 # FP5 e2m2 (tile 2560 bytes): 4-bit piece (e1,e0,m1,m0 = c&15) in a 4-bit
-#   plane at bytes [0,2048) laid out as the e2m3 one; the sign (c>>4) in a
-#   1-bit plane at [2048,2560): lane L owns the 8 bytes at 2048 + 8*L as two
-#   words; word j//4 holds k-steps 4*(j//4)..+3, with P = 4*(j%4) + i//2 the
-#   sign sits at bit P + 16*h.
+#   plane at bytes [0,2048) laid out as the e3m2 one (element i in nibble
+#   slot 2*(i%4) + i//4); the sign (c>>4) in a 1-bit plane at [2048,2560):
+#   lane L owns the 8 bytes at 2048 + 8*L as two words; word j//4 holds
+#   k-steps 4*(j//4)..+3, and the sign of element i of k-step j sits at bit
+#   (7 + 8*(i%4) + 2*(j%4) + i//4) mod 32 (layout v3; v1 and v2 put it at
+#   4*(j%4) + i//2 + 16*(i%2) with the e2m3 nibble order).
 # FP4 e2m1 (tile 2048 bytes): one 4-bit plane at [0,2048) laid out as the FP6
 #   one, holding the whole code, element i in nibble slot i (natural order).
 # ---------------------------------------------------------------------------
@@ -330,10 +332,10 @@ def _slots(fmt, N: int, K: int, n: int, k: int):
         return [(w2, b, 4), (w2, b + 4, 5)] + [(w4, nib + q, q) for q in range(4)]
     if f.name == "e2m2":
         w4 = base + 1024 * (j // 4) + 16 * lane + 4 * (j % 4)
-        nib = 4 * ((i // 2) + 4 * (i % 2))
+        nib = 4 * (2 * (i % 4) + i // 4)
         w1 = base + 2048 + 8 * lane + 4 * (j // 4)
-        P = 4 * (j % 4) + i // 2
-        return [(w4, nib + q, q) for q in range(4)] + [(w1, P + 16 * h, 4)]
+        b1 = (7 + 8 * (i % 4) + 2 * (j % 4) + i // 4) % 32
+        return [(w4, nib + q, q) for q in range(4)] + [(w1, b1, 4)]
     if f.name == "e2m1":
         w4 = base + 1024 * (j // 4) + 16 * lane + 4 * (j % 4)
         return [(w4, 4 * i + q, q) for q in range(4)]

@@ -143,10 +143,14 @@ void pack_tile(int format, const uint8_t* src, int64_t K, uint8_t* tile) {
             d4 |= (c & 0xFu) << (4 * slot);
             break;
           }
-          case FPX_E2M2:
-            w1[lane][j >> 2] |= ((c >> 4) & 1u) << (4 * (j & 3) + (i >> 1) + 16 * h);
-            d4 |= (c & 0xFu) << (4 * slot);
+          case FPX_E2M2: {
+            // As e3m2's 4-bit word; the sign at bit 7 of byte E once the
+            // 1-bit word is rotated right by 2(j%4) + G.
+            const int G = i >> 2, E = i & 3;
+            w1[lane][j >> 2] |= ((c >> 4) & 1u) << ((7 + 8 * E + 2 * (j & 3) + G) & 31);
+            d4 |= (c & 0xFu) << (4 * (2 * E + G));
             break;
+          }
           default:  // FPX_E2M1: whole code, natural nibble order
             d4 |= (c & 0xFu) << (4 * i);
             break;

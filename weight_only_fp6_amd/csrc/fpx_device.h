@@ -127,18 +127,21 @@ __device__ __forceinline__ half8v splice6(uint32_t d2, uint32_t d4, half2v s2) {
   return a;
 }
 
-// FP5 e2m2, k-step j: the 4-bit word d4 as for FP6 (magnitude e1 e0 m1 m0 to
-// fp16 bits 11..8), the sign from the 1-bit word d1 (k-steps 4*(j/4)..+3):
-// pair P = 4*(j%4)+q has its signs at bits P and P+16; rotr(d1, (P-15) mod 32)
-// lands them on fp16 bits 15 and 31.
+// FP5 e2m2, k-step j: the fp16 pattern of v * 2^-14 has all its bits in the
+// high byte too, (s<<7) | (e1 e0 m1 m0).  The 4-bit word is ordered as
+// e3m2's; the 1-bit word d1 (k-steps 4*(j/4)..+3) rotated right by
+// 2*(j%4) + G has the sign of element 4G+E at bit 7 of byte E.  So the
+// e3m2 form applies: one and_or per group, one v_perm_b32 per pair.
 template <int JM4>
 __device__ __forceinline__ half8v splice5(uint32_t d1, uint32_t d4, half2v s2) {
-  constexpr uint32_t kM4 = 0x0F000F00u, kM1 = 0x80008000u;
-  constexpr int r0 = (4 * JM4 + 17) & 31;  // (P - 15) mod 32 for pair 0 of this k-step
-  const uint32_t t0 = ((d4 << 8) & kM4) | (__builtin_amdgcn_alignbit(d1, d1, r0) & kM1);
-  const uint32_t t1 = ((d4 << 4) & kM4) | (__builtin_amdgcn_alignbit(d1, d1, (r0 + 1) & 31) & kM1);
-  const uint32_t t2 = (d4 & kM4) | (__builtin_amdgcn_alignbit(d1, d1, (r0 + 2) & 31) & kM1);
-  const uint32_t t3 = ((d4 >> 4) & kM4) | (__builtin_amdgcn_alignbit(d1, d1, (r0 + 3) & 31) & kM1);
+  constexpr uint32_t kNib = 0x0F0F0F0Fu, kS = 0x80808080u;
+  constexpr uint32_t kLo = 0x010C000Cu, kHi = 0x030C020Cu;  // as in splice6
+  const uint32_t wa = (d4 & kNib) | (__builtin_amdgcn_alignbit(d1, d1, 2 * JM4) & kS);
+  const uint32_t wb = ((d4 >> 4) & kNib) | (__builtin_amdgcn_alignbit(d1, d1, 2 * JM4 + 1) & kS);
+  const uint32_t t0 = __builtin_amdgcn_perm(wa, wa, kLo);
+  const uint32_t t1 = __builtin_amdgcn_perm(wa, wa, kHi);
+  const uint32_t t2 = __builtin_amdgcn_perm(wb, wb, kLo);
+  const uint32_t t3 = __builtin_amdgcn_perm(wb, wb, kHi);
   const half2v h0 = __builtin_bit_cast(half2v, t0) * s2;
   const half2v h1 = __builtin_bit_cast(half2v, t1) * s2;
   const half2v h2 = __builtin_bit_cast(half2v, t2) * s2;
