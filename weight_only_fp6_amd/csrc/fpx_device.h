@@ -1586,7 +1586,9 @@ __global__ __launch_bounds__(64 * NW) void fp6_gemm_tiledl(
     stage_w(wt, hw);
     __builtin_amdgcn_sched_barrier(0);
     read_b(bfr[0], xc, 0);
+    __builtin_amdgcn_sched_barrier(0);
     read_b(bfr[1], xc, 1); splice(afr[1], wc, I1{}); mfmas(afr[0], bfr[0]); interleave(IB{});
+    __builtin_amdgcn_sched_barrier(0);
     read_b(bfr[0], xc, 2); splice(afr[0], wc, I2{}); mfmas(afr[1], bfr[1]); interleave(IB{});
     __builtin_amdgcn_sched_barrier(0);
     vmcnt(WaitW{});
