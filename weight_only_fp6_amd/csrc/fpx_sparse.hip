@@ -468,36 +468,55 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_tiled(
 
   half8v afr[2][TA];
   half16v bfr[B];
+  auto read_b1 = [&](const half8v* buf, int jj, int bi) {
+    const int mm = bi * 16 + r;
+    const int s0 = (8 * jj + 2 * g) ^ (mm & 15);
+    bfr[bi] = __builtin_shufflevector(buf[mm * 32 + s0], buf[mm * 32 + (s0 ^ 1)], 0, 1, 2, 3, 4, 5, 6, 7, 8,
+                                      9, 10, 11, 12, 13, 14, 15);
+  };
   auto read_b = [&](const half8v* buf, int jj) {
 #pragma unroll
-    for (int bi = 0; bi < B; ++bi) {
-      const int mm = bi * 16 + r;
-      const int s0 = (8 * jj + 2 * g) ^ (mm & 15);
-      bfr[bi] = __builtin_shufflevector(buf[mm * 32 + s0], buf[mm * 32 + (s0 ^ 1)], 0, 1, 2, 3, 4, 5, 6, 7, 8,
-                                        9, 10, 11, 12, 13, 14, 15);
-    }
+    for (int bi = 0; bi < B; ++bi) read_b1(buf, jj, bi);
   };
   auto splice = [&](half8v (&dst)[TA], const SpWHalf<TA>& wh, auto JC) {
     constexpr int jj = decltype(JC)::value;
 #pragma unroll
     for (int a = 0; a < TA; ++a) dst[a] = splice6<kE3M2, jj & 1>(wh.h[a].q2[jj >> 1], wh.h[a].q4[jj], s2[a]);
   };
-  auto mfmas = [&](const half8v (&av)[TA], const SpWHalf<TA>& wh, auto JC) {
+  // One k-step's products.  With RD, column group bi's fragment of k-step jn
+  // is read into bfr[bi] right after the last product that uses it, so the
+  // next k-step's reads overlap this one's products in the same registers
+  // (two fragment sets would not fit).  Schedule: 1 MFMA then 3 VALU (the
+  // next splice); with RD the last row block's MFMAs take the 2 LDS reads
+  // of one fragment and 2 VALU each.
+  auto mfmas = [&](const half8v (&av)[TA], const SpWHalf<TA>& wh, auto JC, const half8v* buf, int jn,
+                   auto RD) {
     constexpr int jj = decltype(JC)::value;
+    constexpr bool rd = decltype(RD)::value;
 #pragma unroll
     for (int a = 0; a < TA; ++a)
 #pragma unroll
-      for (int bi = 0; bi < B; ++bi)
+      for (int bi = 0; bi < B; ++bi) {
         acc[a * B + bi] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(
             av[a], bfr[bi], acc[a * B + bi], static_cast<int>(wh.h[a].idx[jj >> 1]), 0, jj & 1);
-  };
-  auto interleave = [&]() {
+        if constexpr (rd) {
+          if (a == TA - 1) read_b1(buf, jn, bi);
+        }
+      }
 #pragma unroll
-    for (int i = 0; i < TA * B; ++i) {
+    for (int i = 0; i < (TA - 1) * B; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (rd) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, rd ? 2 : 3, 0);
+    }
   };
+  using RD1 = std::integral_constant<bool, true>;
+  using RD0 = std::integral_constant<bool, false>;
   using J0 = std::integral_constant<int, 0>;
   using J1 = std::integral_constant<int, 1>;
   using J2 = std::integral_constant<int, 2>;
@@ -516,12 +535,15 @@ __global__ __launch_bounds__(64 * NW) void sp_gemm_tiled(
     __builtin_amdgcn_sched_barrier(0);
     load_wh(wn, hnext);
     __builtin_amdgcn_sched_barrier(0);
-    read_b(cur, 0); splice(afr[1], wc, J1{}); mfmas(afr[0], wc, J0{}); interleave();
-    read_b(cur, 1); splice(afr[0], wc, J2{}); mfmas(afr[1], wc, J1{}); interleave();
-    read_b(cur, 2); splice(afr[1], wc, J3{}); mfmas(afr[0], wc, J2{}); interleave();
-    read_b(cur, 3);
+    read_b(cur, 0);
     __builtin_amdgcn_sched_barrier(0);
-    splice(afr[0], wn, J0{}); mfmas(afr[1], wc, J3{}); interleave();
+    splice(afr[1], wc, J1{}); mfmas(afr[0], wc, J0{}, cur, 1, RD1{});
+    __builtin_amdgcn_sched_barrier(0);
+    splice(afr[0], wc, J2{}); mfmas(afr[1], wc, J1{}, cur, 2, RD1{});
+    __builtin_amdgcn_sched_barrier(0);
+    splice(afr[1], wc, J3{}); mfmas(afr[0], wc, J2{}, cur, 3, RD1{});
+    __builtin_amdgcn_sched_barrier(0);
+    splice(afr[0], wn, J0{}); mfmas(afr[1], wc, J3{}, cur, 0, RD0{});
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitDma);
     __syncthreads();
