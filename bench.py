@@ -83,7 +83,7 @@ def _parse():
     ap.add_argument("--format", default="e3m2", choices=sorted(FORMAT_BITS),
                     help="weight format (e3m2 = FP6 through fp6_linear; others through fpx_linear)")
     ap.add_argument("--sparse", action="store_true",
-                    help="2:4-sparse FP6 e3m2 weights through fp6s_linear (K % 512 == 0)")
+                    help="2:4-sparse FP6 e3m2 weights through fp6s_linear (K %% 512 == 0)")
     ap.add_argument("--no-graph", action="store_true", help="time direct launches instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the fp16 BLAS and read-probe context numbers")
