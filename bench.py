@@ -21,8 +21,9 @@ Also reported, as context:
 * ``fp16_blas``: the same layer as an fp16 torch linear (hipBLASLt) on
   de-quantised weights, with rotated cold copies -- the W16A16 reference the
   FP6-LLM pages normalise their kernel speedups to;
-* ``read_ceiling_gbs``: a plain streaming-read probe over a buffer of the
-  packed-weight size (the practical HBM ceiling at this size);
+* ``read_ceiling_gbs``: a streaming-read probe (plain and non-temporal loads,
+  the best of a few chunk counts) over a buffer of the packed-weight size (the
+  practical HBM ceiling at this size);
 * ``mfma_ceiling_tflops``: a loop of register-only fp16 MFMAs over the whole
   GPU (the practical dense fp16 MFMA ceiling);
 * ``warm_weights``: the same launch with one weight copy reused every time,
@@ -251,19 +252,21 @@ def fp16_blas_context(torch, fp6, stream, pk, sc, x, M, N, K, fmt="e3m2"):
 
 
 def read_ceiling(torch, nbytes, stream):
-    """Plain streaming read of a buffer of nbytes, rotated over >= 1 GiB."""
+    """Streaming read of a buffer of nbytes, rotated over >= 1 GiB: the best of
+    plain and non-temporal loads over a few per-wave chunk counts."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_fp6_amd", "libfp6probe.so"))
-    lib.fp6probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
-                                  ctypes.c_void_p]
+    lib.fp6probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
     nbytes = (nbytes // 1024) * 1024
     R = int(min(64, max(2, math.ceil(ROT_BYTES / nbytes))))
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
     out = torch.zeros(4, dtype=torch.int32, device="cuda")
     best = None
-    for per_wave in (8, 32):
+    for nt, per_wave in ((1, 8), (1, 16), (0, 8), (0, 32)):
         def launch(i):
-            if lib.fp6probe_read(bufs[i % R].data_ptr(), nbytes, per_wave, out.data_ptr(), stream.cuda_stream):
+            if lib.fp6probe_read(bufs[i % R].data_ptr(), nbytes, per_wave, nt, out.data_ptr(),
+                                 stream.cuda_stream):
                 raise RuntimeError("probe launch failed")
         launch(0)
         torch.cuda.synchronize()
