@@ -31,7 +31,8 @@ ALL_VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 14, 15, 16, 17, 18, 19, 20, 2
 KSPLIT = 9
 KSPLIT16 = 12
 KSLICE = 13
-SMALL_M = (KSPLIT, KSPLIT16, KSLICE)   # M <= 16 only
+KRING = 26
+SMALL_M = (KSPLIT, KSPLIT16, KSLICE, KRING)   # M <= 16 only
 
 
 def _bits16(t):
@@ -262,6 +263,77 @@ def test_linear_ksplit_across_workgroups(NK, M):
             assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, variant, splits)
 
 
+@pytest.mark.parametrize("K, per_wg, M", [(K, w, M) for K, ws in ((256, (1, 3)), (2816, (1, 2, 3, 5, 8)),
+                                                                    (5120, (2, 3, 4)), (7168, (3,)), (8192, (2,)))
+                                          for w in ws for M in (1, 5, 16)])
+def test_linear_kring_row_blocks_per_workgroup(K, per_wg, M):
+    # The k-ring kernel: each of 8 waves holds a fixed K slice of X (K/256 = 1
+    # leaves 7 waves with an empty slice and stand-in tiles, 11, 20 and 28
+    # k-tiles give ragged 1/2, 2/3 and 3/4-tile slices) and walks per_wg
+    # row blocks (the last workgroup fewer).  Every output element.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nblocks = (per_wg - 1) * cus + max(cus // 3, 1) if per_wg > 1 else cus - 5
+    N = 16 * nblocks
+    ws = dense_weight_set(N, K, 700 + per_wg + K)
+    X = synth.activations(M, K, 710 + M)
+    yref = y_ref(X, ws.wdq_ref)
+    Xd = torch.from_numpy(X).to(DEV)
+    Pd, Sd = ws.to_device()
+    Y = fp6.linear_plan(Xd, Pd, Sd, N, K, variant=KRING).clone()
+    Y2 = fp6.linear_plan(Xd, Pd, Sd, N, K, variant=KRING)
+    torch.cuda.synchronize()
+    _assert_tol(Y, yref, what=(M, per_wg, K))
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, per_wg, K)
+
+
+def test_kring_one_hot_every_tile_slot():
+    # One-hot activations through the k-ring kernel at K = 7168 (28 k-tiles:
+    # waves own 3 or 4), 3 row blocks per workgroup with a short last
+    # workgroup: columns land in every tile slot of several waves, so every
+    # output must equal a de-quantised weight exactly.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K, M = 16 * (2 * cus + 7), 7168, 16
+    ws = dense_weight_set(N, K, 4242)
+    kt = K // 256
+    cols = []
+    for m in range(M):
+        w = (3 * m + 1) % 8
+        k0, k1 = w * kt // 8, (w + 1) * kt // 8
+        slot = m % (k1 - k0)
+        cols.append((k0 + slot) * 256 + (41 * m + 5) % 256)
+    ks = np.array(cols)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
+    want = ws.wdq_ref[:, ks].T.astype(np.float64)
+    for m_used in (1, 5, 16):
+        Y = fp6.linear_plan(Xd[:m_used].contiguous(), packed, s, N, K, variant=KRING)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), want[:m_used]), m_used
+
+
+def test_kring_rejects_what_it_does_not_cover():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = Prepared(16, 64, 512, seed_w=15, seed_x=16)
+    X, packed, s = p.to_device()
+    with pytest.raises(fp6.FP6Error):      # no K-splits
+        fp6.linear_plan(X, packed, s, 64, 512, variant=KRING, splits=2)
+    X17 = torch.zeros((17, 512), dtype=torch.float16, device=DEV)
+    with pytest.raises(fp6.FP6Error):      # M <= 16
+        fp6.linear_plan(X17, packed, s, 64, 512, variant=KRING)
+    N = 16 * (8 * cus + 1)                 # 9 row blocks per CU
+    big = torch.zeros(fp6.packed_bytes(N, 256), dtype=torch.uint8, device=DEV)
+    sc = torch.zeros(N, dtype=torch.float16, device=DEV)
+    X1 = torch.zeros((1, 256), dtype=torch.float16, device=DEV)
+    with pytest.raises(fp6.FP6Error):
+        fp6.linear_plan(X1, big, sc, N, 256, variant=KRING)
+    Xk = torch.zeros((1, 8448), dtype=torch.float16, device=DEV)
+    wk = torch.zeros(fp6.packed_bytes(64, 8448), dtype=torch.uint8, device=DEV)
+    with pytest.raises(fp6.FP6Error):      # K <= 8192
+        fp6.linear_plan(Xk, wk, s, 64, 8448, variant=KRING)
+
+
 STREAM_K = 25
 
 
@@ -305,7 +377,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     X[np.arange(16), ks] = 1.0
     Xd = torch.from_numpy(X).to(DEV)
     _, packed, s = p.to_device()
-    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (KSLICE, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3), (19, 2), (20, 3), (21, 1), (22, 4), (23, 1), (23, 3), (24, 2), (25, 0)]:
+    for variant, splits in [(0, 0), (1, 1), (1, 4), (2, 1), (2, 3), (3, 2), (4, 1), (5, 1), (5, 3), (6, 1), (6, 2), (7, 2), (8, 1), (KSPLIT, 0), (KSPLIT16, 0), (KSLICE, 0), (14, 1), (15, 2), (16, 1), (10, 1), (10, 3), (11, 2), (17, 1), (17, 3), (18, 1), (18, 3), (19, 2), (20, 3), (21, 1), (22, 4), (23, 1), (23, 3), (24, 2), (25, 0), (KRING, 0)]:
         Y = fp6.linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         got = Y.cpu().numpy().astype(np.float64)
@@ -490,13 +562,17 @@ def test_linear_large_n_or_k(M, N, K):
 # ----------------------------------------------------------------------------
 DENSE_PLANS = [
     ((1, 4096, 4096), (KSLICE, 1)),      # one row block per CU: k-slice
-    ((16, 4096, 2048), (KSLICE, 1)),
-    ((16, 8192, 2048), (KSPLIT, 1)),     # K <= 2048: 8-wave k-split
-    ((16, 11008, 4096), (KSPLIT16, 1)),  # 3 row blocks per workgroup in flight
-    ((16, 8192, 8192), (15, 2)),         # 4 row blocks per k-split workgroup: streaming instead
-    ((16, 5120, 5120), (KSPLIT, 3)),     # 8 waves: fewer idle waves on 10-tile splits
+    ((4, 4096, 8192), (KSLICE, 1)),      # M <= 4, one row block per CU: k-slice
+    ((16, 4096, 2048), (KRING, 1)),      # M > 4, every CU a row block: k-ring
+    ((16, 8192, 2048), (KRING, 1)),      # K <= 4096: k-ring up to 8 row blocks per CU
+    ((16, 28672, 4096), (KRING, 1)),
+    ((16, 11008, 4096), (KRING, 1)),
+    ((16, 8192, 8192), (KRING, 1)),      # longer K: k-ring up to 3 row blocks per CU
+    ((1, 10240, 8192), (KRING, 1)),
+    ((16, 5120, 5120), (KRING, 1)),
+    ((16, 13824, 5120), (15, 1)),        # 4 row blocks per CU at K > 4096: streaming
+    ((16, 2048, 8192), (KSPLIT16, 2)),   # half the CUs with a row block: K split across workgroups
     ((16, 4096, 11008), (15, 4)),
-    ((16, 2048, 8192), (KSPLIT16, 2)),   # 1 row block per workgroup: K split across workgroups
     ((16, 3072, 8192), (KSPLIT, 4)),     # 8 waves: 3 row blocks per workgroup
     ((1, 4096, 11008), (KSLICE, 1)),     # M <= 4, one row block per CU: k-slice up to K = 12288
     ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups

@@ -242,7 +242,7 @@ KERNEL_NAMES = {
     16: "fp6_gemm_xlds<2,4,8>", 17: "fp6_gemm_tiledw<4,2,8>", 18: "fp6_gemm_xlds<1,4,8>",
     19: "fp6_gemm_xlds<2,2,8,MB=2>", 20: "fp6_gemm_xlds<2,2,8,MB=4>", 21: "fp6_gemm_xlds<1,4,8,MB=2>",
     22: "fp6_gemm_xlds<1,2,8,MB=4>", 23: "fp6_gemm_tiledl<8,2,8>", 24: "fp6_gemm_tiledl<4,2,8>",
-    25: "fp6_gemm_tiled_sk<8,2,8>",
+    25: "fp6_gemm_tiled_sk<8,2,8>", 26: "fp6_gemm_kring",
 }
 
 

@@ -998,6 +998,131 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 }
 
 // ---------------------------------------------------------------------------
+// K-ring kernel (memory-bound regime, M <= 16, K <= 8192, at most 8 row
+// blocks per CU).  One 8-wave workgroup per CU owns P consecutive row blocks
+// (P = row blocks over CUs, rounded up) over the whole K range.  Wave w owns
+// the k-tiles [w*KT/8, (w+1)*KT/8) (at most KTW) and keeps their X fragments
+// in registers for the whole kernel, so the loop has no X staging, no LDS
+// read and no barrier.  The wave walks the workgroup's row blocks in order
+// through a register ring of KTW tiles: the next row block's tile t is
+// requested as soon as this row block's tile t has been multiplied, and its
+// row scale right after its first tile.  Each row block's partial tile goes
+// to the wave's LDS region; after one barrier wave i sums row block i over
+// the 8 waves in wave order (deterministic).  When the row blocks divide
+// evenly over the CUs (Llama-70B MLP: 1792 = 7 x 256) every SIMD streams the
+// same number of tiles.  Tiles beyond a wave's range (K/256 not a multiple
+// of 8) are loaded as stand-ins and multiplied by zero X fragments.
+// ---------------------------------------------------------------------------
+template <int F, int KTW>
+__global__ __launch_bounds__(512) void fp6_gemm_kring(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
+    int64_t K, int P) {
+  constexpr int kWaves = 8;
+  // Per wave 8 KB: first the X staging area of one k-tile (16 rows x 512 B),
+  // then the partial tiles of its row blocks (1 KB each, P <= 8).
+  __shared__ __attribute__((aligned(16))) half8v xw[kWaves][512];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nblocks = N >> 4, ktiles = K >> 8;
+  const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
+  const int64_t kw0 = wave * ktiles / kWaves, kw1 = (wave + 1) * ktiles / kWaves;
+  const int ktw = static_cast<int>(kw1 - kw0);  // 0..KTW tiles for this wave
+  const int64_t nb0 = static_cast<int64_t>(blockIdx.x) * P;
+  if (nb0 >= nblocks) return;  // uniform for the workgroup
+  const int pw = static_cast<int>(nblocks - nb0 < P ? nblocks - nb0 : P);
+  auto tile_of = [&](int t) -> int64_t {
+    if (ktw == 0) return 0;
+    return kw0 + (t < ktw ? t : ktw - 1);
+  };
+
+  // X of this wave's k-tiles, loaded coalesced first (instruction i covers
+  // rows 2i, 2i+1, lane -> 16-byte unit xc of row 2i + lane/32; rows beyond
+  // M repeat row M-1, whose accumulator columns are never stored).
+  const int xc = lane & 31;
+  half8v xg[KTW][8];
+#pragma unroll
+  for (int t = 0; t < KTW; ++t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 2 * i + (lane >> 5);
+      const int64_t m = rr < M ? rr : M - 1;
+      xg[t][i] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 256 + 8 * xc);
+    }
+  }
+  // The first row block's tiles with its row scale after the first tile:
+  // the order the loop below issues the next row block's loads in, so that
+  // the compiler's wait counts at the loop head are exact.
+  WStage<F, 1> ring[KTW];
+  auto tile_ptr = [&](int64_t nb, int t) { return wp + nb * Fmt<F>::kTileQuads + lane + tile_of(t) * kstr; };
+  _Float16 sc;
+#pragma unroll
+  for (int t = 0; t < KTW; ++t) {
+    Fmt<F>::template load<true>(ring[t].t[0], tile_ptr(nb0, t), lane);
+    if (t == 0) sc = scales[nb0 * 16 + r];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Stage X through the wave's LDS region into B fragments: unit (rr, c) at
+  // column c ^ rr of row rr, so the 16 lanes of a fragment read hit distinct
+  // banks.  Only this wave uses its region and its LDS operations complete in
+  // order, so no barrier is needed between tiles.
+  half8v xf[KTW][8];
+#pragma unroll
+  for (int t = 0; t < KTW; ++t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 2 * i + (lane >> 5);
+      xw[wave][rr * 32 + (xc ^ rr)] = xg[t][i];
+    }
+    const bool live = t < ktw;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const half8v v = xw[wave][r * 32 + ((4 * j + g) ^ r)];
+      xf[t][j] = live ? v : half8v{};
+    }
+  }
+
+  // Row block i: its tiles are in the ring; as tile t is multiplied, the
+  // ring slot is refilled with tile t of row block i + 1 (NEXT), and its row
+  // scale is requested after its first tile.
+  auto row_block = [&](int i, auto NEXT) {
+    constexpr bool kNext = decltype(NEXT)::value;
+    const half2v s2 = scale2_of<F>(sc);
+    const int64_t nbn = nb0 + i + 1;
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+#define FP6_KR_STEP(J)                                                                     \
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<J>(ring[t].t[0], s2), \
+                                               xf[t][J], acc, 0, 0, 0);
+      FP6_KR_STEP(0) FP6_KR_STEP(1) FP6_KR_STEP(2) FP6_KR_STEP(3)
+      FP6_KR_STEP(4) FP6_KR_STEP(5) FP6_KR_STEP(6) FP6_KR_STEP(7)
+#undef FP6_KR_STEP
+      if constexpr (kNext) {
+        // Fences: left free, the scheduler sinks these loads to the end of
+        // the row block, so the ring would refill a row block at a time.
+        __builtin_amdgcn_sched_barrier(0);
+        Fmt<F>::template load<true>(ring[t].t[0], tile_ptr(nbn, t), lane);
+        if (t == 0) sc = scales[nbn * 16 + r];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    reinterpret_cast<float4v*>(&xw[wave][64 * i])[lane] = acc;
+  };
+  // Straight-line tail: the last row block requests nothing.
+  int i = 0;
+  for (; i + 1 < pw; ++i) row_block(i, std::true_type{});
+  row_block(i, std::false_type{});
+  __syncthreads();
+  if (wave < pw) {
+    float4v sum = reinterpret_cast<const float4v*>(&xw[0][64 * wave])[lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += reinterpret_cast<const float4v*>(&xw[w][64 * wave])[lane];
+    store_y_block(Y, sum, r, M, N, (nb0 + wave) * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // K-slice kernel (memory-bound regime, M <= 16, few row blocks, long K).
 // Like the k-split kernel, WK waves of a workgroup split the K range of a row
 // block and reduce through LDS, but each wave issues the loads of all its
@@ -1912,6 +2037,32 @@ int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t 
   return FP6_E_VALUE;
 }
 
+// K-ring kernel: P = row blocks per CU (rounded up, at most 8), one
+// workgroup per P row blocks; each wave holds ceil(K/256 / 8) <= 4 k-tiles.
+template <int F>
+int launch_kring(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
+                 int64_t K, int cus, hipStream_t stream) {
+  const int64_t nblocks = N >> 4;
+  int P = static_cast<int>(fpx_ceil_div(nblocks, cus));
+  if (P < 1) P = 1;
+  if (P > 8 || M > 16) return FP6_E_VALUE;
+  const dim3 grid(static_cast<unsigned>(fpx_ceil_div(nblocks, P)));
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const u32x4* w = static_cast<const u32x4*>(W);
+  const _Float16* sc = static_cast<const _Float16*>(S);
+  _Float16* y = static_cast<_Float16*>(Y);
+  void* args[] = {&x, &w, &sc, &y, &M, &N, &K, &P};
+  const void* kern = nullptr;
+  switch (fpx_ceil_div(K >> 8, 8)) {
+    case 1: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 1>); break;
+    case 2: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 2>); break;
+    case 3: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 3>); break;
+    case 4: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 4>); break;
+    default: return FP6_E_VALUE;
+  }
+  return hipLaunchKernel(kern, grid, dim3(512), args, 0, stream) == hipSuccess ? FP6_OK : FP6_E_HIP;
+}
+
 template <int F, int A, int D, int NW, int MB = 1>
 int launch_xlds(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                 int64_t K, int splits, float* part, unsigned* cnt, hipStream_t stream) {
@@ -2089,6 +2240,7 @@ int launch_variant(const fpx::LaunchCtx& c) {
     case 23: return launch_tiledl<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 24: return launch_tiledl<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 25: return launch_tiled_sk<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
+    case 26: return launch_kring<F>(X, W, S, Y, M, N, K, c.cus, s);
     default: return FP6_E_VALUE;
   }
 }

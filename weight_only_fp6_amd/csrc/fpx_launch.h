@@ -14,7 +14,7 @@ namespace fpx {
 enum Format : int { kFmtE3M2 = 0, kFmtE2M3 = 1, kFmtE2M2 = 2, kFmtE2M1 = 3, kNumFormats = 4 };
 
 // Kernel configurations reachable through the `variant` argument.
-enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice, kXlds, kTiledSk };
+enum class Kind { kAuto, kStream, kTiled, kKsplit, kKslice, kXlds, kTiledSk, kKring };
 struct KernelCfg {
   Kind kind;
   int a, mb, d;  // stream: row blocks/wave, 16-col blocks/wave, ring depth; tiled: B = mb
@@ -46,10 +46,13 @@ constexpr KernelCfg kCfgs[] = {
     {Kind::kTiled, 2, 8, 8},   // 23: tiled, 256 rows x 128 columns, 8 waves x 2 row blocks, weights staged in LDS
     {Kind::kTiled, 2, 4, 8},   // 24: tiled, 256 rows x 64 columns, 8 waves x 2 row blocks, weights staged in LDS
     {Kind::kTiledSk, 2, 8, 8}, // 25: tiled (as 10), stream-K: one workgroup per CU, equal (tile, half-tile) ranges
+    {Kind::kKring, 1, 1, 8},   // 26: k-ring, M <= 16, K <= 8192, <= 8 row blocks per CU (X in registers)
 };
 constexpr int kNumVariants = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kKsMaxTiles = 32;      // k-split kernels: K <= 8192
 constexpr int kKsliceMaxTiles = 48;  // k-slice kernels: K <= 12288
+constexpr int kKringMaxTiles = 32;   // k-ring kernel: K <= 8192 (4 k-tiles per wave)
+constexpr int kKringMaxRows = 8;     // k-ring kernel: row blocks per workgroup
 
 // One resolved launch: shapes, device pointers, the schedule and the
 // split-K workspace (part/counters are null when splits == 1).

@@ -249,7 +249,27 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
       }
     }
     const bool ks_fits = ks_variant != 0;
-    if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
+    // The k-ring kernel (8 waves, each with a fixed K slice of X in
+    // registers, one workgroup per ceil(N/16 / CUs) row blocks) where
+    // measured faster: up to 3 row blocks per CU, any number up to 8 for K
+    // <= 4096; with one row block per CU only from M = 5 and once more than
+    // 3/4 of the CUs get one (the k-slice kernel is faster at M <= 4:
+    // 1x4096x4096 4.3 against 5.0 us, 4x4096x8192 7.6 against 8.4; the
+    // k-split kernel's K-splits fill the CUs on 16x2048x8192, 8.0 against
+    // 8.1).  Interleaved A/B against the previous plans (us):
+    // 16x10240x8192 17.1 -> 14.8, 1x10240x8192 16.4 -> 13.6, 16x8192x8192
+    // 12.8 -> 12.3, Llama-7B MLP up 16x11008x4096 9.8 -> 9.1, 16x4096x4096
+    // 6.7 -> 5.5, 16x22016x4096 (6 row blocks per CU) 16.3 -> 14.6,
+    // 16x28672x4096 (7) 19.9 -> 17.4.  With more row blocks per CU at longer
+    // K the streaming kernel keeps the lead (Llama-70B MLP 16x28672x8192:
+    // 29.6 against 31.4 us; 16x13824x5120 12.9 against 13.1).
+    const int64_t kr_rows = ceil_div(N >> 4, cus);
+    const bool kr_fits = M <= 16 && splits == 0 && ktiles <= fpx::kKringMaxTiles &&
+                         kr_rows <= fpx::kKringMaxRows && (kr_rows <= 3 || ktiles <= 16) &&
+                         (kr_rows > 1 || (M > 4 && (N >> 4) * 4 > 3 * static_cast<int64_t>(cus)));
+    if (kr_fits) {
+      p.variant = 26;
+    } else if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
       p.variant = 13;
     } else if (M <= 4 && ktiles <= fpx::kKsliceMaxTiles && one_rb_per_cu) {
       // Longer K at M <= 4: the k-slice kernel still beats K-splits (no
@@ -307,7 +327,7 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     p.variant = variant;
   }
   const KernelCfg& c = kCfgs[p.variant];
-  if (c.kind == Kind::kKslice) {
+  if (c.kind == Kind::kKslice || c.kind == Kind::kKring) {
     p.splits = 1;
     return p;
   }
@@ -400,9 +420,14 @@ int linear_impl(int format, const void* X, const void* W, const void* S, void* Y
       (M > 16 || (K >> 8) > fpx::kKsliceMaxTiles || splits > 1))
     return FP6_E_VALUE;
   if (variant > 0 && kCfgs[variant].kind == Kind::kTiledSk && splits != 0) return FP6_E_VALUE;
+  if (variant > 0 && kCfgs[variant].kind == Kind::kKring &&
+      (M > 16 || (K >> 8) > fpx::kKringMaxTiles || splits > 1))
+    return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const int cus = device_cus(dev);
+  if (variant > 0 && kCfgs[variant].kind == Kind::kKring && ceil_div(N >> 4, cus) > fpx::kKringMaxRows)
+    return FP6_E_VALUE;
   const Plan p = choose_plan(M, N, K, cus, variant, splits);
   const KernelCfg& c = kCfgs[p.variant];
   fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus,
