@@ -1011,9 +1011,12 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 // the 8 waves in wave order (deterministic).  When the row blocks divide
 // evenly over the CUs (Llama-70B MLP: 1792 = 7 x 256) every SIMD streams the
 // same number of tiles.  Tiles beyond a wave's range (K/256 not a multiple
-// of 8) are loaded as stand-ins and multiplied by zero X fragments.
+// of 8) are loaded as stand-ins and multiplied by zero X fragments.  With
+// M = 1 (M1) all 16 B-operand columns are X's one row: each lane loads its
+// fragments directly (16 bytes per k-step, 64 distinct bytes per wave
+// instruction), with no staging.
 // ---------------------------------------------------------------------------
-template <int F, int KTW>
+template <int F, int KTW, bool M1 = false>
 __global__ __launch_bounds__(512) void fp6_gemm_kring(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
@@ -1045,9 +1048,13 @@ __global__ __launch_bounds__(512) void fp6_gemm_kring(
   for (int t = 0; t < KTW; ++t) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int rr = 2 * i + (lane >> 5);
-      const int64_t m = rr < M ? rr : M - 1;
-      xg[t][i] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 256 + 8 * xc);
+      if constexpr (M1) {
+        xg[t][i] = *reinterpret_cast<const half8v*>(X + tile_of(t) * 256 + 32 * i + 8 * g);
+      } else {
+        const int rr = 2 * i + (lane >> 5);
+        const int64_t m = rr < M ? rr : M - 1;
+        xg[t][i] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 256 + 8 * xc);
+      }
     }
   }
   // The first row block's tiles with its row scale after the first tile:
@@ -1069,16 +1076,21 @@ __global__ __launch_bounds__(512) void fp6_gemm_kring(
   half8v xf[KTW][8];
 #pragma unroll
   for (int t = 0; t < KTW; ++t) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = 2 * i + (lane >> 5);
-      xw[wave][rr * 32 + (xc ^ rr)] = xg[t][i];
-    }
     const bool live = t < ktw;
+    if constexpr (M1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const half8v v = xw[wave][r * 32 + ((4 * j + g) ^ r)];
-      xf[t][j] = live ? v : half8v{};
+      for (int j = 0; j < 8; ++j) xf[t][j] = live ? xg[t][j] : half8v{};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 2 * i + (lane >> 5);
+        xw[wave][rr * 32 + (xc ^ rr)] = xg[t][i];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const half8v v = xw[wave][r * 32 + ((4 * j + g) ^ r)];
+        xf[t][j] = live ? v : half8v{};
+      }
     }
   }
 
@@ -2053,13 +2065,17 @@ int launch_kring(const void* X, const void* W, const void* S, void* Y, int64_t M
   _Float16* y = static_cast<_Float16*>(Y);
   void* args[] = {&x, &w, &sc, &y, &M, &N, &K, &P};
   const void* kern = nullptr;
+  const bool m1 = M == 1;
+#define FP6_KR_CASE(T)                                                                       \
+  case T:                                                                                    \
+    kern = m1 ? reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, true>)                   \
+              : reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, false>);                 \
+    break;
   switch (fpx_ceil_div(K >> 8, 8)) {
-    case 1: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 1>); break;
-    case 2: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 2>); break;
-    case 3: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 3>); break;
-    case 4: kern = reinterpret_cast<const void*>(&fp6_gemm_kring<F, 4>); break;
+    FP6_KR_CASE(1) FP6_KR_CASE(2) FP6_KR_CASE(3) FP6_KR_CASE(4)
     default: return FP6_E_VALUE;
   }
+#undef FP6_KR_CASE
   return hipLaunchKernel(kern, grid, dim3(512), args, 0, stream) == hipSuccess ? FP6_OK : FP6_E_HIP;
 }
 
