@@ -286,6 +286,20 @@ def test_linear_kring_row_blocks_per_workgroup(K, per_wg, M):
     assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, per_wg, K)
 
 
+@pytest.mark.parametrize("name", ["llama70b_mlp_1x28672x8192", "llama70b_mlp_16x28672x8192",
+                                  "llama7b_mlp_up_16x11008x4096"])
+def test_linear_kring_workload_layers(name):
+    # The k-ring kernel forced on whole workload layers: the Llama-70B MLP
+    # (1792 row blocks = 7 per CU at 256 CUs, K = 8192: 4 k-tiles per wave)
+    # and the Llama-7B MLP up projection.  Every output element.
+    shp = synth.SHAPES[name]
+    p = _full(name)
+    X, packed, s = p.to_device()
+    Y = fp6.linear_plan(X, packed, s, shp.N, shp.K, variant=KRING)
+    torch.cuda.synchronize()
+    _assert_tol(Y, p.y_ref, what=name)
+
+
 def test_kring_one_hot_every_tile_slot():
     # One-hot activations through the k-ring kernel at K = 7168 (28 k-tiles:
     # waves own 3 or 4), 3 row blocks per workgroup with a short last
@@ -571,6 +585,8 @@ DENSE_PLANS = [
     ((1, 10240, 8192), (KRING, 1)),
     ((16, 5120, 5120), (KRING, 1)),
     ((16, 13824, 5120), (15, 1)),        # 4 row blocks per CU at K > 4096: streaming
+    ((16, 18432, 8192), (KRING, 1)),     # 4-wave streaming workgroups would take 1.1 rounds
+    ((4, 25600, 8192), (KRING, 1)),
     ((16, 2048, 8192), (KSPLIT16, 2)),   # half the CUs with a row block: K split across workgroups
     ((16, 4096, 11008), (15, 4)),
     ((16, 3072, 8192), (KSPLIT, 4)),     # 8 waves: 3 row blocks per workgroup

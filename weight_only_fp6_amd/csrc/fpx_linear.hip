@@ -252,7 +252,8 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     // The k-ring kernel (8 waves, each with a fixed K slice of X in
     // registers, one workgroup per ceil(N/16 / CUs) row blocks) where
     // measured faster: up to 3 row blocks per CU, any number up to 8 for K
-    // <= 4096; with one row block per CU only from M = 5 and once more than
+    // <= 4096, 5-7 where the streaming kernel needs more than one round of
+    // workgroups; with one row block per CU only from M = 5 and once more than
     // 3/4 of the CUs get one (the k-slice kernel is faster at M <= 4:
     // 1x4096x4096 4.3 against 5.0 us, 4x4096x8192 7.6 against 8.4; the
     // k-split kernel's K-splits fill the CUs on 16x2048x8192, 8.0 against
@@ -260,12 +261,18 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     // 16x10240x8192 17.1 -> 14.8, 1x10240x8192 16.4 -> 13.6, 16x8192x8192
     // 12.8 -> 12.3, Llama-7B MLP up 16x11008x4096 9.8 -> 9.1, 16x4096x4096
     // 6.7 -> 5.5, 16x22016x4096 (6 row blocks per CU) 16.3 -> 14.6,
-    // 16x28672x4096 (7) 19.9 -> 17.4.  With more row blocks per CU at longer
-    // K the streaming kernel keeps the lead (Llama-70B MLP 16x28672x8192:
-    // 29.6 against 31.4 us; 16x13824x5120 12.9 against 13.1).
+    // 16x28672x4096 (7) 19.9 -> 17.4.  At longer K also between 4 and 7 row
+    // blocks per CU, where the streaming kernel's 4-wave workgroups take more
+    // than one round: 16x18432x8192 30.6 -> 21.4, 16x22016x8192 31.0 ->
+    // 25.9, 16x17920x5120 21.1 -> 15.6, 16x25600x8192 31.6 -> 28.9.  With
+    // one round of streaming workgroups that kernel keeps the lead (Llama-70B
+    // MLP 16x28672x8192, 8-wave workgroups: 29.6 against 31.2 us;
+    // 16x13824x7168 16.1 against 16.8, 16x13824x5120 12.9 against 13.1).
     const int64_t kr_rows = ceil_div(N >> 4, cus);
+    const int64_t nbk = N >> 4, cu64 = cus;
     const bool kr_fits = M <= 16 && splits == 0 && ktiles <= fpx::kKringMaxTiles &&
-                         kr_rows <= fpx::kKringMaxRows && (kr_rows <= 3 || ktiles <= 16) &&
+                         kr_rows <= fpx::kKringMaxRows &&
+                         (kr_rows <= 3 || ktiles <= 16 || (nbk > 4 * cu64 && nbk < 7 * cu64)) &&
                          (kr_rows > 1 || (M > 4 && (N >> 4) * 4 > 3 * static_cast<int64_t>(cus)));
     if (kr_fits) {
       p.variant = 26;
