@@ -224,15 +224,15 @@ int fp6_linear_noalloc(const void* X, const void* packed_W, const void* scales, 
  *    25  as 10, stream-K: one workgroup per CU, each running an equal
  *        contiguous range of (tile, 128-k half-tile) units; a tile's pieces
  *        meet in the fixed-order fix-up
- *    26  k-ring: one 8-wave workgroup per ceil(N/16 / CUs) consecutive row
- *        blocks; each wave keeps a fixed 1/8 of K of X in registers and
- *        streams its tiles of every row block through a register ring; one
- *        fixed-order cross-wave sum; requires M <= 16, K <= 8192, at most 8
- *        row blocks per CU, no K-splits
+ *    26  k-ring: one 8-wave workgroup per P consecutive row blocks and
+ *        K-split; each wave keeps a fixed 1/8 of its split's K of X in
+ *        registers and streams its tiles of every row block through a
+ *        register ring; one fixed-order cross-wave sum, then the split-K
+ *        fix-up.  Requires M <= 16, at most 8192 of K per split (splits 0 =
+ *        the fewest that fit) and P = ceil(N/16 * splits / CUs) <= 8
  *   Streaming and tiled kernels handle any M (16-column groups per pass).
  * splits:  0 = automatic, else the number of K-splits across workgroups
- *          (1..K/256; must be 0 or 1 for variants 13 and 26, 0 for
- *          variant 25).
+ *          (1..K/256; must be 0 or 1 for variant 13, 0 for variant 25).
  * The result equals fp6_linear's up to fp32 summation order.
  * Errors: as fp6_linear, plus FP6_E_VALUE for an unknown variant, a split
  * count out of range, or a shape that variant 9, 12, 13 or 26 does not

@@ -300,6 +300,26 @@ def test_linear_kring_workload_layers(name):
     _assert_tol(Y, p.y_ref, what=name)
 
 
+@pytest.mark.parametrize("NK, M, splits", [(NK, M, sp) for NK in ((4096, 11008), (1024, 8448), (2048, 12288))
+                                            for M in (1, 5, 16) for sp in (0, 2, 3)])
+def test_linear_kring_k_splits(NK, M, splits):
+    # The k-ring kernel with K split across workgroups (automatic: the fewest
+    # splits that leave at most 4 k-tiles per wave) and the fixed-order
+    # fix-up: ragged split and wave ranges, bitwise reproducible.  Every
+    # output element.
+    N, K = NK
+    ws = dense_weight_set(N, K, N + K + 13)
+    X = synth.activations(M, K, M + 17)
+    yref = y_ref(X, ws.wdq_ref)
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
+    Y = fp6.linear_plan(Xd, packed, s, N, K, variant=KRING, splits=splits).clone()
+    Y2 = fp6.linear_plan(Xd, packed, s, N, K, variant=KRING, splits=splits)
+    torch.cuda.synchronize()
+    _assert_tol(Y, yref, what=(M, N, K, splits))
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, splits)
+
+
 def test_kring_one_hot_every_tile_slot():
     # One-hot activations through the k-ring kernel at K = 7168 (28 k-tiles:
     # waves own 3 or 4), 3 row blocks per workgroup with a short last
@@ -331,8 +351,6 @@ def test_kring_rejects_what_it_does_not_cover():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     p = Prepared(16, 64, 512, seed_w=15, seed_x=16)
     X, packed, s = p.to_device()
-    with pytest.raises(fp6.FP6Error):      # no K-splits
-        fp6.linear_plan(X, packed, s, 64, 512, variant=KRING, splits=2)
     X17 = torch.zeros((17, 512), dtype=torch.float16, device=DEV)
     with pytest.raises(fp6.FP6Error):      # M <= 16
         fp6.linear_plan(X17, packed, s, 64, 512, variant=KRING)
@@ -344,8 +362,13 @@ def test_kring_rejects_what_it_does_not_cover():
         fp6.linear_plan(X1, big, sc, N, 256, variant=KRING)
     Xk = torch.zeros((1, 8448), dtype=torch.float16, device=DEV)
     wk = torch.zeros(fp6.packed_bytes(64, 8448), dtype=torch.uint8, device=DEV)
-    with pytest.raises(fp6.FP6Error):      # K <= 8192
-        fp6.linear_plan(Xk, wk, s, 64, 8448, variant=KRING)
+    with pytest.raises(fp6.FP6Error):      # at most 32 k-tiles (4 per wave) per K-split
+        fp6.linear_plan(Xk, wk, s, 64, 8448, variant=KRING, splits=1)
+    N2 = 16 * (4 * cus + 1)                # 2 K-splits x 4+ row blocks: 9 units per CU
+    big2 = torch.zeros(fp6.packed_bytes(N2, 8448), dtype=torch.uint8, device=DEV)
+    sc2 = torch.zeros(N2, dtype=torch.float16, device=DEV)
+    with pytest.raises(fp6.FP6Error):
+        fp6.linear_plan(Xk, big2, sc2, N2, 8448, variant=KRING)
 
 
 STREAM_K = 25

@@ -1014,13 +1014,16 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 // of 8) are loaded as stand-ins and multiplied by zero X fragments.  With
 // M = 1 (M1) all 16 B-operand columns are X's one row: each lane loads its
 // fragments directly (16 bytes per k-step, 64 distinct bytes per wave
-// instruction), with no staging.
+// instruction), with no staging.  With K split across workgroups (splits >
+// 1, for K > 8192) workgroup b runs split b % splits of row group b /
+// splits, and the summed tile of a row block goes through the fixed-order
+// split-K fix-up.
 // ---------------------------------------------------------------------------
 template <int F, int KTW, bool M1 = false>
 __global__ __launch_bounds__(512) void fp6_gemm_kring(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
-    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N,
-    int64_t K, int P) {
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
+    unsigned* __restrict__ counters, int64_t M, int64_t N, int64_t K, int P, int splits) {
   constexpr int kWaves = 8;
   // Per wave 8 KB: first the X staging area of one k-tile (16 rows x 512 B),
   // then the partial tiles of its row blocks (1 KB each, P <= 8).
@@ -1029,9 +1032,11 @@ __global__ __launch_bounds__(512) void fp6_gemm_kring(
   const int r = lane & 15, g = lane >> 4;
   const int64_t nblocks = N >> 4, ktiles = K >> 8;
   const int64_t kstr = nblocks * Fmt<F>::kTileQuads;  // quads between k-tiles of a row block
-  const int64_t kw0 = wave * ktiles / kWaves, kw1 = (wave + 1) * ktiles / kWaves;
+  const int split = static_cast<int>(umod32(blockIdx.x, splits));
+  const int64_t kt0 = split * ktiles / splits, kts = (split + 1) * ktiles / splits - kt0;
+  const int64_t kw0 = kt0 + wave * kts / kWaves, kw1 = kt0 + (wave + 1) * kts / kWaves;
   const int ktw = static_cast<int>(kw1 - kw0);  // 0..KTW tiles for this wave
-  const int64_t nb0 = static_cast<int64_t>(blockIdx.x) * P;
+  const int64_t nb0 = static_cast<int64_t>(udiv32(blockIdx.x, splits)) * P;
   if (nb0 >= nblocks) return;  // uniform for the workgroup
   const int pw = static_cast<int>(nblocks - nb0 < P ? nblocks - nb0 : P);
   auto tile_of = [&](int t) -> int64_t {
@@ -1127,10 +1132,13 @@ __global__ __launch_bounds__(512) void fp6_gemm_kring(
   row_block(i, std::false_type{});
   __syncthreads();
   if (wave < pw) {
-    float4v sum = reinterpret_cast<const float4v*>(&xw[0][64 * wave])[lane];
+    const int64_t nb = nb0 + wave;
+    float4v sum[1] = {reinterpret_cast<const float4v*>(&xw[0][64 * wave])[lane]};
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += reinterpret_cast<const float4v*>(&xw[w][64 * wave])[lane];
-    store_y_block(Y, sum, r, M, N, (nb0 + wave) * 16, g);
+    for (int w = 1; w < kWaves; ++w) sum[0] += reinterpret_cast<const float4v*>(&xw[w][64 * wave])[lane];
+    if (splits > 1 && !splitk_fixup<1>(sum, part + nb * splits * 256, counters + nb, split, splits, lane))
+      return;
+    store_y_block(Y, sum[0], r, M, N, nb * 16, g);
   }
 }
 
@@ -2049,21 +2057,22 @@ int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t 
   return FP6_E_VALUE;
 }
 
-// K-ring kernel: P = row blocks per CU (rounded up, at most 8), one
-// workgroup per P row blocks; each wave holds ceil(K/256 / 8) <= 4 k-tiles.
+// K-ring kernel: P = (row block, K-split) units per CU (rounded up, at most
+// 8), one workgroup per P row blocks and K-split; each wave holds
+// ceil(K/256 / splits / 8) <= 4 k-tiles.
 template <int F>
 int launch_kring(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
-                 int64_t K, int cus, hipStream_t stream) {
+                 int64_t K, int splits, float* part, unsigned* cnt, int cus, hipStream_t stream) {
   const int64_t nblocks = N >> 4;
-  int P = static_cast<int>(fpx_ceil_div(nblocks, cus));
+  int P = static_cast<int>(fpx_ceil_div(nblocks * splits, cus));
   if (P < 1) P = 1;
-  if (P > 8 || M > 16) return FP6_E_VALUE;
-  const dim3 grid(static_cast<unsigned>(fpx_ceil_div(nblocks, P)));
+  if (P > 8 || M > 16 || splits < 1) return FP6_E_VALUE;
+  const dim3 grid(static_cast<unsigned>(fpx_ceil_div(nblocks, P) * splits));
   const _Float16* x = static_cast<const _Float16*>(X);
   const u32x4* w = static_cast<const u32x4*>(W);
   const _Float16* sc = static_cast<const _Float16*>(S);
   _Float16* y = static_cast<_Float16*>(Y);
-  void* args[] = {&x, &w, &sc, &y, &M, &N, &K, &P};
+  void* args[] = {&x, &w, &sc, &y, &part, &cnt, &M, &N, &K, &P, &splits};
   const void* kern = nullptr;
   const bool m1 = M == 1;
 #define FP6_KR_CASE(T)                                                                       \
@@ -2071,7 +2080,7 @@ int launch_kring(const void* X, const void* W, const void* S, void* Y, int64_t M
     kern = m1 ? reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, true>)                   \
               : reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, false>);                 \
     break;
-  switch (fpx_ceil_div(K >> 8, 8)) {
+  switch (fpx_ceil_div(fpx_ceil_div(K >> 8, splits), 8)) {
     FP6_KR_CASE(1) FP6_KR_CASE(2) FP6_KR_CASE(3) FP6_KR_CASE(4)
     default: return FP6_E_VALUE;
   }
@@ -2256,7 +2265,7 @@ int launch_variant(const fpx::LaunchCtx& c) {
     case 23: return launch_tiledl<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 24: return launch_tiledl<F, 4, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
     case 25: return launch_tiled_sk<F, 8, 2, 8>(X, W, S, Y, M, N, K, sp, pt, ct, s);
-    case 26: return launch_kring<F>(X, W, S, Y, M, N, K, c.cus, s);
+    case 26: return launch_kring<F>(X, W, S, Y, M, N, K, sp, pt, ct, c.cus, s);
     default: return FP6_E_VALUE;
   }
 }

@@ -334,8 +334,12 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     p.variant = variant;
   }
   const KernelCfg& c = kCfgs[p.variant];
-  if (c.kind == Kind::kKslice || c.kind == Kind::kKring) {
+  if (c.kind == Kind::kKslice) {
     p.splits = 1;
+    return p;
+  }
+  if (c.kind == Kind::kKring) {  // the fewest K-splits that leave <= 4 k-tiles per wave
+    p.splits = splits > 0 ? splits : static_cast<int>(ceil_div(ktiles, fpx::kKringMaxTiles));
     return p;
   }
   if (c.kind == Kind::kTiledSk) {  // one workgroup per CU
@@ -427,14 +431,14 @@ int linear_impl(int format, const void* X, const void* W, const void* S, void* Y
       (M > 16 || (K >> 8) > fpx::kKsliceMaxTiles || splits > 1))
     return FP6_E_VALUE;
   if (variant > 0 && kCfgs[variant].kind == Kind::kTiledSk && splits != 0) return FP6_E_VALUE;
-  if (variant > 0 && kCfgs[variant].kind == Kind::kKring &&
-      (M > 16 || (K >> 8) > fpx::kKringMaxTiles || splits > 1))
-    return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const int cus = device_cus(dev);
-  if (variant > 0 && kCfgs[variant].kind == Kind::kKring && ceil_div(N >> 4, cus) > fpx::kKringMaxRows)
-    return FP6_E_VALUE;
+  if (variant > 0 && kCfgs[variant].kind == Kind::kKring) {
+    const int64_t ks = splits > 0 ? splits : ceil_div(K >> 8, fpx::kKringMaxTiles);
+    if (M > 16 || ceil_div(K >> 8, ks) > fpx::kKringMaxTiles || ceil_div((N >> 4) * ks, cus) > fpx::kKringMaxRows)
+      return FP6_E_VALUE;
+  }
   const Plan p = choose_plan(M, N, K, cus, variant, splits);
   const KernelCfg& c = kCfgs[p.variant];
   fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus,
