@@ -263,14 +263,17 @@ def test_linear_ksplit_across_workgroups(NK, M):
             assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, variant, splits)
 
 
-@pytest.mark.parametrize("K, per_wg, M", [(K, w, M) for K, ws in ((256, (1, 3)), (2816, (1, 2, 3, 5, 8)),
+@pytest.mark.parametrize("K, per_wg, M", [(K, w, M) for K, ws in ((256, (1, 3)), (2048, (1, 2, 3, 8)),
+                                                                    (2816, (1, 2, 3, 5, 8)),
                                                                     (5120, (2, 3, 4)), (7168, (3,)), (8192, (2,)))
                                           for w in ws for M in (1, 5, 16)])
 def test_linear_kring_row_blocks_per_workgroup(K, per_wg, M):
     # The k-ring kernel: each of 8 waves holds a fixed K slice of X (K/256 = 1
     # leaves 7 waves with an empty slice and stand-in tiles, 11, 20 and 28
     # k-tiles give ragged 1/2, 2/3 and 3/4-tile slices) and walks per_wg
-    # row blocks (the last workgroup fewer).  Every output element.
+    # row blocks (the last workgroup fewer); with one k-tile per wave (K <=
+    # 2048) two row blocks are in flight, odd and even counts.  Every output
+    # element.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nblocks = (per_wg - 1) * cus + max(cus // 3, 1) if per_wg > 1 else cus - 5
     N = 16 * nblocks

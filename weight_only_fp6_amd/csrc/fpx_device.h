@@ -1017,9 +1017,9 @@ __global__ __launch_bounds__(64 * kKsWaves) void fp6_gemm_ksplit(
 // instruction), with no staging.  With K split across workgroups (splits >
 // 1, for K > 8192) workgroup b runs split b % splits of row group b /
 // splits, and the summed tile of a row block goes through the fixed-order
-// split-K fix-up.
+// split-K fix-up.  R row blocks are in flight per wave (ring slot sets).
 // ---------------------------------------------------------------------------
-template <int F, int KTW, bool M1 = false>
+template <int F, int KTW, bool M1 = false, int R = 1>
 __global__ __launch_bounds__(512) void fp6_gemm_kring(
     const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
     const _Float16* __restrict__ scales, _Float16* __restrict__ Y, float* __restrict__ part,
@@ -1065,13 +1065,20 @@ __global__ __launch_bounds__(512) void fp6_gemm_kring(
   // The first row block's tiles with its row scale after the first tile:
   // the order the loop below issues the next row block's loads in, so that
   // the compiler's wait counts at the loop head are exact.
-  WStage<F, 1> ring[KTW];
+  // R row blocks in flight: ring slot set rr holds row blocks rr, rr + R,
+  // ...  Requests past the last row block repeat it (cache hits).
+  WStage<F, 1> ring[R][KTW];
+  const int64_t nb_last = nb0 + pw - 1;
   auto tile_ptr = [&](int64_t nb, int t) { return wp + nb * Fmt<F>::kTileQuads + lane + tile_of(t) * kstr; };
-  _Float16 sc;
+  _Float16 sc[R];
 #pragma unroll
-  for (int t = 0; t < KTW; ++t) {
-    Fmt<F>::template load<true>(ring[t].t[0], tile_ptr(nb0, t), lane);
-    if (t == 0) sc = scales[nb0 * 16 + r];
+  for (int rr = 0; rr < R; ++rr) {
+    const int64_t nb = nb0 + rr < nb_last ? nb0 + rr : nb_last;
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      Fmt<F>::template load<true>(ring[rr][t].t[0], tile_ptr(nb, t), lane);
+      if (t == 0) sc[rr] = scales[nb * 16 + r];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // Stage X through the wave's LDS region into B fragments: unit (rr, c) at
@@ -1099,18 +1106,19 @@ __global__ __launch_bounds__(512) void fp6_gemm_kring(
     }
   }
 
-  // Row block i: its tiles are in the ring; as tile t is multiplied, the
-  // ring slot is refilled with tile t of row block i + 1 (NEXT), and its row
-  // scale is requested after its first tile.
-  auto row_block = [&](int i, auto NEXT) {
+  // Row block i: its tiles are in ring slot set SLOT; as tile t is
+  // multiplied, the slot is refilled with tile t of row block i + R (NEXT),
+  // and its row scale is requested after its first tile.
+  auto row_block = [&](int i, auto SLOT, auto NEXT) {
+    constexpr int kSlot = decltype(SLOT)::value;
     constexpr bool kNext = decltype(NEXT)::value;
-    const half2v s2 = scale2_of<F>(sc);
-    const int64_t nbn = nb0 + i + 1;
+    const half2v s2 = scale2_of<F>(sc[kSlot]);
+    const int64_t nbn = nb0 + i + R < nb_last ? nb0 + i + R : nb_last;
     float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < KTW; ++t) {
-#define FP6_KR_STEP(J)                                                                     \
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<J>(ring[t].t[0], s2), \
+#define FP6_KR_STEP(J)                                                                             \
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Fmt<F>::template step<J>(ring[kSlot][t].t[0], s2), \
                                                xf[t][J], acc, 0, 0, 0);
       FP6_KR_STEP(0) FP6_KR_STEP(1) FP6_KR_STEP(2) FP6_KR_STEP(3)
       FP6_KR_STEP(4) FP6_KR_STEP(5) FP6_KR_STEP(6) FP6_KR_STEP(7)
@@ -1119,17 +1127,24 @@ __global__ __launch_bounds__(512) void fp6_gemm_kring(
         // Fences: left free, the scheduler sinks these loads to the end of
         // the row block, so the ring would refill a row block at a time.
         __builtin_amdgcn_sched_barrier(0);
-        Fmt<F>::template load<true>(ring[t].t[0], tile_ptr(nbn, t), lane);
-        if (t == 0) sc = scales[nbn * 16 + r];
+        Fmt<F>::template load<true>(ring[kSlot][t].t[0], tile_ptr(nbn, t), lane);
+        if (t == 0) sc[kSlot] = scales[nbn * 16 + r];
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     reinterpret_cast<float4v*>(&xw[wave][64 * i])[lane] = acc;
   };
-  // Straight-line tail: the last row block requests nothing.
+  // Groups of R row blocks while a successor exists, then a tail of at most
+  // R row blocks that requests nothing.
   int i = 0;
-  for (; i + 1 < pw; ++i) row_block(i, std::true_type{});
-  row_block(i, std::false_type{});
+  for (; i + R < pw; i += R) {
+    row_block(i, std::integral_constant<int, 0>{}, std::true_type{});
+    if constexpr (R > 1) row_block(i + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  }
+  row_block(i, std::integral_constant<int, 0>{}, std::false_type{});
+  if constexpr (R > 1) {
+    if (i + 1 < pw) row_block(i + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
   __syncthreads();
   if (wave < pw) {
     const int64_t nb = nb0 + wave;
@@ -2059,7 +2074,9 @@ int launch_kslice(const void* X, const void* W, const void* S, void* Y, int64_t 
 
 // K-ring kernel: P = (row block, K-split) units per CU (rounded up, at most
 // 8), one workgroup per P row blocks and K-split; each wave holds
-// ceil(K/256 / splits / 8) <= 4 k-tiles.
+// ceil(K/256 / splits / 8) <= 4 k-tiles.  With one k-tile per wave two row
+// blocks are in flight (16x28672x2048 11.6 -> 10.9 us, 16x8192x2048 5.8 ->
+// 5.6); with 2-3 that was 3-13% slower (16x11008x4096 9.3 -> 10.1 us).
 template <int F>
 int launch_kring(const void* X, const void* W, const void* S, void* Y, int64_t M, int64_t N,
                  int64_t K, int splits, float* part, unsigned* cnt, int cus, hipStream_t stream) {
@@ -2077,8 +2094,8 @@ int launch_kring(const void* X, const void* W, const void* S, void* Y, int64_t M
   const bool m1 = M == 1;
 #define FP6_KR_CASE(T)                                                                       \
   case T:                                                                                    \
-    kern = m1 ? reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, true>)                   \
-              : reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, false>);                 \
+    kern = m1 ? reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, true, (T == 1 ? 2 : 1)>)  \
+              : reinterpret_cast<const void*>(&fp6_gemm_kring<F, T, false, (T == 1 ? 2 : 1)>); \
     break;
   switch (fpx_ceil_div(fpx_ceil_div(K >> 8, splits), 8)) {
     FP6_KR_CASE(1) FP6_KR_CASE(2) FP6_KR_CASE(3) FP6_KR_CASE(4)
