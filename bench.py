@@ -30,8 +30,10 @@ Also reported, as context:
   so that the weights stay cache-resident (labelled: not the metric).
 
 ``value`` and ``ms_per_step`` come from HIP events recorded on the launch
-stream around the K timed steps; ``wall_ms_per_step`` is the host clock
-between the synchronisations that bracket them (it adds the graph launch).
+stream around the K timed steps; a short spin kernel ahead of the first
+event covers the host's submission of the timed graph.  ``wall_ms_per_step``
+is the host clock between the synchronisations that bracket them (it adds the
+spin and the graph launch).
 
 Helper modes for the committed rocprofv3 summaries (see the profile files for
 the exact commands): ``--calibrate-copy`` runs a torch copy of a known size so
@@ -59,7 +61,7 @@ DEFAULT_WORKLOAD = "llama70b_mlp_16x28672x8192"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
 ROT_BYTES = 1 << 30             # >= 1 GiB of rotated copies (> 256 MB Infinity Cache)
-SUBMIT_COVER_CYCLES = 200_000   # spin ahead of the timed region: ~0.1 ms at 2 GHz
+SUBMIT_COVER_CYCLES = 40_000    # spin ahead of the timed region (~0.25 ms measured; its counter is slow)
 COPY_BYTES = 1 << 30            # --calibrate-copy: bytes read (and written) per copy
 CSRC = os.path.join(ROOT, "weight_only_fp6_amd", "csrc")
 KERNEL_SRCS = ("fpx_device.h", "fpx_launch.h", "fpx_linear.hip", "fpx_kern_e3m2.hip",
