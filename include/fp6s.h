@@ -86,17 +86,20 @@ int fp6s_linear(const void* X, const void* packed_W, const void* scales, void* Y
  * most K = 4096 per split and 8 row blocks per workgroup, i.e. N/16 <=
  * 8 * (CUs / splits)); 7 = streaming with X shared through LDS, 8 waves,
  * 1 row block x 32 columns per wave (each spliced k-step feeds both column
- * groups); 8 = the same with 2 row blocks per wave.  Variants 2-5, 7 and 8
- * handle any M.  splits: 0 = automatic, else K-splits across workgroups
- * (1..K/512; variants 2-8).
- * Errors: as fp6_linear_plan, plus FP6_E_VALUE for a shape variant 1 or 6
- * does not cover.
+ * groups); 8 = the same with 2 row blocks per wave; 9 = k-ring (one 8-wave
+ * workgroup per ceil(N/16 / CUs) row blocks, each wave a fixed K slice of X
+ * in registers, a register ring over the row blocks; M <= 16, K <= 8192, at
+ * most 8 row blocks per CU, no K-splits).  Variants 2-5, 7 and 8 handle any
+ * M.  splits: 0 = automatic, else K-splits across workgroups (1..K/512;
+ * variants 2-8).
+ * Errors: as fp6_linear_plan, plus FP6_E_VALUE for a shape variant 1, 6 or
+ * 9 does not cover.
  */
 int fp6s_linear_plan(const void* X, const void* packed_W, const void* scales, void* Y, int64_t M,
                      int64_t N, int64_t K, int variant, int splits, void* stream);
 
 /* fp6s_linear_plan_query -- host: the schedule fp6s_linear would use for
- * (M, N, K) on the current device (*variant 1..8, *splits).  One HIP query.
+ * (M, N, K) on the current device (*variant 1..9, *splits).  One HIP query.
  * Errors: FP6_E_NULL, FP6_E_SHAPE (M >= 1, K % 512 == 0), FP6_E_HIP. */
 int fp6s_linear_plan_query(int64_t M, int64_t N, int64_t K, int* variant, int* splits);
 

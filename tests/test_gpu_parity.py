@@ -633,12 +633,13 @@ DENSE_PLANS = [
 ]
 SPARSE_PLANS = [
     ((1, 4096, 4096), (1, 1)),
-    ((16, 11008, 4096), (6, 1)),
+    ((16, 11008, 4096), (9, 1)),         # 3 row blocks per CU, K = 4096: k-ring
     ((16, 4096, 4096), (6, 1)),          # one row block per CU, M >= 12: k-split
     ((8, 4096, 4096), (1, 1)),           # M <= 11: k-slice
-    ((16, 13824, 5120), (2, 1)),         # 7 row blocks per workgroup: streaming
-    ((16, 8192, 8192), (6, 2)),
-    ((16, 28672, 8192), (2, 1)),
+    ((16, 13824, 5120), (2, 1)),         # K/512 = 10 sparse tiles, ragged over 8 waves: streaming
+    ((16, 8192, 8192), (9, 1)),
+    ((16, 28672, 8192), (9, 1)),         # 7 row blocks per CU: k-ring
+    ((1, 28672, 8192), (9, 1)),
     ((16, 8192, 28672), (3, 4)),
     ((32, 21504, 7168), (8, 3)),
     ((64, 21504, 7168), (4, 3)),

@@ -30,6 +30,7 @@ DEV = torch.device("cuda:0")
 VARIANTS = (0, 2, 3, 4, 5, 7, 8)     # any M; 1 (k-slice) and 6 (k-split) only for M <= 16
 KSLICE = 1
 KSPLIT = 6
+KRING = 9
 
 
 class SpPrepared:
@@ -76,7 +77,7 @@ def test_linear_small_shapes_every_variant(M, NK):
     N, K = NK
     p = SpPrepared(M, N, K, seed_w=N * 3 + K, seed_x=M * 7 + 5)
     X, packed, s = p.to_device()
-    for variant in VARIANTS + ((KSLICE, KSPLIT) if M <= 16 else ()):
+    for variant in VARIANTS + ((KSLICE, KSPLIT, KRING) if M <= 16 else ()):
         Y = fp6.sparse_linear_plan(X, packed, s, N, K, variant=variant)
         torch.cuda.synchronize()
         _assert_tol(Y, p.y_ref, what=(M, N, K, variant))
@@ -130,7 +131,7 @@ def test_linear_one_hot_reproduces_wdq_exactly():
     _, packed, s = p.to_device()
     want = p.wdq_ref[:, ks].T.astype(np.float64)
     for variant, splits in [(0, 0), (1, 0), (2, 1), (2, 3), (3, 1), (3, 2), (4, 1), (4, 2), (5, 1), (5, 4),
-                            (6, 0), (6, 2), (6, 4), (7, 1), (7, 3), (8, 2)]:
+                            (6, 0), (6, 2), (6, 4), (7, 1), (7, 3), (8, 2), (KRING, 0)]:
         Y = fp6.sparse_linear_plan(Xd, packed, s, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (variant, splits)
@@ -180,7 +181,7 @@ def test_sparse_linear_adversarial_rows(M):
     out = fp6.sparse_dequant(packed, sd, N, K)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), wdq.view(np.uint16))
-    for variant, splits in [(0, 0), (2, 2), (3, 1), (4, 2), (5, 1), (7, 2), (8, 1)] + ([(KSLICE, 0), (KSPLIT, 0), (KSPLIT, 3)] if M <= 16 else []):
+    for variant, splits in [(0, 0), (2, 2), (3, 1), (4, 2), (5, 1), (7, 2), (8, 1)] + ([(KSLICE, 0), (KSPLIT, 0), (KSPLIT, 3), (KRING, 0)] if M <= 16 else []):
         Y = fp6.sparse_linear_plan(Xd, packed, sd, N, K, variant=variant, splits=splits)
         torch.cuda.synchronize()
         _assert_tol(Y, y_ref, what=(M, variant, splits))
@@ -205,3 +206,47 @@ def test_sparse_ksplit_row_blocks_per_workgroup(K, per_wg, M):
     Y = fp6.sparse_linear_plan(torch.from_numpy(X).to(DEV), packed, sd, N, K, variant=KSPLIT)
     torch.cuda.synchronize()
     _assert_tol(Y, y_ref(X, ws.wdq_ref), what=(M, per_wg, K))
+
+
+@pytest.mark.parametrize("K, per_wg, M", [(K, w, M) for K, ws in ((512, (1, 3)), (2560, (2,)), (4096, (1, 2, 5, 8)),
+                                                                    (8192, (2, 7))) for w in ws for M in (1, 5, 16)])
+def test_sparse_kring_row_blocks_per_workgroup(K, per_wg, M):
+    # The sparse k-ring kernel: each of 8 waves holds a fixed slice of the
+    # sparse tiles with its X resident (K = 512 leaves 7 waves with stand-in
+    # tiles, 2560 gives ragged 0/1-tile slices, 8192 two tiles per wave),
+    # walks per_wg row blocks (the last workgroup fewer; one tile per wave
+    # keeps two row blocks in flight).  Every output element, bitwise
+    # reproducible.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nblocks = (per_wg - 1) * cus + max(cus // 3, 1) if per_wg > 1 else cus - 5
+    N = 16 * nblocks
+    ws = sparse_weight_set(N, K, 970 + per_wg + K)
+    X = synth.activations(M, K, 980 + M)
+    packed, sd = ws.to_device()
+    Xd = torch.from_numpy(X).to(DEV)
+    Y = fp6.sparse_linear_plan(Xd, packed, sd, N, K, variant=KRING).clone()
+    Y2 = fp6.sparse_linear_plan(Xd, packed, sd, N, K, variant=KRING)
+    torch.cuda.synchronize()
+    _assert_tol(Y, y_ref(X, ws.wdq_ref), what=(M, per_wg, K))
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, per_wg, K)
+
+
+def test_sparse_kring_rejects_what_it_does_not_cover():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = SpPrepared(16, 64, 1024, seed_w=25, seed_x=26)
+    X, packed, s = p.to_device()
+    with pytest.raises(fp6.FP6Error):      # no K-splits
+        fp6.sparse_linear_plan(X, packed, s, 64, 1024, variant=KRING, splits=2)
+    X17 = torch.zeros((17, 1024), dtype=torch.float16, device=DEV)
+    with pytest.raises(fp6.FP6Error):      # M <= 16
+        fp6.sparse_linear_plan(X17, packed, s, 64, 1024, variant=KRING)
+    Xk = torch.zeros((1, 8704), dtype=torch.float16, device=DEV)
+    wk = torch.zeros(fp6.sparse_packed_bytes(64, 8704), dtype=torch.uint8, device=DEV)
+    with pytest.raises(fp6.FP6Error):      # K <= 8192
+        fp6.sparse_linear_plan(Xk, wk, s, 64, 8704, variant=KRING)
+    N = 16 * (8 * cus + 1)                 # 9 row blocks per CU
+    big = torch.zeros(fp6.sparse_packed_bytes(N, 512), dtype=torch.uint8, device=DEV)
+    sc = torch.zeros(N, dtype=torch.float16, device=DEV)
+    X1 = torch.zeros((1, 512), dtype=torch.float16, device=DEV)
+    with pytest.raises(fp6.FP6Error):
+        fp6.sparse_linear_plan(X1, big, sc, N, 512, variant=KRING)

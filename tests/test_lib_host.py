@@ -169,6 +169,9 @@ def test_linear_and_dequant_argument_errors_before_any_hip_call():
     assert L.fp6_linear_plan(A, A, A, A, 17, 16, 256, 9, 0, None) == 8     # k-split: M <= 16
     assert L.fp6_linear_plan(A, A, A, A, 4, 16, 8448, 9, 0, None) == 8     # k-split: K <= 8192
     assert L.fp6_linear_plan(A, A, A, A, 4, 16, 65 * 256, 12, 2, None) == 8  # <= 8192 of K per split
+    assert L.fp6_linear_plan(A, A, A, A, 17, 16, 256, 26, 0, None) == 8    # k-ring: M <= 16
+    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 8448, 26, 1, None) == 8    # k-ring: <= 8192 of K per split
+    assert L.fp6_linear_plan(A, A, A, A, 4, 16, 256, 27, 0, None) == 8     # unknown variant
     # dequant
     assert L.fp6_dequant(A, A, A, 16, 100, None) == 2
     assert L.fp6_dequant(None, A, A, 16, 256, None) == 1
@@ -384,12 +387,15 @@ def test_sparse_errors():
     assert L.fp6s_linear(A, A, A, A, 4, 16, 768, None) == 2          # K % 512
     assert L.fp6s_linear(None, None, None, None, 0, 16, 512, None) == 0
     assert L.fp6s_linear(A + 8, A, A, A, 4, 16, 512, None) == 3
-    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 9, 0, None) == 8
+    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 10, 0, None) == 8
     assert L.fp6s_linear_plan(A, A, A, A, 17, 16, 512, 6, 0, None) == 8     # k-split: M <= 16
     assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 9 * 512, 6, 1, None) == 8  # <= 8 tiles per split
     assert L.fp6s_linear_plan(A, A, A, A, 17, 16, 512, 1, 0, None) == 8    # k-slice: M <= 16
     assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512 * 17, 1, 0, None) == 8  # k-slice: K <= 8192
     assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512, 2, 2, None) == 8    # 2 splits > 1 tile
+    assert L.fp6s_linear_plan(A, A, A, A, 17, 16, 512, 9, 0, None) == 8    # k-ring: M <= 16
+    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 512 * 17, 9, 0, None) == 8  # k-ring: K <= 8192
+    assert L.fp6s_linear_plan(A, A, A, A, 4, 16, 1024, 9, 2, None) == 8   # k-ring: no K-splits
     assert L.fp6s_dequant(A, A, A, 16, 768, None) == 2
     assert L.fp6s_dequant(None, A, A, 16, 512, None) == 1
 

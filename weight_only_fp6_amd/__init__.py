@@ -273,7 +273,7 @@ def dequant(packed, scales, N: int, K: int, out=None, stream=None, fmt: str = "e
 # ---------------------------------------------------------------------------
 SPARSE_KERNEL_NAMES = {1: "sp_gemm_kslice", 2: "sp_gemm_xlds<1,4,4>", 3: "sp_gemm_xlds<2,4,4>",
                        4: "sp_gemm_tiled<4,2,8>", 5: "sp_gemm_tiled<8,2,8>", 6: "sp_gemm_ksplit",
-                       7: "sp_gemm_xlds<1,4,8,MB=2>", 8: "sp_gemm_xlds<2,2,8,MB=2>"}
+                       7: "sp_gemm_xlds<1,4,8,MB=2>", 8: "sp_gemm_xlds<2,2,8,MB=2>", 9: "sp_gemm_kring"}
 
 
 def sparse_packed_bytes(N: int, K: int) -> int:

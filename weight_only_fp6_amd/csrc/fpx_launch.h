@@ -84,11 +84,12 @@ int dequant_e2m1(const void* W, const void* S, void* W16, int64_t N, int64_t K, 
 // 2:4-sparse FP6 (fp6s_*): kernel configurations of fp6s_linear_plan.
 enum SparseVariant : int {
   kSpAuto = 0, kSpKslice = 1, kSpXlds1 = 2, kSpXlds2 = 3, kSpTiled4 = 4, kSpTiled8 = 5, kSpKsplit = 6,
-  kSpXldsMB1 = 7, kSpXldsMB2 = 8, kNumSpVariants = 9
+  kSpXldsMB1 = 7, kSpXldsMB2 = 8, kSpKring = 9, kNumSpVariants = 10
 };
 constexpr int kSpKsliceMaxTiles = 16;  // k-slice: one 512-k tile per wave, 16 waves
 constexpr int kSpKsplitMaxTiles = 8;   // k-split: one 512-k tile per wave and K-split, 8 waves
 constexpr int kSpKsplitMaxRows = 8;    // k-split: row blocks per workgroup
+constexpr int kSpKringMaxTiles = 16;   // k-ring: K <= 8192 (2 sparse tiles per wave)
 int64_t sp_ksplit_rows_per_wg(int64_t N, int cus, int splits);
 int launch_sparse(const LaunchCtx& c);  // c.variant is a SparseVariant
 int dequant_sparse(const void* W, const void* S, void* W16, int64_t N, int64_t K, hipStream_t s);

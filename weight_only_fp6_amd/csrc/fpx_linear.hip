@@ -431,14 +431,15 @@ int linear_impl(int format, const void* X, const void* W, const void* S, void* Y
       (M > 16 || (K >> 8) > fpx::kKsliceMaxTiles || splits > 1))
     return FP6_E_VALUE;
   if (variant > 0 && kCfgs[variant].kind == Kind::kTiledSk && splits != 0) return FP6_E_VALUE;
+  // The k-ring kernel: M <= 16 and at most 32 k-tiles per K-split (checked
+  // before any HIP call), at most 8 (row block, split) units per CU.
+  const bool kring = variant > 0 && kCfgs[variant].kind == Kind::kKring;
+  const int64_t kr_splits = splits > 0 ? splits : ceil_div(K >> 8, fpx::kKringMaxTiles);
+  if (kring && (M > 16 || ceil_div(K >> 8, kr_splits) > fpx::kKringMaxTiles)) return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const int cus = device_cus(dev);
-  if (variant > 0 && kCfgs[variant].kind == Kind::kKring) {
-    const int64_t ks = splits > 0 ? splits : ceil_div(K >> 8, fpx::kKringMaxTiles);
-    if (M > 16 || ceil_div(K >> 8, ks) > fpx::kKringMaxTiles || ceil_div((N >> 4) * ks, cus) > fpx::kKringMaxRows)
-      return FP6_E_VALUE;
-  }
+  if (kring && ceil_div((N >> 4) * kr_splits, cus) > fpx::kKringMaxRows) return FP6_E_VALUE;
   const Plan p = choose_plan(M, N, K, cus, variant, splits);
   const KernelCfg& c = kCfgs[p.variant];
   fpx::LaunchCtx ctx{X, W, S, Y, M, N, K, p.variant, p.splits, nullptr, nullptr, cus,
@@ -520,6 +521,24 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
     if (sp > ktiles / 2) sp = ktiles / 2;
     return static_cast<int>(sp < 1 ? 1 : sp);
   };
+  // The sparse k-ring kernel (one workgroup per ceil(N/16 / CUs) row blocks,
+  // each wave 1 or 2 sparse tiles of X resident) with 2-8 row blocks per CU
+  // and K/512 a multiple of the 8 waves (ragged per-wave ranges leave the
+  // short waves idle: 16x13824x5120 10.8 against 12.5 us).  Interleaved A/B
+  // against the previous plans (us): Llama-70B MLP 16x28672x8192 27.1 ->
+  // 22.6, 1x28672x8192 24.9 -> 19.7, 16x18432x8192 24.5 -> 16.6,
+  // 16x10240x8192 13.4 -> 12.1, 16x22016x4096 12.2 -> 11.0; 16x11008x4096
+  // 8.07 -> 8.02.  At one row block per CU the k-slice and k-split kernels
+  // stay faster (16x4096x4096 5.2 against 5.7).
+  const int64_t sp_kr_rows = ceil_div(N >> 4, cus);
+  const bool sp_kr_fits = variant == fpx::kSpAuto && M <= 16 && splits == 0 &&
+                          ktiles <= fpx::kSpKringMaxTiles && ktiles % 8 == 0 && sp_kr_rows >= 2 &&
+                          sp_kr_rows <= fpx::kKringMaxRows;
+  if (sp_kr_fits) {
+    p.variant = fpx::kSpKring;
+    p.splits = 1;
+    return p;
+  }
   if (variant == fpx::kSpAuto) {
     // One row block per CU: the k-slice kernel up to M = 11, the k-split
     // kernel (X staged once per wave with coalesced loads) from M = 12
@@ -543,7 +562,7 @@ Plan choose_sparse_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, i
     p.splits = splits > 0 ? splits : mb_splits(p.variant);
     return p;
   }
-  if (p.variant == fpx::kSpKslice) {
+  if (p.variant == fpx::kSpKslice || p.variant == fpx::kSpKring) {
     p.splits = 1;
     return p;
   }
@@ -587,9 +606,12 @@ int sparse_linear_impl(const void* X, const void* W, const void* S, void* Y, int
   // (an automatic split count for it is the smallest that fits)
   if (variant == fpx::kSpKsplit && (M > 16 || (splits > 0 && ceil_div(K >> 9, splits) > fpx::kSpKsplitMaxTiles)))
     return FP6_E_VALUE;
+  if (variant == fpx::kSpKring && (M > 16 || (K >> 9) > fpx::kSpKringMaxTiles || splits > 1))
+    return FP6_E_VALUE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP6_E_HIP;
   const int cus = device_cus(dev);
+  if (variant == fpx::kSpKring && ceil_div(N >> 4, cus) > fpx::kKringMaxRows) return FP6_E_VALUE;
   const Plan p = choose_sparse_plan(M, N, K, cus, variant, splits);
   if (p.variant == fpx::kSpKsplit &&
       fpx::sp_ksplit_rows_per_wg(N, cus, p.splits) > fpx::kSpKsplitMaxRows)

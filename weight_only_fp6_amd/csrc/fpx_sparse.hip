@@ -193,6 +193,131 @@ __global__ __launch_bounds__(512) void sp_gemm_ksplit(
 }
 
 // ---------------------------------------------------------------------------
+// K-ring kernel on sparse tiles (M <= 16, K <= 8192, at most 8 row blocks
+// per CU): the dense k-ring kernel's schedule.  One 8-wave workgroup per P
+// consecutive row blocks over the whole K range; wave w owns the sparse
+// tiles [w*KT/8, (w+1)*KT/8) (at most KTW) with their X fragments resident
+// in registers (staged once through the wave's 16 KB LDS region; at M = 1
+// the row is stored once and the fragments are broadcast reads), and walks
+// the row blocks through a register ring of KTW tiles (R row blocks in
+// flight), refilling slot t right after its products.  Partial tiles go to
+// the wave's LDS region; after one barrier wave i sums row block i in wave
+// order.  Tiles past a wave's range are stand-ins multiplied by zero X.
+// ---------------------------------------------------------------------------
+template <int KTW, bool M1, int R>
+__global__ __launch_bounds__(512) void sp_gemm_kring(
+    const _Float16* __restrict__ X, const u32x4* __restrict__ wp,
+    const _Float16* __restrict__ scales, _Float16* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int P) {
+  constexpr int kWaves = 8;
+  __shared__ __attribute__((aligned(32))) half8v xw[kWaves][1024];  // 16 KB per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t nblocks = N >> 4, ktiles = K >> 9;
+  const int64_t kw0 = wave * ktiles / kWaves, kw1 = (wave + 1) * ktiles / kWaves;
+  const int ktw = static_cast<int>(kw1 - kw0);  // 0..KTW sparse tiles for this wave
+  const int64_t nb0 = static_cast<int64_t>(blockIdx.x) * P;
+  if (nb0 >= nblocks) return;  // uniform for the workgroup
+  const int pw = static_cast<int>(nblocks - nb0 < P ? nblocks - nb0 : P);
+  const int64_t nb_last = nb0 + pw - 1;
+  auto tile_of = [&](int t) -> int64_t {
+    if (ktw == 0) return 0;
+    return kw0 + (t < ktw ? t : ktw - 1);
+  };
+  // X of this wave's tiles first (row i of a tile: 16 bytes per lane).
+  constexpr int kXLoads = M1 ? 1 : 16;
+  half8v xg[KTW][kXLoads];
+#pragma unroll
+  for (int t = 0; t < KTW; ++t) {
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      const int64_t m = i < M ? i : M - 1;
+      xg[t][i] = *reinterpret_cast<const half8v*>(X + m * K + tile_of(t) * 512 + 8 * lane);
+    }
+  }
+  // The first R row blocks' tiles, each row scale after its first tile (the
+  // loop's order, so the wait counts at its head are exact).
+  SpTile ring[R][KTW];
+  _Float16 sc[R];
+  auto tile_ptr = [&](int64_t nb, int t) { return wp + (nb * ktiles + tile_of(t)) * kSpTileQuads + lane; };
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int64_t nb = nb0 + rr < nb_last ? nb0 + rr : nb_last;
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      sp_load<true>(ring[rr][t], tile_ptr(nb, t), lane);
+      if (t == 0) sc[rr] = scales[nb * 16 + r];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Stage X: row rr's 32-byte unit u sits at unit u ^ rr of the row.
+  half16v xf[KTW][8];
+#pragma unroll
+  for (int t = 0; t < KTW; ++t) {
+    const bool live = t < ktw;
+    if constexpr (M1) {
+      xw[wave][lane] = xg[t][0];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const half16v v = *reinterpret_cast<const half16v*>(&xw[wave][2 * (4 * j + g)]);
+        xf[t][j] = live ? v : half16v{};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xw[wave][i * 64 + 2 * ((lane >> 1) ^ i) + (lane & 1)] = xg[t][i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const half16v v = *reinterpret_cast<const half16v*>(&xw[wave][r * 64 + 2 * ((4 * j + g) ^ r)]);
+        xf[t][j] = live ? v : half16v{};
+      }
+    }
+  }
+  auto row_block = [&](int i, auto SLOT, auto NEXT) {
+    constexpr int kSlot = decltype(SLOT)::value;
+    constexpr bool kNext = decltype(NEXT)::value;
+    const half2v s2 = scale2_of<kE3M2>(sc[kSlot]);
+    const int64_t nbn = nb0 + i + R < nb_last ? nb0 + i + R : nb_last;
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      const SpTile& st = ring[kSlot][t];
+      acc = sp_mac<0>(st, s2, xf[t][0], acc);
+      acc = sp_mac<1>(st, s2, xf[t][1], acc);
+      acc = sp_mac<2>(st, s2, xf[t][2], acc);
+      acc = sp_mac<3>(st, s2, xf[t][3], acc);
+      acc = sp_mac<4>(st, s2, xf[t][4], acc);
+      acc = sp_mac<5>(st, s2, xf[t][5], acc);
+      acc = sp_mac<6>(st, s2, xf[t][6], acc);
+      acc = sp_mac<7>(st, s2, xf[t][7], acc);
+      if constexpr (kNext) {
+        // Fences keep the refill right after the tile's products.
+        __builtin_amdgcn_sched_barrier(0);
+        sp_load<true>(ring[kSlot][t], tile_ptr(nbn, t), lane);
+        if (t == 0) sc[kSlot] = scales[nbn * 16 + r];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    reinterpret_cast<float4v*>(&xw[wave][64 * i])[lane] = acc;
+  };
+  int i = 0;
+  for (; i + R < pw; i += R) {
+    row_block(i, std::integral_constant<int, 0>{}, std::true_type{});
+    if constexpr (R > 1) row_block(i + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  }
+  row_block(i, std::integral_constant<int, 0>{}, std::false_type{});
+  if constexpr (R > 1) {
+    if (i + 1 < pw) row_block(i + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  __syncthreads();
+  if (wave < pw) {
+    float4v sum = reinterpret_cast<const float4v*>(&xw[0][64 * wave])[lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += reinterpret_cast<const float4v*>(&xw[w][64 * wave])[lane];
+    store_y_block(Y, sum, r, M, N, (nb0 + wave) * 16, g);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming kernel with X shared through LDS (any M, in m-groups of 16).  A
 // wave streams A row blocks over a K range through a register ring of D
 // tiles; the NW waves of a workgroup share each X tile (16 rows x 512 k,
@@ -681,6 +806,32 @@ int launch_sp_ksplit(const fpx::LaunchCtx& c) {
   return hipLaunchKernel(kern, grid, dim3(512), args, 0, c.stream) == hipSuccess ? FP6_OK : FP6_E_HIP;
 }
 
+// Sparse k-ring: P = row blocks per CU (rounded up, <= 8); one sparse tile
+// per wave up to K = 4096 (two row blocks in flight), two up to 8192.
+int launch_sp_kring(const fpx::LaunchCtx& c) {
+  const int64_t nblocks = c.N >> 4;
+  int P = static_cast<int>(fpx_ceil_div(nblocks, c.cus));
+  if (P < 1) P = 1;
+  if (P > 8 || c.M > 16) return FP6_E_VALUE;
+  const dim3 grid(static_cast<unsigned>(fpx_ceil_div(nblocks, P)));
+  const _Float16* x = static_cast<const _Float16*>(c.X);
+  const u32x4* w = static_cast<const u32x4*>(c.W);
+  const _Float16* sc = static_cast<const _Float16*>(c.S);
+  _Float16* y = static_cast<_Float16*>(c.Y);
+  int64_t M = c.M, N = c.N, K = c.K;
+  const bool m1 = M == 1;
+  const void* kern = nullptr;
+  switch (fpx_ceil_div(K >> 9, 8)) {
+    case 1: kern = m1 ? reinterpret_cast<const void*>(&sp_gemm_kring<1, true, 2>)
+                      : reinterpret_cast<const void*>(&sp_gemm_kring<1, false, 2>); break;
+    case 2: kern = m1 ? reinterpret_cast<const void*>(&sp_gemm_kring<2, true, 1>)
+                      : reinterpret_cast<const void*>(&sp_gemm_kring<2, false, 1>); break;
+    default: return FP6_E_VALUE;
+  }
+  void* args[] = {&x, &w, &sc, &y, &M, &N, &K, &P};
+  return hipLaunchKernel(kern, grid, dim3(512), args, 0, c.stream) == hipSuccess ? FP6_OK : FP6_E_HIP;
+}
+
 template <int A, int D, int NW, int MB = 1>
 int launch_sp_xlds(const fpx::LaunchCtx& c) {
   const int64_t ngroups = fpx_ceil_div(c.N >> 4, A), gsets = fpx_ceil_div(ngroups, NW);
@@ -753,6 +904,7 @@ int launch_sparse(const LaunchCtx& c) {
     case kSpKsplit: return launch_sp_ksplit(c);
     case kSpXldsMB1: return launch_sp_xlds<1, 4, 8, 2>(c);
     case kSpXldsMB2: return launch_sp_xlds<2, 2, 8, 2>(c);
+    case kSpKring: return launch_sp_kring(c);
     default: return FP6_E_VALUE;
   }
 }
