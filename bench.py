@@ -61,7 +61,7 @@ DEFAULT_WORKLOAD = "llama70b_mlp_16x28672x8192"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
 ROT_BYTES = 1 << 30             # >= 1 GiB of rotated copies (> 256 MB Infinity Cache)
-SUBMIT_COVER_CYCLES = 40_000    # spin ahead of the timed region (~0.25 ms measured; its counter is slow)
+SUBMIT_COVER_CYCLES = 400_000   # spin ahead of the timed region: ~0.17 ms (its counter runs at ~2.4 GHz)
 COPY_BYTES = 1 << 30            # --calibrate-copy: bytes read (and written) per copy
 CSRC = os.path.join(ROOT, "weight_only_fp6_amd", "csrc")
 KERNEL_SRCS = ("fpx_device.h", "fpx_launch.h", "fpx_linear.hip", "fpx_kern_e3m2.hip",
@@ -559,8 +559,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     # A short spin kernel ahead of the first event keeps the GPU busy while
-    # the host submits the timed graph (tens of microseconds), so that the
-    # events bracket the K launches alone; the wall clock includes both.
+    # the host submits the timed graph (35-70 us measured for 20 launches),
+    # so that the events bracket the K launches alone; the wall clock
+    # includes both.
     torch.cuda._sleep(SUBMIT_COVER_CYCLES)
     ev0.record(stream)
     if args.no_graph:
