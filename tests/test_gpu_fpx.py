@@ -157,6 +157,30 @@ def test_linear_one_hot_reproduces_wdq_exactly(fmt):
         assert np.array_equal(Y.cpu().numpy().astype(np.float64), want), (fmt, variant, splits)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_kring_one_hot_every_tile_slot(fmt):
+    # One-hot activations through the k-ring kernel at K = 8192 (4 k-tiles
+    # per wave) with 3 row blocks per workgroup and a short last one: every
+    # output must equal a de-quantised weight exactly, for every tile slot.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K, M = 16 * (2 * cus + 9), 8192, 16
+    ws = dense_weight_set(N, K, 4343, fmt)
+    cols = []
+    for m in range(M):
+        w = (5 * m + 2) % 8
+        cols.append((4 * w + m % 4) * 256 + (29 * m + 3) % 256)
+    ks = np.array(cols)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
+    want = ws.wdq_ref[:, ks].T.astype(np.float64)
+    for m_used in (1, 16):
+        Y = fp6.linear_plan(Xd[:m_used].contiguous(), packed, s, N, K, variant=26, fmt=fmt)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), want[:m_used]), (fmt, m_used)
+
+
 def test_fpx_format0_matches_fp6_bitwise():
     shp = synth.SHAPES["llama7b_attn_1x4096x4096"]
     p = prepare_shape(shp)

@@ -250,3 +250,28 @@ def test_sparse_kring_rejects_what_it_does_not_cover():
     X1 = torch.zeros((1, 512), dtype=torch.float16, device=DEV)
     with pytest.raises(fp6.FP6Error):
         fp6.sparse_linear_plan(X1, big, sc, N, 512, variant=KRING)
+
+
+def test_sparse_kring_one_hot_every_tile_slot():
+    # One-hot activations through the sparse k-ring kernel at K = 8192 (two
+    # 512-k sparse tiles per wave) with 3 row blocks per workgroup and a
+    # short last one: columns in both tile slots of every wave, kept or
+    # pruned positions alike, so every output equals a de-quantised weight
+    # exactly (zero where the weight was pruned).
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K, M = 16 * (2 * cus + 9), 8192, 16
+    ws = sparse_weight_set(N, K, 4444)
+    cols = []
+    for m in range(M):
+        w = (3 * m + 1) % 8
+        cols.append((2 * w + m % 2) * 512 + (37 * m + 7) % 512)
+    ks = np.array(cols)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, sd = ws.to_device()
+    want = ws.wdq_ref[:, ks].T.astype(np.float64)
+    for m_used in (1, 16):
+        Y = fp6.sparse_linear_plan(Xd[:m_used].contiguous(), packed, sd, N, K, variant=KRING)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), want[:m_used]), m_used
