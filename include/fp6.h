@@ -141,8 +141,10 @@ int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
  * Workspace: when the plan splits K (memory-bound small-M shapes) the library
  * keeps an fp32 partial-sum buffer and a self-resetting counter array per
  * (device, stream), allocated with hipMalloc on first need and grown on
- * demand (growing synchronises that stream once).  Results are bitwise
- * deterministic: split partials are summed in a fixed order.
+ * demand.  A workspace that grows keeps its old buffers allocated until
+ * fp6_release (launches in flight and graphs captured before the growth
+ * still use them).  Results are bitwise deterministic: split partials are
+ * summed in a fixed order.
  * A workspace is kept for every stream that ran a split plan, until
  * fp6_release (a process that creates many streams holds one per stream).
  * Concurrent calls on different streams are safe.  Calls on one stream from
@@ -151,13 +153,14 @@ int fp6_prepack(const uint8_t* codes, const uint16_t* scales,
  * kernels.
  * HIP graph capture: nothing is allocated or cleared per call once the
  * stream's workspace exists, so make one call with the same shape and plan
- * on the capturing stream before capturing; the captured launch keeps the
- * workspace's address, so do not grow it (a larger split-K plan on that
- * stream) while the graph is in use.  Every graph captured on a stream
- * shares that stream's one workspace (partial sums and arrival counters):
- * replay such graphs one after another, never two at once on different
- * streams and never alongside eager split-K calls on the capturing stream,
- * or their partial sums mix.
+ * on the capturing stream before capturing.  The captured launch keeps the
+ * workspace's buffers; a later growth (a larger split-K plan on that
+ * stream) leaves them allocated, so the graph stays valid until
+ * fp6_release, which frees them (do not replay it after that).  Graphs
+ * captured on a stream with the same buffers share them (partial sums and
+ * arrival counters): replay such graphs one after another, never two at
+ * once on different streams and never alongside eager split-K calls on the
+ * capturing stream, or their partial sums mix.
  */
 int fp6_linear(const void* X, const void* packed_W, const void* scales, void* Y,
                int64_t M, int64_t N, int64_t K, void* stream);

@@ -122,3 +122,47 @@ def test_workspace_keeps_the_largest_sizes_for_capture():
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int16), want.view(torch.int16)), (N, K, v, sp, rep)
         del g
+
+
+def test_graph_survives_a_later_workspace_growth():
+    # A graph captured with a small split plan stays valid after a larger
+    # split plan grows the stream's workspace: the grown workspace's old
+    # buffers stay allocated until fp6_release, so every replay of the first
+    # graph still equals its eager result, with eager calls of the larger
+    # plan (on the new buffers) in between.
+    torch.cuda.synchronize()
+    fp6.release()
+    stream = torch.cuda.Stream()
+    small = (16, 4096, 8192, 15, 2)      # streaming, 2 K-splits: 512 KB of partial sums
+    large = (16, 8192, 28672, 18, 8)     # streaming, 8 K-splits: 4 MB, more counters
+    runs = []
+    for i, (M, N, K, v, sp) in enumerate((small, large)):
+        P, S = _prepare(N, K, 950 + i, False)
+        X = torch.from_numpy(synth.activations(M, K, 960 + i)).to(DEV)
+        runs.append((X, P, S, N, K, v, sp))
+    Xs, Ps, Ss, Ns, Ks, vs, sps = runs[0]
+    Xl, Pl, Sl, Nl, Kl, vl, spl = runs[1]
+    with torch.cuda.stream(stream):
+        want_s = fp6.linear_plan(Xs, Ps, Ss, Ns, Ks, variant=vs, splits=sps, stream=stream).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(want_s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fp6.linear_plan(Xs, Ps, Ss, Ns, Ks, variant=vs, splits=sps, out=out, stream=stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        want_l = fp6.linear_plan(Xl, Pl, Sl, Nl, Kl, variant=vl, splits=spl, stream=stream).clone()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want_s.view(torch.int16)), rep
+        with torch.cuda.stream(stream):
+            again = fp6.linear_plan(Xl, Pl, Sl, Nl, Kl, variant=vl, splits=spl, stream=stream)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), want_l.view(torch.int16)), rep
+    del g
+    torch.cuda.synchronize()
+    fp6.release()

@@ -15,6 +15,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "fp6.h"
 #include "fp6s.h"
@@ -52,6 +53,10 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
+// Buffers of workspaces that have grown, per device: launches still in
+// flight and graphs captured before the growth keep using them, so they are
+// freed only by fp6_release.
+std::vector<std::pair<int, void*>> g_retired;
 std::map<int, int> g_cus;
 
 int device_cus(int dev) {
@@ -67,10 +72,11 @@ int device_cus(int dev) {
 
 // Ensure the (device, stream) workspace holds at least the given sizes.  The
 // caller holds g_mu and keeps holding it until the launch that uses the
-// buffers is enqueued: another host thread growing the same workspace (or
-// fp6_release) would otherwise free them in between.  Workspaces are kept
-// per stream until fp6_release, so a process that cycles through many
-// streams with split plans holds one per stream.
+// buffers is enqueued: fp6_release would otherwise free them in between.
+// Workspaces are kept per stream until fp6_release, so a process that cycles
+// through many streams with split plans holds one per stream.  A workspace
+// that grows retires its old buffers instead of freeing them (earlier
+// launches and captured graphs still point at them); fp6_release frees them.
 int get_workspace_locked(int dev, void* stream, size_t part_bytes, size_t counter_count,
                          Workspace** out) {
   Workspace& ws = g_ws[{dev, stream}];
@@ -82,9 +88,8 @@ int get_workspace_locked(int dev, void* stream, size_t part_bytes, size_t counte
     const size_t pb = part_bytes > ws.part_bytes ? part_bytes : ws.part_bytes;
     const size_t cc = counter_count > ws.counter_count ? counter_count : ws.counter_count;
     if (ws.part || ws.counters) {
-      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return FP6_E_HIP;
-      if (ws.part) (void)hipFree(ws.part);
-      if (ws.counters) (void)hipFree(ws.counters);
+      if (ws.part) g_retired.emplace_back(dev, ws.part);
+      if (ws.counters) g_retired.emplace_back(dev, ws.counters);
       ws = Workspace{};
     }
     void* part = nullptr;
@@ -735,7 +740,7 @@ int fpx_dequant(int format, const void* packed_W, const void* scales, void* W16,
 
 int fp6_release(void) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (g_ws.empty()) return FP6_OK;
+  if (g_ws.empty() && g_retired.empty()) return FP6_OK;
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return FP6_E_HIP;
   int st = FP6_OK;
@@ -750,6 +755,16 @@ int fp6_release(void) {
     if (kv.second.counters && hipFree(kv.second.counters) != hipSuccess) st = FP6_E_HIP;
     kv.second = Workspace{};
   }
+  // Retired buffers of grown workspaces, each after its device is idle.
+  std::vector<std::pair<int, void*>> kept;
+  for (const auto& rb : g_retired) {
+    if (hipSetDevice(rb.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipFree(rb.second) != hipSuccess) {
+      st = FP6_E_HIP;
+      kept.push_back(rb);
+    }
+  }
+  g_retired.swap(kept);
   (void)hipSetDevice(cur);
   if (st == FP6_OK) g_ws.clear();
   return st;
