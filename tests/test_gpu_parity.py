@@ -614,7 +614,8 @@ DENSE_PLANS = [
     ((16, 18432, 8192), (KRING, 1)),     # 4-wave streaming workgroups would take 1.1 rounds
     ((4, 25600, 8192), (KRING, 1)),
     ((16, 2048, 8192), (KSPLIT16, 2)),   # half the CUs with a row block: K split across workgroups
-    ((16, 4096, 11008), (15, 4)),
+    ((16, 4096, 11008), (KRING, 2)),     # 8192 < K <= 12288, <= 3 row blocks per CU: k-ring, 2 K-splits
+    ((16, 8192, 10240), (15, 2)),        # 4 per CU: streaming
     ((16, 3072, 8192), (KSPLIT, 4)),     # 8 waves: 3 row blocks per workgroup
     ((1, 4096, 11008), (KSLICE, 1)),     # M <= 4, one row block per CU: k-slice up to K = 12288
     ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups

@@ -279,8 +279,16 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
                          kr_rows <= fpx::kKringMaxRows &&
                          (kr_rows <= 3 || ktiles <= 16 || (nbk > 4 * cu64 && nbk < 7 * cu64)) &&
                          (kr_rows > 1 || (M > 4 && (N >> 4) * 4 > 3 * static_cast<int64_t>(cus)));
-    if (kr_fits) {
-      p.variant = 26;
+    // 8192 < K <= 12288: the k-ring kernel with 2 K-splits (3 k-tiles per
+    // wave) at M = 5..16 while that leaves at most 3 row blocks per CU
+    // (interleaved A/B, us: 16x4096x9216 12.7 -> 11.0, 8x4096x11008 11.4 ->
+    // 10.8, 16x6144x11008 14.6 -> 13.9, 16x4096x12288 12.0 -> 11.6, Llama-7B
+    // MLP down 16x4096x11008 11.4 -> 11.3; 16x8192x10240, 4 per CU: 14.7
+    // against 15.8; M <= 4 keeps the k-slice kernel).
+    const bool kr2_fits = M > 4 && M <= 16 && splits == 0 && ktiles > fpx::kKringMaxTiles &&
+                          ktiles <= fpx::kKringMaxTiles * 3 / 2 && ceil_div(nbk * 2, cu64) <= 3;
+    if (kr_fits || kr2_fits) {
+      p.variant = 26;  // K-splits below: the fewest that leave <= 4 k-tiles per wave
     } else if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
       p.variant = 13;
     } else if (M <= 4 && ktiles <= fpx::kKsliceMaxTiles && one_rb_per_cu) {
