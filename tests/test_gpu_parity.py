@@ -323,6 +323,27 @@ def test_linear_kring_k_splits(NK, M, splits):
     assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, splits)
 
 
+@pytest.mark.parametrize("M, N, K", [(1, 6144, 11008), (4, 5120, 12288), (1, 2048, 11008), (8, 4096, 9216)])
+def test_linear_auto_kring_k_split_layers(M, N, K):
+    # Automatic plans that take the k-ring kernel with 2 K-splits for
+    # 8192 < K <= 12288: 3 row blocks per workgroup at M = 1 (X loaded
+    # directly) and M = 4, one per workgroup on half of the CUs, and 2 per
+    # workgroup at M = 8 (ragged wave ranges of 2-3 k-tiles).  Every output
+    # element, and the plan that produced it.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip("plan thresholds are stated for 256 CUs")
+    assert fp6.plan_query(M, N, K) == (KRING, 2)
+    ws = dense_weight_set(N, K, N + K + 29)
+    X = synth.activations(M, K, M + 31)
+    yref = y_ref(X, ws.wdq_ref)
+    Xd = torch.from_numpy(X).to(DEV)
+    packed, s = ws.to_device()
+    Y = fp6.linear(Xd, packed, s, N, K)
+    torch.cuda.synchronize()
+    _assert_tol(Y, yref, what=(M, N, K))
+
+
 def test_kring_one_hot_every_tile_slot():
     # One-hot activations through the k-ring kernel at K = 7168 (28 k-tiles:
     # waves own 3 or 4), 3 row blocks per workgroup with a short last
@@ -618,6 +639,10 @@ DENSE_PLANS = [
     ((16, 8192, 10240), (15, 2)),        # 4 per CU: streaming
     ((16, 3072, 8192), (KSPLIT, 4)),     # 8 waves: 3 row blocks per workgroup
     ((1, 4096, 11008), (KSLICE, 1)),     # M <= 4, one row block per CU: k-slice up to K = 12288
+    ((3, 3072, 12288), (KSLICE, 1)),     # ... while more than half of the CUs have a row block
+    ((1, 2048, 11008), (KRING, 2)),      # half of them: k-ring, 2 K-splits
+    ((1, 6144, 11008), (KRING, 2)),      # more row blocks than CUs, <= 3 per CU after the split
+    ((4, 5120, 12288), (KRING, 2)),
     ((16, 28672, 8192), (18, 1)),        # streaming, 8 waves, one round of workgroups
     ((16, 57344, 8192), (16, 1)),        # 2 row blocks per wave: one round instead of 1.75
     ((16, 8192, 28672), (15, 2)),        # split while a whole round of 4-wave workgroups fits

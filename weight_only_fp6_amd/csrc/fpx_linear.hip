@@ -280,13 +280,18 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
                          (kr_rows <= 3 || ktiles <= 16 || (nbk > 4 * cu64 && nbk < 7 * cu64)) &&
                          (kr_rows > 1 || (M > 4 && (N >> 4) * 4 > 3 * static_cast<int64_t>(cus)));
     // 8192 < K <= 12288: the k-ring kernel with 2 K-splits (3 k-tiles per
-    // wave) at M = 5..16 while that leaves at most 3 row blocks per CU
-    // (interleaved A/B, us: 16x4096x9216 12.7 -> 11.0, 8x4096x11008 11.4 ->
-    // 10.8, 16x6144x11008 14.6 -> 13.9, 16x4096x12288 12.0 -> 11.6, Llama-7B
-    // MLP down 16x4096x11008 11.4 -> 11.3; 16x8192x10240, 4 per CU: 14.7
-    // against 15.8; M <= 4 keeps the k-slice kernel).
-    const bool kr2_fits = M > 4 && M <= 16 && splits == 0 && ktiles > fpx::kKringMaxTiles &&
-                          ktiles <= fpx::kKringMaxTiles * 3 / 2 && ceil_div(nbk * 2, cu64) <= 3;
+    // wave) while that leaves at most 3 row blocks per CU (interleaved A/B,
+    // us: 16x4096x9216 12.7 -> 11.0, 8x4096x11008 11.4 -> 10.8, 16x6144x11008
+    // 14.6 -> 13.9, 16x4096x12288 12.0 -> 11.6, Llama-7B MLP down
+    // 16x4096x11008 11.4 -> 11.3, 1x6144x11008 14.4 -> 12.6, 1x5120x12288
+    // 12.9 -> 12.0; 16x8192x10240, 4 per CU: 14.7 against 15.8).  At M <= 4
+    // the k-slice kernel keeps layers with one row block for more than half
+    // of the CUs (1x4096x11008 9.8 against 10.2, 2x4096x9216 9.5 against
+    // 10.4, 3x3072x12288 10.0 against 10.2), not narrower ones (1x2048x11008
+    // 8.4 -> 7.8, 4x2048x11008 9.6 -> 8.3).
+    const bool kr2_fits = M <= 16 && splits == 0 && ktiles > fpx::kKringMaxTiles &&
+                          ktiles <= fpx::kKringMaxTiles * 3 / 2 && ceil_div(nbk * 2, cu64) <= 3 &&
+                          (M > 4 || nbk > cu64 || 2 * nbk <= cu64);
     if (kr_fits || kr2_fits) {
       p.variant = 26;  // K-splits below: the fewest that leave <= 4 k-tiles per wave
     } else if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
