@@ -323,13 +323,16 @@ def test_linear_kring_k_splits(NK, M, splits):
     assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), (M, N, K, splits)
 
 
-@pytest.mark.parametrize("M, N, K", [(1, 6144, 11008), (4, 5120, 12288), (1, 2048, 11008), (8, 4096, 9216)])
+@pytest.mark.parametrize("M, N, K", [(1, 6144, 11008), (4, 5120, 12288), (1, 2048, 11008), (8, 4096, 9216),
+                                     (5, 2048, 5120), (16, 2560, 7168)])
 def test_linear_auto_kring_k_split_layers(M, N, K):
-    # Automatic plans that take the k-ring kernel with 2 K-splits for
-    # 8192 < K <= 12288: 3 row blocks per workgroup at M = 1 (X loaded
+    # Automatic plans that take the k-ring kernel with 2 K-splits: for
+    # 8192 < K <= 12288, 3 row blocks per workgroup at M = 1 (X loaded
     # directly) and M = 4, one per workgroup on half of the CUs, and 2 per
-    # workgroup at M = 8 (ragged wave ranges of 2-3 k-tiles).  Every output
-    # element, and the plan that produced it.
+    # workgroup at M = 8 (ragged wave ranges of 2-3 k-tiles); for narrow
+    # layers with K <= 8192, 1-2 k-tiles per wave with one row block per
+    # workgroup, and 2 row blocks per workgroup.  Every output element, and
+    # the plan that produced it.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if cus != 256:
         pytest.skip("plan thresholds are stated for 256 CUs")
@@ -634,10 +637,12 @@ DENSE_PLANS = [
     ((16, 13824, 5120), (15, 1)),        # 4 row blocks per CU at K > 4096: streaming
     ((16, 18432, 8192), (KRING, 1)),     # 4-wave streaming workgroups would take 1.1 rounds
     ((4, 25600, 8192), (KRING, 1)),
-    ((16, 2048, 8192), (KSPLIT16, 2)),   # half the CUs with a row block: K split across workgroups
+    ((16, 2048, 8192), (KRING, 2)),      # half the CUs with a row block: k-ring, 2 K-splits
+    ((8, 2048, 6144), (KRING, 2)),
+    ((16, 3072, 6144), (KSPLIT, 3)),     # 3/4 of them, < 28 k-tiles: k-split kernel, K split
     ((16, 4096, 11008), (KRING, 2)),     # 8192 < K <= 12288, <= 3 row blocks per CU: k-ring, 2 K-splits
     ((16, 8192, 10240), (15, 2)),        # 4 per CU: streaming
-    ((16, 3072, 8192), (KSPLIT, 4)),     # 8 waves: 3 row blocks per workgroup
+    ((16, 3072, 8192), (KRING, 2)),      # 2 row blocks per workgroup at 32 k-tiles
     ((1, 4096, 11008), (KSLICE, 1)),     # M <= 4, one row block per CU: k-slice up to K = 12288
     ((3, 3072, 12288), (KSLICE, 1)),     # ... while more than half of the CUs have a row block
     ((1, 2048, 11008), (KRING, 2)),      # half of them: k-ring, 2 K-splits

@@ -292,7 +292,22 @@ Plan choose_plan(int64_t M, int64_t N, int64_t K, int cus, int variant, int spli
     const bool kr2_fits = M <= 16 && splits == 0 && ktiles > fpx::kKringMaxTiles &&
                           ktiles <= fpx::kKringMaxTiles * 3 / 2 && ceil_div(nbk * 2, cu64) <= 3 &&
                           (M > 4 || nbk > cu64 || 2 * nbk <= cu64);
-    if (kr_fits || kr2_fits) {
+    // 4096 < K <= 8192 at M = 5..16 on layers that give at most 3/4 of the
+    // CUs a row block: the k-ring kernel with 2 K-splits (2 k-tiles per
+    // wave) beats the k-split kernel with K-splits while that leaves one row
+    // block per workgroup (16x2048x8192 8.0 -> 7.2 us, 16x2048x6144 7.8 ->
+    // 7.1, 16x2048x5120 7.6 -> 7.0, 8x2048x8192 7.4 -> 6.9, 12x1536x8192 7.4
+    // -> 6.9, 16x1024x8192 6.9 both), or two at 28 or more k-tiles
+    // (16x3072x8192 9.1 -> 8.6, 8x3072x8192 9.0 -> 8.4, 16x2560x7168 8.6 ->
+    // 8.5; 16x3072x6144 8.2 against 8.5).
+    const bool kr_narrow = M > 4 && M <= 16 && splits == 0 && ktiles > 16 &&
+                           ktiles <= fpx::kKringMaxTiles && one_rb_per_cu && !kr_fits &&
+                           (2 * nbk <= cu64 || ktiles >= 28);
+    if (kr_narrow) {
+      p.variant = 26;
+      p.splits = 2;
+      return p;
+    } else if (kr_fits || kr2_fits) {
       p.variant = 26;  // K-splits below: the fewest that leave <= 4 k-tiles per wave
     } else if (M <= 16 && ktiles <= 16 && one_rb_per_cu) {
       p.variant = 13;
