@@ -140,6 +140,25 @@ def test_linear_k_coverage(fmt, K):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_linear_auto_kring_narrow_layers(fmt):
+    # Automatic plans on narrow layers (at most 3/4 of the CUs with a row
+    # block) with 4096 < K <= 8192 at M = 5..16: the k-ring kernel with 2
+    # K-splits, one row block per workgroup (2048 rows) and two (3072 rows,
+    # 32 k-tiles).  Every output element, and the plan.
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("plan thresholds are stated for 256 CUs")
+    for M, N, K in ((16, 2048, 6144), (8, 3072, 8192)):
+        assert fp6.plan_query(M, N, K) == (26, 2)
+        ws = dense_weight_set(N, K, N + K + 3, fmt)
+        packed, s = ws.to_device()
+        X = synth.activations(M, K, M + 41)
+        yref = y_ref(X, ws.wdq_ref)
+        Y = fp6.linear(torch.from_numpy(X).to(DEV), packed, s, N, K, fmt=fmt)
+        torch.cuda.synchronize()
+        _assert_tol(Y, yref, what=(fmt, M, N, K))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_linear_one_hot_reproduces_wdq_exactly(fmt):
     N, K = 64, 1024
     p = Prepared(16, N, K, seed_w=97, seed_x=3, fmt=fmt)
